@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for the mixed-head SAF attention layer.
+
+This module is shared by the GPU tests, the benchmark and the oracle checks.  It only draws random
+tensors of the shapes and distributions of the workloads; it holds none of the method's arithmetic.
+
+The workloads are the layer shapes the pages report timings for, with synthetic tensors in place of
+trained activations (no dataset or checkpoint is used):
+  - a 124M-parameter decoder layer: 12 heads of width 64, at 4K and 8K context
+    ([Notes §三]; [Paper page] Table 2),
+  - one GPU's share of the 1B run at 8K context ([Notes §四.6]; [Paper page] Table 23),
+  - causal prefill at batch 64 and at 16K context ([Paper page] Table 29),
+plus a tiny fp32 case for exact parity.  Q, K, V and dO are N(0, 1); the replaced heads' a and r are
+random preferences in the same position/distance parametrisation as the pages' "structured random"
+control ([Notes §二.2]).  Citation keys as in the oracle package.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+SEED0 = 1337  # the pages' first seed ([Notes §三])
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    T: int
+    d: int
+    dtype: str            # "f32" or "bf16"
+    n_replaced: int
+    ar_std: float         # standard deviation of a and r
+    backward: bool        # fwd+bwd (True) or forward only
+    index: int            # seed offset
+    calib_N: int = 0      # > 0: also a calibration over calib_N sequences
+    note: str = ""
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def replaced(self, placement: str = "interleaved"):
+        return replaced_mask(self.H, self.n_replaced, placement)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_fwd_f32", 1, 4, 256, 64, "f32", 1, 1.0, False, 0,
+                 note="tiny forward, head 3 replaced, fp32"),
+        Workload("l124m_t4096", 8, 12, 4096, 64, "bf16", 3, 0.5, True, 1,
+                 note="124M-shaped layer at 4K, 25% of heads replaced, fwd+bwd"),
+        Workload("l124m_t8192", 4, 12, 8192, 64, "bf16", 6, 0.5, True, 2,
+                 note="124M-shaped layer at 8K, 50% of heads replaced, fwd+bwd"),
+        Workload("l1b_t8192", 2, 16, 8192, 128, "bf16", 4, 0.5, True, 3, calib_N=32,
+                 note="1B-shaped one-GPU share at 8K, 25% replaced, fwd+bwd; calibration N=32"),
+        Workload("prefill_b64_t4096", 64, 12, 4096, 64, "bf16", 3, 0.5, False, 4,
+                 note="causal prefill, batch 64 at 4K, 25% replaced, forward only"),
+        Workload("prefill_b2_t16384", 2, 12, 16384, 64, "bf16", 3, 0.5, False, 5,
+                 note="causal prefill, batch 2 at 16K, 25% replaced, forward only"),
+    ]
+}
+
+
+def replaced_mask(H: int, R: int, placement: str = "interleaved"):
+    """Which heads are replaced: a list of H ints (1 = fixed pattern).
+
+    interleaved: head h is replaced iff h mod (H/R) == H/R - 1 (R divides H), e.g. {3} of 4,
+    {3, 7, 11} of 12; contiguous: the last R heads.  The pages pick heads by variance across the
+    whole model ([Notes §二.1]); a synthetic layer has no such ranking, so the placement is fixed."""
+    if R == 0:
+        return [0] * H
+    if placement == "interleaved":
+        if H % R:
+            raise ValueError("interleaved placement needs R to divide H")
+        g = H // R
+        return [1 if h % g == g - 1 else 0 for h in range(H)]
+    if placement == "contiguous":
+        return [1 if h >= H - R else 0 for h in range(H)]
+    if placement == "all":
+        return [1] * H
+    raise ValueError(placement)
+
+
+@dataclass
+class LayerInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    dout: torch.Tensor | None
+    a: torch.Tensor
+    r: torch.Tensor
+    replaced: list = field(default_factory=list)
+
+
+def layer_inputs(B, H, T, d, dtype, replaced, ar_std=0.5, seed=SEED0, backward=True,
+                 pat_len=None, device="cpu"):
+    """Draw Q, K, V, dO ~ N(0,1) ([B,H,T,d], then cast to dtype) and a, r ~ N(0, ar_std^2)
+    ([H, pat_len] fp32), in that order, from a CPU generator seeded with `seed`."""
+    g = torch.Generator().manual_seed(seed)
+    P = T if pat_len is None else pat_len
+    shape = (B, H, T, d)
+    q = torch.randn(shape, generator=g).to(dtype)
+    k = torch.randn(shape, generator=g).to(dtype)
+    v = torch.randn(shape, generator=g).to(dtype)
+    dout = torch.randn(shape, generator=g).to(dtype) if backward else None
+    a = torch.randn((H, P), generator=g) * ar_std
+    r = torch.randn((H, P), generator=g) * ar_std
+    out = LayerInputs(q, k, v, dout, a.float(), r.float(), list(replaced))
+    if device != "cpu":
+        for name in ("q", "k", "v", "dout", "a", "r"):
+            t = getattr(out, name)
+            if t is not None:
+                setattr(out, name, t.to(device))
+    return out
+
+
+def workload_inputs(w: Workload, placement="interleaved", device="cpu"):
+    return layer_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.replaced(placement), w.ar_std,
+                        SEED0 + w.index, w.backward, device=device)
+
+
+def calib_inputs(N, H, T, d, dtype, seed=SEED0 + 100, device="cpu"):
+    """Queries and keys of N synthetic calibration sequences, [N, H, T, d], N(0,1)."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((N, H, T, d), generator=g).to(dtype)
+    k = torch.randn((N, H, T, d), generator=g).to(dtype)
+    return q.to(device), k.to(device)
