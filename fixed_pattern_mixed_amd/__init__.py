@@ -1,0 +1,165 @@
+"""Python binding of libsaf.so: the fused mixed-head SAF attention layer on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of libsaf.so.
+PyTorch supplies device memory (outputs and workspaces are torch tensors on the inputs' device)
+and the current HIP stream.  There is no CPU or PyTorch fallback: if the library is missing this
+module raises at import time.
+
+The entry points mirror include/saf.h (same names, same argument order for the raw calls):
+  saf_attn_fwd / saf_attn_bwd / saf_calibrate   raw C-ABI calls (ctypes, integer pointers)
+  fwd(q, k, v, replaced, a, r)  -> (o, lse)
+  bwd(q, k, v, o, dout, lse, replaced, a, r) -> (dq, dk, dv)
+  calibrate(q, k) -> (ahat, svar)
+[Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记" (§二.1 Eq.(1), §二.3 Eq.(3),
+§二.4 for what the three calls compute).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsaf.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libsaf.so is not built (expected at %s); run `python -m fixed_pattern_mixed_amd.build` "
+        "or __graft_entry__.build() first" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SAF_OK, SAF_ERR_INVALID_ARG, SAF_ERR_UNSUPPORTED, SAF_ERR_HIP = 0, 1, 2, 3
+SAF_F32, SAF_BF16 = 0, 1
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_lib.saf_attn_fwd_workspace_size.argtypes = [_i, _i, _i, _i]
+_lib.saf_attn_fwd_workspace_size.restype = _sz
+_lib.saf_attn_bwd_workspace_size.argtypes = [_i, _i, _i, _i]
+_lib.saf_attn_bwd_workspace_size.restype = _sz
+_lib.saf_calibrate_workspace_size.argtypes = [_i, _i, _i, _i]
+_lib.saf_calibrate_workspace_size.restype = _sz
+_lib.saf_last_error.argtypes = []
+_lib.saf_last_error.restype = ctypes.c_char_p
+_lib.saf_attn_fwd.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, ctypes.c_float,
+                              _vp, _vp, _vp, _sz, _vp]
+_lib.saf_attn_fwd.restype = _i
+_lib.saf_attn_bwd.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                              ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.saf_attn_bwd.restype = _i
+_lib.saf_calibrate.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _sz,
+                               _vp]
+_lib.saf_calibrate.restype = _i
+
+# raw entry points, same names as the C ABI
+saf_attn_fwd = _lib.saf_attn_fwd
+saf_attn_bwd = _lib.saf_attn_bwd
+saf_calibrate = _lib.saf_calibrate
+saf_attn_fwd_workspace_size = _lib.saf_attn_fwd_workspace_size
+saf_attn_bwd_workspace_size = _lib.saf_attn_bwd_workspace_size
+saf_calibrate_workspace_size = _lib.saf_calibrate_workspace_size
+
+
+def saf_last_error() -> str:
+    return _lib.saf_last_error().decode()
+
+
+class SafError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s failed (status %d): %s" % (where, status, saf_last_error()))
+
+
+def _check(status, where):
+    if status != SAF_OK:
+        raise SafError(status, where)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SAF_BF16
+    if t.dtype == torch.float32:
+        return SAF_F32
+    raise TypeError("tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _mask(replaced, H):
+    if len(replaced) != H:
+        raise ValueError("replaced must have one entry per head (%d)" % H)
+    return (ctypes.c_uint8 * H)(*[1 if int(x) else 0 for x in replaced])
+
+
+def _stream(dev):
+    import torch
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ws(nbytes, device):
+    import torch
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, replaced, a=None, r=None, scale=None, out=None, lse=None):
+    """Forward of the mixed layer.  q, k, v: [B, H, T, d] (bf16 or fp32, same dtype), replaced:
+    H flags, a, r: [H, pat_len] fp32 on the GPU.  Returns (o, lse)."""
+    import torch
+    B, H, T, d = v.shape
+    dt = _dtype_code(v)
+    o = torch.empty_like(v) if out is None else out
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device) if lse is None else lse
+    ws_n = saf_attn_fwd_workspace_size(B, H, T, d)
+    ws = _ws(ws_n, v.device)
+    pat_len = a.shape[-1] if a is not None else 0
+    st = saf_attn_fwd(dt, B, H, T, d, _ptr(q), _ptr(k), _ptr(v), _mask(replaced, H), _ptr(a),
+                      _ptr(r), pat_len, 0.0 if scale is None else float(scale), _ptr(o), _ptr(lse),
+                      _ptr(ws), ws_n, _stream(v.device))
+    _check(st, "saf_attn_fwd")
+    return o, lse
+
+
+def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None):
+    """Backward of the mixed layer.  Returns (dq, dk, dv); replaced heads get dq = dk = 0."""
+    import torch
+    B, H, T, d = v.shape
+    dt = _dtype_code(v)
+    dq, dk, dv = torch.empty_like(v), torch.empty_like(v), torch.empty_like(v)
+    ws_n = saf_attn_bwd_workspace_size(B, H, T, d)
+    ws = _ws(ws_n, v.device)
+    pat_len = a.shape[-1] if a is not None else 0
+    st = saf_attn_bwd(dt, B, H, T, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                      _mask(replaced, H), _ptr(a), _ptr(r), pat_len,
+                      0.0 if scale is None else float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                      _ptr(ws), ws_n, _stream(v.device))
+    _check(st, "saf_attn_bwd")
+    return dq, dk, dv
+
+
+def calibrate(q, k, scale=None):
+    """Calibration statistics over N sequences: q, k [N, H, T, d].  Returns (ahat [H, T, T] fp32,
+    svar [H] fp64)."""
+    import torch
+    N, H, T, d = q.shape
+    dt = _dtype_code(q)
+    ahat = torch.empty((H, T, T), dtype=torch.float32, device=q.device)
+    svar = torch.empty((H,), dtype=torch.float64, device=q.device)
+    ws_n = saf_calibrate_workspace_size(N, H, T, d)
+    ws = _ws(ws_n, q.device)
+    st = saf_calibrate(dt, N, H, T, d, _ptr(q), _ptr(k), 0.0 if scale is None else float(scale),
+                       _ptr(ahat), _ptr(svar), _ptr(ws), ws_n, _stream(q.device))
+    _check(st, "saf_calibrate")
+    return ahat, svar

@@ -1,0 +1,251 @@
+// saf_api.cpp -- the C ABI of libsaf.so (declared in include/saf.h): argument checks, workspace
+// layout and kernel launch order.  Every check runs before the first HIP call, so a rejected call
+// enqueues nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "../../include/saf.h"
+#include "saf_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+saf_status fail(saf_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+saf_status hip_fail(hipError_t e, const char* where) {
+  return fail(SAF_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxT = 65536;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks common to the layer calls.  Returns SAF_OK or the status to report.
+saf_status check_shape(int B, int H, int T, int d) {
+  if (B < 0 || H < 1 || T < 0) return fail(SAF_ERR_INVALID_ARG, "need B >= 0, H >= 1, T >= 0 (got B=%d H=%d T=%d)", B, H, T);
+  if (H > saf::kMaxHeads) return fail(SAF_ERR_UNSUPPORTED, "H=%d exceeds the supported %d heads", H, saf::kMaxHeads);
+  if (T > kMaxT) return fail(SAF_ERR_UNSUPPORTED, "T=%d exceeds the supported %d", T, kMaxT);
+  if (d != 64 && d != 128) return fail(SAF_ERR_UNSUPPORTED, "head width d=%d is not supported (64 or 128)", d);
+  return SAF_OK;
+}
+
+bool sizes_ok(int B, int H, int T, int d) {
+  return B >= 0 && H >= 1 && H <= saf::kMaxHeads && T >= 0 && T <= kMaxT && (d == 64 || d == 128);
+}
+
+struct Need {
+  const void* p;
+  const char* name;
+};
+
+saf_status check_ptrs(std::initializer_list<Need> ptrs) {
+  for (const Need& n : ptrs) {
+    if (!n.p) return fail(SAF_ERR_INVALID_ARG, "%s is NULL", n.name);
+    if (!aligned16(n.p)) return fail(SAF_ERR_INVALID_ARG, "%s is not 16-byte aligned", n.name);
+  }
+  return SAF_OK;
+}
+
+saf_status check_scale(float scale, int d, float* out) {
+  if (isnan(scale) || isinf(scale)) return fail(SAF_ERR_INVALID_ARG, "scale must be finite");
+  *out = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  return SAF_OK;
+}
+
+saf_status fill_mask(const uint8_t* replaced, int H, uint64_t* rep, bool* any_rep) {
+  memset(rep, 0, sizeof(uint64_t) * (saf::kMaxHeads / 64));
+  if (!replaced) return fail(SAF_ERR_INVALID_ARG, "replaced (host mask) is NULL");
+  *any_rep = false;
+  for (int h = 0; h < H; ++h)
+    if (replaced[h]) {
+      rep[h >> 6] |= 1ull << (h & 63);
+      *any_rep = true;
+    }
+  return SAF_OK;
+}
+
+size_t fwd_ws(int B, int H, int T, int d) {
+  (void)B; (void)H; (void)T; (void)d;
+  return 0;  // the forward needs no scratch
+}
+size_t bwd_ws(int B, int H, int T, int d) {
+  (void)d;
+  return align_up(sizeof(float) * (size_t)B * H * T);  // delta
+}
+size_t calib_tiles(int T, int* nqt, int* nkt) {
+  *nqt = (T + saf::kCalibQTile - 1) / saf::kCalibQTile;
+  *nkt = (T + saf::kCalibKTile - 1) / saf::kCalibKTile;
+  return (size_t)(*nqt) * (*nkt);
+}
+size_t calib_ws(int N, int H, int T, int d) {
+  (void)d;
+  int nqt, nkt;
+  const size_t tiles = calib_tiles(T, &nqt, &nkt);
+  return align_up(sizeof(float) * (size_t)N * H * T) + align_up(sizeof(double) * (size_t)H * tiles);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t saf_attn_fwd_workspace_size(int B, int H, int T, int d) {
+  if (!sizes_ok(B, H, T, d)) return SIZE_MAX;
+  return fwd_ws(B, H, T, d);
+}
+
+size_t saf_attn_bwd_workspace_size(int B, int H, int T, int d) {
+  if (!sizes_ok(B, H, T, d)) return SIZE_MAX;
+  if (B == 0 || T == 0) return 0;
+  return bwd_ws(B, H, T, d);
+}
+
+size_t saf_calibrate_workspace_size(int N, int H, int T, int d) {
+  if (N < 2 || !sizes_ok(1, H, T, d)) return SIZE_MAX;
+  if (T == 0) return 0;
+  return calib_ws(N, H, T, d);
+}
+
+const char* saf_last_error(void) { return g_err; }
+
+saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
+                        const void* v, const uint8_t* replaced, const float* a, const float* r,
+                        int pat_len, float scale, void* o, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  g_err[0] = 0;
+  if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  saf_status st = check_shape(B, H, T, d);
+  if (st != SAF_OK) return st;
+  if (B == 0 || T == 0) return SAF_OK;
+  saf::LayerArgs la;
+  memset(&la, 0, sizeof(la));
+  bool any_rep = false;
+  if ((st = fill_mask(replaced, H, la.rep, &any_rep)) != SAF_OK) return st;
+  bool any_ord = false;
+  for (int h = 0; h < H; ++h) any_ord |= !replaced[h];
+  if (any_ord && (st = check_ptrs({{q, "q"}, {k, "k"}})) != SAF_OK) return st;
+  if ((st = check_ptrs({{v, "v"}, {o, "o"}})) != SAF_OK) return st;
+  if (!lse) return fail(SAF_ERR_INVALID_ARG, "lse is NULL");
+  if (any_rep) {
+    if (!a || !r) return fail(SAF_ERR_INVALID_ARG, "a and r are required when a head is replaced");
+    if (pat_len < T) return fail(SAF_ERR_INVALID_ARG, "pat_len=%d is shorter than T=%d", pat_len, T);
+  }
+  if (ws_bytes < fwd_ws(B, H, T, d)) return fail(SAF_ERR_INVALID_ARG, "workspace too small");
+  float s;
+  if ((st = check_scale(scale, d, &s)) != SAF_OK) return st;
+  (void)ws;
+
+  la.B = B; la.H = H; la.T = T; la.d = d;
+  la.pat_len = pat_len;
+  la.scale = s;
+  la.scale_log2 = s * 1.4426950408889634f;
+  la.q = q; la.k = k; la.v = v;
+  la.a = a; la.r = r;
+  la.lse = lse;
+  la.out = o;
+  hipError_t e = saf::launch_mixed_fwd(la, dt == SAF_BF16, stream);
+  if (e != hipSuccess) return hip_fail(e, "mixed forward launch");
+  return SAF_OK;
+}
+
+saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
+                        const void* v, const void* o, const void* dout, const float* lse,
+                        const uint8_t* replaced, const float* a, const float* r, int pat_len,
+                        float scale, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  g_err[0] = 0;
+  if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  saf_status st = check_shape(B, H, T, d);
+  if (st != SAF_OK) return st;
+  if (B == 0 || T == 0) return SAF_OK;
+  saf::LayerArgs la;
+  memset(&la, 0, sizeof(la));
+  bool any_rep = false;
+  if ((st = fill_mask(replaced, H, la.rep, &any_rep)) != SAF_OK) return st;
+  bool any_ord = false;
+  for (int h = 0; h < H; ++h) any_ord |= !replaced[h];
+  if (any_ord && (st = check_ptrs({{q, "q"}, {k, "k"}, {o, "o"}})) != SAF_OK) return st;
+  if ((st = check_ptrs({{v, "v"}, {dout, "dout"}, {dq, "dq"}, {dk, "dk"}, {dv, "dv"}})) != SAF_OK)
+    return st;
+  if (!lse) return fail(SAF_ERR_INVALID_ARG, "lse is NULL");
+  if (any_rep) {
+    if (!a || !r) return fail(SAF_ERR_INVALID_ARG, "a and r are required when a head is replaced");
+    if (pat_len < T) return fail(SAF_ERR_INVALID_ARG, "pat_len=%d is shorter than T=%d", pat_len, T);
+  }
+  const size_t need = bwd_ws(B, H, T, d);
+  if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
+  if (ws_bytes < need) return fail(SAF_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  float s;
+  if ((st = check_scale(scale, d, &s)) != SAF_OK) return st;
+
+  la.B = B; la.H = H; la.T = T; la.d = d;
+  la.pat_len = pat_len;
+  la.scale = s;
+  la.scale_log2 = s * 1.4426950408889634f;
+  la.q = q; la.k = k; la.v = v; la.o = o; la.dout = dout;
+  la.a = a; la.r = r;
+  la.lse = const_cast<float*>(lse);
+  la.delta = reinterpret_cast<float*>(ws);
+  la.dq = dq; la.dk = dk; la.dv = dv;
+  const bool bf = dt == SAF_BF16;
+  hipError_t e = saf::launch_bwd_pre(la, bf, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  e = saf::launch_bwd_kv(la, bf, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward key-block launch");
+  if (any_ord) {
+    e = saf::launch_bwd_q(la, bf, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward query-block launch");
+  }
+  return SAF_OK;
+}
+
+saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q, const void* k,
+                         float scale, float* ahat, double* svar, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  g_err[0] = 0;
+  if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (N < 2) return fail(SAF_ERR_INVALID_ARG, "N=%d: the variance score needs N >= 2", N);
+  saf_status st = check_shape(1, H, T, d);
+  if (st != SAF_OK) return st;
+  if (T == 0) return SAF_OK;
+  if ((st = check_ptrs({{q, "q"}, {k, "k"}, {ahat, "ahat"}})) != SAF_OK) return st;
+  if (!svar) return fail(SAF_ERR_INVALID_ARG, "svar is NULL");
+  if ((uintptr_t)svar & 7u) return fail(SAF_ERR_INVALID_ARG, "svar is not 8-byte aligned");
+  const size_t need = calib_ws(N, H, T, d);
+  if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
+  if (ws_bytes < need) return fail(SAF_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  float s;
+  if ((st = check_scale(scale, d, &s)) != SAF_OK) return st;
+
+  saf::CalibArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.N = N; ca.H = H; ca.T = T; ca.d = d;
+  ca.scale_log2 = s * 1.4426950408889634f;
+  ca.q = q; ca.k = k;
+  ca.lse2 = reinterpret_cast<float*>(ws);
+  ca.m2 = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + align_up(sizeof(float) * (size_t)N * H * T));
+  ca.ahat = ahat;
+  ca.svar = svar;
+  calib_tiles(T, &ca.n_qt, &ca.n_kt);
+  hipError_t e = saf::launch_calibrate(ca, dt == SAF_BF16, stream);
+  if (e != hipSuccess) return hip_fail(e, "calibration launch");
+  return SAF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+// saf_calib.hip -- streaming calibration statistics: the mean attention map Ahat and the variance
+// score of Eq. (1), over N calibration sequences.
+//
+// [Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记", §二.1, Eq. (1):
+//   Ahat = (1/N) sum_n A^(n),   s_var = sum_n ||A^(n) - Ahat||_F^2 / ((N-1) T^2),
+// with A^(n) = softmax_causal(s Q^(n) K^(n)T) the head's map on sequence n.  The N maps are never
+// stored: at the 1B shape they would be N*H*T^2 values (137 GB in fp32).
+//
+//   calib_lse    : per (sequence, head, 128-query block) the base-2 log-sum-exp of the scaled
+//                  causal scores of every row (an online max / sum over key tiles).
+//   calib_stats  : per (head, 128-query tile I, 64-key tile J): for n = 1..N re-form the score tile
+//                  on the matrix cores, A = exp2(s' S - lse2), and update a per-element running mean
+//                  and sum of squared deviations (Welford) held in registers.  The tile then writes
+//                  its block of Ahat and one fp64 partial sum of squared deviations.  Tiles above
+//                  the diagonal write zeros.
+//   calib_reduce : per head, the fixed-order fp64 sum of the partials -> s_var (deterministic).
+#include "saf_device.h"
+#include "saf_internal.h"
+
+namespace saf {
+namespace {
+
+constexpr int kNT = 256;
+constexpr int kBQ = kCalibQTile;  // 128
+constexpr int kBK = kCalibKTile;  // 64
+
+template <typename TI, int D>
+__global__ __launch_bounds__(kNT) void calib_lse_kernel(CalibArgs p) {
+  constexpr int NS = kBK / 32;
+  constexpr int LDP = D + 16 / (int)sizeof(TI);
+  __shared__ __attribute__((aligned(16))) TI Ks[kBK * LDP];
+
+  const int T = p.T;
+  const int NH = p.N * p.H;
+  const int NHp = (NH + 7) & ~7;
+  const int nqb = (T + kBQ - 1) / kBQ;
+  const int x = blockIdx.x;
+  const int nh = x % NHp;
+  if (nh >= NH) return;
+  const int qb = nqb - 1 - x / NHp;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int q0 = qb * kBQ, qw = q0 + 32 * w, qi = qw + l32;
+  const size_t hoff = (size_t)nh * T * D;  // [N][H] flattened
+  const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
+  const TI* K = reinterpret_cast<const TI*>(p.k) + hoff;
+
+  Frag<TI> qf[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+  float m = -INFINITY, l = 0.f;
+  const int nkt = (min(T, q0 + kBQ) + kBK - 1) / kBK;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * kBK;
+    __syncthreads();
+    stage_rows<TI, D, kBK, LDP, kNT>(Ks, K, k0, T, tid);
+    __syncthreads();
+    if (k0 > qw + 31) continue;
+    float sv[NS][16];
+    bool act[NS];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ks = k0 + 32 * s;
+      act[s] = ks <= qw + 31 && ks < T;
+      if (!act[s]) continue;
+      f32x16 st;
+      zero(st);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = ks + crow(r, hi);
+        const float v = (key <= qi && key < T) ? st[r] * p.scale_log2 : -INFINITY;
+        sv[s][r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m, tmax);
+    const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mnew);
+    float lsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (!act[s]) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lsum += (sv[s][r] == -INFINITY) ? 0.f : exp2f(sv[s][r] - mnew);
+    }
+    l = l * alpha + lsum;
+    m = mnew;
+  }
+  const float lt = l + __shfl_xor(l, 32);
+  if (qi < T && hi == 0) p.lse2[(size_t)nh * T + qi] = m + log2f(lt);
+}
+
+template <typename TI, int D>
+__global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
+  constexpr int NS = kBK / 32;
+  constexpr int LDP = D + 16 / (int)sizeof(TI);
+  __shared__ __attribute__((aligned(16))) TI Ks[kBK * LDP];
+  __shared__ double wsum[kNT / 64];
+
+  const int T = p.T, H = p.H, N = p.N;
+  const int tiles = p.n_qt * p.n_kt;
+  const int x = blockIdx.x;
+  const int h = x / tiles;
+  const int tile = x % tiles;
+  const int I = tile / p.n_kt, J = tile % p.n_kt;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int q0 = I * kBQ, k0 = J * kBK;
+  const int qw = q0 + 32 * w, qi = qw + l32;
+  float* A = p.ahat + (size_t)h * T * T;
+  const bool vec4 = (T & 3) == 0;
+
+  if (k0 > q0 + kBQ - 1) {  // entirely above the diagonal: zeros
+    for (int e = tid; e < kBQ * kBK; e += kNT) {
+      const int qq = q0 + e / kBK, kk = k0 + e % kBK;
+      if (qq < T && kk < T) A[(size_t)qq * T + kk] = 0.f;
+    }
+    if (tid == 0) p.m2[(size_t)h * tiles + tile] = 0.0;
+    return;
+  }
+
+  float mean[NS][16], m2[NS][16];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      mean[s][r] = 0.f;
+      m2[s][r] = 0.f;
+    }
+
+  for (int n = 0; n < N; ++n) {
+    const size_t hoff = ((size_t)n * H + h) * (size_t)T * D;
+    const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
+    const TI* K = reinterpret_cast<const TI*>(p.k) + hoff;
+    const float lse2 = qi < T ? p.lse2[((size_t)n * H + h) * T + qi] : 0.f;
+    const float inv_n = 1.f / (float)(n + 1);
+    __syncthreads();
+    stage_rows<TI, D, kBK, LDP, kNT>(Ks, K, k0, T, tid);
+    __syncthreads();
+    if (k0 > qw + 31) continue;  // this wave's queries see none of the tile's keys
+    Frag<TI> qf[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ks = k0 + 32 * s;
+      if (ks > qw + 31 || ks >= T) continue;
+      f32x16 st;
+      zero(st);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = ks + crow(r, hi);
+        const float a = (key <= qi && key < T && qi < T) ? exp2f(st[r] * p.scale_log2 - lse2) : 0.f;
+        const float dlt = a - mean[s][r];
+        mean[s][r] += dlt * inv_n;
+        m2[s][r] += dlt * (a - mean[s][r]);
+      }
+    }
+  }
+
+  // write the tile of Ahat (lane = query, registers = 4-key runs) and sum the deviations
+  double part = 0.0;
+  if (qi < T) {
+    float* Arow = A + (size_t)qi * T;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kk = k0 + 32 * s + 8 * g + 4 * hi;
+        const float* mv = &mean[s][4 * g];
+        if (vec4 && kk + 3 < T) {
+          *reinterpret_cast<float4*>(Arow + kk) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (kk + e < T) Arow[kk + e] = mv[e];
+        }
+        for (int e = 0; e < 4; ++e) part += (double)m2[s][4 * g + e];
+      }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+  if (lane == 0) wsum[w] = part;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int i = 0; i < kNT / 64; ++i) t += wsum[i];
+    p.m2[(size_t)h * tiles + tile] = t;
+  }
+}
+
+__global__ __launch_bounds__(kNT) void calib_reduce_kernel(CalibArgs p) {
+  __shared__ double red[kNT];
+  const int h = blockIdx.x;
+  const int tiles = p.n_qt * p.n_kt;
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < tiles; i += kNT) acc += p.m2[(size_t)h * tiles + i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = kNT / 2; st >= 1; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0)
+    p.svar[h] = red[0] / ((double)(p.N - 1) * (double)p.T * (double)p.T);
+}
+
+template <typename TI, int D>
+hipError_t launch_calib_t(const CalibArgs& a, hipStream_t s) {
+  const int NHp = (a.N * a.H + 7) & ~7;
+  const long long b1 = (long long)NHp * ((a.T + kBQ - 1) / kBQ);
+  const long long b2 = (long long)a.H * a.n_qt * a.n_kt;
+  if (b1 > 0x7fffffffLL || b2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((calib_lse_kernel<TI, D>), dim3((unsigned)b1), dim3(kNT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((calib_stats_kernel<TI, D>), dim3((unsigned)b2), dim3(kNT), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(calib_reduce_kernel, dim3(a.H), dim3(kNT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_calibrate(const CalibArgs& a, bool bf16_in, hipStream_t s) {
+  if (bf16_in) return a.d == 64 ? launch_calib_t<bf16, 64>(a, s) : launch_calib_t<bf16, 128>(a, s);
+  return a.d == 64 ? launch_calib_t<float, 64>(a, s) : launch_calib_t<float, 128>(a, s);
+}
+
+}  // namespace saf

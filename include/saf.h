@@ -1,0 +1,120 @@
+/*
+ * saf.h -- C ABI of libsaf.so: the fused mixed-head causal attention layer of Selective Attention
+ * Freezing (SAF) on AMD Instinct MI355X (gfx950).
+ *
+ * Citations name the page and the section / equation / table on it:
+ *   [Notes]      "When Can Attention Heads Be Statically Defined?：中文精读笔记" (close-reading notes
+ *                on arXiv 2609.34650v1).
+ *   [Paper page] "When Can Attention Heads Be Statically Defined?" (abstract, captions, tables).
+ *
+ * The layer ([Notes §二.4, Fig. 2]): per layer, some heads are "replaced".  An ordinary head computes
+ *     O = softmax_causal(s Q K^T) V,  s = 1/sqrt(d) by default                        [Notes §一]
+ * A replaced head has no query or key; its fixed causal pattern is rebuilt from two length-T
+ * vectors, an absolute-position preference a and a relative-distance preference r,
+ *     P(i,j) = exp(a[j] + r[i-j]) / Z(i)  for j <= i,  0 for j > i,
+ *     Z(i)   = sum_{k<=i} exp(a[k] + r[i-k])                         [Notes §二.3, Eq.(3)]
+ * (0-based: a[j] is the preference for key position j, r[delta] for distance delta = i - j) and
+ * mixes the current values: O = P V.  Both kinds run in one launch.  In the backward pass an
+ * ordinary head gets the full softmax gradient (dQ, dK, dV); a replaced head only dV = P^T dO,
+ * because a and r are frozen buffers and the output does not depend on its Q or K
+ * ([Notes §二.4]).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major [B][H][T][d] (batch, head, position, channel) in the element type
+ *    `dt`: SAF_F32 (fp32 everywhere) or SAF_BF16 (bf16 storage, fp32 accumulation inside).  Per-row
+ *    statistics (lse) are fp32 [B][H][T].  a and r are fp32 [H][pat_len] (only the rows of
+ *    replaced heads are read; positions 0..T-1 of each row are used, so a pattern fitted at a
+ *    longer length serves shorter inputs: row i depends on positions <= i only).
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, 16-byte aligned, allocated
+ *    and owned by the caller.  `replaced` is a HOST array of H bytes (nonzero = replaced head).
+ *  - `ws` is a caller-owned device workspace of at least the size returned by the matching
+ *    *_workspace_size() call (256-byte aligned); the library never allocates device memory and
+ *    holds no pointer after returning.
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns without waiting;
+ *    outputs are valid once the stream has completed, and inputs must stay unchanged until then.
+ *  - `scale` <= 0 selects 1/sqrt(d).  It applies to ordinary heads only (a and r are logits as
+ *    they stand).
+ *  - Supported: d in {64, 128}; 1 <= H <= 256; T <= 65536; B >= 0.  B == 0 or T == 0 is an empty
+ *    call: SAF_OK, nothing enqueued, pointers not inspected.
+ *  - Errors: every call returns a status and never aborts.  Arguments are checked BEFORE any HIP
+ *    call, so a call that returns SAF_ERR_INVALID_ARG or SAF_ERR_UNSUPPORTED has enqueued nothing
+ *    and written nothing.  A failed launch returns SAF_ERR_HIP.  saf_last_error() gives the text
+ *    of the calling thread's last non-OK status.
+ *  - The Q and K slices of replaced heads are never read (they may hold anything, NaN included),
+ *    nor are the a / r rows of ordinary heads.
+ */
+#ifndef SAF_H_
+#define SAF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAF_OK = 0,
+  SAF_ERR_INVALID_ARG = 1, /* a null / misaligned pointer, a size out of range, a short workspace */
+  SAF_ERR_UNSUPPORTED = 2, /* a valid request this build does not serve (d not in {64,128}, ...) */
+  SAF_ERR_HIP = 3          /* a HIP launch failed; the HIP error text is in saf_last_error()     */
+} saf_status;
+
+typedef enum { SAF_F32 = 0, SAF_BF16 = 1 } saf_dtype;
+
+/* Bytes of device workspace each call needs (0 for an empty call, SIZE_MAX if the sizes are out of
+ * range).  The sizes depend on the shapes only. */
+size_t saf_attn_fwd_workspace_size(int B, int H, int T, int d);
+size_t saf_attn_bwd_workspace_size(int B, int H, int T, int d);
+size_t saf_calibrate_workspace_size(int N, int H, int T, int d);
+
+/*
+ * Forward of the mixed layer.                                  [Notes §二.4, Fig. 2; Eq.(3)]
+ *   q, k, v : [B][H][T][d] dt     o : [B][H][T][d] dt (written)
+ *   lse     : [B][H][T] fp32 (written): for an ordinary head the natural-log logsumexp of the
+ *             scaled causal scores of row i; for a replaced head log Z(i) (the same for every b).
+ *             The backward pass reads it back.
+ *   replaced: [H] host bytes;  a, r : [H][pat_len] fp32 device, pat_len >= T.
+ */
+saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
+                        const void* v, const uint8_t* replaced, const float* a, const float* r,
+                        int pat_len, float scale, void* o, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * Backward of the mixed layer, given dout = dL/dO and the forward's o and lse.   [Notes §二.4]
+ *   ordinary head: dq, dk, dv of softmax attention;
+ *   replaced head: dv = P^T dout, and dq = dk = 0 (written as zeros).  No gradient for a or r.
+ *   q, k, v, o, dout : [B][H][T][d] dt;   lse : [B][H][T] fp32 as written by saf_attn_fwd for
+ *   the same q, k, v, replaced, a, r, scale;   dq, dk, dv : [B][H][T][d] dt (written).
+ */
+saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
+                        const void* v, const void* o, const void* dout, const float* lse,
+                        const uint8_t* replaced, const float* a, const float* r, int pat_len,
+                        float scale, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * Calibration statistics over N sequences.                       [Notes §二.1, Eq.(1)]
+ *   q, k : [N][H][T][d] dt, the queries and keys of the N calibration sequences; the maps
+ *          A^(n) = softmax_causal(s Q^(n) K^(n)T) are formed tile by tile and never stored.
+ *   ahat : [H][T][T] fp32 (written): the mean map (1/N) sum_n A^(n), zeros above the diagonal.
+ *   svar : [H] fp64 (written): sum_n ||A^(n) - ahat||_F^2 / ((N-1) T^2), every one of the T^2
+ *          entries counted.  N >= 2.
+ */
+saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q, const void* k,
+                         float scale, float* ahat, double* svar, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Text of the calling thread's last non-OK status ("" if none).  Valid until the thread's next
+ * call into the library. */
+const char* saf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAF_H_ */

@@ -1,0 +1,122 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point include/saf.h declares, sizes
+its workspaces, and rejects invalid arguments before any HIP call (so no GPU is needed here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "saf.h")
+
+saf = pytest.importorskip("fixed_pattern_mixed_amd")
+
+FAKE = 0x100000  # an aligned, never-dereferenced stand-in pointer: each case fails validation first
+SIZE_MAX = 2 ** 64 - 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(saf_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"saf_attn_fwd", "saf_attn_bwd", "saf_calibrate", "saf_last_error"} <= set(names)
+    lib = ctypes.CDLL(saf.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), "libsaf.so does not export " + n
+
+
+def test_workspace_sizes():
+    assert saf.saf_attn_fwd_workspace_size(8, 12, 4096, 64) == 0
+    assert saf.saf_attn_bwd_workspace_size(8, 12, 4096, 64) == 8 * 12 * 4096 * 4
+    assert saf.saf_attn_bwd_workspace_size(0, 12, 4096, 64) == 0
+    n = saf.saf_calibrate_workspace_size(32, 16, 8192, 128)
+    assert n >= 32 * 16 * 8192 * 4 + 16 * 64 * 128 * 8
+    assert saf.saf_attn_bwd_workspace_size(8, 12, 4096, 96) == SIZE_MAX
+    assert saf.saf_calibrate_workspace_size(1, 16, 8192, 128) == SIZE_MAX
+
+
+def _mask(*bits):
+    return (ctypes.c_uint8 * len(bits))(*bits)
+
+
+def fwd(dt=1, B=2, H=4, T=64, d=64, q=FAKE, k=FAKE, v=FAKE, rep=None, a=FAKE, r=FAKE, pat=64,
+        scale=0.0, o=FAKE, lse=FAKE):
+    rep = _mask(0, 0, 0, 1) if rep is None else rep
+    return saf.saf_attn_fwd(dt, B, H, T, d, q, k, v, rep, a, r, pat, scale, o, lse, None, 0, None)
+
+
+def bwd(dt=1, B=2, H=4, T=64, d=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE, g=FAKE, lse=FAKE, rep=None,
+        a=FAKE, r=FAKE, pat=64, scale=0.0, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, ws_n=0):
+    rep = _mask(0, 0, 0, 1) if rep is None else rep
+    return saf.saf_attn_bwd(dt, B, H, T, d, q, k, v, o, g, lse, rep, a, r, pat, scale, dq, dk, dv,
+                            ws, ws_n, None)
+
+
+@pytest.mark.parametrize("case,kw,status", [
+    ("unsupported d", dict(d=96), saf.SAF_ERR_UNSUPPORTED),
+    ("too many heads", dict(H=300, rep=_mask(*([0] * 300))), saf.SAF_ERR_UNSUPPORTED),
+    ("T too long", dict(T=70000, pat=70000), saf.SAF_ERR_UNSUPPORTED),
+    ("negative T", dict(T=-1), saf.SAF_ERR_INVALID_ARG),
+    ("no heads", dict(H=0), saf.SAF_ERR_INVALID_ARG),
+    ("unknown dtype", dict(dt=7), saf.SAF_ERR_INVALID_ARG),
+    ("null q", dict(q=None), saf.SAF_ERR_INVALID_ARG),
+    ("misaligned v", dict(v=FAKE + 2), saf.SAF_ERR_INVALID_ARG),
+    ("null mask", dict(rep=ctypes.POINTER(ctypes.c_uint8)()), saf.SAF_ERR_INVALID_ARG),
+    ("null a with a replaced head", dict(a=None), saf.SAF_ERR_INVALID_ARG),
+    ("pattern shorter than T", dict(pat=63), saf.SAF_ERR_INVALID_ARG),
+    ("null lse", dict(lse=None), saf.SAF_ERR_INVALID_ARG),
+    ("NaN scale", dict(scale=float("nan"), pat=64, lse=None), saf.SAF_ERR_INVALID_ARG),
+])
+def test_forward_rejects(case, kw, status):
+    assert fwd(**kw) == status, saf.saf_last_error()
+    assert saf.saf_last_error() != ""
+
+
+def test_forward_empty_calls_are_noops():
+    assert fwd(B=0, q=None, k=None, v=None, o=None, lse=None) == saf.SAF_OK
+    assert fwd(T=0, q=None, k=None, v=None, o=None, lse=None) == saf.SAF_OK
+
+
+def test_ordinary_only_layer_needs_no_pattern():
+    # no replaced head: a / r may be NULL; the call then fails on the missing lse, not on a / r
+    st = fwd(rep=_mask(0, 0, 0, 0), a=None, r=None, lse=None)
+    assert st == saf.SAF_ERR_INVALID_ARG and "lse" in saf.saf_last_error()
+
+
+def test_replaced_only_layer_needs_no_qk():
+    st = fwd(rep=_mask(1, 1, 1, 1), q=None, k=None, lse=None)
+    assert st == saf.SAF_ERR_INVALID_ARG and "lse" in saf.saf_last_error()
+
+
+@pytest.mark.parametrize("case,kw,status", [
+    ("unsupported d", dict(d=32), saf.SAF_ERR_UNSUPPORTED),
+    ("null ws", dict(ws=None, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+    ("short ws", dict(ws_n=100), saf.SAF_ERR_INVALID_ARG),
+    ("misaligned ws", dict(ws=FAKE + 16, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+    ("null dk", dict(dk=None, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+    ("null dout", dict(g=None, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+    ("pattern shorter than T", dict(pat=10, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+])
+def test_backward_rejects(case, kw, status):
+    assert bwd(**kw) == status, saf.saf_last_error()
+
+
+@pytest.mark.parametrize("case,dt,N,H,T,d,status", [
+    ("one sequence", 1, 1, 4, 64, 64, saf.SAF_ERR_INVALID_ARG),
+    ("unsupported d", 1, 4, 4, 64, 80, saf.SAF_ERR_UNSUPPORTED),
+    ("unknown dtype", 5, 4, 4, 64, 64, saf.SAF_ERR_INVALID_ARG),
+    ("no heads", 1, 4, 0, 64, 64, saf.SAF_ERR_INVALID_ARG),
+])
+def test_calibrate_rejects(case, dt, N, H, T, d, status):
+    st = saf.saf_calibrate(dt, N, H, T, d, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == status, saf.saf_last_error()
+
+
+def test_calibrate_short_workspace():
+    need = saf.saf_calibrate_workspace_size(4, 2, 64, 64)
+    st = saf.saf_calibrate(1, 4, 2, 64, 64, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == saf.SAF_ERR_INVALID_ARG and "workspace" in saf.saf_last_error()

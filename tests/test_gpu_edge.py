@@ -1,0 +1,104 @@
+"""Edge cases of the mixed layer on the GPU: what replaced heads must never read, degenerate
+patterns, a pattern longer than the input, repeatability, and a non-default stream."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import TOL, check_bwd, check_fwd
+
+pytestmark = pytest.mark.gpu
+
+
+def _saf():
+    import fixed_pattern_mixed_amd as saf
+    return saf
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_replaced_heads_never_read_q_k(dtype):
+    saf = _saf()
+    B, H, T, d = 2, 4, 190, 64
+    rep = synth.replaced_mask(H, 2, "interleaved")
+    g = synth.layer_inputs(B, H, T, d, dtype, rep, seed=3, device="cuda")
+    o1, l1 = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    d1 = saf.bwd(g.q, g.k, g.v, o1, g.dout, l1, rep, g.a, g.r)
+    q2, k2 = g.q.clone(), g.k.clone()
+    for h in range(H):
+        if rep[h]:
+            q2[:, h] = float("nan")
+            k2[:, h] = float("nan")
+    o2, l2 = saf.fwd(q2, k2, g.v, rep, g.a, g.r)
+    d2 = saf.bwd(q2, k2, g.v, o2, g.dout, l2, rep, g.a, g.r)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for x, y in zip(d1, d2):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("big", [float("-inf"), -1e4])
+def test_identity_pattern_copies_v(dtype, big):
+    """r[0] = 0 and r[delta >= 1] very negative: the fixed pattern is the identity, so O = V and
+    dV = dO exactly."""
+    saf = _saf()
+    B, H, T, d = 2, 2, 150, 128
+    rep = [1, 1]
+    g = synth.layer_inputs(B, H, T, d, dtype, rep, seed=4, device="cuda")
+    r = torch.full_like(g.r, big)
+    r[:, 0] = 0.0
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, r)
+    dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, r)
+    torch.cuda.synchronize()
+    assert torch.equal(o, g.v)
+    assert torch.equal(dv, g.dout)
+    assert torch.allclose(lse, g.a[None, :, :T].expand(B, H, T), atol=1e-6)
+
+
+def test_pattern_longer_than_input_uses_prefix():
+    saf = _saf()
+    B, H, T, d = 1, 4, 100, 64
+    rep = synth.replaced_mask(H, 2)
+    g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=6, device="cuda", pat_len=333)
+    o1, l1 = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    o2, l2 = saf.fwd(g.q, g.k, g.v, rep, g.a[:, :T].contiguous(), g.r[:, :T].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_bitwise_repeatable():
+    saf = _saf()
+    B, H, T, d = 2, 12, 700, 64
+    rep = synth.replaced_mask(H, 3)
+    g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=8, device="cuda")
+    outs = []
+    for _ in range(2):
+        o, l = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+        outs.append((o, l) + saf.bwd(g.q, g.k, g.v, o, g.dout, l, rep, g.a, g.r))
+    torch.cuda.synchronize()
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+def test_non_default_stream():
+    saf = _saf()
+    B, H, T, d = 1, 4, 333, 128
+    rep = synth.replaced_mask(H, 1)
+    x = synth.layer_inputs(B, H, T, d, torch.float32, rep, seed=9)
+    g = synth.layer_inputs(B, H, T, d, torch.float32, rep, seed=9, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+        dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
+    s.synchronize()
+    heads = [(0, h) for h in range(H)]
+    check_fwd(x, o, lse, heads, None, TOL[torch.float32], "stream")
+    check_bwd(x, dq, dk, dv, heads, None, None, TOL[torch.float32], "stream")
+
+
+def test_empty_batch_is_noop():
+    saf = _saf()
+    g = synth.layer_inputs(0, 4, 64, 64, torch.bfloat16, [0, 0, 0, 1], seed=1, device="cuda")
+    o, lse = saf.fwd(g.q, g.k, g.v, [0, 0, 0, 1], g.a, g.r)
+    assert o.shape == (0, 4, 64, 64)

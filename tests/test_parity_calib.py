@@ -1,0 +1,89 @@
+"""Calibration statistics on the GPU (through the C ABI) against the fp64 oracle: the mean map
+Ahat and the Eq. (1) variance score ([Notes §二.1]), plus the mean-optimality identity checked on
+the GPU's own outputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import TOL, cpu64, norm_err, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _saf():
+    import fixed_pattern_mixed_amd as saf
+    return saf
+
+
+SMALL = [
+    # N, H, T, d, dtype
+    (4, 2, 200, 64, torch.float32),
+    (2, 1, 1, 64, torch.float32),
+    (3, 2, 129, 128, torch.float32),
+    (5, 3, 256, 64, torch.bfloat16),
+    (8, 2, 1024, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("N,H,T,d,dtype", SMALL,
+                         ids=["N%dH%dT%dd%d-%s" % (c[0], c[1], c[2], c[3], str(c[4])[6:]) for c in SMALL])
+def test_calibrate_full_compare(N, H, T, d, dtype):
+    saf = _saf()
+    q, k = synth.calib_inputs(N, H, T, d, dtype, seed=31 + T)
+    ahat, svar = saf.calibrate(q.cuda(), k.cuda())
+    torch.cuda.synchronize()
+    ga, gs = cpu64(ahat), cpu64(svar)
+    for h in range(H):
+        ra, dev = oracle.head_calibrate(q[:, h], k[:, h])
+        rs = dev.sum() / ((N - 1) * T * T)
+        assert norm_err(ga[h], ra) <= TOL[dtype], (h, norm_err(ga[h], ra))
+        assert np.all(ga[h][np.triu_indices(T, 1)] == 0.0)
+        if rs == 0.0:
+            assert abs(gs[h]) <= 1e-12
+        else:
+            assert abs(gs[h] - rs) / rs <= TOL[dtype], (h, gs[h], rs)
+
+
+def test_mean_optimality_identity_on_gpu_outputs():
+    """For any fixed P: (1/(N T^2)) sum_n ||A^(n) - P||^2 = ((N-1)/N) s_var + ||P - Ahat||^2/T^2
+    ([Notes §二.2], Appendix B.1), with Ahat and s_var from the GPU and the maps from torch."""
+    saf = _saf()
+    N, H, T, d = 6, 2, 96, 64
+    q, k = synth.calib_inputs(N, H, T, d, torch.float32, seed=5)
+    ahat, svar = saf.calibrate(q.cuda(), k.cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    for h in range(H):
+        s = (q[:, h].double() @ k[:, h].double().transpose(-1, -2)) / math.sqrt(d)
+        s = s.masked_fill(torch.ones(T, T, dtype=torch.bool).triu(1), float("-inf"))
+        maps = torch.softmax(s, -1).numpy()
+        P = rng.random((T, T))
+        lhs = ((maps - P) ** 2).sum() / (N * T * T)
+        rhs = (N - 1) / N * float(svar[h]) + ((P - cpu64(ahat[h])) ** 2).sum() / (T * T)
+        assert abs(lhs - rhs) <= 1e-5 * lhs
+
+
+def test_calibrate_full_size_sampled():
+    """The 1B-shaped calibration (N=32, H=16, T=8192, d=128, bf16): sampled rows of Ahat against
+    the oracle, and properties that hold at any size (rows sum to 1, zeros above the diagonal,
+    0 <= s_var)."""
+    saf = _saf()
+    w = synth.WORKLOADS["l1b_t8192"]
+    N, H, T, d = w.calib_N, w.H, w.T, w.d
+    q, k = synth.calib_inputs(N, H, T, d, torch.bfloat16)
+    ahat, svar = saf.calibrate(q.cuda(), k.cuda())
+    torch.cuda.synchronize()
+    rows = sample_rows(T, 12, seed=9)
+    idx = torch.as_tensor(rows, dtype=torch.long, device="cuda")
+    for h in (0, H - 1):
+        ra, _ = oracle.head_calibrate(q[:, h], k[:, h], rows=rows)
+        got = cpu64(ahat[h].index_select(0, idx))
+        assert norm_err(got, ra) <= TOL[torch.bfloat16]
+    sums = ahat.double().sum(-1)
+    assert torch.allclose(sums, torch.ones_like(sums), atol=1e-4)
+    assert torch.count_nonzero(torch.triu(ahat[0], 1)) == 0
+    assert torch.isfinite(svar).all() and (svar >= 0).all()
