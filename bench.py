@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused mixed-head SAF attention layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input held in HBM: the
+mixed forward (ordinary and replaced heads in one grid) followed by the mixed backward (delta
+preprocess, key-block kernel, query-block kernel).  Forward-only workloads (prefill) time the
+forward alone.  Prints ONE JSON line.
+
+The default workload is the 124M-shaped layer of the pages' main update benchmark: B=8, H=12
+heads of width 64, T=4096, bf16, 3 of 12 heads replaced ([Notes §三]; [Paper page] Table 2).
+Algorithmic flops per (batch, head) over the T(T+1)/2 causal entries: ordinary forward 4d,
+ordinary backward 10d, replaced forward 2d, replaced backward 2d per entry.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-variants]
+
+[Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记";
+[Paper page] = "When Can Attention Heads Be Statically Defined?".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "mixed-head attn fwd+bwd tokens/s and TFLOP/s at 1 GPU; % of bf16 MFMA peak"
+# MI355X dense bf16 matrix peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU (AMD's published 2.5 PFLOP/s)
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_flops(B, T, d, replaced):
+    """Algorithmic flops of one launch of each kernel (GEMM work the method defines)."""
+    c = T * (T + 1) / 2.0
+    n_rep = sum(1 for x in replaced if x)
+    n_ord = len(replaced) - n_rep
+    return {
+        "mixed_fwd": B * c * (n_ord * 4 * d + n_rep * 2 * d),
+        "bwd_kv": B * c * (n_ord * 8 * d + n_rep * 2 * d),   # S, dP, dV, dK (ordinary); dV (replaced)
+        "bwd_q": B * c * (n_ord * 2 * d),                     # dQ
+        "bwd_pre": 0.0,
+    }
+
+
+def total_flops(B, T, d, replaced, backward):
+    kf = kernel_flops(B, T, d, replaced)
+    return kf["mixed_fwd"] + (kf["bwd_kv"] + kf["bwd_q"] if backward else 0.0)
+
+
+class Layer:
+    """Preallocated buffers and raw C-ABI calls for one layer shape (no allocation per step)."""
+
+    def __init__(self, saf, torch, w, replaced, dev):
+        import synth
+        self.saf, self.w, self.rep = saf, w, list(replaced)
+        x = synth.layer_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, replaced, w.ar_std,
+                               synth.SEED0 + w.index, backward=True, device=dev)
+        self.x = x
+        B, H, T, d = w.B, w.H, w.T, w.d
+        self.o = torch.empty_like(x.v)
+        self.lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = (torch.empty_like(x.v) for _ in range(3))
+        nb = max(saf.saf_attn_bwd_workspace_size(B, H, T, d), 256)
+        nf = max(saf.saf_attn_fwd_workspace_size(B, H, T, d), 256)
+        self.ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.ws_f = torch.empty(nf, dtype=torch.uint8, device=dev)
+        self.nb, self.nf = nb, nf
+        self.mask = saf._mask(replaced, H)
+        self.dt = saf.SAF_BF16 if w.dtype == "bf16" else saf.SAF_F32
+        self.stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def fwd(self):
+        s, w, x = self.saf, self.w, self.x
+        st = s.saf_attn_fwd(self.dt, w.B, w.H, w.T, w.d, x.q.data_ptr(), x.k.data_ptr(),
+                            x.v.data_ptr(), self.mask, x.a.data_ptr(), x.r.data_ptr(),
+                            x.a.shape[1], 0.0, self.o.data_ptr(), self.lse.data_ptr(),
+                            self.ws_f.data_ptr(), self.nf, self.stream)
+        s._check(st, "saf_attn_fwd")
+
+    def bwd(self):
+        s, w, x = self.saf, self.w, self.x
+        st = s.saf_attn_bwd(self.dt, w.B, w.H, w.T, w.d, x.q.data_ptr(), x.k.data_ptr(),
+                            x.v.data_ptr(), self.o.data_ptr(), x.dout.data_ptr(),
+                            self.lse.data_ptr(), self.mask, x.a.data_ptr(), x.r.data_ptr(),
+                            x.a.shape[1], 0.0, self.dq.data_ptr(), self.dk.data_ptr(),
+                            self.dv.data_ptr(), self.ws_b.data_ptr(), self.nb, self.stream)
+        s._check(st, "saf_attn_bwd")
+
+    def step(self):
+        self.fwd()
+        if self.w.backward:
+            self.bwd()
+
+
+def time_steps(torch, layer, steps, warmup, trace=None):
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    if trace is not None:
+        trace.begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if trace is not None:
+        trace.end()
+        trace.collect()
+    return (t1 - t0) / steps
+
+
+def cpu_baseline(w, replaced, n_seq=2):
+    """The fp64 oracle, as it stands, on the first n_seq sequences of the same workload."""
+    import oracle
+    import synth
+    x = synth.layer_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, replaced, w.ar_std,
+                           synth.SEED0 + w.index, backward=w.backward)
+    heads = [(b, h) for b in range(n_seq) for h in range(w.H)]
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.layer_fwd(x.q, x.k, x.v, replaced, x.a, x.r, heads=heads)
+    if w.backward:
+        oracle.layer_bwd(x.q, x.k, x.v, x.dout, replaced, x.a, x.r, heads=heads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n_seq * w.T / dt,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d sequences (all %d heads, full T=%d, %s) in %.1f s"
+                  % (n_seq, w.B, w.H, w.T, "fwd+bwd" if w.backward else "fwd", dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="l124m_t4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this layer has no exchange between GPUs and this "
+              "build runs on a single MI355X (--gpus %d, WORLD_SIZE %d requested)"
+              % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fixed_pattern_mixed_amd as saf
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    replaced = w.replaced()
+    layer = Layer(saf, torch, w, replaced, dev)
+    trace = saf.KernelTrace(capacity=4 * (args.steps + 1))
+    t_step = time_steps(torch, layer, args.steps, args.warmup, trace)
+    tokens = w.B * w.T
+    flops = total_flops(w.B, w.T, w.d, replaced, w.backward)
+    kf = kernel_flops(w.B, w.T, w.d, replaced)
+
+    kernels = {}
+    for name, s in trace.summary().items():
+        ent = {"avg_ms": round(s["avg_ms"], 4), "launches": s["launches"]}
+        if kf.get(name):
+            ent["tflops"] = round(kf[name] / (s["avg_ms"] * 1e-3) / 1e12, 1)
+        kernels[name] = ent
+    trace.close()
+    dom = max(trace.summary().items(), key=lambda kv: kv[1]["total_ms"])[0]
+    dom_ms = trace.summary()[dom]["avg_ms"]
+    achieved = kf[dom] / (dom_ms * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / t_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d,
+                   "replaced_heads": [h for h, x in enumerate(replaced) if x],
+                   "pass": "fwd+bwd" if w.backward else "fwd",
+                   "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"},
+        "tflops": round(flops / t_step / 1e12, 1),
+        "pct_bf16_peak": round(100 * flops / t_step / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+
+    if not args.no_variants:
+        var = {}
+        for label, rr in (("all_ordinary", [0] * w.H), ("all_replaced", [1] * w.H)):
+            lv = Layer(saf, torch, w, rr, dev)
+            tv = time_steps(torch, lv, max(5, args.steps // 3), 2)
+            fv = total_flops(w.B, w.T, w.d, rr, w.backward)
+            var[label] = {"ms_per_step": round(tv * 1e3, 4), "tflops": round(fv / tv / 1e12, 1),
+                          "pct_bf16_peak": round(100 * fv / tv / 1e12 / PEAK_BF16_TFLOPS, 2)}
+            del lv
+        var["mixed_speedup_vs_all_ordinary"] = round(var["all_ordinary"]["ms_per_step"] / (t_step * 1e3), 4)
+        var["replaced_vs_ordinary_time_per_head"] = round(
+            var["all_replaced"]["ms_per_step"] / var["all_ordinary"]["ms_per_step"], 4)
+        out["variants"] = var
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, replaced)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,7 +26,26 @@ if not os.path.exists(LIB_PATH):
         "libsaf.so is not built (expected at %s); run `python -m fixed_pattern_mixed_amd.build` "
         "or __graft_entry__.build() first" % LIB_PATH)
 
+# PyTorch provides the device memory and streams handed to the library, so the library must run on
+# the same HIP runtime instance as PyTorch.  Importing torch first makes the dynamic loader bind
+# libsaf.so's libamdhip64.so.7 dependency to the runtime torch already loaded; loading libsaf.so
+# first would map a second, separate runtime, to which torch's stream handles mean nothing.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError("more than one HIP runtime is mapped into this process (%s); import torch "
+                      "before anything loads libsaf.so" % ", ".join(_hip_runtimes()))
 
 SAF_OK, SAF_ERR_INVALID_ARG, SAF_ERR_UNSUPPORTED, SAF_ERR_HIP = 0, 1, 2, 3
 SAF_F32, SAF_BF16 = 0, 1
@@ -163,3 +182,67 @@ def calibrate(q, k, scale=None):
                        _ptr(ahat), _ptr(svar), _ptr(ws), ws_n, _stream(q.device))
     _check(st, "saf_calibrate")
     return ahat, svar
+
+
+# ------------------------------------------------------------------ per-kernel timing (profiling)
+class SafKernelEvent(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("start", _vp), ("stop", _vp)]
+
+
+_lib.saf_trace_begin.argtypes = [ctypes.POINTER(SafKernelEvent), _i]
+_lib.saf_trace_begin.restype = _i
+_lib.saf_trace_end.argtypes = []
+_lib.saf_trace_end.restype = _i
+saf_trace_begin = _lib.saf_trace_begin
+saf_trace_end = _lib.saf_trace_end
+
+# The HIP runtime torch loaded (same SONAME, so dlopen returns the instance already mapped).
+_hip = ctypes.CDLL("libamdhip64.so.7")
+_hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
+_hip.hipEventCreate.restype = _i
+_hip.hipEventDestroy.argtypes = [_vp]
+_hip.hipEventDestroy.restype = _i
+_hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+_hip.hipEventElapsedTime.restype = _i
+
+
+class KernelTrace:
+    """Times every kernel the library launches between begin() and end() with HIP events recorded
+    on the launching stream (saf_trace_begin / saf_trace_end).  Accumulates per-kernel durations
+    over many begin/end rounds; read them after the stream has completed."""
+
+    def __init__(self, capacity=16):
+        self.cap = capacity
+        self.ev = (SafKernelEvent * capacity)()
+        for e in self.ev:
+            for f in ("start", "stop"):
+                h = _vp()
+                if _hip.hipEventCreate(ctypes.byref(h)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                setattr(e, f, h)
+        self.samples = {}
+        self._n = 0
+
+    def begin(self):
+        _check(saf_trace_begin(self.ev, self.cap), "saf_trace_begin")
+
+    def end(self):
+        """Stop recording; must be followed by a stream synchronisation before collect()."""
+        self._n = saf_trace_end()
+
+    def collect(self):
+        ms = ctypes.c_float()
+        for e in self.ev[:self._n]:
+            if _hip.hipEventElapsedTime(ctypes.byref(ms), e.start, e.stop) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            self.samples.setdefault(e.name.decode(), []).append(ms.value)
+        self._n = 0
+
+    def summary(self):
+        return {k: {"launches": len(v), "avg_ms": sum(v) / len(v), "total_ms": sum(v)}
+                for k, v in self.samples.items()}
+
+    def close(self):
+        for e in self.ev:
+            _hip.hipEventDestroy(e.start)
+            _hip.hipEventDestroy(e.stop)

@@ -79,6 +79,34 @@ saf_status fill_mask(const uint8_t* replaced, int H, uint64_t* rep, bool* any_re
   return SAF_OK;
 }
 
+// ---- optional per-kernel event tracing (saf_trace_begin / saf_trace_end)
+struct Trace {
+  saf_kernel_event* ev = nullptr;
+  int cap = 0;
+  int n = 0;
+};
+thread_local Trace g_trace;
+
+// Launch one kernel through `fn`, bracketed by the caller's trace events when tracing is on.
+template <typename F>
+hipError_t traced(const char* name, hipStream_t s, F&& fn) {
+  Trace& t = g_trace;
+  const bool rec = t.ev && t.n < t.cap;
+  if (rec) {
+    hipError_t e = hipEventRecord(t.ev[t.n].start, s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = fn();
+  if (e != hipSuccess) return e;
+  if (rec) {
+    t.ev[t.n].name = name;
+    e = hipEventRecord(t.ev[t.n].stop, s);
+    if (e != hipSuccess) return e;
+    ++t.n;
+  }
+  return hipSuccess;
+}
+
 size_t fwd_ws(int B, int H, int T, int d) {
   (void)B; (void)H; (void)T; (void)d;
   return 0;  // the forward needs no scratch
@@ -122,6 +150,21 @@ size_t saf_calibrate_workspace_size(int N, int H, int T, int d) {
 
 const char* saf_last_error(void) { return g_err; }
 
+saf_status saf_trace_begin(saf_kernel_event* ev, int capacity) {
+  g_err[0] = 0;
+  if (!ev || capacity < 1) return fail(SAF_ERR_INVALID_ARG, "trace needs an event array and capacity >= 1");
+  g_trace.ev = ev;
+  g_trace.cap = capacity;
+  g_trace.n = 0;
+  return SAF_OK;
+}
+
+int saf_trace_end(void) {
+  const int n = g_trace.n;
+  g_trace = Trace();
+  return n;
+}
+
 saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
                         const void* v, const uint8_t* replaced, const float* a, const float* r,
                         int pat_len, float scale, void* o, float* lse, void* ws, size_t ws_bytes,
@@ -157,7 +200,8 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
   la.a = a; la.r = r;
   la.lse = lse;
   la.out = o;
-  hipError_t e = saf::launch_mixed_fwd(la, dt == SAF_BF16, stream);
+  const bool bf = dt == SAF_BF16;
+  hipError_t e = traced("mixed_fwd", stream, [&] { return saf::launch_mixed_fwd(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "mixed forward launch");
   return SAF_OK;
 }
@@ -203,12 +247,12 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
   la.delta = reinterpret_cast<float*>(ws);
   la.dq = dq; la.dk = dk; la.dv = dv;
   const bool bf = dt == SAF_BF16;
-  hipError_t e = saf::launch_bwd_pre(la, bf, stream);
+  hipError_t e = traced("bwd_pre", stream, [&] { return saf::launch_bwd_pre(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-  e = saf::launch_bwd_kv(la, bf, stream);
+  e = traced("bwd_kv", stream, [&] { return saf::launch_bwd_kv(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward key-block launch");
   if (any_ord) {
-    e = saf::launch_bwd_q(la, bf, stream);
+    e = traced("bwd_q", stream, [&] { return saf::launch_bwd_q(la, bf, stream); });
     if (e != hipSuccess) return hip_fail(e, "backward query-block launch");
   }
   return SAF_OK;
@@ -243,8 +287,13 @@ saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q
   ca.ahat = ahat;
   ca.svar = svar;
   calib_tiles(T, &ca.n_qt, &ca.n_kt);
-  hipError_t e = saf::launch_calibrate(ca, dt == SAF_BF16, stream);
-  if (e != hipSuccess) return hip_fail(e, "calibration launch");
+  const bool bf = dt == SAF_BF16;
+  hipError_t e = traced("calib_lse", stream, [&] { return saf::launch_calib_lse(ca, bf, stream); });
+  if (e != hipSuccess) return hip_fail(e, "calibration statistics launch");
+  e = traced("calib_stats", stream, [&] { return saf::launch_calib_stats(ca, bf, stream); });
+  if (e != hipSuccess) return hip_fail(e, "calibration tile launch");
+  e = traced("calib_reduce", stream, [&] { return saf::launch_calib_reduce(ca, stream); });
+  if (e != hipSuccess) return hip_fail(e, "calibration reduction launch");
   return SAF_OK;
 }
 

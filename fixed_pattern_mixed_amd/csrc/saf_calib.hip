@@ -212,26 +212,35 @@ __global__ __launch_bounds__(kNT) void calib_reduce_kernel(CalibArgs p) {
 }
 
 template <typename TI, int D>
-hipError_t launch_calib_t(const CalibArgs& a, hipStream_t s) {
+hipError_t launch_lse_t(const CalibArgs& a, hipStream_t s) {
   const int NHp = (a.N * a.H + 7) & ~7;
-  const long long b1 = (long long)NHp * ((a.T + kBQ - 1) / kBQ);
-  const long long b2 = (long long)a.H * a.n_qt * a.n_kt;
-  if (b1 > 0x7fffffffLL || b2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((calib_lse_kernel<TI, D>), dim3((unsigned)b1), dim3(kNT), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((calib_stats_kernel<TI, D>), dim3((unsigned)b2), dim3(kNT), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(calib_reduce_kernel, dim3(a.H), dim3(kNT), 0, s, a);
+  const long long blocks = (long long)NHp * ((a.T + kBQ - 1) / kBQ);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((calib_lse_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename TI, int D>
+hipError_t launch_stats_t(const CalibArgs& a, hipStream_t s) {
+  const long long blocks = (long long)a.H * a.n_qt * a.n_kt;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((calib_stats_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_calibrate(const CalibArgs& a, bool bf16_in, hipStream_t s) {
-  if (bf16_in) return a.d == 64 ? launch_calib_t<bf16, 64>(a, s) : launch_calib_t<bf16, 128>(a, s);
-  return a.d == 64 ? launch_calib_t<float, 64>(a, s) : launch_calib_t<float, 128>(a, s);
+hipError_t launch_calib_lse(const CalibArgs& a, bool bf16_in, hipStream_t s) {
+  if (bf16_in) return a.d == 64 ? launch_lse_t<bf16, 64>(a, s) : launch_lse_t<bf16, 128>(a, s);
+  return a.d == 64 ? launch_lse_t<float, 64>(a, s) : launch_lse_t<float, 128>(a, s);
+}
+hipError_t launch_calib_stats(const CalibArgs& a, bool bf16_in, hipStream_t s) {
+  if (bf16_in) return a.d == 64 ? launch_stats_t<bf16, 64>(a, s) : launch_stats_t<bf16, 128>(a, s);
+  return a.d == 64 ? launch_stats_t<float, 64>(a, s) : launch_stats_t<float, 128>(a, s);
+}
+hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(calib_reduce_kernel, dim3(a.H), dim3(kNT), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace saf

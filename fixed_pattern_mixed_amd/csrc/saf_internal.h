@@ -50,7 +50,9 @@ hipError_t launch_mixed_fwd(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_q(const LayerArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_calibrate(const CalibArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_calib_lse(const CalibArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_calib_stats(const CalibArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s);
 
 // Tile geometry shared by the host (workspace sizing) and the kernels.
 constexpr int kCalibQTile = 128;  // queries per calibration statistics tile

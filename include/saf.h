@@ -113,6 +113,26 @@ saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q
  * call into the library. */
 const char* saf_last_error(void);
 
+/*
+ * Per-kernel timing (off by default), for profiling a layer from the host.
+ * saf_trace_begin(ev, capacity): until saf_trace_end(), every kernel that a call made on this
+ * thread launches is bracketed by hipEventRecord(ev[i].start) / hipEventRecord(ev[i].stop) on that
+ * call's stream, filling ev[0], ev[1], ... in launch order and setting ev[i].name to a static
+ * string naming the kernel.  Launches beyond `capacity` are not recorded.  The caller creates the
+ * events (hipEventCreate, on the current device) and owns them and the array; the library only
+ * records into them.  saf_trace_end() stops recording and returns the number of entries filled.
+ * Errors: SAF_ERR_INVALID_ARG if ev is NULL or capacity < 1.  A failed event record makes the
+ * traced call return SAF_ERR_HIP.
+ */
+typedef struct {
+  const char* name;
+  hipEvent_t start;
+  hipEvent_t stop;
+} saf_kernel_event;
+
+saf_status saf_trace_begin(saf_kernel_event* ev, int capacity);
+int saf_trace_end(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,8 +57,9 @@ class _Lib:
         lib.orc_head_calibrate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp,
                                            ctypes.c_double, ctypes.c_int, _ip, _dp, _dp]
         lib.orc_calibrate_maps.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
+        lib.orc_num_threads.argtypes = []
         for f in (lib.orc_head_fwd, lib.orc_head_pattern, lib.orc_head_bwd,
-                  lib.orc_head_calibrate, lib.orc_calibrate_maps):
+                  lib.orc_head_calibrate, lib.orc_calibrate_maps, lib.orc_num_threads):
             f.restype = ctypes.c_int
         self.c = lib
 
@@ -118,6 +119,11 @@ def _rows(rows, T):
 def _check(rc, what):
     if rc != 0:
         raise ValueError("oracle rejected the arguments of " + what)
+
+
+def num_threads():
+    """Threads the oracle's parallel loops use."""
+    return int(_load().orc_num_threads())
 
 
 # ------------------------------------------------------------------------------ one head slice

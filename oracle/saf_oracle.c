@@ -41,6 +41,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_EXPORT __attribute__((visibility("default")))
 
@@ -344,4 +347,13 @@ ORC_EXPORT int orc_calibrate_maps(int N, int T, const double* maps, double* ahat
     }
   *svar = acc / ((double)(N - 1) * (double)T * (double)T);
   return 0;
+}
+
+/* Number of threads the parallel loops above use (for reporting the CPU baseline). */
+ORC_EXPORT int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

@@ -120,3 +120,8 @@ def test_calibrate_short_workspace():
     need = saf.saf_calibrate_workspace_size(4, 2, 64, 64)
     st = saf.saf_calibrate(1, 4, 2, 64, 64, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, need - 1, None)
     assert st == saf.SAF_ERR_INVALID_ARG and "workspace" in saf.saf_last_error()
+
+
+def test_single_hip_runtime_in_process():
+    """The binding must share PyTorch's HIP runtime (one libamdhip64 mapped in the process)."""
+    assert len(saf._hip_runtimes()) == 1, saf._hip_runtimes()
