@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libsaf.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libsaf.so is not built (expected at %s); run `python -m fixed_pattern_mixed_amd.build` "
+        "libsaf.so is not built (expected at %s); run `python fixed_pattern_mixed_amd/build.py` "
         "or __graft_entry__.build() first" % LIB_PATH)
 
 # PyTorch provides the device memory and streams handed to the library, so the library must run on
@@ -62,11 +62,15 @@ _lib.saf_calibrate_workspace_size.argtypes = [_i, _i, _i, _i]
 _lib.saf_calibrate_workspace_size.restype = _sz
 _lib.saf_last_error.argtypes = []
 _lib.saf_last_error.restype = ctypes.c_char_p
-_lib.saf_attn_fwd.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, ctypes.c_float,
-                              _vp, _vp, _vp, _sz, _vp]
+_lib.saf_pattern_size.argtypes = [_i, _i]
+_lib.saf_pattern_size.restype = _sz
+_lib.saf_pattern_prepare.argtypes = [_i, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+_lib.saf_pattern_prepare.restype = _i
+_lib.saf_attn_fwd.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp,
+                              ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
 _lib.saf_attn_fwd.restype = _i
 _lib.saf_attn_bwd.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
-                              ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
+                              _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.saf_attn_bwd.restype = _i
 _lib.saf_calibrate.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _sz,
                                _vp]
@@ -79,6 +83,8 @@ saf_calibrate = _lib.saf_calibrate
 saf_attn_fwd_workspace_size = _lib.saf_attn_fwd_workspace_size
 saf_attn_bwd_workspace_size = _lib.saf_attn_bwd_workspace_size
 saf_calibrate_workspace_size = _lib.saf_calibrate_workspace_size
+saf_pattern_size = _lib.saf_pattern_size
+saf_pattern_prepare = _lib.saf_pattern_prepare
 
 
 def saf_last_error() -> str:
@@ -133,9 +139,23 @@ def _ws(nbytes, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def fwd(q, k, v, replaced, a=None, r=None, scale=None, out=None, lse=None):
+def prepare_pattern(replaced, a, r):
+    """Prepared pattern of the replaced heads (a, r: [H, pat_len] fp32 on the GPU), to pass as
+    `pattern=` to fwd / bwd with the same replaced, a and r.  Returns a uint8 device tensor."""
+    import torch
+    H, P = a.shape
+    n = saf_pattern_size(H, P)
+    buf = torch.empty(max(n, 1), dtype=torch.uint8, device=a.device)
+    st = saf_pattern_prepare(H, _mask(replaced, H), _ptr(a), _ptr(r), P, _ptr(buf), n,
+                             _stream(a.device))
+    _check(st, "saf_pattern_prepare")
+    return buf
+
+
+def fwd(q, k, v, replaced, a=None, r=None, scale=None, out=None, lse=None, pattern=None):
     """Forward of the mixed layer.  q, k, v: [B, H, T, d] (bf16 or fp32, same dtype), replaced:
-    H flags, a, r: [H, pat_len] fp32 on the GPU.  Returns (o, lse)."""
+    H flags, a, r: [H, pat_len] fp32 on the GPU, pattern: optional prepare_pattern() result.
+    Returns (o, lse)."""
     import torch
     B, H, T, d = v.shape
     dt = _dtype_code(v)
@@ -145,13 +165,13 @@ def fwd(q, k, v, replaced, a=None, r=None, scale=None, out=None, lse=None):
     ws = _ws(ws_n, v.device)
     pat_len = a.shape[-1] if a is not None else 0
     st = saf_attn_fwd(dt, B, H, T, d, _ptr(q), _ptr(k), _ptr(v), _mask(replaced, H), _ptr(a),
-                      _ptr(r), pat_len, 0.0 if scale is None else float(scale), _ptr(o), _ptr(lse),
-                      _ptr(ws), ws_n, _stream(v.device))
+                      _ptr(r), pat_len, _ptr(pattern), 0.0 if scale is None else float(scale),
+                      _ptr(o), _ptr(lse), _ptr(ws), ws_n, _stream(v.device))
     _check(st, "saf_attn_fwd")
     return o, lse
 
 
-def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None):
+def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None, pattern=None):
     """Backward of the mixed layer.  Returns (dq, dk, dv); replaced heads get dq = dk = 0."""
     import torch
     B, H, T, d = v.shape
@@ -161,7 +181,7 @@ def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None):
     ws = _ws(ws_n, v.device)
     pat_len = a.shape[-1] if a is not None else 0
     st = saf_attn_bwd(dt, B, H, T, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                      _mask(replaced, H), _ptr(a), _ptr(r), pat_len,
+                      _mask(replaced, H), _ptr(a), _ptr(r), pat_len, _ptr(pattern),
                       0.0 if scale is None else float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
                       _ptr(ws), ws_n, _stream(v.device))
     _check(st, "saf_attn_bwd")

@@ -1,6 +1,7 @@
 """Build libsaf.so (HIP kernels for gfx950 + the C-ABI host code) in-tree with hipcc.
 
-Usage: python -m fixed_pattern_mixed_amd.build   (or call build()).  Every call recompiles.
+Usage: python fixed_pattern_mixed_amd/build.py [-v]   (or __graft_entry__.build()).  Every call
+recompiles.  (Run it by path: importing the package would load the library being rebuilt.)
 """
 from __future__ import annotations
 
@@ -13,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsaf.so")
-SOURCES = ["saf_api.cpp", "saf_fwd.hip", "saf_bwd.hip", "saf_calib.hip"]
+SOURCES = ["saf_api.cpp", "saf_pattern.hip", "saf_fwd.hip", "saf_bwd.hip", "saf_calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -107,13 +107,35 @@ hipError_t traced(const char* name, hipStream_t s, F&& fn) {
   return hipSuccess;
 }
 
+size_t pattern_bytes(int H, int P) {
+  return align_up(sizeof(float) * (size_t)saf::pattern_stride(P) * H);
+}
 size_t fwd_ws(int B, int H, int T, int d) {
-  (void)B; (void)H; (void)T; (void)d;
-  return 0;  // the forward needs no scratch
+  (void)B; (void)d;
+  return pattern_bytes(H, T);  // the prepared pattern, when the caller passes none
 }
 size_t bwd_ws(int B, int H, int T, int d) {
   (void)d;
-  return align_up(sizeof(float) * (size_t)B * H * T);  // delta
+  return pattern_bytes(H, T) + align_up(sizeof(float) * (size_t)B * H * T);  // pattern, delta
+}
+
+// Point la.pat at the caller's prepared pattern, or prepare one for length T at ws.
+saf_status setup_pattern(saf::LayerArgs& la, bool any_rep, const void* pattern, int T, void* ws,
+                         hipStream_t stream, const char* what) {
+  if (!any_rep) return SAF_OK;
+  if (pattern) {
+    la.pat.base = const_cast<float*>(reinterpret_cast<const float*>(pattern));
+    la.pat.P = la.pat_len;
+  } else {
+    la.pat.base = reinterpret_cast<float*>(ws);
+    la.pat.P = T;
+  }
+  la.pat.stride = saf::pattern_stride(la.pat.P);
+  if (!pattern) {
+    hipError_t e = traced("pattern_prepare", stream, [&] { return saf::launch_pattern_prepare(la, stream); });
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return SAF_OK;
 }
 size_t calib_tiles(int T, int* nqt, int* nkt) {
   *nqt = (T + saf::kCalibQTile - 1) / saf::kCalibQTile;
@@ -150,6 +172,35 @@ size_t saf_calibrate_workspace_size(int N, int H, int T, int d) {
 
 const char* saf_last_error(void) { return g_err; }
 
+size_t saf_pattern_size(int H, int pat_len) {
+  if (H < 1 || H > saf::kMaxHeads || pat_len < 0 || pat_len > kMaxT) return SIZE_MAX;
+  return pattern_bytes(H, pat_len);
+}
+
+saf_status saf_pattern_prepare(int H, const uint8_t* replaced, const float* a, const float* r,
+                               int pat_len, void* pattern, size_t pattern_bytes_given,
+                               hipStream_t stream) {
+  g_err[0] = 0;
+  if (H < 1) return fail(SAF_ERR_INVALID_ARG, "need H >= 1 (got %d)", H);
+  if (H > saf::kMaxHeads) return fail(SAF_ERR_UNSUPPORTED, "H=%d exceeds the supported %d heads", H, saf::kMaxHeads);
+  if (pat_len < 0) return fail(SAF_ERR_INVALID_ARG, "pat_len=%d is negative", pat_len);
+  if (pat_len > kMaxT) return fail(SAF_ERR_UNSUPPORTED, "pat_len=%d exceeds the supported %d", pat_len, kMaxT);
+  saf::LayerArgs la;
+  memset(&la, 0, sizeof(la));
+  bool any_rep = false;
+  saf_status st = fill_mask(replaced, H, la.rep, &any_rep);
+  if (st != SAF_OK) return st;
+  if (!any_rep || pat_len == 0) return SAF_OK;
+  if (!a || !r) return fail(SAF_ERR_INVALID_ARG, "a and r are required when a head is replaced");
+  if (!pattern) return fail(SAF_ERR_INVALID_ARG, "pattern is NULL");
+  if (((uintptr_t)pattern & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "pattern is not 256-byte aligned");
+  if (pattern_bytes_given < pattern_bytes(H, pat_len))
+    return fail(SAF_ERR_INVALID_ARG, "pattern buffer too small (%zu < %zu bytes)", pattern_bytes_given, pattern_bytes(H, pat_len));
+  la.H = H; la.T = pat_len; la.pat_len = pat_len;
+  la.a = a; la.r = r;
+  return setup_pattern(la, true, nullptr, pat_len, pattern, stream, "pattern preparation");
+}
+
 saf_status saf_trace_begin(saf_kernel_event* ev, int capacity) {
   g_err[0] = 0;
   if (!ev || capacity < 1) return fail(SAF_ERR_INVALID_ARG, "trace needs an event array and capacity >= 1");
@@ -167,8 +218,8 @@ int saf_trace_end(void) {
 
 saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
                         const void* v, const uint8_t* replaced, const float* a, const float* r,
-                        int pat_len, float scale, void* o, float* lse, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        int pat_len, const void* pattern, float scale, void* o, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   saf_status st = check_shape(B, H, T, d);
@@ -187,10 +238,16 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
     if (!a || !r) return fail(SAF_ERR_INVALID_ARG, "a and r are required when a head is replaced");
     if (pat_len < T) return fail(SAF_ERR_INVALID_ARG, "pat_len=%d is shorter than T=%d", pat_len, T);
   }
-  if (ws_bytes < fwd_ws(B, H, T, d)) return fail(SAF_ERR_INVALID_ARG, "workspace too small");
+  if (any_rep && pattern && ((uintptr_t)pattern & (kAlign - 1)) != 0)
+    return fail(SAF_ERR_INVALID_ARG, "pattern is not 256-byte aligned");
+  if (any_rep && !pattern) {
+    const size_t need = fwd_ws(B, H, T, d);
+    if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL (needed to prepare the pattern)");
+    if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
+    if (ws_bytes < need) return fail(SAF_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  }
   float s;
   if ((st = check_scale(scale, d, &s)) != SAF_OK) return st;
-  (void)ws;
 
   la.B = B; la.H = H; la.T = T; la.d = d;
   la.pat_len = pat_len;
@@ -200,6 +257,7 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
   la.a = a; la.r = r;
   la.lse = lse;
   la.out = o;
+  if ((st = setup_pattern(la, any_rep, pattern, T, ws, stream, "pattern preparation")) != SAF_OK) return st;
   const bool bf = dt == SAF_BF16;
   hipError_t e = traced("mixed_fwd", stream, [&] { return saf::launch_mixed_fwd(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "mixed forward launch");
@@ -209,8 +267,8 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
 saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
                         const void* v, const void* o, const void* dout, const float* lse,
                         const uint8_t* replaced, const float* a, const float* r, int pat_len,
-                        float scale, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        const void* pattern, float scale, void* dq, void* dk, void* dv, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   saf_status st = check_shape(B, H, T, d);
@@ -230,6 +288,8 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
     if (!a || !r) return fail(SAF_ERR_INVALID_ARG, "a and r are required when a head is replaced");
     if (pat_len < T) return fail(SAF_ERR_INVALID_ARG, "pat_len=%d is shorter than T=%d", pat_len, T);
   }
+  if (any_rep && pattern && ((uintptr_t)pattern & (kAlign - 1)) != 0)
+    return fail(SAF_ERR_INVALID_ARG, "pattern is not 256-byte aligned");
   const size_t need = bwd_ws(B, H, T, d);
   if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL");
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
@@ -244,8 +304,9 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
   la.q = q; la.k = k; la.v = v; la.o = o; la.dout = dout;
   la.a = a; la.r = r;
   la.lse = const_cast<float*>(lse);
-  la.delta = reinterpret_cast<float*>(ws);
+  la.delta = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + pattern_bytes(H, T));
   la.dq = dq; la.dk = dk; la.dv = dv;
+  if ((st = setup_pattern(la, any_rep, pattern, T, ws, stream, "pattern preparation")) != SAF_OK) return st;
   const bool bf = dt == SAF_BF16;
   hipError_t e = traced("bwd_pre", stream, [&] { return saf::launch_bwd_pre(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");

@@ -107,6 +107,61 @@ __device__ __forceinline__ Frag<TI> gather_col(const TI* tile, int row0, int col
   return f;
 }
 
+// Column fragment of a row-major LDS tile (row stride LDP elements): slot e holds
+// tile[row0 + perm_row(e, lane/32)][col0 + lane%32], i.e. the k16-step operand of a product that
+// contracts over the tile's rows.
+//   bf16: two transposing LDS reads (ds_read_b64_tr_b16).  Within each 16-lane group the hardware
+//         gathers the 64-bit row segments the 16 lanes address (lane j: row j/4, columns 4*(j%4)..)
+//         into columns: lane i receives rows 0..3 of column i.  One read covers slots 0..3 (rows
+//         row0 + 4*hi + 0..3), the second slots 4..7 (rows row0 + 8 + 4*hi + 0..3).
+//   fp32: eight scalar LDS reads.
+typedef short v4i16 __attribute__((__vector_size__(8)));
+typedef short v8i16 __attribute__((__vector_size__(16)));
+
+template <int LDP>
+__device__ __forceinline__ Frag<bf16> col_frag_impl(const bf16* tile, int row0, int col0, int lane) {
+  const int j = lane & 15, g = (lane >> 4) & 1, hi = lane >> 5;
+  const bf16* p0 = tile + (row0 + 4 * hi + (j >> 2)) * LDP + col0 + 16 * g + 4 * (j & 3);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 8 * LDP));
+  const v8i16 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, c);
+  return f;
+}
+template <int LDP>
+__device__ __forceinline__ Frag<float> col_frag_impl(const float* tile, int row0, int col0, int lane) {
+  const int hi = lane >> 5, col = col0 + (lane & 31);
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = tile[(row0 + perm_row(e, hi)) * LDP + col];
+  return f;
+}
+template <typename TI, int LDP>
+__device__ __forceinline__ Frag<TI> col_frag(const TI* tile, int row0, int col0, int lane) {
+  return col_frag_impl<LDP>(tile, row0, col0, lane);
+}
+
+// Sum of a fragment's eight values (bf16: two-way dot products with 1, fp32 accumulation).
+__device__ __forceinline__ float frag_sum(const Frag<bf16>& f) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2 x = {f.v[2 * k], f.v[2 * k + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(x, one, s, false);
+  }
+  return s;
+}
+__device__ __forceinline__ float frag_sum(const Frag<float>& f) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += f.v[e];
+  return s;
+}
+
 // Copy rows [row0, row0+ROWS) of a [T][D] global matrix into a padded LDS tile (row stride LDP
 // elements); rows >= T are filled with zeros.  All NT threads of the block take part.
 template <typename TI, int D, int ROWS, int LDP, int NT>

@@ -2,20 +2,23 @@
 // launch grid.
 //
 // [Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记".
-//   ordinary head: O = softmax_causal(s Q K^T) V                                   [Notes §一]
-//   replaced head: O = P V with P(i,j) = exp(a[j] + r[i-j]) / Z(i) on j <= i      [Notes §二.3, Eq.(3)]
+//   ordinary head: O = softmax_causal(s Q K^T) V                                  [Notes §一]
+//   replaced head: O = P V, P(i,j) = exp(a[j] + r[i-j]) / Z(i) on j <= i         [Notes §二.3, Eq.(3)]
 // The fused kernel the pages describe runs ordinary heads as online-softmax tiles and rebuilds the
-// fixed heads' causal tiles in registers from the two preference vectors before multiplying by the
-// current V ([Notes §二.4, Fig. 2]).  Here both head kinds share one grid and one key-tile loop:
-// a work item is one (batch, head, 128-query block); 4 waves own 32 queries each.
+// fixed heads' causal tiles in registers from the two preference vectors and Z before the product
+// with the current V ([Notes §二.4, Fig. 2]).  Here a work item is one (batch, head, 128-query
+// block); its 4 waves own 32 queries each and sweep the key tiles at or below the diagonal.  The
+// next key tile is loaded into registers while the current one is multiplied, then written to LDS.
 //
-// Per key tile (BK keys, staged to LDS):
-//   ordinary:  S^T = K Q^T on the matrix cores (lane = query, registers = keys), online softmax in
-//              base 2 with the running max / sum per lane, then O^T += V^T P^T on the matrix cores.
-//   replaced:  the logits a[j] + r[i-j] come from a / r windows in LDS (no Q, no K, no QK^T), then
-//              the same online normalisation and the same O^T += V^T P^T.
-// The online normalisation makes the row normaliser Z(i) a by-product (lse = log Z(i)), so a
-// replaced item needs no separate pass over a and r.
+//   ordinary: S^T = K Q^T on the matrix cores (lane = query, registers = keys); base-2 online
+//             softmax with a lazily updated running maximum (the accumulator is rescaled only when
+//             the tile maximum exceeds the running one by more than 2^8); O^T += V^T P^T, where
+//             V^T fragments come from the row-major V tile through transposing LDS reads.
+//   replaced: no Q, no K, no QK^T and no softmax: each entry is ea[j] * er[i-j] (one multiply)
+//             from LDS windows of the prepared pattern, the row is scaled by 1/Z'(i) at the end;
+//             where the prepared pattern flags the product form as inaccurate, the entry is
+//             exp(a[j] + r[i-j] - log Z(i)) instead.  Windows hold 0 (or -inf) at future and
+//             out-of-range positions, so no per-entry mask is evaluated.
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -27,154 +30,209 @@ constexpr int kNT = 256;  // threads per block (4 waves)
 
 template <typename TI, int D>
 struct FwdCfg {
-  static constexpr int BK = sizeof(TI) == 2 ? 64 : 32;  // keys per staged tile
-  static constexpr int NS = BK / 32;                    // 32-key subtiles per tile
-  static constexpr int LDP = D + 16 / (int)sizeof(TI);  // padded LDS row (elements)
+  static constexpr bool BF = sizeof(TI) == 2;
+  static constexpr int BK = BF ? 64 : 32;                // keys per staged tile
+  static constexpr int NS = BK / 32;                     // 32-key subtiles per tile
+  static constexpr int LDP = D + 16 / (int)sizeof(TI);   // padded LDS row (elements)
+  static constexpr int EPC = 16 / (int)sizeof(TI);       // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                    // chunks per row
+  static constexpr int CPT = BK * CPR / kNT;             // chunks per thread per tile
+  static constexpr int WIN = BK + kBQ;                   // distance window
 };
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kNT) void mixed_fwd_kernel(LayerArgs p) {
+struct Prefetch {
+  uint4 k[FwdCfg<TI, D>::CPT];
+  uint4 v[FwdCfg<TI, D>::CPT];
+  float aw, rw;
+};
+
+template <typename TI, int D>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void mixed_fwd_kernel(LayerArgs p) {
   using C = FwdCfg<TI, D>;
-  constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP;
+  constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP, EPC = C::EPC, CPR = C::CPR, CPT = C::CPT;
+  constexpr int WIN = C::WIN;
   __shared__ __attribute__((aligned(16))) TI Ks[BK * LDP];
   __shared__ __attribute__((aligned(16))) TI Vs[BK * LDP];
-  __shared__ float as2[BK];             // a[key] * log2(e) for the tile's keys
-  __shared__ float rs2[BK + kBQ];       // r[delta] * log2(e) for the tile's distance window
+  __shared__ __attribute__((aligned(16))) float awin[BK];  // ea (or a*log2e) of the tile's keys
+  __shared__ float rwin[WIN];                              // er (or r*log2e) of its distances
 
   const int T = p.T, H = p.H;
   const int BH = p.B * H;
-  const int BHp = (BH + 7) & ~7;        // pad so that x % 8 (the XCD) depends on (b, h) only
+  const int BHp = (BH + 7) & ~7;  // pad so that blockIdx % 8 (the XCD) depends on (b, h) only
   const int nqb = (T + kBQ - 1) / kBQ;
   const int x = blockIdx.x;
   const int bh = x % BHp;
   if (bh >= BH) return;
-  const int qb = nqb - 1 - x / BHp;     // heaviest query blocks first
+  const int qb = nqb - 1 - x / BHp;  // heaviest query blocks first
   const int b = bh / H, h = bh % H;
   const bool rep = is_replaced(p.rep, h);
+  const bool fact = rep && p.pat.flag(h)[0] != 0;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int q0 = qb * kBQ;
-  const int qw = q0 + w * 32;           // the wave's first query
-  const int qi = qw + l32;              // the lane's query
+  const int qw = q0 + w * 32;  // the wave's first query
+  const int qi = qw + l32;     // the lane's query
   const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
   const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
   const TI* K = reinterpret_cast<const TI*>(p.k) + hoff;
   const TI* V = reinterpret_cast<const TI*>(p.v) + hoff;
-  const float* arow = p.a + (size_t)h * p.pat_len;
-  const float* rrow = p.r + (size_t)h * p.pat_len;
+  const float* arow = rep ? (fact ? p.pat.ea(h) : p.a + (size_t)h * p.pat_len) : nullptr;
+  const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
+  const float wscale = fact ? 1.f : kLog2e;            // window values: ea/er, or a, r in log2 units
+  const float wfill = fact ? 0.f : -INFINITY;          // weight-zero filler
 
   const int kend = min(T, q0 + kBQ);
   const int nkt = (kend + BK - 1) / BK;
 
+  // ---- staging: global -> registers (next tile) -> LDS
+  Prefetch<TI, D> pf;
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * kNT;
+      const int row = idx / CPR, cc = idx % CPR;
+      const int g = k0 + row;
+      const size_t off = (size_t)g * D + cc * EPC;
+      pf.v[c] = g < T ? *reinterpret_cast<const uint4*>(V + off) : make_uint4(0u, 0u, 0u, 0u);
+      if (!rep) pf.k[c] = g < T ? *reinterpret_cast<const uint4*>(K + off) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (rep) {
+      const int d0 = q0 - k0 - (BK - 1);
+      if (tid < BK) pf.aw = (k0 + tid < T) ? arow[k0 + tid] * wscale : wfill;
+      if (tid < WIN) {
+        const int dist = d0 + tid;
+        pf.rw = (dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * kNT;
+      const int row = idx / CPR, cc = idx % CPR;
+      *reinterpret_cast<uint4*>(Vs + row * LDP + cc * EPC) = pf.v[c];
+      if (!rep) *reinterpret_cast<uint4*>(Ks + row * LDP + cc * EPC) = pf.k[c];
+    }
+    if (rep) {
+      if (tid < BK) awin[tid] = pf.aw;
+      if (tid < WIN) rwin[tid] = pf.rw;
+    }
+  };
+
   Frag<TI> qf[D / 16];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    if (!rep && qi < T)
-      qf[t] = load8(Q + (size_t)qi * D + 16 * t + 8 * hi);
-    else
-      qf[t] = zero_frag<TI>();
-  }
+  for (int t = 0; t < D / 16; ++t)
+    qf[t] = (!rep && qi < T) ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+  const float lz_q = (rep && qi < T) ? p.pat.lz(h)[qi] : 0.f;
+  const float lz2_q = lz_q * kLog2e;
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) zero(oacc[c]);
   float m = -INFINITY, l = 0.f;
+  const float c2 = p.scale_log2;
+
+  load_tile(0);
+  store_tile();
+  __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BK;
-    const int d0 = q0 - k0 - (BK - 1);  // smallest distance in the tile's window
-    __syncthreads();
-    stage_rows<TI, D, BK, LDP, kNT>(Vs, V, k0, T, tid);
-    if (!rep) {
-      stage_rows<TI, D, BK, LDP, kNT>(Ks, K, k0, T, tid);
-    } else {
-      for (int j = tid; j < BK; j += kNT)
-        as2[j] = (k0 + j < T) ? arow[k0 + j] * kLog2e : -INFINITY;
-      for (int j = tid; j < BK + kBQ; j += kNT) {
-        const int dist = d0 + j;
-        rs2[j] = (dist >= 0 && dist < T) ? rrow[dist] * kLog2e : -INFINITY;
-      }
-    }
-    __syncthreads();
+    if (kt + 1 < nkt) load_tile(k0 + BK);
 
-    if (k0 > qw + 31) continue;  // whole tile above this wave's diagonal (wave-uniform)
-
-    float pv[NS][16];
-    bool act[NS];
-    float tmax = -INFINITY;
+    // 32-key subtiles visible to this wave, one at a time: scores -> probabilities -> O^T += V^T P^T
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
-      act[s] = ks <= qw + 31 && ks < T;
-      if (!act[s]) continue;
+      if (ks > qw + 31 || ks >= T) break;  // wave-uniform: the rest of the tile is masked out
+      float pv[16];
       if (!rep) {
         f32x16 st;
         zero(st);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const Frag<TI> kf = load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi);
-          mma16(st, kf, qf[t]);
+        for (int t = 0; t < D / 16; ++t)
+          mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
+        float tmax = -INFINITY;
+        if ((ks + 31 > qw) || (ks + 31 >= T)) {  // subtile crosses the diagonal or the end
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = ks + crow(r, hi);
+            pv[r] = (key <= qi && key < T) ? st[r] : -INFINITY;
+            tmax = fmaxf(tmax, pv[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pv[r] = st[r];
+            tmax = fmaxf(tmax, st[r]);
+          }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c2;
+        // lazy maximum: keep the running one while the subtile stays within 2^8 of it
+        const float mnew = (tmax > m + 8.f) ? tmax : m;
+        if (__any(mnew != m)) {
+          const float alpha = exp2f(m - mnew);
+          l *= alpha;
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
+          m = mnew;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ks + crow(r, hi);
-          const float v = (key <= qi && key < T) ? st[r] * p.scale_log2 : -INFINITY;
-          pv[s][r] = v;
-          tmax = fmaxf(tmax, v);
+        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(pv[r], c2, -m));
+      } else if (fact) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int kk = 32 * s + 8 * g + 4 * hi;      // tile-relative first key of the run
+          const float4 a4 = *reinterpret_cast<const float4*>(awin + kk);
+          const int xr = (qi - q0) + (BK - 1) - kk;    // window index of distance qi - key
+          pv[4 * g + 0] = a4.x * rwin[xr];
+          pv[4 * g + 1] = a4.y * rwin[xr - 1];
+          pv[4 * g + 2] = a4.z * rwin[xr - 2];
+          pv[4 * g + 3] = a4.w * rwin[xr - 3];
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = ks + crow(r, hi);
-          float v = -INFINITY;
-          if (key <= qi && key < T) v = as2[key - k0] + rs2[qi - key - d0];
-          pv[s][r] = v;
-          tmax = fmaxf(tmax, v);
+        for (int g = 0; g < 4; ++g) {
+          const int kk = 32 * s + 8 * g + 4 * hi;
+          const float4 a4 = *reinterpret_cast<const float4*>(awin + kk);
+          const int xr = (qi - q0) + (BK - 1) - kk;
+          pv[4 * g + 0] = __builtin_amdgcn_exp2f(a4.x + rwin[xr] - lz2_q);
+          pv[4 * g + 1] = __builtin_amdgcn_exp2f(a4.y + rwin[xr - 1] - lz2_q);
+          pv[4 * g + 2] = __builtin_amdgcn_exp2f(a4.z + rwin[xr - 2] - lz2_q);
+          pv[4 * g + 3] = __builtin_amdgcn_exp2f(a4.w + rwin[xr - 3] - lz2_q);
         }
       }
-    }
-    // online normalisation in base 2 (both halves of the wave hold the same queries)
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mnew);
-    float lsum = 0.f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (!act[s]) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = (pv[s][r] == -INFINITY) ? 0.f : exp2f(pv[s][r] - mnew);
-        pv[s][r] = e;
-        lsum += e;
-      }
-    }
-    l = l * alpha + lsum;
-    m = mnew;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
-
-    // O^T[dcol][query] += V^T[dcol][key] P^T[key][query]
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (!act[s]) continue;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const Frag<TI> pf = to_frag<TI>(&pv[s][8 * u]);
+        const Frag<TI> pfr = to_frag<TI>(&pv[8 * u]);
+        if (!rep) l += frag_sum(pfr);
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          const Frag<TI> vf = gather_col<TI, LDP>(Vs, 32 * s + 16 * u, 32 * c + l32, hi);
-          mma16(oacc[c], vf, pf);
-        }
+        for (int c = 0; c < D / 32; ++c)
+          mma16(oacc[c], col_frag<TI, LDP>(Vs, 32 * s + 16 * u, 32 * c, lane), pfr);
       }
+    }
+
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      store_tile();
+      __syncthreads();
     }
   }
 
-  if (qi >= T) return;
   const float lt = l + __shfl_xor(l, 32);
-  const float inv = 1.f / lt;
+  if (qi >= T) return;
+  float inv, lse;
+  if (!rep) {
+    inv = 1.f / lt;
+    lse = (m + log2f(lt)) * kLn2;
+  } else {
+    inv = fact ? p.pat.invz(h)[qi] : 1.f;
+    lse = lz_q;
+  }
   TI* O = reinterpret_cast<TI*>(p.out) + hoff + (size_t)qi * D;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
@@ -184,7 +242,7 @@ __global__ __launch_bounds__(kNT) void mixed_fwd_kernel(LayerArgs p) {
       store4(O + dc, oacc[c][4 * g] * inv, oacc[c][4 * g + 1] * inv, oacc[c][4 * g + 2] * inv,
              oacc[c][4 * g + 3] * inv);
     }
-  if (hi == 0) p.lse[((size_t)b * H + h) * T + qi] = (m + log2f(lt)) * kLn2;
+  if (hi == 0) p.lse[((size_t)b * H + h) * T + qi] = lse;
 }
 
 template <typename TI, int D>

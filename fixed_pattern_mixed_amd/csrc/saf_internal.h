@@ -9,6 +9,30 @@ namespace saf {
 
 constexpr int kMaxHeads = 256;
 
+// Prepared fixed pattern of the replaced heads (the compact form of Eq. (3): alpha, rho and the
+// input-independent row normaliser Z).  For head h, with P the prepared length and
+// Ma = max a, Mr = max r over [0, P):
+//   ea[k]   = exp(a[k] - Ma),   er[k] = exp(r[k] - Mr)            (fp32, k < P)
+//   invz[i] = 1 / Z'(i),        Z'(i) = sum_{k<=i} ea[k] er[i-k]  (accumulated in fp64)
+//   lz[i]   = log Z(i) = log Z'(i) + Ma + Mr                      (natural log)
+//   meta[0] = 1 if the factorised product ea[j] er[i-j] / Z'(i) is accurate for every row (no row
+//             normaliser below 2^-60, so every product that matters is a normal float), else 0;
+//             with 0 the kernels use exp(a[j] + r[i-j] - lz[i]) instead, and lz is formed with a
+//             per-row maximum.
+// Slots of ordinary heads are left untouched.
+struct PatternView {
+  float* base;
+  int P;              // prepared length
+  int stride;         // floats per head
+  __host__ __device__ float* ea(int h) const { return base + (size_t)h * stride; }
+  __host__ __device__ float* er(int h) const { return ea(h) + P; }
+  __host__ __device__ float* invz(int h) const { return ea(h) + 2 * (size_t)P; }
+  __host__ __device__ float* lz(int h) const { return ea(h) + 3 * (size_t)P; }
+  __host__ __device__ int* flag(int h) const { return reinterpret_cast<int*>(ea(h) + 4 * (size_t)P); }
+};
+
+__host__ __device__ inline int pattern_stride(int P) { return ((4 * P + 64) + 63) / 64 * 64; }
+
 // Per-call description of the mixed layer, passed to kernels by value.
 struct LayerArgs {
   int B, H, T, d;
@@ -24,7 +48,7 @@ struct LayerArgs {
   const float* a;    // [H][pat_len]
   const float* r;    // [H][pat_len]
   float* lse;        // [B][H][T] natural-log row normalisers (forward writes, backward reads)
-  float* lz2;        // [H][T] workspace: log2 Z(i) of replaced heads
+  PatternView pat;   // prepared pattern of the replaced heads
   float* delta;      // [B][H][T] workspace: rowsum(dO * O) of ordinary heads
   void* out;         // forward: o
   void* dq;
@@ -46,6 +70,7 @@ struct CalibArgs {
 
 // Each launcher enqueues its kernels on `stream` and returns the first HIP error (hipSuccess if
 // none).  Shapes were validated by the caller.
+hipError_t launch_pattern_prepare(const LayerArgs& a, hipStream_t s);
 hipError_t launch_mixed_fwd(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);

@@ -72,17 +72,34 @@ size_t saf_attn_bwd_workspace_size(int B, int H, int T, int d);
 size_t saf_calibrate_workspace_size(int N, int H, int T, int d);
 
 /*
+ * Prepared fixed pattern (optional).                            [Notes §二.3, Eq.(3); §二.4]
+ * The replaced heads' pattern is stored as a and r plus the row normaliser Z(i), which does not
+ * depend on the input, so it can be formed once when a pattern is installed instead of on every
+ * call.  saf_pattern_prepare fills `pattern` (device memory of saf_pattern_size(H, pat_len)
+ * bytes, 256-byte aligned, caller-owned) for every position < pat_len of the replaced heads'
+ * rows of a and r ([H][pat_len] fp32 device).  The result may be passed to saf_attn_fwd and
+ * saf_attn_bwd with the same replaced mask, a, r and pat_len, for any T <= pat_len; it must not be
+ * modified while such calls are in flight.  Errors as below; nothing is enqueued on error.
+ */
+size_t saf_pattern_size(int H, int pat_len);
+saf_status saf_pattern_prepare(int H, const uint8_t* replaced, const float* a, const float* r,
+                               int pat_len, void* pattern, size_t pattern_bytes,
+                               hipStream_t stream);
+
+/*
  * Forward of the mixed layer.                                  [Notes §二.4, Fig. 2; Eq.(3)]
  *   q, k, v : [B][H][T][d] dt     o : [B][H][T][d] dt (written)
  *   lse     : [B][H][T] fp32 (written): for an ordinary head the natural-log logsumexp of the
  *             scaled causal scores of row i; for a replaced head log Z(i) (the same for every b).
  *             The backward pass reads it back.
  *   replaced: [H] host bytes;  a, r : [H][pat_len] fp32 device, pat_len >= T.
+ *   pattern : NULL, or a pattern prepared by saf_pattern_prepare for (H, replaced, a, r, pat_len);
+ *             with NULL the call prepares what it needs in its workspace (for length T).
  */
 saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
                         const void* v, const uint8_t* replaced, const float* a, const float* r,
-                        int pat_len, float scale, void* o, float* lse, void* ws, size_t ws_bytes,
-                        hipStream_t stream);
+                        int pat_len, const void* pattern, float scale, void* o, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward of the mixed layer, given dout = dL/dO and the forward's o and lse.   [Notes §二.4]
@@ -90,12 +107,13 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
  *   replaced head: dv = P^T dout, and dq = dk = 0 (written as zeros).  No gradient for a or r.
  *   q, k, v, o, dout : [B][H][T][d] dt;   lse : [B][H][T] fp32 as written by saf_attn_fwd for
  *   the same q, k, v, replaced, a, r, scale;   dq, dk, dv : [B][H][T][d] dt (written).
+ *   pattern : as for saf_attn_fwd (NULL or prepared).
  */
 saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
                         const void* v, const void* o, const void* dout, const float* lse,
                         const uint8_t* replaced, const float* a, const float* r, int pat_len,
-                        float scale, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                        hipStream_t stream);
+                        const void* pattern, float scale, void* dq, void* dk, void* dv, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 /*
  * Calibration statistics over N sequences.                       [Notes §二.1, Eq.(1)]

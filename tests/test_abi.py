@@ -30,8 +30,10 @@ def test_exports_every_declared_symbol():
 
 
 def test_workspace_sizes():
-    assert saf.saf_attn_fwd_workspace_size(8, 12, 4096, 64) == 0
-    assert saf.saf_attn_bwd_workspace_size(8, 12, 4096, 64) == 8 * 12 * 4096 * 4
+    pat = saf.saf_pattern_size(12, 4096)
+    assert pat >= 12 * 4 * 4096 * 4
+    assert saf.saf_attn_fwd_workspace_size(8, 12, 4096, 64) == pat
+    assert saf.saf_attn_bwd_workspace_size(8, 12, 4096, 64) == pat + 8 * 12 * 4096 * 4
     assert saf.saf_attn_bwd_workspace_size(0, 12, 4096, 64) == 0
     n = saf.saf_calibrate_workspace_size(32, 16, 8192, 128)
     assert n >= 32 * 16 * 8192 * 4 + 16 * 64 * 128 * 8
@@ -44,16 +46,17 @@ def _mask(*bits):
 
 
 def fwd(dt=1, B=2, H=4, T=64, d=64, q=FAKE, k=FAKE, v=FAKE, rep=None, a=FAKE, r=FAKE, pat=64,
-        scale=0.0, o=FAKE, lse=FAKE):
+        scale=0.0, o=FAKE, lse=FAKE, ws=FAKE, ws_n=0):
     rep = _mask(0, 0, 0, 1) if rep is None else rep
-    return saf.saf_attn_fwd(dt, B, H, T, d, q, k, v, rep, a, r, pat, scale, o, lse, None, 0, None)
+    return saf.saf_attn_fwd(dt, B, H, T, d, q, k, v, rep, a, r, pat, None, scale, o, lse, ws, ws_n,
+                            None)
 
 
 def bwd(dt=1, B=2, H=4, T=64, d=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE, g=FAKE, lse=FAKE, rep=None,
         a=FAKE, r=FAKE, pat=64, scale=0.0, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, ws_n=0):
     rep = _mask(0, 0, 0, 1) if rep is None else rep
-    return saf.saf_attn_bwd(dt, B, H, T, d, q, k, v, o, g, lse, rep, a, r, pat, scale, dq, dk, dv,
-                            ws, ws_n, None)
+    return saf.saf_attn_bwd(dt, B, H, T, d, q, k, v, o, g, lse, rep, a, r, pat, None, scale, dq,
+                            dk, dv, ws, ws_n, None)
 
 
 @pytest.mark.parametrize("case,kw,status", [
@@ -69,7 +72,9 @@ def bwd(dt=1, B=2, H=4, T=64, d=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE, g=FAKE, lse=
     ("null a with a replaced head", dict(a=None), saf.SAF_ERR_INVALID_ARG),
     ("pattern shorter than T", dict(pat=63), saf.SAF_ERR_INVALID_ARG),
     ("null lse", dict(lse=None), saf.SAF_ERR_INVALID_ARG),
-    ("NaN scale", dict(scale=float("nan"), pat=64, lse=None), saf.SAF_ERR_INVALID_ARG),
+    ("NaN scale", dict(scale=float("nan"), ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+    ("short workspace for the pattern", dict(ws_n=100), saf.SAF_ERR_INVALID_ARG),
+    ("null workspace for the pattern", dict(ws=None, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
 ])
 def test_forward_rejects(case, kw, status):
     assert fwd(**kw) == status, saf.saf_last_error()
@@ -114,6 +119,23 @@ def test_backward_rejects(case, kw, status):
 def test_calibrate_rejects(case, dt, N, H, T, d, status):
     st = saf.saf_calibrate(dt, N, H, T, d, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == status, saf.saf_last_error()
+
+
+@pytest.mark.parametrize("case,H,P,a,pat,n,status", [
+    ("no heads", 0, 64, FAKE, FAKE, 1 << 20, saf.SAF_ERR_INVALID_ARG),
+    ("too many heads", 300, 64, FAKE, FAKE, 1 << 20, saf.SAF_ERR_UNSUPPORTED),
+    ("null a", 4, 64, None, FAKE, 1 << 20, saf.SAF_ERR_INVALID_ARG),
+    ("null buffer", 4, 64, FAKE, None, 1 << 20, saf.SAF_ERR_INVALID_ARG),
+    ("misaligned buffer", 4, 64, FAKE, FAKE + 64, 1 << 20, saf.SAF_ERR_INVALID_ARG),
+    ("short buffer", 4, 64, FAKE, FAKE, 64, saf.SAF_ERR_INVALID_ARG),
+])
+def test_pattern_prepare_rejects(case, H, P, a, pat, n, status):
+    rep = _mask(*([0, 0, 0, 1] * 75)[:max(H, 1)])
+    assert saf.saf_pattern_prepare(H, rep, a, FAKE, P, pat, n, None) == status, saf.saf_last_error()
+
+
+def test_pattern_prepare_without_replaced_heads_is_noop():
+    assert saf.saf_pattern_prepare(4, _mask(0, 0, 0, 0), None, None, 64, None, 0, None) == saf.SAF_OK
 
 
 def test_calibrate_short_workspace():

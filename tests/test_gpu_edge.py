@@ -102,3 +102,59 @@ def test_empty_batch_is_noop():
     g = synth.layer_inputs(0, 4, 64, 64, torch.bfloat16, [0, 0, 0, 1], seed=1, device="cuda")
     o, lse = saf.fwd(g.q, g.k, g.v, [0, 0, 0, 1], g.a, g.r)
     assert o.shape == (0, 4, 64, 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prepared_pattern_matches_call_prepared(dtype):
+    saf = _saf()
+    B, H, T, d = 2, 4, 300, 64
+    rep = synth.replaced_mask(H, 2)
+    g = synth.layer_inputs(B, H, T, d, dtype, rep, seed=12, device="cuda")
+    pat = saf.prepare_pattern(rep, g.a, g.r)
+    o1, l1 = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    o2, l2 = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)
+    d1 = saf.bwd(g.q, g.k, g.v, o1, g.dout, l1, rep, g.a, g.r)
+    d2 = saf.bwd(g.q, g.k, g.v, o2, g.dout, l2, rep, g.a, g.r, pattern=pat)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for x, y in zip(d1, d2):
+        assert torch.equal(x, y)
+
+
+def test_pattern_prepared_longer_than_input():
+    """A pattern prepared at its fitted length serves a shorter input (row i only sees <= i)."""
+    saf = _saf()
+    B, H, T, d, P = 1, 4, 100, 64, 333
+    rep = synth.replaced_mask(H, 2)
+    x = synth.layer_inputs(B, H, T, d, torch.float32, rep, seed=13, pat_len=P)
+    g = synth.layer_inputs(B, H, T, d, torch.float32, rep, seed=13, device="cuda", pat_len=P)
+    pat = saf.prepare_pattern(rep, g.a, g.r)
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)
+    dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, pattern=pat)
+    torch.cuda.synchronize()
+    heads = [(0, h) for h in range(H)]
+    check_fwd(x, o, lse, heads, None, TOL[torch.float32], "prefix")
+    check_bwd(x, dq, dk, dv, heads, None, None, TOL[torch.float32], "prefix")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_wide_range_pattern_uses_exponential_form(dtype):
+    """A pattern whose factorised weights would underflow (one key preferred by 200 nats, so
+    exp(a - max a) is 0 in fp32 for every other key) must still match the oracle: the kernels
+    switch to exp(a[j] + r[i-j] - log Z(i)) for such a head."""
+    saf = _saf()
+    B, H, T, d = 1, 4, 257, 64
+    rep = [0, 1, 0, 1]
+    x = synth.layer_inputs(B, H, T, d, dtype, rep, ar_std=1.0, seed=14)
+    x.a[1, T - 1] = 200.0
+    x.a[3, 5] = 150.0
+    x.r[3, 7] = -300.0
+    g = synth.layer_inputs(B, H, T, d, dtype, rep, ar_std=1.0, seed=14, device="cuda")
+    g.a.copy_(x.a)
+    g.r.copy_(x.r)
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
+    torch.cuda.synchronize()
+    heads = [(0, h) for h in range(H)]
+    check_fwd(x, o, lse, heads, None, TOL[dtype], "wide")
+    check_bwd(x, dq, dk, dv, heads, None, None, TOL[dtype], "wide")
