@@ -14,11 +14,11 @@
 //             softmax with a lazily updated running maximum (the accumulator is rescaled only when
 //             the tile maximum exceeds the running one by more than 2^8); O^T += V^T P^T, where
 //             V^T fragments come from the row-major V tile through transposing LDS reads.
-//   replaced: no Q, no K, no QK^T and no softmax: each entry is ea[j] * er[i-j] (one multiply)
-//             from LDS windows of the prepared pattern, the row is scaled by 1/Z'(i) at the end;
-//             where the prepared pattern flags the product form as inaccurate, the entry is
-//             exp(a[j] + r[i-j] - log Z(i)) instead.  Windows hold 0 (or -inf) at future and
-//             out-of-range positions, so no per-entry mask is evaluated.
+//   replaced: no Q, no K, no QK^T and no running maximum: each entry is ea[j] * er[i-j] (one
+//             multiply) from LDS windows of the prepared pattern, and the row is divided by the sum
+//             of its entries at the end; where the prepared pattern flags the product form as
+//             inaccurate, the entry is exp(a[j] + r[i-j] - log Z(i)) instead.  Windows hold 0 (or
+//             -inf) at future and out-of-range positions, so no per-entry mask is evaluated.
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
     qf[t] = (!rep && qi < T) ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
-  const float lz_q = (rep && qi < T) ? p.pat.lz(h)[qi] : 0.f;
+  const float lz_q = (rep && !fact && qi < T) ? p.pat.lz(h)[qi] : 0.f;
   const float lz2_q = lz_q * kLog2e;
 
   f32x16 oacc[D / 32];
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const Frag<TI> pfr = to_frag<TI>(&pv[8 * u]);
-        if (!rep) l += frag_sum(pfr);
+        l += frag_sum(pfr);
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
           mma16(oacc[c], col_frag<TI, LDP>(Vs, 32 * s + 16 * u, 32 * c, lane), pfr);
@@ -223,16 +223,13 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
     }
   }
 
+  // Row normaliser: the sum of the probabilities exactly as they entered the product (after the
+  // operand rounding), so that every row's weights sum to one.  Replaced rows: l ~ Z'(i) (product
+  // form, lse = log l + max a + max r) or l ~ 1 (exponential form, lse = log Z(i) + log l).
   const float lt = l + __shfl_xor(l, 32);
   if (qi >= T) return;
-  float inv, lse;
-  if (!rep) {
-    inv = 1.f / lt;
-    lse = (m + log2f(lt)) * kLn2;
-  } else {
-    inv = fact ? p.pat.invz(h)[qi] : 1.f;
-    lse = lz_q;
-  }
+  const float inv = 1.f / lt;
+  const float lse = !rep ? (m + log2f(lt)) * kLn2 : (fact ? p.pat.shift(h) : lz_q) + logf(lt);
   TI* O = reinterpret_cast<TI*>(p.out) + hoff + (size_t)qi * D;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)

@@ -10,15 +10,14 @@ namespace saf {
 constexpr int kMaxHeads = 256;
 
 // Prepared fixed pattern of the replaced heads (the compact form of Eq. (3): alpha, rho and the
-// input-independent row normaliser Z).  For head h, with P the prepared length and
+// input-independent row normaliser).  For head h, with P the prepared length and
 // Ma = max a, Mr = max r over [0, P):
-//   ea[k]   = exp(a[k] - Ma),   er[k] = exp(r[k] - Mr)            (fp32, k < P)
-//   invz[i] = 1 / Z'(i),        Z'(i) = sum_{k<=i} ea[k] er[i-k]  (accumulated in fp64)
-//   lz[i]   = log Z(i) = log Z'(i) + Ma + Mr                      (natural log)
-//   meta[0] = 1 if the factorised product ea[j] er[i-j] / Z'(i) is accurate for every row (no row
-//             normaliser below 2^-60, so every product that matters is a normal float), else 0;
-//             with 0 the kernels use exp(a[j] + r[i-j] - lz[i]) instead, and lz is formed with a
-//             per-row maximum.
+//   ea[k]  = exp(a[k] - Ma),   er[k] = exp(r[k] - Mr)              (fp32, k < P)
+//   lz[i]  = log Z(i)  (natural log; formed with a per-row maximum, used by the exponential form)
+//   meta   = { flag, shift = Ma + Mr }
+// flag = 1 if the factorised entries ea[j] er[i-j] are accurate for every row: Z'(i) =
+// sum_{k<=i} ea[k] er[i-k] >= 2^-60 for all i (accumulated in fp64), so every product that
+// carries weight is a normal fp32 number.  With flag = 0 the kernels use exp(a[j] + r[i-j] - lz[i]).
 // Slots of ordinary heads are left untouched.
 struct PatternView {
   float* base;
@@ -26,12 +25,12 @@ struct PatternView {
   int stride;         // floats per head
   __host__ __device__ float* ea(int h) const { return base + (size_t)h * stride; }
   __host__ __device__ float* er(int h) const { return ea(h) + P; }
-  __host__ __device__ float* invz(int h) const { return ea(h) + 2 * (size_t)P; }
-  __host__ __device__ float* lz(int h) const { return ea(h) + 3 * (size_t)P; }
-  __host__ __device__ int* flag(int h) const { return reinterpret_cast<int*>(ea(h) + 4 * (size_t)P); }
+  __host__ __device__ float* lz(int h) const { return ea(h) + 2 * (size_t)P; }
+  __host__ __device__ int* flag(int h) const { return reinterpret_cast<int*>(ea(h) + 3 * (size_t)P); }
+  __device__ float shift(int h) const { return reinterpret_cast<const float*>(flag(h))[1]; }
 };
 
-__host__ __device__ inline int pattern_stride(int P) { return ((4 * P + 64) + 63) / 64 * 64; }
+__host__ __device__ inline int pattern_stride(int P) { return ((3 * P + 64) + 63) / 64 * 64; }
 
 // Per-call description of the mixed layer, passed to kernels by value.
 struct LayerArgs {
@@ -50,6 +49,7 @@ struct LayerArgs {
   float* lse;        // [B][H][T] natural-log row normalisers (forward writes, backward reads)
   PatternView pat;   // prepared pattern of the replaced heads
   float* delta;      // [B][H][T] workspace: rowsum(dO * O) of ordinary heads
+  float* dqacc;      // [B][H][T][d] workspace: fp32 dQ accumulator of ordinary heads
   void* out;         // forward: o
   void* dq;
   void* dk;
@@ -73,8 +73,8 @@ struct CalibArgs {
 hipError_t launch_pattern_prepare(const LayerArgs& a, hipStream_t s);
 hipError_t launch_mixed_fwd(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_bwd_q(const LayerArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_main(const LayerArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_dq_finalize(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_lse(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_stats(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s);

@@ -8,13 +8,15 @@
 //   exp(a[j] + r[i-j] - log Z(i)) = ea[j] * er[i-j] / Z'(i),
 //   ea = exp(a - max a),  er = exp(r - max r),  Z'(i) = sum_{k<=i} ea[k] er[i-k],
 // which is the same quantity (the factors exp(max a) and exp(max r) cancel) and lets the tile
-// kernels rebuild a pattern entry with one multiply instead of an exponential.  Z' is accumulated
-// in fp64 over the fp32 products that the tile kernels use.
+// kernels rebuild a pattern entry with one multiply instead of an exponential.  The tile kernels
+// normalise each row by the sum of its entries as they entered the matrix product; Z' is formed
+// here, in fp64 over the same fp32 products, only to decide whether the product form is accurate.
 //
 //   pattern_exp   : per replaced head, max a / max r, then ea and er.
-//   pattern_z     : per (256-row block, replaced head): Z'(i) -> 1/Z'(i), log Z(i), and the
-//                   accuracy flag (cleared if some Z'(i) < 2^-60).
-//   pattern_lz    : only for a head whose flag was cleared: log Z(i) from a per-row maximum.
+//   pattern_z     : per (256-row block, replaced head): Z'(i) and the accuracy flag (cleared if
+//                   some Z'(i) < 2^-60).
+//   pattern_lz    : log Z(i) from a per-row maximum (the exponential form's normaliser); skipped
+//                   for heads whose flag is set.
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -89,13 +91,7 @@ __global__ __launch_bounds__(kNT) void pattern_z_kernel(LayerArgs p, HeadList hl
       for (int kk = 0; kk < kNT; ++kk) acc += (double)eas[kk] * (double)ers[base - kk];
     }
   }
-  if (i < P) {
-    int* meta = p.pat.flag(h);
-    const float shift = reinterpret_cast<const float*>(meta)[1];
-    p.pat.invz(h)[i] = (float)(1.0 / acc);
-    p.pat.lz(h)[i] = (float)(log(acc) + (double)shift);
-    if (!(acc >= 0x1p-60)) meta[0] = 0;
-  }
+  if (i < P && !(acc >= 0x1p-60)) p.pat.flag(h)[0] = 0;
 }
 
 // log Z(i) with a per-row maximum (only for heads whose factorised form is not accurate).

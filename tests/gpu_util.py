@@ -8,7 +8,10 @@ import torch
 import oracle
 
 TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
-TOL_LSE = 1e-4  # row statistics are fp32 in both paths
+# Row log-normalisers: fp32 arithmetic, but on the bf16 path the normaliser is the sum of the
+# probabilities after their rounding to bf16 (relative error <= 2^-9 per term, hence in the sum),
+# so |d lse| <= 2^-9 there.
+TOL_LSE = {torch.float32: 1e-4, torch.bfloat16: 2.0 ** -9}
 
 
 def cpu64(t):
@@ -64,7 +67,8 @@ def check_fwd(x, o, lse, heads, rows, tol, what=""):
         e = norm_err(cpu64(o[b, h].index_select(0, idx)), ro)
         el = norm_err(cpu64(lse[b, h].index_select(0, idx)), rl, floor=1.0)
         assert e <= tol, "%s o[b=%d,h=%d] normwise error %.3e > %.1e" % (what, b, h, e, tol)
-        assert el <= TOL_LSE, "%s lse[b=%d,h=%d] error %.3e" % (what, b, h, el)
+        tl = TOL_LSE[o.dtype]
+        assert el <= tl, "%s lse[b=%d,h=%d] error %.3e > %.1e" % (what, b, h, el, tl)
         worst = max(worst, e)
     return worst
 
