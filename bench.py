@@ -158,6 +158,9 @@ def main():
     ap.add_argument("--workload", default="l124m_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device-to-device copies of MIB MiB (calibrates the HBM "
+                         "byte counters of a profiler against a known size) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -168,6 +171,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+        return
 
     import fixed_pattern_mixed_amd as saf
     import synth

@@ -167,9 +167,15 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     }
     if (tid < BQ) {
       const int q = q0 + tid;
-      const float l = q < T ? lse[q] : 0.f;
-      // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse)
-      pf.rs = fact ? expf(shift - l) : l * kLog2e;
+      // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
+      // Rows past the end get weight 0 (their dO rows are zero, and an unbounded weight times a
+      // zero row would not be zero).
+      if (q < T) {
+        const float l = lse[q];
+        pf.rs = fact ? expf(shift - l) : l * kLog2e;
+      } else {
+        pf.rs = fact ? 0.f : INFINITY;
+      }
       pf.dl = (!rep && q < T) ? dlt[q] : 0.f;
     }
     if (rep && tid < WIN) {
