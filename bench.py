@@ -47,6 +47,25 @@ def kernel_flops(B, T, d, replaced):
     }
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter record
+    (profiles/hbm_traffic.json), or None if there is none or the kernel's source files changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload, {}).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for fn in rec["sources"]:
+        with open(os.path.join(ROOT, "fixed_pattern_mixed_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return rec["bytes"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def total_flops(B, T, d, replaced, backward):
     kf = kernel_flops(B, T, d, replaced)
     return kf["mixed_fwd"] + (kf["bwd_main"] if backward else 0.0)
@@ -208,7 +227,8 @@ def main():
     achieved = kf[dom] / (dom_ms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(w.name, dom)}
 
     out = {
         "metric": METRIC,
