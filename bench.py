@@ -3,7 +3,7 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input held in HBM: the
 mixed forward (ordinary and replaced heads in one grid) followed by the mixed backward (delta
-preprocess, the fused key-block kernel, dQ finalisation).  Forward-only workloads (prefill) time the
+preprocess, key-block kernel, query-block dQ kernel).  Forward-only workloads (prefill) time the
 forward alone.  Prints ONE JSON line.
 
 The default workload is the 124M-shaped layer of the pages' main update benchmark: B=8, H=12
@@ -41,9 +41,9 @@ def kernel_flops(B, T, d, replaced):
     n_ord = len(replaced) - n_rep
     return {
         "mixed_fwd": B * c * (n_ord * 4 * d + n_rep * 2 * d),    # S, PV (ordinary); PV (replaced)
-        "bwd_main": B * c * (n_ord * 10 * d + n_rep * 2 * d),    # S, dP, dV, dK, dQ; dV
+        "bwd_kv": B * c * (n_ord * 8 * d + n_rep * 2 * d),      # S, dP, dV, dK; dV (replaced)
+        "bwd_dq": B * c * (n_ord * 2 * d),                   # dQ (S, dP re-formed: not counted)
         "bwd_pre": 0.0,
-        "dq_finalize": 0.0,
     }
 
 
@@ -68,7 +68,7 @@ def measured_traffic(workload, kernel):
 
 def total_flops(B, T, d, replaced, backward):
     kf = kernel_flops(B, T, d, replaced)
-    return kf["mixed_fwd"] + (kf["bwd_main"] if backward else 0.0)
+    return kf["mixed_fwd"] + (kf["bwd_kv"] + kf["bwd_dq"] if backward else 0.0)
 
 
 class Layer:

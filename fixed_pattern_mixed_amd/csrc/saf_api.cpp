@@ -115,9 +115,8 @@ size_t fwd_ws(int B, int H, int T, int d) {
   return pattern_bytes(H, T);  // the prepared pattern, when the caller passes none
 }
 size_t bwd_ws(int B, int H, int T, int d) {
-  // pattern, delta [B][H][T], fp32 dQ accumulator [B][H][T][d]
-  return pattern_bytes(H, T) + align_up(sizeof(float) * (size_t)B * H * T) +
-         align_up(sizeof(float) * (size_t)B * H * T * d);
+  (void)d;
+  return pattern_bytes(H, T) + align_up(sizeof(float) * (size_t)B * H * T);  // pattern, delta
 }
 
 // Point la.pat at the caller's prepared pattern, or prepare one for length T at ws.
@@ -306,17 +305,17 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
   la.a = a; la.r = r;
   la.lse = const_cast<float*>(lse);
   la.delta = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + pattern_bytes(H, T));
-  la.dqacc = reinterpret_cast<float*>(reinterpret_cast<char*>(la.delta) +
-                                      align_up(sizeof(float) * (size_t)B * H * T));
   la.dq = dq; la.dk = dk; la.dv = dv;
   if ((st = setup_pattern(la, any_rep, pattern, T, ws, stream, "pattern preparation")) != SAF_OK) return st;
   const bool bf = dt == SAF_BF16;
   hipError_t e = traced("bwd_pre", stream, [&] { return saf::launch_bwd_pre(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-  e = traced("bwd_main", stream, [&] { return saf::launch_bwd_main(la, bf, stream); });
+  e = traced("bwd_kv", stream, [&] { return saf::launch_bwd_kv(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward key-block launch");
-  e = traced("dq_finalize", stream, [&] { return saf::launch_dq_finalize(la, bf, stream); });
-  if (e != hipSuccess) return hip_fail(e, "backward dQ finalisation launch");
+  if (any_ord) {
+    e = traced("bwd_dq", stream, [&] { return saf::launch_bwd_dq(la, bf, stream); });
+    if (e != hipSuccess) return hip_fail(e, "backward query-block launch");
+  }
   return SAF_OK;
 }
 

@@ -12,24 +12,22 @@
 //             or exp(a[j] + r[i-j] - lse_i) where the prepared pattern flags that form.
 //
 // Kernels (one stream):
-//   bwd_pre      : delta_i = rowsum(dO o O) of ordinary heads, and zeroes their fp32 dQ
-//                  accumulator rows.
-//   bwd_main     : one work item per (batch, head, 128-key block), both head kinds in one grid,
-//                  heaviest blocks (lowest keys, most query tiles) first.  4 waves own 32 keys each
-//                  (lane = key) and sweep the 64-query tiles at or below the diagonal:
-//                    S = Q K^T, dP = dO V^T  (K, V fragments in registers, Q, dO rows from LDS),
-//                    dV^T += dO^T P, dK^T += Q^T dS  (Q^T, dO^T through transposing LDS reads),
-//                    dS -> LDS, then dQ_tile = dS K over the block's 128 keys (K block resident in
-//                    LDS), added into the fp32 accumulator with one coalesced atomic per element.
-//                  Replaced items form P from the prepared pattern and accumulate dV only.
-//   dq_finalize  : dQ = s * accumulator in the tensor's type; zeros for replaced heads.
-// Five matrix products per (query, key) entry of an ordinary head, one of a replaced head.  The
-// dQ sum order depends on the atomics' arrival order, so dQ may differ in its last bits from run
-// to run; dK and dV are accumulated in registers in a fixed order.
+//   bwd_pre : delta_i = rowsum(dO o O) of ordinary heads.
+//   bwd_kv  : one work item per (batch, head, 128-key block), both head kinds in one grid, heaviest
+//             (lowest) key blocks first.  4 waves own 32 keys each (lane = key) and sweep the query
+//             tiles at or below the diagonal: S = Q K^T and dP = dO V^T (K, V fragments in
+//             registers, Q and dO rows from LDS), dV^T += dO^T P and dK^T += Q^T dS (Q and dO also
+//             staged transposed, so those operands are single 16-byte LDS reads).  Replaced items
+//             form P from the prepared pattern and accumulate dV only; they also write the zero dQ
+//             and dK rows of their keys.
+//   bwd_dq  : one work item per (batch, ordinary head, 128-query block), lane = query: S^T = K Q^T,
+//             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal (K
+//             staged both row-major and transposed).
+// Every output element is written by exactly one work item and summed in a fixed order, so the
+// backward is bitwise repeatable.  S and dP are formed twice (once per kernel): seven products per
+// entry of an ordinary head instead of five, traded for having no atomic traffic.
 #include "saf_device.h"
 #include "saf_internal.h"
-
-#include <algorithm>
 
 namespace saf {
 namespace {
@@ -53,50 +51,41 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(LayerArgs p) {
     const Frag<TI> gf = load8(reinterpret_cast<const TI*>(p.dout) + row * D + part * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)of.v[e] * (float)gf.v[e];
-    float4* z = reinterpret_cast<float4*>(p.dqacc + row * D + part * 8);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
   if (valid && part == 0) p.delta[row] = acc;
 }
 
-// ------------------------------------------------------------------------------------ bwd_main
+// ------------------------------------------------------------------------------------ bwd_kv
 template <typename TI, int D>
-struct BwdCfg {
-  static constexpr bool BF = sizeof(TI) == 2;
-  static constexpr int BKV = 128;                        // keys per work item (4 waves x 32)
-  static constexpr int BQ = BF ? 64 : 32;                // queries per staged tile
-  static constexpr int NS = BQ / 32;                     // 32-query subtiles per tile
-  static constexpr int LDP = D + 16 / (int)sizeof(TI);   // padded row of Q / dO / K tiles
-  static constexpr int LDS_ = BQ + 16 / (int)sizeof(TI); // padded row of the dS tile [key][query]
-  static constexpr int EPC = 16 / (int)sizeof(TI);
-  static constexpr int CPR = D / EPC;                    // 16-byte chunks per row
-  static constexpr int CPT = BQ * CPR / kNT;             // chunks per thread per staged tile
-  static constexpr int WIN = BQ + BKV;                   // distance window of replaced items
-  static constexpr int NBLK = NS * (D / 32);             // 32x32 dQ blocks per query tile
+struct KvCfg {
+  static constexpr int BKV = 128;                         // keys per work item (4 waves x 32)
+  static constexpr int BQ = sizeof(TI) == 2 ? 64 : 32;    // queries per staged tile
+  static constexpr int NS = BQ / 32;                      // 32-query subtiles per tile
+  static constexpr int LDP = D + 16 / (int)sizeof(TI);    // padded row of the Q / dO tiles
+  static constexpr int LDT = BQ + 16 / (int)sizeof(TI);   // padded row of the transposed tiles
+  static constexpr int WIN = BQ + BKV;                    // distance window of replaced items
 };
 
 template <typename TI, int D>
-struct BwdPrefetch {
-  uint4 q[BwdCfg<TI, D>::CPT];
-  uint4 g[BwdCfg<TI, D>::CPT];
+struct KvPrefetch {
+  Blocks4<TI, D, KvCfg<TI, D>::BQ, kNT> q, g;
   float rs, dl, rw;
 };
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bwd_main_kernel(LayerArgs p) {
-  using C = BwdCfg<TI, D>;
-  constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, LDS_ = C::LDS_;
-  constexpr int EPC = C::EPC, CPR = C::CPR, CPT = C::CPT, WIN = C::WIN, NBLK = C::NBLK;
-  __shared__ __attribute__((aligned(16))) TI Qs[BQ * LDP];
-  __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDP];      // dO tile
-  __shared__ __attribute__((aligned(16))) TI Kb[BKV * LDP];     // the block's keys (for dQ)
-  __shared__ __attribute__((aligned(16))) TI dSs[BKV * LDS_];   // dS tile, [key][query]
-  __shared__ __attribute__((aligned(16))) float rss[BQ];        // row statistic per query
-  __shared__ __attribute__((aligned(16))) float dls[BQ];        // delta per query
-  __shared__ float rwin[WIN];                                   // replaced: er / r*log2e window
+__global__ __launch_bounds__(kNT)
+__attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bwd_kv_kernel(LayerArgs p) {
+  using C = KvCfg<TI, D>;
+  constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, LDT = C::LDT, WIN = C::WIN;
+  __shared__ __attribute__((aligned(16))) TI Qs[BQ * LDP];   // Q tile, rows
+  __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDP];   // dO tile, rows
+  __shared__ __attribute__((aligned(16))) TI QT[D * LDT];    // Q tile transposed [dim][query]
+  __shared__ __attribute__((aligned(16))) TI GT[D * LDT];    // dO tile transposed [dcol][query]
+  __shared__ __attribute__((aligned(16))) float rss[BQ];     // row statistic per query
+  __shared__ __attribute__((aligned(16))) float dls[BQ];     // delta per query
+  __shared__ float rwin[WIN];                                // replaced: er / r*log2e window
 
   const int T = p.T, H = p.H;
   const int BH = p.B * H;
@@ -128,23 +117,13 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   const float shift = fact ? p.pat.shift(h) : 0.f;
   const float c2 = p.scale_log2;
 
-  // the block's K rows -> LDS (ordinary items), K / V fragments of the lane's key -> registers
   Frag<TI> kf[D / 16], vf[D / 16];
-  if (!rep) {
-    for (int c = tid; c < BKV * CPR; c += kNT) {
-      const int row = c / CPR, cc = c % CPR;
-      const int g = kb0 + row;
-      *reinterpret_cast<uint4*>(Kb + row * LDP + cc * EPC) =
-          g < T ? *reinterpret_cast<const uint4*>(K + (size_t)g * D + cc * EPC) : make_uint4(0u, 0u, 0u, 0u);
-    }
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      kf[t] = kj < T ? load8(K + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
-      vf[t] = kj < T ? load8(V + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
-    }
+  for (int t = 0; t < D / 16; ++t) {
+    kf[t] = (!rep && kj < T) ? load8(K + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
+    vf[t] = (!rep && kj < T) ? load8(V + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
   }
-  // replaced: the lane's key preference (ea, or a*log2e)
-  float akey = 0.f;
+  float akey = 0.f;  // replaced: the lane's key preference (ea, or a*log2e)
   if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
 
   f32x16 dvT[D / 32], dkT[D / 32];
@@ -154,22 +133,15 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     zero(dkT[c]);
   }
 
-  BwdPrefetch<TI, D> pf;
+  KvPrefetch<TI, D> pf;
   auto load_tile = [&](int q0) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kNT;
-      const int row = idx / CPR, cc = idx % CPR;
-      const int g = q0 + row;
-      const size_t off = (size_t)g * D + cc * EPC;
-      pf.g[c] = g < T ? *reinterpret_cast<const uint4*>(G + off) : make_uint4(0u, 0u, 0u, 0u);
-      if (!rep) pf.q[c] = g < T ? *reinterpret_cast<const uint4*>(Q + off) : make_uint4(0u, 0u, 0u, 0u);
-    }
+    pf.g.load(G, q0, T, tid);
+    if (!rep) pf.q.load(Q, q0, T, tid);
     if (tid < BQ) {
       const int q = q0 + tid;
       // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
-      // Rows past the end get weight 0 (their dO rows are zero, and an unbounded weight times a
-      // zero row would not be zero).
+      // Rows past the end get weight 0 (their dO rows are zero; an unbounded weight times a zero
+      // row would not be zero).
       if (q < T) {
         const float l = lse[q];
         pf.rs = fact ? expf(shift - l) : l * kLog2e;
@@ -184,12 +156,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     }
   };
   auto store_tile = [&]() {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kNT;
-      const int row = idx / CPR, cc = idx % CPR;
-      *reinterpret_cast<uint4*>(Gs + row * LDP + cc * EPC) = pf.g[c];
-      if (!rep) *reinterpret_cast<uint4*>(Qs + row * LDP + cc * EPC) = pf.q[c];
+    pf.g.template store_cols<LDT>(GT, tid);
+    if (!rep) {
+      pf.g.template store_rows<LDP>(Gs, tid);
+      pf.q.template store_rows<LDP>(Qs, tid);
+      pf.q.template store_cols<LDT>(QT, tid);
     }
     if (tid < BQ) {
       rss[tid] = pf.rs;
@@ -204,7 +175,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 
   for (int qt = qt0; qt < nqt; ++qt) {
     const int q0 = qt * BQ;
-    __syncthreads();  // previous tile's readers are done with Qs / Gs / dSs
+    __syncthreads();  // the previous tile's readers are done
     store_tile();
     __syncthreads();
     if (qt + 1 < nqt) load_tile(q0 + BQ);
@@ -212,16 +183,9 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int qs = q0 + 32 * s;
-      const bool live = (qs + 31 >= kw) && (qs < T) && (kw < T);  // wave-uniform
-      float pr[16], ds[16];
-      if (!live) {
-        if (!rep) {  // nothing visible: this wave's part of the dS tile is zero
-#pragma unroll
-          for (int g = 0; g < 4; ++g) store4(dSs + (32 * w + l32) * LDS_ + 32 * s + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
-        }
-        continue;
-      }
+      if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
       const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
+      float pr[16], ds[16];
       if (!rep) {
         f32x16 st, dpt;
         zero(st);
@@ -270,41 +234,12 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
-          mma16(dvT[c], col_frag<TI, LDP>(Gs, 32 * s + 16 * u, 32 * c, lane), pfr);
+          mma16(dvT[c], tt_frag<TI, LDT>(GT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
         if (!rep) {
           const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
 #pragma unroll
           for (int c = 0; c < D / 32; ++c)
-            mma16(dkT[c], col_frag<TI, LDP>(Qs, 32 * s + 16 * u, 32 * c, lane), sfr);
-        }
-      }
-      if (!rep) {  // dS -> LDS as [key][query]
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          store4(dSs + (32 * w + l32) * LDS_ + 32 * s + 8 * g + 4 * hi, ds[4 * g], ds[4 * g + 1],
-                 ds[4 * g + 2], ds[4 * g + 3]);
-      }
-    }
-
-    if (!rep) {
-      __syncthreads();  // the whole dS tile [128 keys][BQ queries] is in LDS
-      // dQ[q][dim] += sum over the block's keys of dS[q][key] K[key][dim]; wave w takes 32x32
-      // output blocks w, w+4, ...: block n covers queries 32*(n % NS), dims 32*(n / NS).
-#pragma unroll
-      for (int n = w; n < NBLK; n += 4) {
-        const int sq = n % NS, cd = n / NS;
-        if (q0 + 32 * sq >= T || q0 + 32 * sq + 31 < kb0) continue;
-        f32x16 acc;
-        zero(acc);
-#pragma unroll
-        for (int k = 0; k < BKV / 16; ++k)
-          mma16(acc, col_frag<TI, LDS_>(dSs, 16 * k, 32 * sq, lane),
-                col_frag<TI, LDP>(Kb, 16 * k, 32 * cd, lane));
-        float* dst = p.dqacc + hoff + 32 * cd + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = q0 + 32 * sq + crow(r, hi);
-          if (q < T) unsafeAtomicAdd(dst + (size_t)q * D, acc[r]);
+            mma16(dkT[c], tt_frag<TI, LDT>(QT, 32 * s + 16 * u, 32 * c + l32, hi), sfr);
         }
       }
     }
@@ -313,7 +248,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   if (kj >= T) return;
   TI* dV = reinterpret_cast<TI*>(p.dv) + hoff + (size_t)kj * D;
   TI* dK = reinterpret_cast<TI*>(p.dk) + hoff + (size_t)kj * D;
-  const float vs = rep ? (fact ? akey : 1.f) : 1.f;  // product form: the key's factor ea[kj]
+  const float vs = fact ? akey : 1.f;  // product form: the key's factor ea[kj]
   const float ks = rep ? 0.f : p.scale;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
@@ -325,22 +260,155 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       store4(dK + dc, dkT[c][4 * g] * ks, dkT[c][4 * g + 1] * ks, dkT[c][4 * g + 2] * ks,
              dkT[c][4 * g + 3] * ks);
     }
+  if (rep) {  // a replaced head's query gradient is zero
+    TI* dQ = reinterpret_cast<TI*>(p.dq) + hoff + (size_t)kj * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
+  }
 }
 
-// ------------------------------------------------------------------------------------ dq_finalize
+// ------------------------------------------------------------------------------------ bwd_dq
 template <typename TI, int D>
-__global__ __launch_bounds__(kNT) void dq_finalize_kernel(LayerArgs p) {
-  const long long n4 = (long long)p.B * p.H * p.T * D / 4;  // groups of 4 elements
-  for (long long i = (long long)blockIdx.x * kNT + threadIdx.x; i < n4; i += (long long)gridDim.x * kNT) {
-    const long long e = i * 4;
-    const int h = (int)((e / ((long long)p.T * D)) % p.H);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!is_replaced(p.rep, h)) {
-      v = *reinterpret_cast<const float4*>(p.dqacc + e);
-      v.x *= p.scale; v.y *= p.scale; v.z *= p.scale; v.w *= p.scale;
-    }
-    store4(reinterpret_cast<TI*>(p.dq) + e, v.x, v.y, v.z, v.w);
+struct DqCfg {
+  static constexpr int BQ = 128;                          // queries per work item (4 waves x 32)
+  static constexpr int BK = sizeof(TI) == 2 ? 64 : 32;    // keys per staged tile
+  static constexpr int NS = BK / 32;
+  static constexpr int LDP = D + 16 / (int)sizeof(TI);
+  static constexpr int LDT = BK + 16 / (int)sizeof(TI);
+  static constexpr int EPC = 16 / (int)sizeof(TI);
+  static constexpr int CPR = D / EPC;
+  static constexpr int CPT = BK * CPR / kNT;
+};
+
+template <typename TI, int D>
+struct DqPrefetch {
+  Blocks4<TI, D, DqCfg<TI, D>::BK, kNT> k;
+  uint4 v[DqCfg<TI, D>::CPT];
+};
+
+template <typename TI, int D>
+__global__ __launch_bounds__(kNT)
+__attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel(LayerArgs p) {
+  using C = DqCfg<TI, D>;
+  constexpr int BQ = C::BQ, BK = C::BK, NS = C::NS, LDP = C::LDP, LDT = C::LDT;
+  constexpr int EPC = C::EPC, CPR = C::CPR, CPT = C::CPT;
+  __shared__ __attribute__((aligned(16))) TI Ks[BK * LDP];   // K tile, rows
+  __shared__ __attribute__((aligned(16))) TI KT[D * LDT];    // K tile transposed [dim][key]
+  __shared__ __attribute__((aligned(16))) TI Vs[BK * LDP];   // V tile, rows
+
+  const int T = p.T, H = p.H;
+  const int BH = p.B * H;
+  const int BHp = (BH + 7) & ~7;
+  const int nqb = (T + BQ - 1) / BQ;
+  const int x = blockIdx.x;
+  const int bh = x % BHp;
+  if (bh >= BH) return;
+  const int qb = nqb - 1 - x / BHp;  // heaviest query blocks first
+  const int b = bh / H, h = bh % H;
+  if (is_replaced(p.rep, h)) return;  // replaced heads: zero dQ rows come from bwd_kv
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int q0 = qb * BQ;
+  const int qw = q0 + 32 * w;
+  const int qi = qw + l32;
+  const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+  const size_t soff = ((size_t)b * H + h) * (size_t)T;
+  const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
+  const TI* K = reinterpret_cast<const TI*>(p.k) + hoff;
+  const TI* V = reinterpret_cast<const TI*>(p.v) + hoff;
+  const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
+
+  Frag<TI> qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+    gf[t] = qi < T ? load8(G + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
   }
+  const float lse2 = qi < T ? p.lse[soff + qi] * kLog2e : 0.f;
+  const float dl = qi < T ? p.delta[soff + qi] : 0.f;
+  const float c2 = p.scale_log2;
+
+  f32x16 dqT[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) zero(dqT[c]);
+
+  DqPrefetch<TI, D> pf;
+  auto load_tile = [&](int k0) {
+    pf.k.load(K, k0, T, tid);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * kNT;
+      const int row = idx / CPR, cc = idx % CPR;
+      const int g = k0 + row;
+      pf.v[c] = g < T ? *reinterpret_cast<const uint4*>(V + (size_t)g * D + cc * EPC)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_tile = [&]() {
+    pf.k.template store_rows<LDP>(Ks, tid);
+    pf.k.template store_cols<LDT>(KT, tid);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * kNT;
+      const int row = idx / CPR, cc = idx % CPR;
+      *reinterpret_cast<uint4*>(Vs + row * LDP + cc * EPC) = pf.v[c];
+    }
+  };
+
+  const int kend = min(T, q0 + BQ);
+  const int nkt = (kend + BK - 1) / BK;
+  load_tile(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BK;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < nkt) load_tile(k0 + BK);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ks = k0 + 32 * s;
+      if (ks > qw + 31 || ks >= T) break;  // wave-uniform: the rest of the tile is masked out
+      f32x16 st, dpt;
+      zero(st);
+      zero(dpt);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
+        mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t]);
+      }
+      const bool edge = (ks + 31 > qw) || (ks + 31 >= T);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
+        if (edge) {
+          const int key = ks + crow(r, hi);
+          pp = (key <= qi && key < T) ? pp : 0.f;
+        }
+        ds[r] = pp * (dpt[r] - dl);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const Frag<TI> sf = to_frag<TI>(&ds[8 * u]);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+          mma16(dqT[c], tt_frag<TI, LDT>(KT, 32 * s + 16 * u, 32 * c + l32, hi), sf);
+      }
+    }
+  }
+
+  if (qi >= T) return;
+  TI* dQ = reinterpret_cast<TI*>(p.dq) + hoff + (size_t)qi * D;
+  const float sc = p.scale;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      store4(dQ + 32 * c + 8 * g + 4 * hi, dqT[c][4 * g] * sc, dqT[c][4 * g + 1] * sc,
+             dqT[c][4 * g + 2] * sc, dqT[c][4 * g + 3] * sc);
 }
 
 template <typename TI, int D>
@@ -354,19 +422,20 @@ hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
 }
 
 template <typename TI, int D>
-hipError_t launch_main_t(const LayerArgs& a, hipStream_t s) {
+hipError_t launch_kv_t(const LayerArgs& a, hipStream_t s) {
   const int BHp = (a.B * a.H + 7) & ~7;
-  const long long blocks = (long long)BHp * ((a.T + BwdCfg<TI, D>::BKV - 1) / BwdCfg<TI, D>::BKV);
+  const long long blocks = (long long)BHp * ((a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_main_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL((bwd_kv_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename TI, int D>
-hipError_t launch_fin_t(const LayerArgs& a, hipStream_t s) {
-  const long long n4 = (long long)a.B * a.H * a.T * D / 4;
-  const long long blocks = std::min<long long>((n4 + kNT - 1) / kNT, 8192);
-  hipLaunchKernelGGL((dq_finalize_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+hipError_t launch_dq_t(const LayerArgs& a, hipStream_t s) {
+  const int BHp = (a.B * a.H + 7) & ~7;
+  const long long blocks = (long long)BHp * ((a.T + DqCfg<TI, D>::BQ - 1) / DqCfg<TI, D>::BQ);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dq_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -376,13 +445,13 @@ hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16_in, hipStream_t s) {
   if (bf16_in) return a.d == 64 ? launch_pre_t<bf16, 64>(a, s) : launch_pre_t<bf16, 128>(a, s);
   return a.d == 64 ? launch_pre_t<float, 64>(a, s) : launch_pre_t<float, 128>(a, s);
 }
-hipError_t launch_bwd_main(const LayerArgs& a, bool bf16_in, hipStream_t s) {
-  if (bf16_in) return a.d == 64 ? launch_main_t<bf16, 64>(a, s) : launch_main_t<bf16, 128>(a, s);
-  return a.d == 64 ? launch_main_t<float, 64>(a, s) : launch_main_t<float, 128>(a, s);
+hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16_in, hipStream_t s) {
+  if (bf16_in) return a.d == 64 ? launch_kv_t<bf16, 64>(a, s) : launch_kv_t<bf16, 128>(a, s);
+  return a.d == 64 ? launch_kv_t<float, 64>(a, s) : launch_kv_t<float, 128>(a, s);
 }
-hipError_t launch_dq_finalize(const LayerArgs& a, bool bf16_in, hipStream_t s) {
-  if (bf16_in) return a.d == 64 ? launch_fin_t<bf16, 64>(a, s) : launch_fin_t<bf16, 128>(a, s);
-  return a.d == 64 ? launch_fin_t<float, 64>(a, s) : launch_fin_t<float, 128>(a, s);
+hipError_t launch_bwd_dq(const LayerArgs& a, bool bf16_in, hipStream_t s) {
+  if (bf16_in) return a.d == 64 ? launch_dq_t<bf16, 64>(a, s) : launch_dq_t<bf16, 128>(a, s);
+  return a.d == 64 ? launch_dq_t<float, 64>(a, s) : launch_dq_t<float, 128>(a, s);
 }
 
 }  // namespace saf

@@ -162,6 +162,122 @@ __device__ __forceinline__ float frag_sum(const Frag<float>& f) {
   return s;
 }
 
+// ---- Transposed, permuted LDS tiles ---------------------------------------------------------------
+// A tile that a product contracts over its rows (keys or queries) is also kept transposed in LDS,
+// TT[col][tpos(row)] with row stride LDT, where inside each 16-row group row k = 8a + 4h + b is
+// placed at 8h + 4a + b (bits 2 and 3 swapped).  Slot e of lane half hi in a k16 step then reads
+// row 16u + perm_row(e, hi) at position 16u + 8*hi + e: the 8 values of a fragment are contiguous
+// and come from one 16-byte LDS read.
+__device__ __forceinline__ int tpos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+template <typename TI, int LDT>
+__device__ __forceinline__ Frag<TI> tt_frag(const TI* tt, int row0, int col, int hi) {
+  return load8(tt + col * LDT + row0 + 8 * hi);
+}
+
+// 4 consecutive elements of one row (bf16: 8 bytes, fp32: 16 bytes)
+template <typename TI>
+struct Quad;
+template <>
+struct Quad<bf16> {
+  uint2 v;
+};
+template <>
+struct Quad<float> {
+  uint4 v;
+};
+
+__device__ __forceinline__ Quad<bf16> load_quad(const bf16* p) {
+  Quad<bf16> q;
+  q.v = *reinterpret_cast<const uint2*>(p);
+  return q;
+}
+__device__ __forceinline__ Quad<float> load_quad(const float* p) {
+  Quad<float> q;
+  q.v = *reinterpret_cast<const uint4*>(p);
+  return q;
+}
+__device__ __forceinline__ void store_quad(bf16* p, const Quad<bf16>& q) { *reinterpret_cast<uint2*>(p) = q.v; }
+__device__ __forceinline__ void store_quad(float* p, const Quad<float>& q) { *reinterpret_cast<uint4*>(p) = q.v; }
+template <typename TI>
+__device__ __forceinline__ Quad<TI> zero_quad() {
+  Quad<TI> q;
+  q.v = {};
+  return q;
+}
+
+// 4x4 transpose: in[i] = row i (columns 0..3)  ->  out[j] = column j (rows 0..3)
+__device__ __forceinline__ void transpose4(const Quad<bf16>* in, Quad<bf16>* out) {
+  // bf16 pairs: word = (low half, high half).  v_perm picks bytes of {S0, S1}: selector bytes 0-3
+  // address S1, 4-7 address S0.
+  const uint32_t lo_lo = 0x05040100u;  // (S1.lo16, S0.lo16)
+  const uint32_t hi_hi = 0x07060302u;  // (S1.hi16, S0.hi16)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    // column 2j uses the low halves of word j, column 2j+1 the high halves
+    const uint32_t a0 = j == 0 ? in[0].v.x : in[0].v.y, a1 = j == 0 ? in[1].v.x : in[1].v.y;
+    const uint32_t a2 = j == 0 ? in[2].v.x : in[2].v.y, a3 = j == 0 ? in[3].v.x : in[3].v.y;
+    out[2 * j].v.x = __builtin_amdgcn_perm(a1, a0, lo_lo);
+    out[2 * j].v.y = __builtin_amdgcn_perm(a3, a2, lo_lo);
+    out[2 * j + 1].v.x = __builtin_amdgcn_perm(a1, a0, hi_hi);
+    out[2 * j + 1].v.y = __builtin_amdgcn_perm(a3, a2, hi_hi);
+  }
+}
+__device__ __forceinline__ void transpose4(const Quad<float>* in, Quad<float>* out) {
+  out[0].v = make_uint4(in[0].v.x, in[1].v.x, in[2].v.x, in[3].v.x);
+  out[1].v = make_uint4(in[0].v.y, in[1].v.y, in[2].v.y, in[3].v.y);
+  out[2].v = make_uint4(in[0].v.z, in[1].v.z, in[2].v.z, in[3].v.z);
+  out[3].v = make_uint4(in[0].v.w, in[1].v.w, in[2].v.w, in[3].v.w);
+}
+
+// Staging of a ROWS x D tile in 4x4 blocks: each thread owns NB blocks; block n of thread tid
+// covers rows 4*(i / (D/4)) .. +3 and columns 4*(i % (D/4)) .. +3 with i = tid + n*NT.
+template <typename TI, int D, int ROWS, int NT>
+struct Blocks4 {
+  static constexpr int PER_ROW = D / 4;
+  static constexpr int NBLK = ROWS * D / 16;             // 4x4 blocks in the tile
+  static constexpr int NB = (NBLK + NT - 1) / NT;        // per thread (the last may be partial)
+  Quad<TI> q[NB][4];
+  // rows >= T are zero
+  __device__ __forceinline__ void load(const TI* g, int row0, int T, int tid) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int i = tid + n * NT;
+      if (NBLK % NT != 0 && i >= NBLK) break;
+      const int r = 4 * (i / PER_ROW), c = 4 * (i % PER_ROW);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int row = row0 + r + k;
+        q[n][k] = row < T ? load_quad(g + (size_t)row * D + c) : zero_quad<TI>();
+      }
+    }
+  }
+  template <int LDP>
+  __device__ __forceinline__ void store_rows(TI* lds, int tid) const {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int i = tid + n * NT;
+      if (NBLK % NT != 0 && i >= NBLK) break;
+      const int r = 4 * (i / PER_ROW), c = 4 * (i % PER_ROW);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) store_quad(lds + (r + k) * LDP + c, q[n][k]);
+    }
+  }
+  template <int LDT>
+  __device__ __forceinline__ void store_cols(TI* tt, int tid) const {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int i = tid + n * NT;
+      if (NBLK % NT != 0 && i >= NBLK) break;
+      const int r = 4 * (i / PER_ROW), c = 4 * (i % PER_ROW);
+      Quad<TI> t[4];
+      transpose4(q[n], t);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) store_quad(tt + (c + k) * LDT + tpos(r), t[k]);
+    }
+  }
+};
+
 // Copy rows [row0, row0+ROWS) of a [T][D] global matrix into a padded LDS tile (row stride LDP
 // elements); rows >= T are filled with zeros.  All NT threads of the block take part.
 template <typename TI, int D, int ROWS, int LDP, int NT>

@@ -13,7 +13,8 @@
 //   ordinary: S^T = K Q^T on the matrix cores (lane = query, registers = keys); base-2 online
 //             softmax with a lazily updated running maximum (the accumulator is rescaled only when
 //             the tile maximum exceeds the running one by more than 2^8); O^T += V^T P^T, where
-//             V^T fragments come from the row-major V tile through transposing LDS reads.
+//             the V tile is staged transposed (and key-permuted) so that a V^T fragment is one
+//             16-byte LDS read.
 //   replaced: no Q, no K, no QK^T and no running maximum: each entry is ea[j] * er[i-j] (one
 //             multiply) from LDS windows of the prepared pattern, and the row is divided by the sum
 //             of its entries at the end; where the prepared pattern flags the product form as
@@ -37,23 +38,24 @@ struct FwdCfg {
   static constexpr int EPC = 16 / (int)sizeof(TI);       // elements per 16-byte chunk
   static constexpr int CPR = D / EPC;                    // chunks per row
   static constexpr int CPT = BK * CPR / kNT;             // chunks per thread per tile
+  static constexpr int LDT = BK + 16 / (int)sizeof(TI);  // padded row of the transposed V tile
   static constexpr int WIN = BK + kBQ;                   // distance window
 };
 
 template <typename TI, int D>
 struct Prefetch {
   uint4 k[FwdCfg<TI, D>::CPT];
-  uint4 v[FwdCfg<TI, D>::CPT];
+  Blocks4<TI, D, FwdCfg<TI, D>::BK, kNT> v;
   float aw, rw;
 };
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void mixed_fwd_kernel(LayerArgs p) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void mixed_fwd_kernel(LayerArgs p) {
   using C = FwdCfg<TI, D>;
   constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP, EPC = C::EPC, CPR = C::CPR, CPT = C::CPT;
-  constexpr int WIN = C::WIN;
+  constexpr int WIN = C::WIN, LDT = C::LDT;
   __shared__ __attribute__((aligned(16))) TI Ks[BK * LDP];
-  __shared__ __attribute__((aligned(16))) TI Vs[BK * LDP];
+  __shared__ __attribute__((aligned(16))) TI VT[D * LDT];   // V tile transposed: [dcol][key]
   __shared__ __attribute__((aligned(16))) float awin[BK];  // ea (or a*log2e) of the tile's keys
   __shared__ float rwin[WIN];                              // er (or r*log2e) of its distances
 
@@ -89,14 +91,16 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
   // ---- staging: global -> registers (next tile) -> LDS
   Prefetch<TI, D> pf;
   auto load_tile = [&](int k0) {
+    pf.v.load(V, k0, T, tid);
+    if (!rep) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kNT;
-      const int row = idx / CPR, cc = idx % CPR;
-      const int g = k0 + row;
-      const size_t off = (size_t)g * D + cc * EPC;
-      pf.v[c] = g < T ? *reinterpret_cast<const uint4*>(V + off) : make_uint4(0u, 0u, 0u, 0u);
-      if (!rep) pf.k[c] = g < T ? *reinterpret_cast<const uint4*>(K + off) : make_uint4(0u, 0u, 0u, 0u);
+      for (int c = 0; c < CPT; ++c) {
+        const int idx = tid + c * kNT;
+        const int row = idx / CPR, cc = idx % CPR;
+        const int g = k0 + row;
+        pf.k[c] = g < T ? *reinterpret_cast<const uint4*>(K + (size_t)g * D + cc * EPC)
+                        : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
     if (rep) {
       const int d0 = q0 - k0 - (BK - 1);
@@ -108,12 +112,14 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
     }
   };
   auto store_tile = [&]() {
+    pf.v.template store_cols<LDT>(VT, tid);
+    if (!rep) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kNT;
-      const int row = idx / CPR, cc = idx % CPR;
-      *reinterpret_cast<uint4*>(Vs + row * LDP + cc * EPC) = pf.v[c];
-      if (!rep) *reinterpret_cast<uint4*>(Ks + row * LDP + cc * EPC) = pf.k[c];
+      for (int c = 0; c < CPT; ++c) {
+        const int idx = tid + c * kNT;
+        const int row = idx / CPR, cc = idx % CPR;
+        *reinterpret_cast<uint4*>(Ks + row * LDP + cc * EPC) = pf.k[c];
+      }
     }
     if (rep) {
       if (tid < BK) awin[tid] = pf.aw;
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
         l += frag_sum(pfr);
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
-          mma16(oacc[c], col_frag<TI, LDP>(Vs, 32 * s + 16 * u, 32 * c, lane), pfr);
+          mma16(oacc[c], tt_frag<TI, LDT>(VT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
       }
     }
 

@@ -49,7 +49,6 @@ struct LayerArgs {
   float* lse;        // [B][H][T] natural-log row normalisers (forward writes, backward reads)
   PatternView pat;   // prepared pattern of the replaced heads
   float* delta;      // [B][H][T] workspace: rowsum(dO * O) of ordinary heads
-  float* dqacc;      // [B][H][T][d] workspace: fp32 dQ accumulator of ordinary heads
   void* out;         // forward: o
   void* dq;
   void* dk;
@@ -73,8 +72,8 @@ struct CalibArgs {
 hipError_t launch_pattern_prepare(const LayerArgs& a, hipStream_t s);
 hipError_t launch_mixed_fwd(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_bwd_main(const LayerArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_dq_finalize(const LayerArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_dq(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_lse(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_stats(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s);

@@ -33,7 +33,7 @@ def test_workspace_sizes():
     pat = saf.saf_pattern_size(12, 4096)
     assert pat >= 12 * 3 * 4096 * 4
     assert saf.saf_attn_fwd_workspace_size(8, 12, 4096, 64) == pat
-    assert saf.saf_attn_bwd_workspace_size(8, 12, 4096, 64) == pat + 8 * 12 * 4096 * 4 * (1 + 64)
+    assert saf.saf_attn_bwd_workspace_size(8, 12, 4096, 64) == pat + 8 * 12 * 4096 * 4
     assert saf.saf_attn_bwd_workspace_size(0, 12, 4096, 64) == 0
     n = saf.saf_calibrate_workspace_size(32, 16, 8192, 128)
     assert n >= 32 * 16 * 8192 * 4 + 16 * 64 * 128 * 8

@@ -69,9 +69,8 @@ def test_pattern_longer_than_input_uses_prefix():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_repeatable():
-    """Forward, dK and dV are bitwise repeatable; dQ is summed with atomics in arrival order, so
-    only its last bits may change between runs."""
+def test_bitwise_repeatable():
+    """Every output element is written by one work item and summed in a fixed order."""
     saf = _saf()
     B, H, T, d = 2, 12, 700, 64
     rep = synth.replaced_mask(H, 3)
@@ -81,10 +80,8 @@ def test_repeatable():
         o, l = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
         outs.append((o, l) + saf.bwd(g.q, g.k, g.v, o, g.dout, l, rep, g.a, g.r))
     torch.cuda.synchronize()
-    (o1, l1, dq1, dk1, dv1), (o2, l2, dq2, dk2, dv2) = outs
-    for x, y in ((o1, o2), (l1, l2), (dk1, dk2), (dv1, dv2)):
+    for x, y in zip(*outs):
         assert torch.equal(x, y)
-    assert float((dq1.float() - dq2.float()).abs().max()) <= 1e-2 * float(dq1.float().abs().max())
 
 
 def test_non_default_stream():
