@@ -169,10 +169,14 @@ __device__ __forceinline__ float frag_sum(const Frag<float>& f) {
 // row 16u + perm_row(e, hi) at position 16u + 8*hi + e: the 8 values of a fragment are contiguous
 // and come from one 16-byte LDS read.
 __device__ __forceinline__ int tpos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// Bank swizzle of a transposed tile: position p of row `col` is stored at p ^ tswz(col).  It flips
+// bits 3-4 of the position (whole 8-element groups, so fragments stay contiguous) by bits 4-5 of
+// the row, which spreads the staging writes of 16 rows four apart over all LDS banks.
+__device__ __forceinline__ int tswz(int col) { return ((col >> 4) & 3) << 3; }
 
 template <typename TI, int LDT>
 __device__ __forceinline__ Frag<TI> tt_frag(const TI* tt, int row0, int col, int hi) {
-  return load8(tt + col * LDT + row0 + 8 * hi);
+  return load8(tt + col * LDT + ((row0 + 8 * hi) ^ tswz(col)));
 }
 
 // 4 consecutive elements of one row (bf16: 8 bytes, fp32: 16 bytes)
@@ -230,21 +234,30 @@ __device__ __forceinline__ void transpose4(const Quad<float>* in, Quad<float>* o
   out[3].v = make_uint4(in[0].v.w, in[1].v.w, in[2].v.w, in[3].v.w);
 }
 
-// Staging of a ROWS x D tile in 4x4 blocks: each thread owns NB blocks; block n of thread tid
-// covers rows 4*(i / (D/4)) .. +3 and columns 4*(i % (D/4)) .. +3 with i = tid + n*NT.
+// Staging of a ROWS x D tile in 4x4 blocks: each thread owns NB blocks; block n of thread tid,
+// i = tid + n*NT, covers rows 4*rg .. +3 and columns 4*cg .. +3 with
+//   cg = i%16 + 16*(i / ROWS*4),  rg = g with bits 0 and 1 swapped, g = (i/16) % (ROWS/4).
+// 16 consecutive lanes take one row group and 64 consecutive columns (coalesced global loads); a
+// 32-lane LDS write phase touches 16 rows of the transposed tile at two positions 8 bytes apart,
+// which with tswz puts its 64 bank accesses on 64 different banks.
 template <typename TI, int D, int ROWS, int NT>
 struct Blocks4 {
-  static constexpr int PER_ROW = D / 4;
+  static_assert(D % 64 == 0 && ROWS % 4 == 0, "tile shape");
   static constexpr int NBLK = ROWS * D / 16;             // 4x4 blocks in the tile
   static constexpr int NB = (NBLK + NT - 1) / NT;        // per thread (the last may be partial)
   Quad<TI> q[NB][4];
+  __device__ __forceinline__ static int col_of(int i) { return 4 * ((i & 15) + 16 * (i / (4 * ROWS))); }
+  __device__ __forceinline__ static int row_of(int i) {
+    const int g = (i >> 4) % (ROWS / 4);
+    return 4 * ((g & ~3) | ((g & 1) << 1) | ((g & 2) >> 1));
+  }
   // rows >= T are zero
   __device__ __forceinline__ void load(const TI* g, int row0, int T, int tid) {
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int i = tid + n * NT;
       if (NBLK % NT != 0 && i >= NBLK) break;
-      const int r = 4 * (i / PER_ROW), c = 4 * (i % PER_ROW);
+      const int r = row_of(i), c = col_of(i);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int row = row0 + r + k;
@@ -258,7 +271,7 @@ struct Blocks4 {
     for (int n = 0; n < NB; ++n) {
       const int i = tid + n * NT;
       if (NBLK % NT != 0 && i >= NBLK) break;
-      const int r = 4 * (i / PER_ROW), c = 4 * (i % PER_ROW);
+      const int r = row_of(i), c = col_of(i);
 #pragma unroll
       for (int k = 0; k < 4; ++k) store_quad(lds + (r + k) * LDP + c, q[n][k]);
     }
@@ -269,11 +282,11 @@ struct Blocks4 {
     for (int n = 0; n < NB; ++n) {
       const int i = tid + n * NT;
       if (NBLK % NT != 0 && i >= NBLK) break;
-      const int r = 4 * (i / PER_ROW), c = 4 * (i % PER_ROW);
+      const int r = row_of(i), c = col_of(i);
       Quad<TI> t[4];
       transpose4(q[n], t);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) store_quad(tt + (c + k) * LDT + tpos(r), t[k]);
+      for (int k = 0; k < 4; ++k) store_quad(tt + (c + k) * LDT + (tpos(r) ^ tswz(c + k)), t[k]);
     }
   }
 };
