@@ -9,10 +9,11 @@
 // with the current V ([Notes §二.4, Fig. 2]).  Here a work item is one (batch, head, 128-query
 // block); its 4 waves own 32 queries each and sweep the key tiles at or below the diagonal.  The
 // next key tile is loaded into registers while the current one is multiplied, then written to LDS.
+// Each kind of item runs its own copy of the tile loop (no per-tile branching on the head kind).
 //
 //   ordinary: S^T = K Q^T on the matrix cores (lane = query, registers = keys); base-2 online
 //             softmax with a lazily updated running maximum (the accumulator is rescaled only when
-//             the tile maximum exceeds the running one by more than 2^8); O^T += V^T P^T, where
+//             the subtile maximum exceeds the running one by more than 2^8); O^T += V^T P^T, where
 //             the V tile is staged transposed (and key-permuted) so that a V^T fragment is one
 //             16-byte LDS read.
 //   replaced: no Q, no K, no QK^T and no running maximum: each entry is ea[j] * er[i-j] (one
@@ -23,16 +24,25 @@
 #include "saf_device.h"
 #include "saf_internal.h"
 
+#ifndef SAF_FWD_BK
+#define SAF_FWD_BK 64
+#endif
+#ifndef SAF_FWD_W64
+#define SAF_FWD_W64 4  // minimum waves per SIMD requested for d = 64 (fits in 128 VGPRs)
+#endif
+
 namespace saf {
 namespace {
 
 constexpr int kBQ = 128;  // queries per work item
 constexpr int kNT = 256;  // threads per block (4 waves)
 
+enum Kind { kOrdinary = 0, kProduct = 1, kExponential = 2 };
+
 template <typename TI, int D>
 struct FwdCfg {
   static constexpr bool BF = sizeof(TI) == 2;
-  static constexpr int BK = BF ? 64 : 32;                // keys per staged tile
+  static constexpr int BK = BF ? SAF_FWD_BK : 32;        // keys per staged tile
   static constexpr int NS = BK / 32;                     // 32-key subtiles per tile
   static constexpr int LDP = D + 16 / (int)sizeof(TI);   // padded LDS row (elements)
   static constexpr int EPC = 16 / (int)sizeof(TI);       // elements per 16-byte chunk
@@ -40,98 +50,95 @@ struct FwdCfg {
   static constexpr int CPT = BK * CPR / kNT;             // chunks per thread per tile
   static constexpr int LDT = BK + 16 / (int)sizeof(TI);  // padded row of the transposed V tile
   static constexpr int WIN = BK + kBQ;                   // distance window
+  static constexpr int WPT = (WIN + kNT - 1) / kNT;      // window values per thread
 };
 
-template <typename TI, int D>
-struct Prefetch {
-  uint4 k[FwdCfg<TI, D>::CPT];
-  Blocks4<TI, D, FwdCfg<TI, D>::BK, kNT> v;
-  float aw, rw;
+template <typename TI>
+struct FwdSmem {
+  TI* Ks;       // [BK][LDP]   K tile (ordinary items)
+  TI* VT;       // [D][LDT]    V tile transposed, key-permuted, swizzled
+  float* awin;  // [BK]        ea (or a*log2e) of the tile's keys
+  float* rwin;  // [WIN]       er (or r*log2e) of the tile's distance window
 };
 
-template <typename TI, int D>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void mixed_fwd_kernel(LayerArgs p) {
+struct FwdItem {
+  int b, h, q0, T, H;
+  size_t hoff;
+};
+
+template <typename TI, int D, int KIND>
+__device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& sm,
+                                         const FwdItem& it) {
   using C = FwdCfg<TI, D>;
   constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP, EPC = C::EPC, CPR = C::CPR, CPT = C::CPT;
-  constexpr int WIN = C::WIN, LDT = C::LDT;
-  __shared__ __attribute__((aligned(16))) TI Ks[BK * LDP];
-  __shared__ __attribute__((aligned(16))) TI VT[D * LDT];   // V tile transposed: [dcol][key]
-  __shared__ __attribute__((aligned(16))) float awin[BK];  // ea (or a*log2e) of the tile's keys
-  __shared__ float rwin[WIN];                              // er (or r*log2e) of its distances
-
-  const int T = p.T, H = p.H;
-  const int BH = p.B * H;
-  const int BHp = (BH + 7) & ~7;  // pad so that blockIdx % 8 (the XCD) depends on (b, h) only
-  const int nqb = (T + kBQ - 1) / kBQ;
-  const int x = blockIdx.x;
-  const int bh = x % BHp;
-  if (bh >= BH) return;
-  const int qb = nqb - 1 - x / BHp;  // heaviest query blocks first
-  const int b = bh / H, h = bh % H;
-  const bool rep = is_replaced(p.rep, h);
-  const bool fact = rep && p.pat.flag(h)[0] != 0;
-
+  constexpr int LDT = C::LDT, WIN = C::WIN, WPT = C::WPT;
+  constexpr bool ORD = KIND == kOrdinary, FACT = KIND == kProduct;
+  const int T = it.T, h = it.h, q0 = it.q0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int q0 = qb * kBQ;
   const int qw = q0 + w * 32;  // the wave's first query
   const int qi = qw + l32;     // the lane's query
-  const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
-  const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
-  const TI* K = reinterpret_cast<const TI*>(p.k) + hoff;
-  const TI* V = reinterpret_cast<const TI*>(p.v) + hoff;
-  const float* arow = rep ? (fact ? p.pat.ea(h) : p.a + (size_t)h * p.pat_len) : nullptr;
-  const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
-  const float wscale = fact ? 1.f : kLog2e;            // window values: ea/er, or a, r in log2 units
-  const float wfill = fact ? 0.f : -INFINITY;          // weight-zero filler
+  const TI* Q = reinterpret_cast<const TI*>(p.q) + it.hoff;
+  const TI* K = reinterpret_cast<const TI*>(p.k) + it.hoff;
+  const TI* V = reinterpret_cast<const TI*>(p.v) + it.hoff;
+  const float* arow = ORD ? nullptr : (FACT ? p.pat.ea(h) : p.a + (size_t)h * p.pat_len);
+  const float* rrow = ORD ? nullptr : (FACT ? p.pat.er(h) : p.r + (size_t)h * p.pat_len);
+  const float wscale = FACT ? 1.f : kLog2e;    // window values: ea/er, or a, r in log2 units
+  const float wfill = FACT ? 0.f : -INFINITY;  // weight-zero filler
 
   const int kend = min(T, q0 + kBQ);
   const int nkt = (kend + BK - 1) / BK;
 
   // ---- staging: global -> registers (next tile) -> LDS
-  Prefetch<TI, D> pf;
+  uint4 kreg[ORD ? CPT : 1];
+  Blocks4<TI, D, BK, kNT> vreg;
+  float awr = 0.f, rwr[WPT];
   auto load_tile = [&](int k0) {
-    pf.v.load(V, k0, T, tid);
-    if (!rep) {
+    vreg.load(V, k0, T, tid);
+    if (ORD) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + c * kNT;
         const int row = idx / CPR, cc = idx % CPR;
         const int g = k0 + row;
-        pf.k[c] = g < T ? *reinterpret_cast<const uint4*>(K + (size_t)g * D + cc * EPC)
+        kreg[c] = g < T ? *reinterpret_cast<const uint4*>(K + (size_t)g * D + cc * EPC)
                         : make_uint4(0u, 0u, 0u, 0u);
       }
-    }
-    if (rep) {
+    } else {
       const int d0 = q0 - k0 - (BK - 1);
-      if (tid < BK) pf.aw = (k0 + tid < T) ? arow[k0 + tid] * wscale : wfill;
-      if (tid < WIN) {
-        const int dist = d0 + tid;
-        pf.rw = (dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
+      if (tid < BK) awr = (k0 + tid < T) ? arow[k0 + tid] * wscale : wfill;
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) {
+        const int x = tid + j * kNT;
+        const int dist = d0 + x;
+        rwr[j] = (x < WIN && dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
       }
     }
   };
   auto store_tile = [&]() {
-    pf.v.template store_cols<LDT>(VT, tid);
-    if (!rep) {
+    vreg.template store_cols<LDT>(sm.VT, tid);
+    if (ORD) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int idx = tid + c * kNT;
         const int row = idx / CPR, cc = idx % CPR;
-        *reinterpret_cast<uint4*>(Ks + row * LDP + cc * EPC) = pf.k[c];
+        *reinterpret_cast<uint4*>(sm.Ks + row * LDP + cc * EPC) = kreg[c];
       }
-    }
-    if (rep) {
-      if (tid < BK) awin[tid] = pf.aw;
-      if (tid < WIN) rwin[tid] = pf.rw;
+    } else {
+      if (tid < BK) sm.awin[tid] = awr;
+#pragma unroll
+      for (int j = 0; j < WPT; ++j)
+        if (tid + j * kNT < WIN) sm.rwin[tid + j * kNT] = rwr[j];
     }
   };
 
-  Frag<TI> qf[D / 16];
+  Frag<TI> qf[ORD ? D / 16 : 1];
+  if (ORD) {
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    qf[t] = (!rep && qi < T) ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
-  const float lz_q = (rep && !fact && qi < T) ? p.pat.lz(h)[qi] : 0.f;
+    for (int t = 0; t < D / 16; ++t)
+      qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+  }
+  const float lz_q = (KIND == kExponential && qi < T) ? p.pat.lz(h)[qi] : 0.f;
   const float lz2_q = lz_q * kLog2e;
 
   f32x16 oacc[D / 32];
@@ -154,12 +161,12 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void m
       const int ks = k0 + 32 * s;
       if (ks > qw + 31 || ks >= T) break;  // wave-uniform: the rest of the tile is masked out
       float pv[16];
-      if (!rep) {
+      if (ORD) {
         f32x16 st;
         zero(st);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-          mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
+          mma16(st, load8(sm.Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
         float tmax = -INFINITY;
         if ((ks + 31 > qw) || (ks + 31 >= T)) {  // subtile crosses the diagonal or the end
 #pragma unroll
@@ -189,27 +196,18 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void m
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(pv[r], c2, -m));
-      } else if (fact) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int kk = 32 * s + 8 * g + 4 * hi;      // tile-relative first key of the run
-          const float4 a4 = *reinterpret_cast<const float4*>(awin + kk);
-          const int xr = (qi - q0) + (BK - 1) - kk;    // window index of distance qi - key
-          pv[4 * g + 0] = a4.x * rwin[xr];
-          pv[4 * g + 1] = a4.y * rwin[xr - 1];
-          pv[4 * g + 2] = a4.z * rwin[xr - 2];
-          pv[4 * g + 3] = a4.w * rwin[xr - 3];
-        }
       } else {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int kk = 32 * s + 8 * g + 4 * hi;
-          const float4 a4 = *reinterpret_cast<const float4*>(awin + kk);
-          const int xr = (qi - q0) + (BK - 1) - kk;
-          pv[4 * g + 0] = __builtin_amdgcn_exp2f(a4.x + rwin[xr] - lz2_q);
-          pv[4 * g + 1] = __builtin_amdgcn_exp2f(a4.y + rwin[xr - 1] - lz2_q);
-          pv[4 * g + 2] = __builtin_amdgcn_exp2f(a4.z + rwin[xr - 2] - lz2_q);
-          pv[4 * g + 3] = __builtin_amdgcn_exp2f(a4.w + rwin[xr - 3] - lz2_q);
+          const int kk = 32 * s + 8 * g + 4 * hi;    // tile-relative first key of the run
+          const float4 a4 = *reinterpret_cast<const float4*>(sm.awin + kk);
+          const int xr = (qi - q0) + (BK - 1) - kk;  // window index of distance qi - key
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float rv = sm.rwin[xr - e];
+            pv[4 * g + e] = FACT ? av[e] * rv : __builtin_amdgcn_exp2f(av[e] + rv - lz2_q);
+          }
         }
       }
 #pragma unroll
@@ -218,7 +216,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void m
         l += frag_sum(pfr);
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
-          mma16(oacc[c], tt_frag<TI, LDT>(VT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
+          mma16(oacc[c], tt_frag<TI, LDT>(sm.VT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
       }
     }
 
@@ -235,8 +233,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void m
   const float lt = l + __shfl_xor(l, 32);
   if (qi >= T) return;
   const float inv = 1.f / lt;
-  const float lse = !rep ? (m + log2f(lt)) * kLn2 : (fact ? p.pat.shift(h) : lz_q) + logf(lt);
-  TI* O = reinterpret_cast<TI*>(p.out) + hoff + (size_t)qi * D;
+  const float lse = ORD ? (m + log2f(lt)) * kLn2 : (FACT ? p.pat.shift(h) : lz_q) + logf(lt);
+  TI* O = reinterpret_cast<TI*>(p.out) + it.hoff + (size_t)qi * D;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
 #pragma unroll
@@ -245,7 +243,39 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void m
       store4(O + dc, oacc[c][4 * g] * inv, oacc[c][4 * g + 1] * inv, oacc[c][4 * g + 2] * inv,
              oacc[c][4 * g + 3] * inv);
     }
-  if (hi == 0) p.lse[((size_t)b * H + h) * T + qi] = lse;
+  if (hi == 0) p.lse[((size_t)it.b * it.H + h) * T + qi] = lse;
+}
+
+template <typename TI, int D>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? SAF_FWD_W64 : 2)))
+void mixed_fwd_kernel(LayerArgs p) {
+  using C = FwdCfg<TI, D>;
+  __shared__ __attribute__((aligned(16))) TI Ks[C::BK * C::LDP];
+  __shared__ __attribute__((aligned(16))) TI VT[D * C::LDT];
+  __shared__ __attribute__((aligned(16))) float awin[C::BK];
+  __shared__ float rwin[C::WIN];
+
+  const int T = p.T, H = p.H;
+  const int BH = p.B * H;
+  const int BHp = (BH + 7) & ~7;  // pad so that blockIdx % 8 (the XCD) depends on (b, h) only
+  const int nqb = (T + kBQ - 1) / kBQ;
+  const int x = blockIdx.x;
+  const int bh = x % BHp;
+  if (bh >= BH) return;
+  FwdItem it;
+  it.T = T;
+  it.H = H;
+  it.b = bh / H;
+  it.h = bh % H;
+  it.q0 = (nqb - 1 - x / BHp) * kBQ;  // heaviest query blocks first
+  it.hoff = ((size_t)it.b * H + it.h) * (size_t)T * D;
+  const FwdSmem<TI> sm{Ks, VT, awin, rwin};
+  if (!is_replaced(p.rep, it.h))
+    fwd_item<TI, D, kOrdinary>(p, sm, it);
+  else if (p.pat.flag(it.h)[0] != 0)
+    fwd_item<TI, D, kProduct>(p, sm, it);
+  else
+    fwd_item<TI, D, kExponential>(p, sm, it);
 }
 
 template <typename TI, int D>
