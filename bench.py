@@ -142,6 +142,55 @@ def time_steps(torch, layer, steps, warmup, trace=None):
     return (t1 - t0) / steps
 
 
+def calibration(torch, saf, w, steps=3):
+    """Time saf_calibrate on the workload's calibration shape (N sequences of its H, T, d; Q, K
+    N(0,1) bf16, drawn on the GPU).  Algorithmic work: two passes of s Q K^T over the causal entries
+    (row statistics, then the mean / deviation tiles): 4d flops per entry per sequence per head."""
+    N, H, T, d = w.calib_N, w.H, w.T, w.d
+    g = torch.Generator(device="cuda").manual_seed(1437)
+    q = torch.randn((N, H, T, d), device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((N, H, T, d), device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+    ahat = torch.empty((H, T, T), dtype=torch.float32, device="cuda")
+    svar = torch.empty((H,), dtype=torch.float64, device="cuda")
+    nws = saf.saf_calibrate_workspace_size(N, H, T, d)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    call = lambda: saf._check(saf.saf_calibrate(saf.SAF_BF16, N, H, T, d, q.data_ptr(), k.data_ptr(),  # noqa: E731
+                                                0.0, ahat.data_ptr(), svar.data_ptr(), ws.data_ptr(),
+                                                nws, stream), "saf_calibrate")
+    call()
+    torch.cuda.synchronize()
+    trace = saf.KernelTrace(capacity=4 * steps)
+    trace.begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    trace.end()
+    trace.collect()
+    c = T * (T + 1) / 2.0
+    kf = {"calib_lse": N * H * c * 2 * d, "calib_stats": N * H * c * 2 * d, "calib_reduce": 0.0}
+    kernels = {}
+    for name, st in trace.summary().items():
+        ent = {"avg_ms": round(st["avg_ms"], 4), "launches": st["launches"]}
+        if kf.get(name):
+            ent["tflops"] = round(kf[name] / (st["avg_ms"] * 1e-3) / 1e12, 1)
+        kernels[name] = ent
+    dom = max(trace.summary().items(), key=lambda kv: kv[1]["total_ms"])[0]
+    ach = kf[dom] / (trace.summary()[dom]["avg_ms"] * 1e-3) / 1e12
+    trace.close()
+    flops = kf["calib_lse"] + kf["calib_stats"]
+    return {"workload": "%s calibration: N=%d, H=%d, T=%d, d=%d, bf16" % (w.name, N, H, T, d),
+            "ms": round(dt * 1e3, 3), "tflops": round(flops / dt / 1e12, 1),
+            "pct_bf16_peak": round(100 * flops / dt / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "ahat_write_gbs": round(4.0 * H * T * T / dt / 1e9, 1), "kernels": kernels,
+            "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(w.name + "_calibration", dom)}}
+
+
 def cpu_baseline(w, replaced, min_seconds=10.0):
     """The fp64 oracle, as it stands, on whole sequences of the same workload (all heads, full T),
     one after another until at least min_seconds of CPU work (or the whole batch) is done."""
@@ -177,6 +226,9 @@ def main():
     ap.add_argument("--workload", default="l124m_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true")
+    ap.add_argument("--calibration-workload", default="l1b_t8192",
+                    help="workload whose calibration shape (N sequences) is timed")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (calibrates the HBM "
                          "byte counters of a profiler against a known size) and exit")
@@ -267,6 +319,11 @@ def main():
         var["replaced_vs_ordinary_time_per_head"] = round(
             var["all_replaced"]["ms_per_step"] / var["all_ordinary"]["ms_per_step"], 4)
         out["variants"] = var
+
+    if not args.no_calibration:
+        cw = synth.WORKLOADS[args.calibration_workload]
+        if cw.calib_N:
+            out["calibration"] = calibration(torch, saf, cw)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, replaced)
