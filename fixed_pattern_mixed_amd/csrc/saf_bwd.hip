@@ -277,15 +277,12 @@ struct DqCfg {
   static constexpr int NS = BK / 32;
   static constexpr int LDP = D + 16 / (int)sizeof(TI);
   static constexpr int LDT = BK + 16 / (int)sizeof(TI);
-  static constexpr int EPC = 16 / (int)sizeof(TI);
-  static constexpr int CPR = D / EPC;
-  static constexpr int CPT = BK * CPR / kNT;
 };
 
 template <typename TI, int D>
 struct DqPrefetch {
   Blocks4<TI, D, DqCfg<TI, D>::BK, kNT> k;
-  uint4 v[DqCfg<TI, D>::CPT];
+  Chunks<TI, D, DqCfg<TI, D>::BK, kNT> v;
 };
 
 template <typename TI, int D>
@@ -293,7 +290,6 @@ __global__ __launch_bounds__(kNT)
 __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel(LayerArgs p) {
   using C = DqCfg<TI, D>;
   constexpr int BQ = C::BQ, BK = C::BK, NS = C::NS, LDP = C::LDP, LDT = C::LDT;
-  constexpr int EPC = C::EPC, CPR = C::CPR, CPT = C::CPT;
   __shared__ __attribute__((aligned(16))) TI Ks[BK * LDP];   // K tile, rows
   __shared__ __attribute__((aligned(16))) TI KT[D * LDT];    // K tile transposed [dim][key]
   __shared__ __attribute__((aligned(16))) TI Vs[BK * LDP];   // V tile, rows
@@ -338,24 +334,12 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   DqPrefetch<TI, D> pf;
   auto load_tile = [&](int k0) {
     pf.k.load(K, k0, T, tid);
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kNT;
-      const int row = idx / CPR, cc = idx % CPR;
-      const int g = k0 + row;
-      pf.v[c] = g < T ? *reinterpret_cast<const uint4*>(V + (size_t)g * D + cc * EPC)
-                      : make_uint4(0u, 0u, 0u, 0u);
-    }
+    pf.v.load(V, k0, T, tid);
   };
   auto store_tile = [&]() {
     pf.k.template store_rows<LDP>(Ks, tid);
     pf.k.template store_cols<LDT>(KT, tid);
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * kNT;
-      const int row = idx / CPR, cc = idx % CPR;
-      *reinterpret_cast<uint4*>(Vs + row * LDP + cc * EPC) = pf.v[c];
-    }
+    pf.v.template store<LDP>(Vs, tid);
   };
 
   const int kend = min(T, q0 + BQ);

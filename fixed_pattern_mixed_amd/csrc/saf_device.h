@@ -251,8 +251,19 @@ struct Blocks4 {
     const int g = (i >> 4) % (ROWS / 4);
     return 4 * ((g & ~3) | ((g & 1) << 1) | ((g & 2) >> 1));
   }
-  // rows >= T are zero
+  // rows >= T are zero; a tile entirely inside [0, T) takes the branch-free path
   __device__ __forceinline__ void load(const TI* g, int row0, int T, int tid) {
+    if (row0 + ROWS <= T) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int i = tid + n * NT;
+        if (NBLK % NT != 0 && i >= NBLK) break;
+        const TI* src = g + (size_t)(row0 + row_of(i)) * D + col_of(i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[n][k] = load_quad(src + (size_t)k * D);
+      }
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int i = tid + n * NT;
@@ -287,6 +298,38 @@ struct Blocks4 {
       transpose4(q[n], t);
 #pragma unroll
       for (int k = 0; k < 4; ++k) store_quad(tt + (c + k) * LDT + (tpos(r) ^ tswz(c + k)), t[k]);
+    }
+  }
+};
+
+// Rows [row0, row0+ROWS) of a [T][D] matrix as 16-byte chunks: chunk c of thread tid is
+// idx = tid + c*NT -> row idx / (D/EPC), chunk idx % (D/EPC).  Rows >= T are zero.
+template <typename TI, int D, int ROWS, int NT>
+struct Chunks {
+  static constexpr int EPC = 16 / sizeof(TI);
+  static constexpr int CPR = D / EPC;
+  static constexpr int CPT = ROWS * CPR / NT;
+  static_assert(CPT * NT == ROWS * CPR, "tile must split evenly into chunks");
+  uint4 v[CPT];
+  __device__ __forceinline__ void load(const TI* g, int row0, int T, int tid) {
+    const bool full = row0 + ROWS <= T;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const int row = row0 + idx / CPR;
+      const TI* src = g + (size_t)row * D + (idx % CPR) * EPC;
+      if (full)
+        v[c] = *reinterpret_cast<const uint4*>(src);
+      else
+        v[c] = row < T ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  template <int LDP>
+  __device__ __forceinline__ void store(TI* lds, int tid) const {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      *reinterpret_cast<uint4*>(lds + (idx / CPR) * LDP + (idx % CPR) * EPC) = v[c];
     }
   }
 };

@@ -45,9 +45,6 @@ struct FwdCfg {
   static constexpr int BK = BF ? SAF_FWD_BK : 32;        // keys per staged tile
   static constexpr int NS = BK / 32;                     // 32-key subtiles per tile
   static constexpr int LDP = D + 16 / (int)sizeof(TI);   // padded LDS row (elements)
-  static constexpr int EPC = 16 / (int)sizeof(TI);       // elements per 16-byte chunk
-  static constexpr int CPR = D / EPC;                    // chunks per row
-  static constexpr int CPT = BK * CPR / kNT;             // chunks per thread per tile
   static constexpr int LDT = BK + 16 / (int)sizeof(TI);  // padded row of the transposed V tile
   static constexpr int WIN = BK + kBQ;                   // distance window
   static constexpr int WPT = (WIN + kNT - 1) / kNT;      // window values per thread
@@ -70,7 +67,7 @@ template <typename TI, int D, int KIND>
 __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& sm,
                                          const FwdItem& it) {
   using C = FwdCfg<TI, D>;
-  constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP, EPC = C::EPC, CPR = C::CPR, CPT = C::CPT;
+  constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP;
   constexpr int LDT = C::LDT, WIN = C::WIN, WPT = C::WPT;
   constexpr bool ORD = KIND == kOrdinary, FACT = KIND == kProduct;
   const int T = it.T, h = it.h, q0 = it.q0;
@@ -90,20 +87,13 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   const int nkt = (kend + BK - 1) / BK;
 
   // ---- staging: global -> registers (next tile) -> LDS
-  uint4 kreg[ORD ? CPT : 1];
+  Chunks<TI, D, BK, kNT> kreg;
   Blocks4<TI, D, BK, kNT> vreg;
   float awr = 0.f, rwr[WPT];
   auto load_tile = [&](int k0) {
     vreg.load(V, k0, T, tid);
     if (ORD) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int idx = tid + c * kNT;
-        const int row = idx / CPR, cc = idx % CPR;
-        const int g = k0 + row;
-        kreg[c] = g < T ? *reinterpret_cast<const uint4*>(K + (size_t)g * D + cc * EPC)
-                        : make_uint4(0u, 0u, 0u, 0u);
-      }
+      kreg.load(K, k0, T, tid);
     } else {
       const int d0 = q0 - k0 - (BK - 1);
       if (tid < BK) awr = (k0 + tid < T) ? arow[k0 + tid] * wscale : wfill;
@@ -118,12 +108,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   auto store_tile = [&]() {
     vreg.template store_cols<LDT>(sm.VT, tid);
     if (ORD) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int idx = tid + c * kNT;
-        const int row = idx / CPR, cc = idx % CPR;
-        *reinterpret_cast<uint4*>(sm.Ks + row * LDP + cc * EPC) = kreg[c];
-      }
+      kreg.template store<LDP>(sm.Ks, tid);
     } else {
       if (tid < BK) sm.awin[tid] = awr;
 #pragma unroll
@@ -247,7 +232,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
 }
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? SAF_FWD_W64 : 2)))
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? SAF_FWD_W64 : 2)))
 void mixed_fwd_kernel(LayerArgs p) {
   using C = FwdCfg<TI, D>;
   __shared__ __attribute__((aligned(16))) TI Ks[C::BK * C::LDP];
