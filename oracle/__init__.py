@@ -15,6 +15,10 @@ What it computes:
   backward        ordinary: dq, dk, dv; replaced: dv = P^T dO, dq = dk = 0   [Notes §二.4]
   calibration     Ahat = mean_n A^(n), s_var = sum_n ||A^(n)-Ahat||_F^2 / ((N-1) T^2)
                                                                              [Notes §二.1, Eq.(1)]
+  KL score        mean_n,i KL(A^(n)_i || Ahat_i) (the alternative selector)  [Notes §二.1]
+  head selection  ascending score across layers, k = round(r L H)            [Notes §二.1]
+  pattern grad    dL/da, dL/dr when a replaced head's pattern is trained     [Paper page] Table 14
+  compact fit     Adam on the row-wise cross-entropy to Ahat                 [Notes §二.3]
 """
 from __future__ import annotations
 
@@ -57,9 +61,19 @@ class _Lib:
         lib.orc_head_calibrate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp,
                                            ctypes.c_double, ctypes.c_int, _ip, _dp, _dp]
         lib.orc_calibrate_maps.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
+        lib.orc_head_kl_score.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp,
+                                          ctypes.c_double, ctypes.c_int, _ip, _dp]
+        lib.orc_kl_maps.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp]
+        lib.orc_head_pattern_grad.argtypes = [ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp,
+                                              _dp, _dp]
+        lib.orc_fit_loss_grad.argtypes = [ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.orc_fit_pattern.argtypes = [ctypes.c_int, _dp, ctypes.c_int, ctypes.c_double, _dp,
+                                        _dp, _dp, _dp]
         lib.orc_num_threads.argtypes = []
         for f in (lib.orc_head_fwd, lib.orc_head_pattern, lib.orc_head_bwd,
-                  lib.orc_head_calibrate, lib.orc_calibrate_maps, lib.orc_num_threads):
+                  lib.orc_head_calibrate, lib.orc_calibrate_maps, lib.orc_head_kl_score,
+                  lib.orc_kl_maps, lib.orc_head_pattern_grad, lib.orc_fit_loss_grad,
+                  lib.orc_fit_pattern, lib.orc_num_threads):
             f.restype = ctypes.c_int
         self.c = lib
 
@@ -205,6 +219,87 @@ def calibrate_maps(maps):
     return ahat, sv.value
 
 
+def head_kl_score(q, k, scale=None, rows=None):
+    """Row-wise forward-KL terms of one head from q, k [N, T, d]: kl[x] = sum_n KL(A^(n)_i ||
+    Ahat_i) for row i = rows[x]; the head's score is kl.sum() / (N T) over all rows."""
+    lib = _load()
+    q, k = _f64(q), _f64(k)
+    N, T, d = q.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    rows, rp = _rows(rows, T)
+    kl = np.zeros(len(rows))
+    _check(lib.orc_head_kl_score(N, T, d, _p(q), _p(k), scale, len(rows), rp, _p(kl)),
+           "head_kl_score")
+    return kl
+
+
+def kl_maps(maps):
+    """Forward-KL score from dense maps [N, T, T]."""
+    lib = _load()
+    maps = _f64(maps)
+    N, T, _ = maps.shape
+    out = ctypes.c_double(0.0)
+    _check(lib.orc_kl_maps(N, T, _p(maps), ctypes.byref(out)), "kl_maps")
+    return out.value
+
+
+def head_pattern_grad(v, dout, a, r):
+    """dL/da, dL/dr [T] of one replaced-head slice (v, dout [T, d]; a, r at least T long)."""
+    lib = _load()
+    v, dout = _f64(v), _f64(dout)
+    T, d = v.shape
+    a, r = _f64(a)[:T].copy(), _f64(r)[:T].copy()
+    da, dr = np.zeros(T), np.zeros(T)
+    _check(lib.orc_head_pattern_grad(T, d, _p(v), _p(dout), _p(a), _p(r), _p(da), _p(dr)),
+           "head_pattern_grad")
+    return da, dr
+
+
+def fit_loss_grad(ahat, a, r):
+    """Mean row cross-entropy of the pattern (a, r) against ahat [T, T] and its gradient."""
+    lib = _load()
+    ahat = _f64(ahat)
+    T = ahat.shape[0]
+    a, r = _f64(a), _f64(r)
+    ga, gr = np.zeros(T), np.zeros(T)
+    loss = ctypes.c_double(0.0)
+    _check(lib.orc_fit_loss_grad(T, _p(ahat), _p(a), _p(r), ctypes.byref(loss), _p(ga), _p(gr)),
+           "fit_loss_grad")
+    return loss.value, ga, gr
+
+
+def fit_pattern(ahat, steps=400, lr=0.05):
+    """Compact fit of one target pattern ahat [T, T].  Returns (a, r, loss, mean row KL)."""
+    lib = _load()
+    ahat = _f64(ahat)
+    T = ahat.shape[0]
+    a, r = np.zeros(T), np.zeros(T)
+    loss, kl = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check(lib.orc_fit_pattern(T, _p(ahat), int(steps), float(lr), _p(a), _p(r),
+                               ctypes.byref(loss), ctypes.byref(kl)), "fit_pattern")
+    return a, r, loss.value, kl.value
+
+
+def select_heads(score, ratio, accepted=None):
+    """Head selection ([Notes §二.1]): every head of every layer ranked by ascending score, ties
+    by (layer, head); k = round(ratio * L * H) with halves to even (Python's round); the first k
+    ranked heads that are accepted (all when accepted is None) are selected.  score [L, H].
+    Returns (replaced [L, H] uint8, number selected)."""
+    score = np.asarray(score, dtype=np.float64)
+    L, H = score.shape
+    k = round(ratio * L * H)
+    ranked = sorted((float(score[l, h]), l, h) for l in range(L) for h in range(H))
+    out = np.zeros((L, H), dtype=np.uint8)
+    taken = 0
+    for _, l, h in ranked:
+        if taken == k:
+            break
+        if accepted is None or accepted[l][h]:
+            out[l, h] = 1
+            taken += 1
+    return out, taken
+
+
 # ------------------------------------------------------------------------------ whole layer
 def _heads(B, H, heads):
     return [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
@@ -235,6 +330,29 @@ def layer_bwd(q, k, v, dout, replaced, a, r, scale=None, heads=None, qrows=None,
             out[(b, h)] = head_bwd(0, v[b, h], dout[b, h], q=q[b, h], k=k[b, h], scale=scale,
                                    qrows=qrows, krows=krows)
     return out
+
+
+def pattern_grad(v, dout, replaced, a, r, heads=None):
+    """dL/da, dL/dr of the replaced heads, summed over batch: {h: (da [T], dr [T])}."""
+    B, H, T, d = v.shape
+    out = {}
+    for h in (range(H) if heads is None else heads):
+        if not replaced[h]:
+            continue
+        da, dr = np.zeros(T), np.zeros(T)
+        for b in range(B):
+            x, y = head_pattern_grad(v[b, h], dout[b, h], a[h], r[h])
+            da += x
+            dr += y
+        out[h] = (da, dr)
+    return out
+
+
+def kl_score(q, k, scale=None, heads=None):
+    """Forward-KL score per head over N sequences, q, k [N, H, T, d]: {h: s_kl}."""
+    N, H, T, d = q.shape
+    return {h: float(head_kl_score(q[:, h], k[:, h], scale=scale).sum()) / (N * T)
+            for h in (range(H) if heads is None else heads)}
 
 
 def calibrate(q, k, scale=None, heads=None, rows=None):

@@ -24,6 +24,9 @@
  *                   replaced: dV = P^T dO only, alpha and rho are frozen      [Notes §二.4]
  *   calibration     Ahat = (1/N) sum_n A^(n);  s_var = sum_n ||A^(n) - Ahat||_F^2 / ((N-1) T^2)
  *                                                                             [Notes §二.1, Eq.(1)]
+ *   KL score        mean over sequences and rows of KL(A^(n)_i || Ahat_i)     [Notes §二.1]
+ *   pattern grad    dL/da, dL/dr of a replaced head whose pattern is trained  [Paper page] Table 14
+ *   compact fit     a, r minimising the row-wise cross-entropy to Ahat by Adam [Notes §二.3]
  * A row's softmax is evaluated as exp(t_j - m) / sum_k exp(t_k - m) with m the row maximum, which is
  * the same quantity as exp(t_j) / sum_k exp(t_k) (the common factor exp(-m) cancels) but cannot
  * overflow.  The log normaliser is reported as m + log(sum_k exp(t_k - m)) = log sum_k exp(t_k).
@@ -35,6 +38,8 @@
  *   - key j is visible to query i iff j <= i (self included) for both head kinds.
  *   - -inf in a or r is allowed and gives weight 0; a row whose entries are all -inf is undefined.
  *   - Eq. (1) counts all T^2 entries (the upper triangle is 0 in every map and in the mean).
+ *   - the "row-wise forward KL" selector is KL(A^(n)_i || Ahat_i), averaged over n and rows.
+ *   - the compact fit starts from a = r = 0 with Adam step size lr (the pages give neither).
  *
  * Return value of every entry point: 0 on success, -1 on an invalid argument (nothing written).
  */
@@ -346,6 +351,207 @@ ORC_EXPORT int orc_calibrate_maps(int N, int T, const double* maps, double* ahat
       acc += x * x;
     }
   *svar = acc / ((double)(N - 1) * (double)T * (double)T);
+  return 0;
+}
+
+/*
+ * Row-wise forward-KL score of one head (the alternative selector of [Notes §二.1]; the pages name
+ * it but print no formula, so the plainest reading is taken: the KL divergence of each sequence's
+ * row from the mean row, summed).  For each listed row i:
+ *   kl[x] = sum_n sum_{j<=i} A^(n)(i,j) * ln(A^(n)(i,j) / Ahat(i,j)),   Ahat = mean_n A^(n),
+ * a term with A^(n)(i,j) = 0 counting 0.  The score of the head is sum_x kl[x] / (N T) over all rows.
+ */
+ORC_EXPORT int orc_head_kl_score(int N, int T, int d, const double* q, const double* k,
+                                 double scale, int nrows, const int* rows, double* kl) {
+  if (N < 2 || T < 1 || d < 1 || !q || !k || !kl || !rows_ok(T, nrows, rows)) return -1;
+#pragma omp parallel
+  {
+    double* t = (double*)malloc(sizeof(double) * (size_t)T);
+    double* A = (double*)malloc(sizeof(double) * (size_t)N * T);
+    double* mean = (double*)malloc(sizeof(double) * (size_t)T);
+#pragma omp for schedule(dynamic, 4)
+    for (int x = 0; x < nrows; ++x) {
+      const int i = rows[x];
+      for (int n = 0; n < N; ++n) {
+        ordinary_logits(d, q + (size_t)n * T * d, k + (size_t)n * T * d, scale, i, t);
+        softmax_row(i, t, A + (size_t)n * T);
+      }
+      for (int j = 0; j <= i; ++j) {
+        double s = 0.0;
+        for (int n = 0; n < N; ++n) s += A[(size_t)n * T + j];
+        mean[j] = s / N;
+      }
+      double acc = 0.0;
+      for (int n = 0; n < N; ++n)
+        for (int j = 0; j <= i; ++j) {
+          const double an = A[(size_t)n * T + j];
+          if (an > 0.0) acc += an * log(an / mean[j]);
+        }
+      kl[x] = acc;
+    }
+    free(t);
+    free(A);
+    free(mean);
+  }
+  return 0;
+}
+
+/* The same score from N dense maps [N][T][T] (tiny T only): *skl = sum_n sum_i KL / (N T). */
+ORC_EXPORT int orc_kl_maps(int N, int T, const double* maps, double* skl) {
+  if (N < 2 || T < 1 || !maps || !skl) return -1;
+  const size_t TT = (size_t)T * T;
+  double acc = 0.0;
+  for (size_t e = 0; e < TT; ++e) {
+    double s = 0.0;
+    for (int n = 0; n < N; ++n) s += maps[(size_t)n * TT + e];
+    const double mean = s / N;
+    for (int n = 0; n < N; ++n) {
+      const double an = maps[(size_t)n * TT + e];
+      if (an > 0.0) acc += an * log(an / mean);
+    }
+  }
+  *skl = acc / ((double)N * (double)T);
+  return 0;
+}
+
+/*
+ * Gradient of the loss with respect to a replaced head's pattern logits, one (batch, head) slice
+ * (the trainable-pattern variant of [Paper page] Table 14, where a and r are trained instead of
+ * frozen).  The pattern row is p_i = softmax over j <= i of t(i,j) = a(j) + r(i-j) ([Notes Eq.(3)])
+ * and o_i = sum_j p_i(j) v_j.  With g(i,j) = dL/dp_i(j) = dout_i . v_j the softmax chain rule gives
+ *   dL/dt(i,j) = p_i(j) * (g(i,j) - sum_k p_i(k) g(i,k)),
+ * and t(i,j) depends on a(j) and r(i-j) with coefficient 1, so
+ *   da[j] += sum_{i>=j} dL/dt(i,j),   dr[delta] += sum_i dL/dt(i, i-delta).
+ * ACCUMULATES into da[0..T-1] and dr[0..T-1] (the caller sums slices of the same head over batch).
+ * Rows are split into contiguous per-thread ranges and the per-thread sums are added in thread
+ * order, so a fixed thread count gives the same bits on every run.
+ */
+ORC_EXPORT int orc_head_pattern_grad(int T, int d, const double* v, const double* dout,
+                                     const double* a, const double* r, double* da, double* dr) {
+  if (T < 1 || d < 1 || !v || !dout || !a || !r || !da || !dr) return -1;
+  int nth = 1;
+#ifdef _OPENMP
+  nth = omp_get_max_threads();
+#endif
+  double* part = (double*)calloc((size_t)nth * 2 * T, sizeof(double));
+#pragma omp parallel num_threads(nth)
+  {
+    int th = 0;
+#ifdef _OPENMP
+    th = omp_get_thread_num();
+#endif
+    double* pa = part + (size_t)th * 2 * T;
+    double* pr = pa + T;
+    double* t = (double*)malloc(sizeof(double) * (size_t)T);
+    double* p = (double*)malloc(sizeof(double) * (size_t)T);
+    double* g = (double*)malloc(sizeof(double) * (size_t)T);
+#pragma omp for schedule(static)
+    for (int i = 0; i < T; ++i) {
+      replaced_logits(a, r, i, t);
+      softmax_row(i, t, p);
+      const double* gi = dout + (size_t)i * d;
+      double pg = 0.0;
+      for (int j = 0; j <= i; ++j) {
+        const double* vj = v + (size_t)j * d;
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc += gi[c] * vj[c];
+        g[j] = acc;
+        pg += p[j] * acc;
+      }
+      for (int j = 0; j <= i; ++j) {
+        const double dt = p[j] * (g[j] - pg);
+        pa[j] += dt;
+        pr[i - j] += dt;
+      }
+    }
+    free(t);
+    free(p);
+    free(g);
+  }
+  for (int th = 0; th < nth; ++th)
+    for (int x = 0; x < T; ++x) {
+      da[x] += part[(size_t)th * 2 * T + x];
+      dr[x] += part[(size_t)th * 2 * T + T + x];
+    }
+  free(part);
+  return 0;
+}
+
+/*
+ * Compact fit of one head's target pattern Ahat [T][T] by a, r ([Notes §二.3]: the row-wise
+ * cross-entropy against the target pattern is minimised; [Notes §二.3] / Appendix A.2: 400 Adam
+ * steps, mean row KL at most 0.2 nat to accept).  The loss, averaged over rows, is
+ *   L(a, r) = -(1/T) sum_i sum_{j<=i} Ahat(i,j) ln p_i(j),   p_i = softmax_j (a(j) + r(i-j)),
+ * and its gradient by the chain rule of the log-softmax is
+ *   dL/dt(i,j) = (1/T) (p_i(j) * sum_k Ahat(i,k) - Ahat(i,j)),
+ *   dL/da(j) = sum_{i>=j} dL/dt(i,j),   dL/dr(delta) = sum_i dL/dt(i, i-delta).
+ * orc_fit_loss_grad evaluates L and (if ga, gr are not NULL) the gradient at (a, r).
+ */
+ORC_EXPORT int orc_fit_loss_grad(int T, const double* ahat, const double* a, const double* r,
+                                 double* loss, double* ga, double* gr) {
+  if (T < 1 || !ahat || !a || !r || !loss) return -1;
+  double* t = (double*)malloc(sizeof(double) * (size_t)T);
+  double* p = (double*)malloc(sizeof(double) * (size_t)T);
+  if (ga) memset(ga, 0, sizeof(double) * (size_t)T);
+  if (gr) memset(gr, 0, sizeof(double) * (size_t)T);
+  double L = 0.0;
+  for (int i = 0; i < T; ++i) {
+    const double* ai = ahat + (size_t)i * T;
+    replaced_logits(a, r, i, t);
+    const double lz = softmax_row(i, t, p);
+    double rowsum = 0.0;
+    for (int j = 0; j <= i; ++j) {
+      rowsum += ai[j];
+      if (ai[j] != 0.0) L -= ai[j] * (t[j] - lz);  /* ln p_i(j) = t(i,j) - ln Z(i) */
+    }
+    if (ga || gr)
+      for (int j = 0; j <= i; ++j) {
+        const double g = (p[j] * rowsum - ai[j]) / T;
+        if (ga) ga[j] += g;
+        if (gr) gr[i - j] += g;
+      }
+  }
+  *loss = L / T;
+  free(t);
+  free(p);
+  return 0;
+}
+
+/*
+ * The fit itself: a = r = 0 (the uniform causal pattern), then `steps` Adam updates of (a, r) on L
+ * with step size lr and the usual moment rates (beta1 = 0.9, beta2 = 0.999, eps = 1e-8, bias
+ * correction on both moments).  On return a, r hold the fitted logits, *loss the final L and *kl
+ * the mean row KL(Ahat_i || p_i) = L + (1/T) sum Ahat ln Ahat (the acceptance measure).
+ */
+ORC_EXPORT int orc_fit_pattern(int T, const double* ahat, int steps, double lr, double* a,
+                               double* r, double* loss, double* kl) {
+  if (T < 1 || steps < 0 || !(lr > 0.0) || !ahat || !a || !r || !loss || !kl) return -1;
+  const double b1 = 0.9, b2 = 0.999, eps = 1e-8;
+  double* g = (double*)malloc(sizeof(double) * 2 * (size_t)T);
+  double* m = (double*)calloc(2 * (size_t)T, sizeof(double));
+  double* v = (double*)calloc(2 * (size_t)T, sizeof(double));
+  memset(a, 0, sizeof(double) * (size_t)T);
+  memset(r, 0, sizeof(double) * (size_t)T);
+  double L = 0.0;
+  for (int s = 1; s <= steps; ++s) {
+    orc_fit_loss_grad(T, ahat, a, r, &L, g, g + T);
+    const double c1 = 1.0 - pow(b1, s), c2 = 1.0 - pow(b2, s);
+    for (int x = 0; x < 2 * T; ++x) {
+      m[x] = b1 * m[x] + (1.0 - b1) * g[x];
+      v[x] = b2 * v[x] + (1.0 - b2) * g[x] * g[x];
+      double* w = x < T ? &a[x] : &r[x - T];
+      *w -= lr * (m[x] / c1) / (sqrt(v[x] / c2) + eps);
+    }
+  }
+  orc_fit_loss_grad(T, ahat, a, r, &L, NULL, NULL);
+  double ent = 0.0;
+  for (size_t e = 0; e < (size_t)T * T; ++e)
+    if (ahat[e] > 0.0) ent += ahat[e] * log(ahat[e]);
+  *loss = L;
+  *kl = L + ent / T;
+  free(g);
+  free(m);
+  free(v);
   return 0;
 }
 

@@ -332,10 +332,240 @@ def check_causal_prefix():
         assert _rel(o1, o2[:T1]) <= 1e-15 and np.abs(l1 - l2[:T1]).max() <= 1e-14
 
 
+# ------------------------------------------------ forward-KL selector and head selection ([Notes §二.1])
+def check_kl_golden():
+    g = read_golden("kl_n2_t2.txt")
+    maps = np.stack([g["A1"].reshape(2, 2), g["A2"].reshape(2, 2)])
+    assert abs(oracle.kl_maps(maps) * 4 - g["kl_sum"][0]) <= 1e-15
+
+
+def check_kl_vs_library():
+    """The streamed score equals KL by scipy (rel_entr) on dense maps built by torch, and the
+    Jensen-gap form (1/T) sum_i [H(Ahat_i) - mean_n H(A^(n)_i)] with scipy's entropy."""
+    import scipy.stats
+    rng = np.random.default_rng(30)
+    N, T, d = 4, 9, 5
+    q, k = rng.normal(size=(N, T, d)), rng.normal(size=(N, T, d))
+    maps = _torch_maps(q, k, 1.0 / math.sqrt(d))
+    ahat = maps.mean(0)
+    rows = oracle.head_kl_score(q, k)
+    for i in range(T):
+        want = sum(scipy.special.rel_entr(maps[n, i, :i + 1], ahat[i, :i + 1]).sum() for n in range(N))
+        assert abs(rows[i] - want) <= 1e-13 * max(1.0, want)
+    skl = rows.sum() / (N * T)
+    jensen = np.mean([scipy.stats.entropy(ahat[i, :i + 1]) -
+                      np.mean([scipy.stats.entropy(maps[n, i, :i + 1]) for n in range(N)])
+                      for i in range(T)])
+    assert abs(skl - jensen) <= 1e-13 and skl > 0.0
+    assert abs(oracle.kl_maps(maps) - skl) <= 1e-14
+
+
+def check_kl_special_cases():
+    """Identical maps or Q = 0 (every map uniform) give a score of exactly 0."""
+    rng = np.random.default_rng(31)
+    N, T, d = 3, 7, 4
+    q, k = rng.normal(size=(1, T, d)), rng.normal(size=(1, T, d))
+    assert abs(oracle.head_kl_score(np.repeat(q, N, 0), np.repeat(k, N, 0)).sum()) <= 1e-14
+    assert abs(oracle.head_kl_score(np.zeros((N, T, d)), rng.normal(size=(N, T, d))).sum()) <= 1e-14
+
+
+def check_select_golden():
+    g = read_golden("select_ties.txt")
+    score = g["score"].reshape(2, 3)
+    for key, ratio in (("sel_half", 0.5), ("sel_quarter", 0.25), ("sel_twelfth", 1 / 12)):
+        sel, n = oracle.select_heads(score, ratio)
+        assert np.array_equal(sel.ravel(), g[key].astype(np.uint8)) and n == int(g[key].sum())
+    acc = g["accepted"].reshape(2, 3).astype(np.uint8)
+    sel, n = oracle.select_heads(score, 0.5, accepted=acc)
+    assert np.array_equal(sel.ravel(), g["sel_half_accepted"].astype(np.uint8)) and n == 3
+
+
+def check_select_brute_force():
+    """With distinct scores the selection is the unique k-subset of accepted heads of least total
+    score (brute force over all subsets)."""
+    import itertools
+    rng = np.random.default_rng(32)
+    L, H = 3, 4
+    for trial in range(4):
+        score = rng.random((L, H))
+        acc = (rng.random((L, H)) < 0.75).astype(np.uint8) if trial % 2 else None
+        heads = [(l, h) for l in range(L) for h in range(H) if acc is None or acc[l, h]]
+        for ratio in (0.0, 0.1, 0.25, 0.5, 0.75, 1.0):
+            k = min(round(ratio * L * H), len(heads))
+            best = min(itertools.combinations(heads, k), key=lambda c: sum(score[x] for x in c))
+            sel, n = oracle.select_heads(score, ratio, accepted=acc)
+            assert n == k and set(zip(*np.nonzero(sel))) == set(best)
+
+
+# ------------------------------------------- trainable pattern: dL/da, dL/dr ([Paper page] Table 14)
+def _pattern_loss(v, g, a, r):
+    o, _ = oracle.head_fwd(1, v, a=a, r=r)
+    return float((o * g).sum())
+
+
+def check_pattern_grad_finite_differences():
+    rng = np.random.default_rng(40)
+    T, d, h = 7, 3, 1e-6
+    v, g = rng.normal(size=(T, d)), rng.normal(size=(T, d))
+    a, r = rng.normal(size=T), rng.normal(size=T)
+    da, dr = oracle.head_pattern_grad(v, g, a, r)
+    for vec, grad in ((a, da), (r, dr)):
+        for x in range(T):
+            old = vec[x]
+            vec[x] = old + h
+            lp = _pattern_loss(v, g, a, r)
+            vec[x] = old - h
+            lm = _pattern_loss(v, g, a, r)
+            vec[x] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[x]) <= 1e-7 * max(1.0, abs(fd))
+
+
+def check_pattern_grad_vs_autograd():
+    """torch autograd in float64 through a dense masked softmax (library routine)."""
+    rng = np.random.default_rng(41)
+    T, d = 10, 4
+    v, g = rng.normal(size=(T, d)), rng.normal(size=(T, d))
+    a, r = rng.normal(size=T), rng.normal(size=T)
+    ta = torch.tensor(a, requires_grad=True)
+    tr = torch.tensor(r, requires_grad=True)
+    idx = torch.arange(T)
+    dist = (idx[:, None] - idx[None, :]).clamp(min=0)
+    logits = ta[None, :] + tr[dist]
+    logits = logits.masked_fill(idx[None, :] > idx[:, None], float("-inf"))
+    o = torch.softmax(logits, -1) @ torch.tensor(v)
+    (o * torch.tensor(g)).sum().backward()
+    da, dr = oracle.head_pattern_grad(v, g, a, r)
+    assert _rel(da, ta.grad.numpy()) <= 1e-13 and _rel(dr, tr.grad.numpy()) <= 1e-13
+
+
+def check_pattern_grad_invariants():
+    """Shifting every a, every r, or (a(j) + b j, r(delta) + b delta) leaves each row's pattern
+    unchanged (a constant per row cancels), so sum da = 0, sum dr = 0 and
+    sum_j j da(j) + sum_delta delta dr(delta) = 0.  Equal value rows give zero gradient."""
+    rng = np.random.default_rng(42)
+    T, d = 12, 3
+    v, g = rng.normal(size=(T, d)), rng.normal(size=(T, d))
+    a, r = rng.normal(size=T), rng.normal(size=T)
+    da, dr = oracle.head_pattern_grad(v, g, a, r)
+    pos = np.arange(T)
+    scale = np.abs(da).max() + np.abs(dr).max()
+    assert abs(da.sum()) <= 1e-13 * scale and abs(dr.sum()) <= 1e-13 * scale
+    assert abs(pos @ da + pos @ dr) <= 1e-12 * T * scale
+    da0, dr0 = oracle.head_pattern_grad(np.tile(v[:1], (T, 1)), g, a, r)
+    assert np.abs(da0).max() <= 1e-14 and np.abs(dr0).max() <= 1e-14
+
+
+# ------------------------------------------------------------- compact fit of a, r ([Notes §二.3])
+def _dense_pattern(a, r):
+    """Eq. (3) pattern by scipy's softmax over masked logits (library routine)."""
+    T = len(a)
+    idx = np.arange(T)
+    t = a[None, :] + r[np.clip(idx[:, None] - idx[None, :], 0, None)]
+    t = np.where(idx[None, :] <= idx[:, None], t, -np.inf)
+    return scipy.special.softmax(t, axis=1)
+
+
+def _random_target(rng, T, normalise=True):
+    M = np.zeros((T, T))
+    for i in range(T):
+        M[i, :i + 1] = rng.dirichlet(np.ones(i + 1))
+    if not normalise:
+        M *= rng.uniform(0.5, 2.0, size=(T, 1))
+    return M
+
+
+def check_fit_loss_vs_autograd():
+    """L and its gradient against torch autograd (float64) of -(1/T) sum Ahat * log_softmax,
+    with row-stochastic targets and with rows of other sums."""
+    rng = np.random.default_rng(50)
+    T = 9
+    idx = torch.arange(T)
+    dist = (idx[:, None] - idx[None, :]).clamp(min=0)
+    mask = idx[None, :] > idx[:, None]
+    for normalise in (True, False):
+        M = _random_target(rng, T, normalise)
+        a, r = rng.normal(size=T), rng.normal(size=T)
+        ta = torch.tensor(a, requires_grad=True)
+        tr = torch.tensor(r, requires_grad=True)
+        lsm = torch.log_softmax((ta[None, :] + tr[dist]).masked_fill(mask, float("-inf")), -1)
+        loss = -(torch.tensor(M) * lsm.masked_fill(mask, 0.0)).sum() / T
+        loss.backward()
+        L, ga, gr = oracle.fit_loss_grad(M, a, r)
+        assert abs(L - loss.item()) <= 1e-13 * abs(L)
+        assert _rel(ga, ta.grad.numpy()) <= 1e-12 and _rel(gr, tr.grad.numpy()) <= 1e-12
+
+
+def check_fit_gauge():
+    """L is unchanged by (a(j) + b j + c1, r(delta) + b delta + c2); the gradient sums vanish."""
+    rng = np.random.default_rng(51)
+    T = 11
+    M = _random_target(rng, T)
+    a, r = rng.normal(size=T), rng.normal(size=T)
+    pos = np.arange(T)
+    L0, ga, gr = oracle.fit_loss_grad(M, a, r)
+    L1, _, _ = oracle.fit_loss_grad(M, a + 0.7 * pos + 1.3, r + 0.7 * pos - 2.1)
+    assert abs(L1 - L0) <= 1e-12 * abs(L0)
+    assert abs(ga.sum()) <= 1e-14 and abs(gr.sum()) <= 1e-14
+    assert abs(pos @ ga + pos @ gr) <= 1e-13 * T
+
+
+def check_fit_adam_vs_library():
+    """25 steps of the fit equal torch.optim.Adam (float64, default moment rates) on the same loss
+    written with torch's log_softmax."""
+    rng = np.random.default_rng(52)
+    T, steps, lr = 8, 25, 0.1
+    M = _random_target(rng, T)
+    idx = torch.arange(T)
+    dist = (idx[:, None] - idx[None, :]).clamp(min=0)
+    mask = idx[None, :] > idx[:, None]
+    ta = torch.zeros(T, dtype=torch.float64, requires_grad=True)
+    tr = torch.zeros(T, dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.Adam([ta, tr], lr=lr)
+    tm = torch.tensor(M)
+    for _ in range(steps):
+        opt.zero_grad()
+        lsm = torch.log_softmax((ta[None, :] + tr[dist]).masked_fill(mask, float("-inf")), -1)
+        (-(tm * lsm.masked_fill(mask, 0.0)).sum() / T).backward()
+        opt.step()
+    a, r, _, _ = oracle.fit_pattern(M, steps=steps, lr=lr)
+    assert np.abs(a - ta.detach().numpy()).max() <= 1e-11
+    assert np.abs(r - tr.detach().numpy()).max() <= 1e-11
+
+
+def check_fit_recovers_eq3_and_matches_moments():
+    """A target of the form of Eq. (3) is recovered (mean row KL ~ 0, same pattern); for any
+    target the fitted pattern's column and diagonal sums equal the target's (the sufficient
+    statistics of the notes: the optimum matches both marginals), and KL = L + (1/T) sum A ln A."""
+    rng = np.random.default_rng(53)
+    T = 24
+    a0, r0 = rng.normal(size=T), np.r_[3.0, rng.normal(size=T - 1) * 0.5]
+    P0 = _dense_pattern(a0, r0)
+    a, r, L, kl = oracle.fit_pattern(P0, steps=400, lr=0.1)
+    assert 0.0 <= kl + 1e-14 and kl <= 1e-8
+    assert np.abs(_dense_pattern(a, r) - P0).max() <= 1e-4
+    M = _random_target(rng, 16)
+    a, r, L, kl = oracle.fit_pattern(M, steps=400, lr=0.1)
+    P = _dense_pattern(a, r)
+    T = 16
+    col = lambda X: X.sum(0)
+    diag = lambda X: np.array([np.trace(X, offset=-dl) for dl in range(T)])
+    assert np.abs(col(P) - col(M)).max() <= 1e-6 and np.abs(diag(P) - diag(M)).max() <= 1e-6
+    ent = (M[M > 0] * np.log(M[M > 0])).sum()
+    assert abs(kl - (L + ent / T)) <= 1e-13 and kl > 0.0
+    lsm = np.log(np.where(P > 0, P, 1.0))
+    want_kl = np.mean([(M[i, :i + 1] * (np.log(M[i, :i + 1]) - lsm[i, :i + 1])).sum() for i in range(T)])
+    assert abs(kl - want_kl) <= 1e-12
+
+
 ALL_CHECKS = [
     check_pattern_invariants, check_eq3_worked, check_identity_pattern, check_uniform_prefix_mean,
     check_constant_r_and_constant_a, check_ordinary_vs_library, check_two_key_example, check_t1,
     check_backward_finite_differences, check_backward_vs_autograd, check_backward_invariants,
     check_eq1_golden, check_eq1_brute_force, check_calibrate_qk_route, check_calibrate_q0,
     check_mean_optimality_identity, check_row_subsets, check_causal_prefix,
+    check_kl_golden, check_kl_vs_library, check_kl_special_cases, check_select_golden,
+    check_select_brute_force, check_pattern_grad_finite_differences,
+    check_pattern_grad_vs_autograd, check_pattern_grad_invariants, check_fit_loss_vs_autograd,
+    check_fit_gauge, check_fit_adam_vs_library, check_fit_recovers_eq3_and_matches_moments,
 ]

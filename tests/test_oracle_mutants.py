@@ -39,6 +39,24 @@ MUTANTS = [
     ("Eq.(1) normaliser T instead of T^2",
      "*svar = acc / ((double)(N - 1) * (double)T * (double)T);",
      "*svar = acc / ((double)(N - 1) * (double)T);"),
+    ("KL score: entropy instead of divergence", "if (an > 0.0) acc += an * log(an / mean[j]);",
+     "if (an > 0.0) acc += an * log(an);"),
+    ("KL score: mean of the wrong entry", "if (an > 0.0) acc += an * log(an / mean[j]);",
+     "if (an > 0.0) acc += an * log(an / mean[i]);"),
+    ("KL maps: normaliser N T^2", "*skl = acc / ((double)N * (double)T);",
+     "*skl = acc / ((double)N * (double)T * (double)T);"),
+    ("pattern grad: r gradient by key", "pr[i - j] += dt;", "pr[j] += dt;"),
+    ("pattern grad: a gradient by distance", "pa[j] += dt;", "pa[i - j] += dt;"),
+    ("pattern grad: softmax row term dropped", "const double dt = p[j] * (g[j] - pg);",
+     "const double dt = p[j] * g[j];"),
+    ("pattern grad: row term unweighted", "pg += p[j] * acc;", "pg += acc;"),
+    ("fit: row sums taken as 1", "rowsum += ai[j];", "rowsum = 1.0;"),
+    ("fit: r gradient by key", "if (gr) gr[i - j] += g;", "if (gr) gr[j] += g;"),
+    ("fit: Adam without bias correction", "*w -= lr * (m[x] / c1) / (sqrt(v[x] / c2) + eps);",
+     "*w -= lr * m[x] / (sqrt(v[x]) + eps);"),
+    ("fit: second-moment rate", "const double b1 = 0.9, b2 = 0.999, eps = 1e-8;",
+     "const double b1 = 0.9, b2 = 0.99, eps = 1e-8;"),
+    ("fit: KL without the entropy term", "*kl = L + ent / T;", "*kl = L;"),
 ]
 
 
