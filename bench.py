@@ -156,7 +156,7 @@ def calibration(torch, saf, w, steps=3):
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     call = lambda: saf._check(saf.saf_calibrate(saf.SAF_BF16, N, H, T, d, q.data_ptr(), k.data_ptr(),  # noqa: E731
-                                                0.0, ahat.data_ptr(), svar.data_ptr(), ws.data_ptr(),
+                                                0.0, ahat.data_ptr(), svar.data_ptr(), None, ws.data_ptr(),
                                                 nws, stream), "saf_calibrate")
     call()
     torch.cuda.synchronize()

@@ -9,7 +9,8 @@ The entry points mirror include/saf.h (same names, same argument order for the r
   saf_attn_fwd / saf_attn_bwd / saf_calibrate   raw C-ABI calls (ctypes, integer pointers)
   fwd(q, k, v, replaced, a, r)  -> (o, lse)
   bwd(q, k, v, o, dout, lse, replaced, a, r) -> (dq, dk, dv)
-  calibrate(q, k) -> (ahat, svar)
+  calibrate(q, k) -> (ahat, svar[, skl])
+  select_heads(score, ratio, accepted) -> (replaced [L, H], n)
 [Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记" (§二.1 Eq.(1), §二.3 Eq.(3),
 §二.4 for what the three calls compute).
 """
@@ -72,14 +73,17 @@ _lib.saf_attn_fwd.restype = _i
 _lib.saf_attn_bwd.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                               _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.saf_attn_bwd.restype = _i
-_lib.saf_calibrate.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _sz,
-                               _vp]
+_lib.saf_calibrate.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
+                               _sz, _vp]
 _lib.saf_calibrate.restype = _i
+_lib.saf_select_heads.argtypes = [_i, _i, _vp, _vp, ctypes.c_double, _vp, ctypes.POINTER(_i)]
+_lib.saf_select_heads.restype = _i
 
 # raw entry points, same names as the C ABI
 saf_attn_fwd = _lib.saf_attn_fwd
 saf_attn_bwd = _lib.saf_attn_bwd
 saf_calibrate = _lib.saf_calibrate
+saf_select_heads = _lib.saf_select_heads
 saf_attn_fwd_workspace_size = _lib.saf_attn_fwd_workspace_size
 saf_attn_bwd_workspace_size = _lib.saf_attn_bwd_workspace_size
 saf_calibrate_workspace_size = _lib.saf_calibrate_workspace_size
@@ -188,20 +192,37 @@ def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None, pattern=Non
     return dq, dk, dv
 
 
-def calibrate(q, k, scale=None):
+def calibrate(q, k, scale=None, kl=False):
     """Calibration statistics over N sequences: q, k [N, H, T, d].  Returns (ahat [H, T, T] fp32,
-    svar [H] fp64)."""
+    svar [H] fp64), plus skl [H] fp64 (the forward-KL score) when kl is True."""
     import torch
     N, H, T, d = q.shape
     dt = _dtype_code(q)
     ahat = torch.empty((H, T, T), dtype=torch.float32, device=q.device)
     svar = torch.empty((H,), dtype=torch.float64, device=q.device)
+    skl = torch.empty((H,), dtype=torch.float64, device=q.device) if kl else None
     ws_n = saf_calibrate_workspace_size(N, H, T, d)
     ws = _ws(ws_n, q.device)
     st = saf_calibrate(dt, N, H, T, d, _ptr(q), _ptr(k), 0.0 if scale is None else float(scale),
-                       _ptr(ahat), _ptr(svar), _ptr(ws), ws_n, _stream(q.device))
+                       _ptr(ahat), _ptr(svar), _ptr(skl) if kl else None, _ptr(ws), ws_n,
+                       _stream(q.device))
     _check(st, "saf_calibrate")
-    return ahat, svar
+    return (ahat, svar, skl) if kl else (ahat, svar)
+
+
+def select_heads(score, ratio, accepted=None):
+    """Head selection over a model: score [L, H] (host), ratio r.  Returns (replaced [L, H] uint8
+    numpy array, number selected).  Host-only library call (no GPU work)."""
+    import numpy as np
+    sc = np.ascontiguousarray(np.asarray(score, dtype=np.float64))
+    L, H = sc.shape
+    acc = None if accepted is None else np.ascontiguousarray(np.asarray(accepted, dtype=np.uint8))
+    out = np.zeros((L, H), dtype=np.uint8)
+    n = ctypes.c_int(0)
+    st = saf_select_heads(L, H, sc.ctypes.data, None if acc is None else acc.ctypes.data,
+                          float(ratio), out.ctypes.data, ctypes.byref(n))
+    _check(st, "saf_select_heads")
+    return out, n.value
 
 
 # ------------------------------------------------------------------ per-kernel timing (profiling)

@@ -7,6 +7,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
 #include <initializer_list>
 
 #include "../../include/saf.h"
@@ -146,7 +150,7 @@ size_t calib_ws(int N, int H, int T, int d) {
   (void)d;
   int nqt, nkt;
   const size_t tiles = calib_tiles(T, &nqt, &nkt);
-  return align_up(sizeof(float) * (size_t)N * H * T) + align_up(sizeof(double) * (size_t)H * tiles);
+  return align_up(sizeof(float) * (size_t)N * H * T) + 2 * align_up(sizeof(double) * (size_t)H * tiles);
 }
 
 }  // namespace
@@ -320,8 +324,8 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
 }
 
 saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q, const void* k,
-                         float scale, float* ahat, double* svar, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+                         float scale, float* ahat, double* svar, double* skl, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   if (N < 2) return fail(SAF_ERR_INVALID_ARG, "N=%d: the variance score needs N >= 2", N);
@@ -331,6 +335,7 @@ saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q
   if ((st = check_ptrs({{q, "q"}, {k, "k"}, {ahat, "ahat"}})) != SAF_OK) return st;
   if (!svar) return fail(SAF_ERR_INVALID_ARG, "svar is NULL");
   if ((uintptr_t)svar & 7u) return fail(SAF_ERR_INVALID_ARG, "svar is not 8-byte aligned");
+  if ((uintptr_t)skl & 7u) return fail(SAF_ERR_INVALID_ARG, "skl is not 8-byte aligned");
   const size_t need = calib_ws(N, H, T, d);
   if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL");
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
@@ -347,7 +352,9 @@ saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q
   ca.m2 = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + align_up(sizeof(float) * (size_t)N * H * T));
   ca.ahat = ahat;
   ca.svar = svar;
-  calib_tiles(T, &ca.n_qt, &ca.n_kt);
+  ca.skl = skl;
+  const size_t tiles = calib_tiles(T, &ca.n_qt, &ca.n_kt);
+  ca.klp = reinterpret_cast<double*>(reinterpret_cast<char*>(ca.m2) + align_up(sizeof(double) * (size_t)H * tiles));
   const bool bf = dt == SAF_BF16;
   hipError_t e = traced("calib_lse", stream, [&] { return saf::launch_calib_lse(ca, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "calibration statistics launch");
@@ -355,6 +362,36 @@ saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q
   if (e != hipSuccess) return hip_fail(e, "calibration tile launch");
   e = traced("calib_reduce", stream, [&] { return saf::launch_calib_reduce(ca, stream); });
   if (e != hipSuccess) return hip_fail(e, "calibration reduction launch");
+  return SAF_OK;
+}
+
+saf_status saf_select_heads(int L, int H, const double* score, const uint8_t* accepted,
+                            double ratio, uint8_t* replaced, int* n_selected) {
+  g_err[0] = 0;
+  if (L < 1 || H < 1 || (long long)L * H > (1LL << 24))
+    return fail(SAF_ERR_INVALID_ARG, "L=%d, H=%d: need L, H >= 1 and L*H <= 2^24", L, H);
+  if (!score || !replaced || !n_selected) return fail(SAF_ERR_INVALID_ARG, "score, replaced or n_selected is NULL");
+  if (!(ratio >= 0.0 && ratio <= 1.0)) return fail(SAF_ERR_INVALID_ARG, "ratio %g is not in [0, 1]", ratio);
+  const int n = L * H;
+  for (int x = 0; x < n; ++x)
+    if (std::isnan(score[x])) return fail(SAF_ERR_INVALID_ARG, "score of layer %d head %d is NaN", x / H, x % H);
+  // k = round(ratio * L * H), halves to even
+  const double want = ratio * (double)n, fl = std::floor(want);
+  int k = (int)fl;
+  if (want - fl > 0.5 || (want - fl == 0.5 && (k & 1))) ++k;
+  std::vector<int> order(n);
+  for (int x = 0; x < n; ++x) order[x] = x;
+  // ascending score; equal scores keep (layer, head) order, which is the index order
+  std::stable_sort(order.begin(), order.end(), [&](int u, int v) { return score[u] < score[v]; });
+  memset(replaced, 0, (size_t)n);
+  int taken = 0;
+  for (int x = 0; x < n && taken < k; ++x) {
+    const int idx = order[x];
+    if (accepted && !accepted[idx]) continue;
+    replaced[idx] = 1;
+    ++taken;
+  }
+  *n_selected = taken;
   return SAF_OK;
 }
 

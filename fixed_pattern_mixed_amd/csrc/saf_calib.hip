@@ -13,7 +13,12 @@
 //                  and sum of squared deviations (Welford) held in registers.  The tile then writes
 //                  its block of Ahat and one fp64 partial sum of squared deviations.  Tiles above
 //                  the diagonal write zeros.
-//   calib_reduce : per head, the fixed-order fp64 sum of the partials -> s_var (deterministic).
+//                  With the forward-KL score requested, the tile also sums A log A over the N
+//                  sequences and subtracts N Ahat log Ahat of the finished mean: per entry this is
+//                  sum_n A^(n) log(A^(n) / Ahat), since sum_n A^(n) = N Ahat ([Notes §二.1] names a
+//                  row-wise forward-KL selector; its terms summed over a row are KL(A^(n)_i || Ahat_i)).
+//   calib_reduce : per head, the fixed-order fp64 sum of the partials -> s_var, and the KL score
+//                  sum / (N T) (deterministic).
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -94,12 +99,12 @@ __global__ __launch_bounds__(kNT) void calib_lse_kernel(CalibArgs p) {
   if (qi < T && hi == 0) p.lse2[(size_t)nh * T + qi] = m + log2f(lt);
 }
 
-template <typename TI, int D>
+template <typename TI, int D, bool KL>
 __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
   constexpr int NS = kBK / 32;
   constexpr int LDP = D + 16 / (int)sizeof(TI);
   __shared__ __attribute__((aligned(16))) TI Ks[kBK * LDP];
-  __shared__ double wsum[kNT / 64];
+  __shared__ double wsum[kNT / 64], wkl[kNT / 64];
 
   const int T = p.T, H = p.H, N = p.N;
   const int tiles = p.n_qt * p.n_kt;
@@ -119,7 +124,10 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
       const int qq = q0 + e / kBK, kk = k0 + e % kBK;
       if (qq < T && kk < T) A[(size_t)qq * T + kk] = 0.f;
     }
-    if (tid == 0) p.m2[(size_t)h * tiles + tile] = 0.0;
+    if (tid == 0) {
+      p.m2[(size_t)h * tiles + tile] = 0.0;
+      if (KL) p.klp[(size_t)h * tiles + tile] = 0.0;
+    }
     return;
   }
 
@@ -131,6 +139,7 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
       mean[s][r] = 0.f;
       m2[s][r] = 0.f;
     }
+  double ent = 0.0;  // sum over n and this lane's entries of A log2 A (KL score only)
 
   for (int n = 0; n < N; ++n) {
     const size_t hoff = ((size_t)n * H + h) * (size_t)T * D;
@@ -146,6 +155,7 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
       qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+    float ent_n = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
@@ -157,12 +167,16 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = ks + crow(r, hi);
-        const float a = (key <= qi && key < T && qi < T) ? exp2f(st[r] * p.scale_log2 - lse2) : 0.f;
+        const bool valid = key <= qi && key < T && qi < T;
+        const float x = st[r] * p.scale_log2 - lse2;  // log2 A
+        const float a = valid ? exp2f(x) : 0.f;
         const float dlt = a - mean[s][r];
         mean[s][r] += dlt * inv_n;
         m2[s][r] += dlt * (a - mean[s][r]);
+        if (KL) ent_n += valid ? a * x : 0.f;
       }
     }
+    if (KL) ent += (double)ent_n;
   }
 
   // write the tile of Ahat (lane = query, registers = 4-key runs) and sum the deviations
@@ -184,31 +198,64 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
         for (int e = 0; e < 4; ++e) part += (double)m2[s][4 * g + e];
       }
   }
+  double kpart = 0.0;
+  if (KL) {
+    double mlogm = 0.0;  // sum of Ahat log2 Ahat over this lane's entries (0 where Ahat = 0)
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-  if (lane == 0) wsum[w] = part;
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float mv = mean[s][r];
+        if (mv > 0.f) mlogm += (double)(mv * log2f(mv));
+      }
+    kpart = ent - (double)N * mlogm;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    part += __shfl_xor(part, o);
+    if (KL) kpart += __shfl_xor(kpart, o);
+  }
+  if (lane == 0) {
+    wsum[w] = part;
+    wkl[w] = kpart;
+  }
   __syncthreads();
   if (tid == 0) {
-    double t = 0.0;
-    for (int i = 0; i < kNT / 64; ++i) t += wsum[i];
+    double t = 0.0, tk = 0.0;
+    for (int i = 0; i < kNT / 64; ++i) {
+      t += wsum[i];
+      tk += wkl[i];
+    }
     p.m2[(size_t)h * tiles + tile] = t;
+    if (KL) p.klp[(size_t)h * tiles + tile] = tk;
   }
 }
 
 __global__ __launch_bounds__(kNT) void calib_reduce_kernel(CalibArgs p) {
-  __shared__ double red[kNT];
+  __shared__ double red[kNT], redk[kNT];
   const int h = blockIdx.x;
   const int tiles = p.n_qt * p.n_kt;
-  double acc = 0.0;
-  for (int i = threadIdx.x; i < tiles; i += kNT) acc += p.m2[(size_t)h * tiles + i];
+  const bool kl = p.skl != nullptr;
+  double acc = 0.0, acck = 0.0;
+  for (int i = threadIdx.x; i < tiles; i += kNT) {
+    acc += p.m2[(size_t)h * tiles + i];
+    if (kl) acck += p.klp[(size_t)h * tiles + i];
+  }
   red[threadIdx.x] = acc;
+  redk[threadIdx.x] = acck;
   __syncthreads();
   for (int st = kNT / 2; st >= 1; st >>= 1) {
-    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    if ((int)threadIdx.x < st) {
+      red[threadIdx.x] += red[threadIdx.x + st];
+      redk[threadIdx.x] += redk[threadIdx.x + st];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
     p.svar[h] = red[0] / ((double)(p.N - 1) * (double)p.T * (double)p.T);
+    // partials are in log2 units: times ln 2 for nats
+    if (kl) p.skl[h] = redk[0] * 0.69314718055994531 / ((double)p.N * (double)p.T);
+  }
 }
 
 template <typename TI, int D>
@@ -224,7 +271,10 @@ template <typename TI, int D>
 hipError_t launch_stats_t(const CalibArgs& a, hipStream_t s) {
   const long long blocks = (long long)a.H * a.n_qt * a.n_kt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((calib_stats_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  if (a.skl)
+    hipLaunchKernelGGL((calib_stats_kernel<TI, D, true>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  else
+    hipLaunchKernelGGL((calib_stats_kernel<TI, D, false>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 

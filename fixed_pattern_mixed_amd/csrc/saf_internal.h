@@ -62,8 +62,10 @@ struct CalibArgs {
   const void* k;
   float* lse2;       // [N][H][T] workspace: log2-sum-exp2 of scaled scores
   double* m2;        // [H][tiles] workspace: per-tile sums of squared deviations
+  double* klp;       // [H][tiles] workspace: per-tile KL sums (log2 units), when skl is requested
   float* ahat;       // [H][T][T]
   double* svar;      // [H]
+  double* skl;       // [H] or nullptr: forward-KL score
   int n_qt, n_kt;    // query / key tile counts of the statistics grid
 };
 

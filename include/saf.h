@@ -122,10 +122,30 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
  *   ahat : [H][T][T] fp32 (written): the mean map (1/N) sum_n A^(n), zeros above the diagonal.
  *   svar : [H] fp64 (written): sum_n ||A^(n) - ahat||_F^2 / ((N-1) T^2), every one of the T^2
  *          entries counted.  N >= 2.
+ *   skl  : [H] fp64 (written) or NULL (not computed): the row-wise forward-KL score, the mean over
+ *          sequences n and rows i of KL(A^(n)_i || ahat_i) in nats ([Notes §二.1] names this
+ *          alternative selector without a formula; this is its plainest reading).
  */
 saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q, const void* k,
-                         float scale, float* ahat, double* svar, void* ws, size_t ws_bytes,
-                         hipStream_t stream);
+                         float scale, float* ahat, double* svar, double* skl, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Head selection across a whole model.                             [Notes §二.1]
+ *   score    : [L][H] host fp64, one score per head of each of L layers (s_var, or s_kl); lower
+ *              means the head is easier to replace by a fixed pattern.  NaN is rejected.
+ *   accepted : [L][H] host bytes or NULL.  A zero marks a candidate whose compact fit failed the
+ *              acceptance test ([Notes §二.3]: mean row KL above 0.2 nat); it is skipped and the
+ *              next head in order is taken.  NULL accepts every head.
+ *   ratio    : replacement ratio r in [0, 1]; k = round(r L H) heads are selected, halves rounded
+ *              to even.
+ *   replaced : [L][H] host bytes (written): 1 for the selected heads, the first k accepted heads of
+ *              the ascending order of score, equal scores ordered by (layer, head).
+ *   n_selected : (written) the number selected, fewer than k only when fewer heads are accepted.
+ * Host memory only; makes no HIP call.
+ */
+saf_status saf_select_heads(int L, int H, const double* score, const uint8_t* accepted,
+                            double ratio, uint8_t* replaced, int* n_selected);
 
 /* Text of the calling thread's last non-OK status ("" if none).  Valid until the thread's next
  * call into the library. */

@@ -117,7 +117,7 @@ def test_backward_rejects(case, kw, status):
     ("no heads", 1, 4, 0, 64, 64, saf.SAF_ERR_INVALID_ARG),
 ])
 def test_calibrate_rejects(case, dt, N, H, T, d, status):
-    st = saf.saf_calibrate(dt, N, H, T, d, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, 1 << 30, None)
+    st = saf.saf_calibrate(dt, N, H, T, d, FAKE, FAKE, 0.0, FAKE, FAKE, None, FAKE, 1 << 30, None)
     assert st == status, saf.saf_last_error()
 
 
@@ -140,7 +140,7 @@ def test_pattern_prepare_without_replaced_heads_is_noop():
 
 def test_calibrate_short_workspace():
     need = saf.saf_calibrate_workspace_size(4, 2, 64, 64)
-    st = saf.saf_calibrate(1, 4, 2, 64, 64, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, need - 1, None)
+    st = saf.saf_calibrate(1, 4, 2, 64, 64, FAKE, FAKE, 0.0, FAKE, FAKE, None, FAKE, need - 1, None)
     assert st == saf.SAF_ERR_INVALID_ARG and "workspace" in saf.saf_last_error()
 
 

@@ -1,6 +1,6 @@
 """Calibration statistics on the GPU (through the C ABI) against the fp64 oracle: the mean map
-Ahat and the Eq. (1) variance score ([Notes §二.1]), plus the mean-optimality identity checked on
-the GPU's own outputs."""
+Ahat, the Eq. (1) variance score and the row-wise forward-KL score ([Notes §二.1]), plus the
+mean-optimality identity checked on the GPU's own outputs."""
 import math
 
 import numpy as np
@@ -34,9 +34,13 @@ SMALL = [
 def test_calibrate_full_compare(N, H, T, d, dtype):
     saf = _saf()
     q, k = synth.calib_inputs(N, H, T, d, dtype, seed=31 + T)
-    ahat, svar = saf.calibrate(q.cuda(), k.cuda())
+    ahat, svar, skl = saf.calibrate(q.cuda(), k.cuda(), kl=True)
+    ahat2, svar2 = saf.calibrate(q.cuda(), k.cuda())
     torch.cuda.synchronize()
-    ga, gs = cpu64(ahat), cpu64(svar)
+    # the KL score is an extra output: Ahat and s_var are the same with or without it
+    assert torch.equal(ahat, ahat2) and torch.equal(svar, svar2)
+    ga, gs, gk = cpu64(ahat), cpu64(svar), cpu64(skl)
+    rk = oracle.kl_score(q, k)
     for h in range(H):
         ra, dev = oracle.head_calibrate(q[:, h], k[:, h])
         rs = dev.sum() / ((N - 1) * T * T)
@@ -46,6 +50,23 @@ def test_calibrate_full_compare(N, H, T, d, dtype):
             assert abs(gs[h]) <= 1e-12
         else:
             assert abs(gs[h] - rs) / rs <= TOL[dtype], (h, gs[h], rs)
+        assert abs(gk[h] - rk[h]) <= TOL[dtype] * rk[h] + 1e-6, (h, gk[h], rk[h])
+
+
+def test_kl_score_identical_sequences_and_uniform_maps():
+    """N copies of one sequence, or Q = 0 (every map uniform): s_var = 0 and s_kl = 0 up to
+    rounding, at a size that spans many tiles (T = 1000, ragged)."""
+    saf = _saf()
+    N, H, T, d = 4, 2, 1000, 128
+    q, k = synth.calib_inputs(1, H, T, d, torch.bfloat16, seed=77)
+    q, k = q.expand(N, -1, -1, -1).contiguous(), k.expand(N, -1, -1, -1).contiguous()
+    _, svar, skl = saf.calibrate(q.cuda(), k.cuda(), kl=True)
+    torch.cuda.synchronize()
+    assert float(svar.abs().max()) <= 1e-12
+    assert float(skl.abs().max()) <= 1e-5
+    _, svar, skl = saf.calibrate(torch.zeros_like(q).cuda(), k.cuda(), kl=True)
+    torch.cuda.synchronize()
+    assert float(svar.abs().max()) <= 1e-12 and float(skl.abs().max()) <= 1e-5
 
 
 def test_mean_optimality_identity_on_gpu_outputs():
@@ -75,7 +96,7 @@ def test_calibrate_full_size_sampled():
     w = synth.WORKLOADS["l1b_t8192"]
     N, H, T, d = w.calib_N, w.H, w.T, w.d
     q, k = synth.calib_inputs(N, H, T, d, torch.bfloat16)
-    ahat, svar = saf.calibrate(q.cuda(), k.cuda())
+    ahat, svar, skl = saf.calibrate(q.cuda(), k.cuda(), kl=True)
     torch.cuda.synchronize()
     rows = sample_rows(T, 12, seed=9)
     idx = torch.as_tensor(rows, dtype=torch.long, device="cuda")
@@ -87,3 +108,4 @@ def test_calibrate_full_size_sampled():
     assert torch.allclose(sums, torch.ones_like(sums), atol=1e-4)
     assert torch.count_nonzero(torch.triu(ahat[0], 1)) == 0
     assert torch.isfinite(svar).all() and (svar >= 0).all()
+    assert torch.isfinite(skl).all() and (skl >= 0).all()
