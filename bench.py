@@ -191,6 +191,46 @@ def calibration(torch, saf, w, steps=3):
                          "traffic": measured_traffic(w.name + "_calibration", dom)}}
 
 
+def pattern_gradient(torch, saf, layer, steps):
+    """Time saf_attn_bwd_pattern (dL/da, dL/dr of the replaced heads, for a pattern that is trained
+    instead of frozen: [Paper page] Table 14) on the layer's own forward outputs.  Algorithmic
+    work: G = dO V^T over the replaced heads' causal entries, 2d flops per entry."""
+    w, x = layer.w, layer.x
+    B, H, T, d = w.B, w.H, w.T, w.d
+    n_rep = sum(1 for z in layer.rep if z)
+    if n_rep == 0 or not w.backward:
+        return None
+    layer.fwd()
+    da, dr = torch.zeros_like(x.a), torch.zeros_like(x.r)
+    nws = saf.saf_attn_bwd_pattern_workspace_size(B, H, T, d)
+    ws = torch.empty(nws, dtype=torch.uint8, device=x.v.device)
+    call = lambda: saf._check(saf.saf_attn_bwd_pattern(  # noqa: E731
+        layer.dt, B, H, T, d, x.v.data_ptr(), layer.o.data_ptr(), x.dout.data_ptr(),
+        layer.lse.data_ptr(), layer.mask, x.a.data_ptr(), x.r.data_ptr(), x.a.shape[1],
+        layer.pattern.data_ptr(), da.data_ptr(), dr.data_ptr(), ws.data_ptr(), nws,
+        layer.stream), "saf_attn_bwd_pattern")
+    call()
+    torch.cuda.synchronize()
+    trace = saf.KernelTrace(capacity=4 * steps)
+    trace.begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    trace.end()
+    trace.collect()
+    flops = B * n_rep * (T * (T + 1) / 2.0) * 2 * d
+    kernels = {}
+    for name, st in trace.summary().items():
+        ent = {"avg_ms": round(st["avg_ms"], 4), "launches": st["launches"]}
+        if name == "bwd_pattern":
+            ent["tflops"] = round(flops / (st["avg_ms"] * 1e-3) / 1e12, 1)
+        kernels[name] = ent
+    trace.close()
+    return {"ms": round(dt * 1e3, 4), "kernels": kernels}
+
+
 def cpu_baseline(w, replaced, min_seconds=10.0):
     """The fp64 oracle, as it stands, on whole sequences of the same workload (all heads, full T),
     one after another until at least min_seconds of CPU work (or the whole batch) is done."""
@@ -227,6 +267,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
+    ap.add_argument("--no-pattern-grad", action="store_true")
     ap.add_argument("--calibration-workload", default="l1b_t8192",
                     help="workload whose calibration shape (N sequences) is timed")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -319,6 +360,12 @@ def main():
         var["replaced_vs_ordinary_time_per_head"] = round(
             var["all_replaced"]["ms_per_step"] / var["all_ordinary"]["ms_per_step"], 4)
         out["variants"] = var
+
+    if not args.no_pattern_grad:
+        pg = pattern_gradient(torch, saf, layer, max(5, args.steps // 3))
+        if pg is not None:
+            pg["step_with_trainable_pattern_ms"] = round(t_step * 1e3 + pg["ms"], 4)
+            out["trainable_pattern_gradient"] = pg
 
     if not args.no_calibration:
         cw = synth.WORKLOADS[args.calibration_workload]

@@ -11,6 +11,7 @@ The entry points mirror include/saf.h (same names, same argument order for the r
   bwd(q, k, v, o, dout, lse, replaced, a, r) -> (dq, dk, dv)
   calibrate(q, k) -> (ahat, svar[, skl])
   select_heads(score, ratio, accepted) -> (replaced [L, H], n)
+  bwd_pattern(v, o, dout, lse, replaced, a, r) -> (da, dr)   trained-pattern gradient
 [Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记" (§二.1 Eq.(1), §二.3 Eq.(3),
 §二.4 for what the three calls compute).
 """
@@ -76,6 +77,11 @@ _lib.saf_attn_bwd.restype = _i
 _lib.saf_calibrate.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
                                _sz, _vp]
 _lib.saf_calibrate.restype = _i
+_lib.saf_attn_bwd_pattern_workspace_size.argtypes = [_i, _i, _i, _i]
+_lib.saf_attn_bwd_pattern_workspace_size.restype = _sz
+_lib.saf_attn_bwd_pattern.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                                      _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.saf_attn_bwd_pattern.restype = _i
 _lib.saf_select_heads.argtypes = [_i, _i, _vp, _vp, ctypes.c_double, _vp, ctypes.POINTER(_i)]
 _lib.saf_select_heads.restype = _i
 
@@ -84,6 +90,8 @@ saf_attn_fwd = _lib.saf_attn_fwd
 saf_attn_bwd = _lib.saf_attn_bwd
 saf_calibrate = _lib.saf_calibrate
 saf_select_heads = _lib.saf_select_heads
+saf_attn_bwd_pattern = _lib.saf_attn_bwd_pattern
+saf_attn_bwd_pattern_workspace_size = _lib.saf_attn_bwd_pattern_workspace_size
 saf_attn_fwd_workspace_size = _lib.saf_attn_fwd_workspace_size
 saf_attn_bwd_workspace_size = _lib.saf_attn_bwd_workspace_size
 saf_calibrate_workspace_size = _lib.saf_calibrate_workspace_size
@@ -190,6 +198,24 @@ def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None, pattern=Non
                       _ptr(ws), ws_n, _stream(v.device))
     _check(st, "saf_attn_bwd")
     return dq, dk, dv
+
+
+def bwd_pattern(v, o, dout, lse, replaced, a, r, pattern=None, da=None, dr=None):
+    """Gradient of a trained pattern: returns (da, dr) [H, pat_len] fp32; rows of replaced heads
+    written (summed over the batch), rows of ordinary heads zero (fresh tensors) or untouched."""
+    import torch
+    B, H, T, d = v.shape
+    dt = _dtype_code(v)
+    pat_len = a.shape[-1]
+    da = torch.zeros_like(a) if da is None else da
+    dr = torch.zeros_like(r) if dr is None else dr
+    ws_n = saf_attn_bwd_pattern_workspace_size(B, H, T, d)
+    ws = _ws(ws_n, v.device)
+    st = saf_attn_bwd_pattern(dt, B, H, T, d, _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                              _mask(replaced, H), _ptr(a), _ptr(r), pat_len, _ptr(pattern),
+                              _ptr(da), _ptr(dr), _ptr(ws), ws_n, _stream(v.device))
+    _check(st, "saf_attn_bwd_pattern")
+    return da, dr
 
 
 def calibrate(q, k, scale=None, kl=False):

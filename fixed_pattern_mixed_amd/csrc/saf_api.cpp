@@ -123,6 +123,13 @@ size_t bwd_ws(int B, int H, int T, int d) {
   return pattern_bytes(H, T) + align_up(sizeof(float) * (size_t)B * H * T);  // pattern, delta
 }
 
+size_t pgrad_ws(int B, int H, int T, int d) {
+  (void)d;
+  const size_t nkb = (size_t)(T + saf::pattern_grad_key_block() - 1) / saf::pattern_grad_key_block();
+  return pattern_bytes(H, T) + 2 * align_up(sizeof(float) * (size_t)B * H * T) +
+         align_up(sizeof(float) * (size_t)B * H * nkb * T);  // pattern, delta, da / dr partials
+}
+
 // Point la.pat at the caller's prepared pattern, or prepare one for length T at ws.
 saf_status setup_pattern(saf::LayerArgs& la, bool any_rep, const void* pattern, int T, void* ws,
                          hipStream_t stream, const char* what) {
@@ -166,6 +173,12 @@ size_t saf_attn_bwd_workspace_size(int B, int H, int T, int d) {
   if (!sizes_ok(B, H, T, d)) return SIZE_MAX;
   if (B == 0 || T == 0) return 0;
   return bwd_ws(B, H, T, d);
+}
+
+size_t saf_attn_bwd_pattern_workspace_size(int B, int H, int T, int d) {
+  if (!sizes_ok(B, H, T, d)) return SIZE_MAX;
+  if (B == 0 || T == 0) return 0;
+  return pgrad_ws(B, H, T, d);
 }
 
 size_t saf_calibrate_workspace_size(int N, int H, int T, int d) {
@@ -320,6 +333,68 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
     e = traced("bwd_dq", stream, [&] { return saf::launch_bwd_dq(la, bf, stream); });
     if (e != hipSuccess) return hip_fail(e, "backward query-block launch");
   }
+  return SAF_OK;
+}
+
+saf_status saf_attn_bwd_pattern(saf_dtype dt, int B, int H, int T, int d, const void* v,
+                                const void* o, const void* dout, const float* lse,
+                                const uint8_t* replaced, const float* a, const float* r, int pat_len,
+                                const void* pattern, float* da, float* dr, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  saf_status st = check_shape(B, H, T, d);
+  if (st != SAF_OK) return st;
+  saf::LayerArgs la;
+  memset(&la, 0, sizeof(la));
+  bool any_rep = false;
+  if ((st = fill_mask(replaced, H, la.rep, &any_rep)) != SAF_OK) return st;
+  if (!any_rep) return SAF_OK;  // no replaced head: nothing to write
+  if (!a || !r) return fail(SAF_ERR_INVALID_ARG, "a and r are required when a head is replaced");
+  if (pat_len < T) return fail(SAF_ERR_INVALID_ARG, "pat_len=%d is shorter than T=%d", pat_len, T);
+  if (!da || !dr) return fail(SAF_ERR_INVALID_ARG, "da and dr are required");
+  if (((uintptr_t)da & 3u) || ((uintptr_t)dr & 3u)) return fail(SAF_ERR_INVALID_ARG, "da or dr is not 4-byte aligned");
+  saf::HeadList rl;
+  rl.n = 0;
+  for (int h = 0; h < H; ++h)
+    if (replaced[h]) rl.h[rl.n++] = (uint8_t)h;
+  if (B == 0 || T == 0) {
+    // an empty batch or sequence: the gradient is zero; clear the rows with the reduce kernel
+    if (pat_len == 0) return SAF_OK;
+    la.B = 0; la.H = H; la.T = 0; la.pat_len = pat_len;
+    la.da = da; la.dr = dr;
+    hipError_t e = traced("pattern_grad_reduce", stream, [&] { return saf::launch_pattern_grad_reduce(la, rl, stream); });
+    return e == hipSuccess ? SAF_OK : hip_fail(e, "pattern gradient reduction launch");
+  }
+  if ((st = check_ptrs({{v, "v"}, {o, "o"}, {dout, "dout"}})) != SAF_OK) return st;
+  if (!lse) return fail(SAF_ERR_INVALID_ARG, "lse is NULL");
+  if (pattern && ((uintptr_t)pattern & (kAlign - 1)) != 0)
+    return fail(SAF_ERR_INVALID_ARG, "pattern is not 256-byte aligned");
+  const size_t need = pgrad_ws(B, H, T, d);
+  if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
+  if (ws_bytes < need) return fail(SAF_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+
+  la.B = B; la.H = H; la.T = T; la.d = d;
+  la.pat_len = pat_len;
+  la.v = v; la.o = o; la.dout = dout;
+  la.a = a; la.r = r;
+  la.lse = const_cast<float*>(lse);
+  char* base = reinterpret_cast<char*>(ws) + pattern_bytes(H, T);
+  const size_t slab = align_up(sizeof(float) * (size_t)B * H * T);
+  la.delta = reinterpret_cast<float*>(base);
+  la.delta_rep = 1;
+  la.dap = reinterpret_cast<float*>(base + slab);
+  la.drp = reinterpret_cast<float*>(base + 2 * slab);
+  la.da = da; la.dr = dr;
+  if ((st = setup_pattern(la, true, pattern, T, ws, stream, "pattern preparation")) != SAF_OK) return st;
+  const bool bf = dt == SAF_BF16;
+  hipError_t e = traced("bwd_pre", stream, [&] { return saf::launch_bwd_pre(la, bf, stream); });
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  e = traced("bwd_pattern", stream, [&] { return saf::launch_bwd_pattern(la, rl, bf, stream); });
+  if (e != hipSuccess) return hip_fail(e, "pattern gradient launch");
+  e = traced("pattern_grad_reduce", stream, [&] { return saf::launch_pattern_grad_reduce(la, rl, stream); });
+  if (e != hipSuccess) return hip_fail(e, "pattern gradient reduction launch");
   return SAF_OK;
 }
 

@@ -12,7 +12,8 @@
 //             or exp(a[j] + r[i-j] - lse_i) where the prepared pattern flags that form.
 //
 // Kernels (one stream):
-//   bwd_pre : delta_i = rowsum(dO o O) of ordinary heads.
+//   bwd_pre : delta_i = rowsum(dO o O) of ordinary heads (of replaced heads for the pattern
+//             gradient, which reuses this kernel).
 //   bwd_kv  : one work item per (batch, head, 128-key block), both head kinds in one grid, heaviest
 //             (lowest) key blocks first.  4 waves own 32 keys each (lane = key) and sweep the query
 //             tiles at or below the diagonal: S = Q K^T and dP = dO V^T (K, V fragments in
@@ -45,8 +46,8 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(LayerArgs p) {
   float acc = 0.f;
   const bool valid = row < total;
   const int h = valid ? (int)((row / p.T) % p.H) : 0;
-  const bool ord = valid && !is_replaced(p.rep, h);
-  if (ord) {
+  const bool want = valid && (is_replaced(p.rep, h) == (p.delta_rep != 0));
+  if (want) {
     const Frag<TI> of = load8(reinterpret_cast<const TI*>(p.o) + row * D + part * 8);
     const Frag<TI> gf = load8(reinterpret_cast<const TI*>(p.dout) + row * D + part * 8);
 #pragma unroll

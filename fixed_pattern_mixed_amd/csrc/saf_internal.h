@@ -48,7 +48,13 @@ struct LayerArgs {
   const float* r;    // [H][pat_len]
   float* lse;        // [B][H][T] natural-log row normalisers (forward writes, backward reads)
   PatternView pat;   // prepared pattern of the replaced heads
-  float* delta;      // [B][H][T] workspace: rowsum(dO * O) of ordinary heads
+  float* delta;      // [B][H][T] workspace: rowsum(dO * O) of ordinary heads (delta_rep = 0)
+                     // or of replaced heads (delta_rep = 1)
+  int delta_rep;
+  float* dap;        // pattern gradient workspace: [B*R][T] per-(batch, replaced head) da
+  float* drp;        // [B*R][key blocks][T] per-block dr partials by distance
+  float* da;         // [H][pat_len] outputs (rows of replaced heads)
+  float* dr;
   void* out;         // forward: o
   void* dq;
   void* dk;
@@ -69,6 +75,12 @@ struct CalibArgs {
   int n_qt, n_kt;    // query / key tile counts of the statistics grid
 };
 
+// The replaced heads of a call, in head order (kernels map a compact index to the head).
+struct HeadList {
+  int n;
+  uint8_t h[kMaxHeads];
+};
+
 // Each launcher enqueues its kernels on `stream` and returns the first HIP error (hipSuccess if
 // none).  Shapes were validated by the caller.
 hipError_t launch_pattern_prepare(const LayerArgs& a, hipStream_t s);
@@ -76,6 +88,9 @@ hipError_t launch_mixed_fwd(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dq(const LayerArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_pattern(const LayerArgs& a, const HeadList& rl, bool bf16, hipStream_t s);
+hipError_t launch_pattern_grad_reduce(const LayerArgs& a, const HeadList& rl, hipStream_t s);
+int pattern_grad_key_block();  // keys per work item of bwd_pattern (sizes the dr partials)
 hipError_t launch_calib_lse(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_stats(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s);

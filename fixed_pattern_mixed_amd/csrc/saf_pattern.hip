@@ -25,11 +25,6 @@ namespace {
 
 constexpr int kNT = 256;
 
-struct HeadList {
-  int n;
-  uint8_t h[kMaxHeads];
-};
-
 __global__ __launch_bounds__(kNT) void pattern_exp_kernel(LayerArgs p, HeadList hl) {
   __shared__ float red_a[kNT], red_r[kNT];
   const int h = hl.h[blockIdx.x];

@@ -1,0 +1,246 @@
+// saf_pattern_bwd.hip -- gradient of the loss with respect to the replaced heads' pattern logits
+// a and r, for the variant in which the fixed pattern is trained instead of frozen
+// ([Paper page] Table 14, "trainable mean"; the method itself keeps a and r as frozen buffers).
+//
+// [Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记".
+// A replaced head's row is the softmax over j <= i of the logits t(i,j) = a[j] + r[i-j]
+// ([Notes §二.3, Eq. (3)]) and O_i = sum_j P(i,j) V_j.  With G(i,j) = dO_i . V_j and
+// delta_i = dO_i . O_i = sum_j P(i,j) G(i,j), the chain rule of the softmax gives
+//   dT(i,j) = P(i,j) (G(i,j) - delta_i),
+//   da[j] = sum_b sum_{i>=j} dT(i,j),      dr[k] = sum_b sum_i dT(i, i-k).
+//
+//   bwd_pattern  : one work item per (batch, replaced head, 128-key block), 4 waves x 32 keys
+//                  (lane = key), sweeping the query tiles at or below the diagonal.  G on the
+//                  matrix cores (V of the lane's key in registers, dO rows from LDS), P from the
+//                  prepared pattern, dT.  da: per-lane column sums, written once per key.
+//                  dr: each wave adds dT into two LDS windows indexed by distance, one per lane
+//                  half, so no two lanes of one instruction add to the same address and the order
+//                  of the additions is fixed.  After each query tile the block sums, in a fixed
+//                  order, the window entries of the distances no later tile of the block reaches
+//                  and writes them once to the block's partial row.
+//   pattern_grad_reduce : per (replaced head, position) the fixed-order sum of the partials over
+//                  batch and key blocks -> da, dr (zeros at positions T .. pat_len-1).
+// Everything is summed in a fixed order, so the result is bitwise repeatable.
+#include "saf_device.h"
+#include "saf_internal.h"
+
+namespace saf {
+namespace {
+
+constexpr int kNT = 256;
+
+template <typename TI, int D>
+struct PgCfg {
+  static constexpr int BKV = 128;                         // keys per work item (4 waves x 32)
+  static constexpr int BQ = sizeof(TI) == 2 ? 64 : 32;    // queries per staged tile
+  static constexpr int NS = BQ / 32;                      // 32-query subtiles per tile
+  static constexpr int LDP = D + 16 / (int)sizeof(TI);    // padded row of the dO tile
+  static constexpr int WIN = BQ + BKV;                    // distance window of r (or er)
+  static constexpr int RING = 256;                        // distance ring per wave and lane half
+  // live distances of one wave span at most BQ + BKV - 1 values between two flushes
+  static_assert(BQ + BKV - 1 <= RING, "distance ring too small");
+};
+
+struct PgPrefetch {
+  float rs, dl, rw;
+};
+
+template <typename TI, int D>
+__global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList rl) {
+  using C = PgCfg<TI, D>;
+  constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, WIN = C::WIN, RING = C::RING;
+  __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDP];  // dO tile, rows
+  __shared__ __attribute__((aligned(16))) float rss[BQ];    // row scale (product form) or lse*log2e
+  __shared__ __attribute__((aligned(16))) float dls[BQ];    // delta per query
+  __shared__ float rwin[WIN];                               // er (product form) or r*log2e
+  __shared__ float ring[4][2][RING];                        // dT by distance, per wave and lane half
+
+  const int T = p.T;
+  const int R = rl.n;
+  const int BR = p.B * R;
+  const int BRp = (BR + 7) & ~7;
+  const int x = blockIdx.x;
+  const int br = x % BRp;
+  if (br >= BR) return;
+  const int kb = x / BRp;  // low key blocks see the most query tiles: heaviest first
+  const int b = br / R, h = rl.h[br % R];
+  const bool fact = p.pat.flag(h)[0] != 0;
+  const int nkb = (T + BKV - 1) / BKV;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int kb0 = kb * BKV;
+  const int kw = kb0 + 32 * w;  // the wave's first key
+  const int kj = kw + l32;      // the lane's key
+  const bool kval = kj < T;
+  const size_t hoff = ((size_t)b * p.H + h) * (size_t)T * D;
+  const size_t soff = ((size_t)b * p.H + h) * (size_t)T;
+  const TI* V = reinterpret_cast<const TI*>(p.v) + hoff;
+  const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
+  const float* lse = p.lse + soff;
+  const float* dlt = p.delta + soff;
+  const float* rrow = fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len;
+  const float wscale = fact ? 1.f : kLog2e;
+  const float wfill = fact ? 0.f : -INFINITY;
+  const float shift = fact ? p.pat.shift(h) : 0.f;
+  float* drp = p.drp + ((size_t)br * nkb + kb) * T;  // this block's partial row, by distance
+
+  for (int e = tid; e < 4 * 2 * RING; e += kNT) (&ring[0][0][0])[e] = 0.f;
+
+  Frag<TI> vf[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) vf[t] = kval ? load8(V + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
+  // the key's factor: ea[kj] (product form) or a[kj]*log2e (exponential form)
+  float akey = 0.f;
+  if (kval) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
+  float col = 0.f;  // sum over this lane's rows of dT(i, kj)
+
+  Chunks<TI, D, BQ, kNT> gch;
+  PgPrefetch pf;
+  auto load_tile = [&](int q0) {
+    gch.load(G, q0, T, tid);
+    if (tid < BQ) {
+      const int q = q0 + tid;
+      if (q < T) {
+        const float l = lse[q];
+        pf.rs = fact ? expf(shift - l) : l * kLog2e;
+        pf.dl = dlt[q];
+      } else {
+        pf.rs = fact ? 0.f : INFINITY;  // rows past the end get weight 0
+        pf.dl = 0.f;
+      }
+    }
+    if (tid < WIN) {
+      const int dist = q0 - (kb0 + BKV - 1) + tid;
+      pf.rw = (dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
+    }
+  };
+  auto store_tile = [&]() {
+    gch.template store<LDP>(Gs, tid);
+    if (tid < BQ) {
+      rss[tid] = pf.rs;
+      dls[tid] = pf.dl;
+    }
+    if (tid < WIN) rwin[tid] = pf.rw;
+  };
+  // Sum the rings' entries for distances [lo, lo + n) in a fixed order, clear them, and write
+  // the non-negative ones to the partial row (every distance in [0, T - kb0) exactly once).
+  auto flush = [&](int lo, int n) {
+    for (int e = tid; e < n; e += kNT) {
+      const int dd = lo + e;
+      const int slot = dd & (RING - 1);
+      float s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          s += ring[ww][hh][slot];
+          ring[ww][hh][slot] = 0.f;
+        }
+      if (dd >= 0) drp[dd] = s;
+    }
+  };
+
+  const int nqt = (T + BQ - 1) / BQ;
+  const int qt0 = kb0 / BQ;
+  load_tile(qt0 * BQ);
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int q0 = qt * BQ;
+    __syncthreads();  // the previous tile's readers and ring writers are done
+    // after the tile at q0 - BQ, no later tile of this block reaches a distance below
+    // q0 - kb0 - (BKV - 1): flush the BQ distances that became final
+    if (qt > qt0) flush(q0 - BQ - kb0 - (BKV - 1), BQ);
+    store_tile();
+    __syncthreads();
+    if (qt + 1 < nqt) load_tile(q0 + BQ);
+
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int qs = q0 + 32 * s;
+      if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
+      f32x16 gt;
+      zero(gt);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) mma16(gt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
+        const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+        const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q = q0 + qr + e;
+          const float rv = rwin[xr + e];
+          const float pp = fact ? rv * lv[e] * akey : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
+          const bool valid = kval && q >= kj && q < T;
+          const float dt = valid ? pp * (gt[4 * g + e] - dv[e]) : 0.f;
+          col += dt;
+          if (valid) atomicAdd(&ring[w][hi][(q - kj) & (RING - 1)], dt);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  {  // the remaining distances, up to T - 1 - kb0
+    const int lo = (nqt - 1) * BQ - kb0 - (BKV - 1);
+    flush(lo, T - kb0 - lo);
+  }
+  col += __shfl_xor(col, 32);
+  if (hi == 0 && kval) p.dap[(size_t)br * T + kj] = col;
+}
+
+__global__ __launch_bounds__(kNT) void pattern_grad_reduce_kernel(LayerArgs p, HeadList rl, int bkv) {
+  const int rr = blockIdx.y, h = rl.h[rr];
+  const int x = blockIdx.x * kNT + threadIdx.x;  // position (key or distance)
+  if (x >= p.pat_len) return;
+  const int T = p.T, R = rl.n;
+  float* da = p.da + (size_t)h * p.pat_len;
+  float* dr = p.dr + (size_t)h * p.pat_len;
+  if (x >= T) {
+    da[x] = 0.f;
+    dr[x] = 0.f;
+    return;
+  }
+  const int nkb = (T + bkv - 1) / bkv;
+  const int kbe = (T - 1 - x) / bkv + 1;  // key blocks that reach distance x: kb * bkv <= T-1-x
+  double sa = 0.0, sr = 0.0;
+  for (int b = 0; b < p.B; ++b) {
+    const size_t br = (size_t)b * R + rr;
+    sa += p.dap[br * T + x];
+    for (int kb = 0; kb < kbe; ++kb) sr += p.drp[(br * nkb + kb) * T + x];
+  }
+  da[x] = (float)sa;
+  dr[x] = (float)sr;
+}
+
+template <typename TI, int D>
+hipError_t launch_t(const LayerArgs& a, const HeadList& rl, hipStream_t s) {
+  using C = PgCfg<TI, D>;
+  const int BRp = (a.B * rl.n + 7) & ~7;
+  const long long blocks = (long long)BRp * ((a.T + C::BKV - 1) / C::BKV);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_pattern_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a, rl);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int pattern_grad_key_block() { return PgCfg<bf16, 64>::BKV; }
+
+hipError_t launch_bwd_pattern(const LayerArgs& a, const HeadList& rl, bool bf16_in, hipStream_t s) {
+  static_assert(PgCfg<bf16, 64>::BKV == PgCfg<float, 128>::BKV, "one key block size for all types");
+  if (bf16_in) return a.d == 64 ? launch_t<bf16, 64>(a, rl, s) : launch_t<bf16, 128>(a, rl, s);
+  return a.d == 64 ? launch_t<float, 64>(a, rl, s) : launch_t<float, 128>(a, rl, s);
+}
+
+hipError_t launch_pattern_grad_reduce(const LayerArgs& a, const HeadList& rl, hipStream_t s) {
+  const dim3 grid((a.pat_len + kNT - 1) / kNT, rl.n);
+  hipLaunchKernelGGL(pattern_grad_reduce_kernel, grid, dim3(kNT), 0, s, a, rl, pattern_grad_key_block());
+  return hipGetLastError();
+}
+
+}  // namespace saf

@@ -116,6 +116,27 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
                         size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Gradient with respect to the replaced heads' pattern, for a pattern that is trained instead of
+ * frozen ([Paper page] Table 14, "trainable mean"; saf_attn_bwd treats a and r as frozen).
+ * With P(i,j) = exp(a[j] + r[i-j]) / Z(i) on j <= i ([Notes §二.3, Eq.(3)]), G(i,j) = dout_i . v_j
+ * and delta_i = dout_i . o_i:
+ *   dT(i,j) = P(i,j) (G(i,j) - delta_i),  da[j] = sum_b sum_{i>=j} dT(i,j),
+ *   dr[k] = sum_b sum_i dT(i, i-k).
+ *   v, o, dout : [B][H][T][d] dt;  lse : [B][H][T] fp32 as written by saf_attn_fwd;
+ *   replaced, a, r, pat_len, pattern : as for saf_attn_fwd.
+ *   da, dr : [H][pat_len] fp32 device (written for the replaced heads' rows, summed over the
+ *            batch; zeros at positions T .. pat_len-1; rows of ordinary heads are not touched).
+ * The result is bitwise repeatable.  With no replaced head nothing is enqueued.
+ * Workspace: saf_attn_bwd_pattern_workspace_size(B, H, T, d) bytes, 256-byte aligned.
+ */
+size_t saf_attn_bwd_pattern_workspace_size(int B, int H, int T, int d);
+saf_status saf_attn_bwd_pattern(saf_dtype dt, int B, int H, int T, int d, const void* v,
+                                const void* o, const void* dout, const float* lse,
+                                const uint8_t* replaced, const float* a, const float* r, int pat_len,
+                                const void* pattern, float* da, float* dr, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/*
  * Calibration statistics over N sequences.                       [Notes §二.1, Eq.(1)]
  *   q, k : [N][H][T][d] dt, the queries and keys of the N calibration sequences; the maps
  *          A^(n) = softmax_causal(s Q^(n) K^(n)T) are formed tile by tile and never stored.

@@ -147,3 +147,39 @@ def test_calibrate_short_workspace():
 def test_single_hip_runtime_in_process():
     """The binding must share PyTorch's HIP runtime (one libamdhip64 mapped in the process)."""
     assert len(saf._hip_runtimes()) == 1, saf._hip_runtimes()
+
+
+def pgrad(dt=1, B=2, H=4, T=64, d=64, v=FAKE, o=FAKE, g=FAKE, lse=FAKE, rep=None, a=FAKE, r=FAKE,
+          pat=64, da=FAKE, dr=FAKE, ws=FAKE, ws_n=0):
+    rep = _mask(0, 0, 0, 1) if rep is None else rep
+    return saf.saf_attn_bwd_pattern(dt, B, H, T, d, v, o, g, lse, rep, a, r, pat, None, da, dr, ws,
+                                    ws_n, None)
+
+
+@pytest.mark.parametrize("case,kw,status", [
+    ("unsupported d", dict(d=96), saf.SAF_ERR_UNSUPPORTED),
+    ("unknown dtype", dict(dt=3), saf.SAF_ERR_INVALID_ARG),
+    ("null a", dict(a=None), saf.SAF_ERR_INVALID_ARG),
+    ("pattern shorter than T", dict(pat=32), saf.SAF_ERR_INVALID_ARG),
+    ("null da", dict(da=None), saf.SAF_ERR_INVALID_ARG),
+    ("misaligned dr", dict(dr=FAKE + 2), saf.SAF_ERR_INVALID_ARG),
+    ("null v", dict(v=None, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+    ("null lse", dict(lse=None, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+    ("null ws", dict(ws=None, ws_n=1 << 30), saf.SAF_ERR_INVALID_ARG),
+    ("short ws", dict(ws_n=1000), saf.SAF_ERR_INVALID_ARG),
+])
+def test_pattern_gradient_rejects(case, kw, status):
+    assert pgrad(**kw) == status, saf.saf_last_error()
+
+
+def test_pattern_gradient_without_replaced_heads_is_noop():
+    assert pgrad(rep=_mask(0, 0, 0, 0), v=None, a=None, r=None, da=None, dr=None, ws=None) == saf.SAF_OK
+
+
+def test_pattern_gradient_workspace():
+    B, H, T = 8, 12, 4096
+    n = saf.saf_attn_bwd_pattern_workspace_size(B, H, T, 64)
+    # pattern, delta, per-(batch, head) da partials, per-key-block dr partials (128-key blocks)
+    assert n >= saf.saf_pattern_size(H, T) + 2 * B * H * T * 4 + B * H * (T // 128) * T * 4
+    assert saf.saf_attn_bwd_pattern_workspace_size(0, H, T, 64) == 0
+    assert saf.saf_attn_bwd_pattern_workspace_size(B, H, T, 80) == SIZE_MAX
