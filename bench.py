@@ -181,7 +181,9 @@ def calibration(torch, saf, w, steps=3):
     ach = kf[dom] / (trace.summary()[dom]["avg_ms"] * 1e-3) / 1e12
     trace.close()
     flops = kf["calib_lse"] + kf["calib_stats"]
+    fit = fit_timing(torch, saf, ahat, stream)
     return {"workload": "%s calibration: N=%d, H=%d, T=%d, d=%d, bf16" % (w.name, N, H, T, d),
+            "fit": fit,
             "ms": round(dt * 1e3, 3), "tflops": round(flops / dt / 1e12, 1),
             "pct_bf16_peak": round(100 * flops / dt / 1e12 / PEAK_BF16_TFLOPS, 2),
             "ahat_write_gbs": round(4.0 * H * T * T / dt / 1e9, 1), "kernels": kernels,
@@ -229,6 +231,41 @@ def pattern_gradient(torch, saf, layer, steps):
         kernels[name] = ent
     trace.close()
     return {"ms": round(dt * 1e3, 4), "kernels": kernels}
+
+
+def fit_timing(torch, saf, ahat, stream, steps=400, lr=0.1, reps=2):
+    """Time saf_fit_pattern (400 Adam steps on the row-wise cross-entropy, fp64) on the
+    calibration's mean maps, every head fitted.  Per step: three length-T causal convolutions per
+    head (3 T(T+1)/2 fp64 multiply-adds); the marginal pass reads ahat once (4 T^2 bytes per head)."""
+    H, T, _ = ahat.shape
+    a = torch.empty((H, T), dtype=torch.float32, device=ahat.device)
+    r = torch.empty_like(a)
+    kl = torch.empty((H,), dtype=torch.float64, device=ahat.device)
+    nws = saf.saf_fit_pattern_workspace_size(H, T)
+    ws = torch.empty(nws, dtype=torch.uint8, device=ahat.device)
+    call = lambda: saf._check(saf.saf_fit_pattern(H, T, ahat.data_ptr(), steps, lr, a.data_ptr(),  # noqa: E731
+                                                  r.data_ptr(), kl.data_ptr(), None, ws.data_ptr(),
+                                                  nws, stream), "saf_fit_pattern")
+    call()
+    torch.cuda.synchronize()
+    trace = saf.KernelTrace(capacity=(2 * steps + 8) * reps)
+    trace.begin()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    trace.end()
+    trace.collect()
+    kernels = {name: {"avg_ms": round(st["avg_ms"], 4), "launches": st["launches"]}
+               for name, st in trace.summary().items()}
+    trace.close()
+    fma = 3.0 * H * T * (T + 1) / 2.0 * steps
+    klh = kl.cpu().tolist()
+    return {"heads": H, "T": T, "steps": steps, "lr": lr, "ms": round(dt * 1e3, 3),
+            "fp64_tflops": round(2 * fma / dt / 1e12, 2), "kernels": kernels,
+            "kl_min": round(min(klh), 4), "kl_max": round(max(klh), 4),
+            "accepted_at_0.2_nat": sum(1 for x in klh if x <= 0.2)}
 
 
 def cpu_baseline(w, replaced, min_seconds=10.0):

@@ -12,6 +12,7 @@ The entry points mirror include/saf.h (same names, same argument order for the r
   calibrate(q, k) -> (ahat, svar[, skl])
   select_heads(score, ratio, accepted) -> (replaced [L, H], n)
   bwd_pattern(v, o, dout, lse, replaced, a, r) -> (da, dr)   trained-pattern gradient
+  fit_pattern(ahat, steps, lr) -> (a, r, kl, loss)            compact fit of target maps
 [Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记" (§二.1 Eq.(1), §二.3 Eq.(3),
 §二.4 for what the three calls compute).
 """
@@ -82,6 +83,11 @@ _lib.saf_attn_bwd_pattern_workspace_size.restype = _sz
 _lib.saf_attn_bwd_pattern.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                       _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.saf_attn_bwd_pattern.restype = _i
+_lib.saf_fit_pattern_workspace_size.argtypes = [_i, _i]
+_lib.saf_fit_pattern_workspace_size.restype = _sz
+_lib.saf_fit_pattern.argtypes = [_i, _i, _vp, _i, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _sz,
+                                 _vp]
+_lib.saf_fit_pattern.restype = _i
 _lib.saf_select_heads.argtypes = [_i, _i, _vp, _vp, ctypes.c_double, _vp, ctypes.POINTER(_i)]
 _lib.saf_select_heads.restype = _i
 
@@ -90,6 +96,8 @@ saf_attn_fwd = _lib.saf_attn_fwd
 saf_attn_bwd = _lib.saf_attn_bwd
 saf_calibrate = _lib.saf_calibrate
 saf_select_heads = _lib.saf_select_heads
+saf_fit_pattern = _lib.saf_fit_pattern
+saf_fit_pattern_workspace_size = _lib.saf_fit_pattern_workspace_size
 saf_attn_bwd_pattern = _lib.saf_attn_bwd_pattern
 saf_attn_bwd_pattern_workspace_size = _lib.saf_attn_bwd_pattern_workspace_size
 saf_attn_fwd_workspace_size = _lib.saf_attn_fwd_workspace_size
@@ -234,6 +242,23 @@ def calibrate(q, k, scale=None, kl=False):
                        _stream(q.device))
     _check(st, "saf_calibrate")
     return (ahat, svar, skl) if kl else (ahat, svar)
+
+
+def fit_pattern(ahat, steps=400, lr=0.1):
+    """Compact fit of target maps ahat [H, T, T] fp32 (GPU).  Returns (a [H, T], r [H, T] fp32,
+    kl [H] fp64 mean row KL, loss [H] fp64)."""
+    import torch
+    H, T, _ = ahat.shape
+    a = torch.empty((H, T), dtype=torch.float32, device=ahat.device)
+    r = torch.empty_like(a)
+    kl = torch.empty((H,), dtype=torch.float64, device=ahat.device)
+    loss = torch.empty_like(kl)
+    ws_n = saf_fit_pattern_workspace_size(H, T)
+    ws = _ws(ws_n, ahat.device)
+    st = saf_fit_pattern(H, T, _ptr(ahat), int(steps), float(lr), _ptr(a), _ptr(r), _ptr(kl),
+                         _ptr(loss), _ptr(ws), ws_n, _stream(ahat.device))
+    _check(st, "saf_fit_pattern")
+    return a, r, kl, loss
 
 
 def select_heads(score, ratio, accepted=None):

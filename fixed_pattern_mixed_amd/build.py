@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsaf.so")
 SOURCES = ["saf_api.cpp", "saf_pattern.hip", "saf_fwd.hip", "saf_bwd.hip", "saf_pattern_bwd.hip",
-           "saf_calib.hip"]
+           "saf_calib.hip", "saf_fit.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

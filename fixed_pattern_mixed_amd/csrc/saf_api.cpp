@@ -125,9 +125,26 @@ size_t bwd_ws(int B, int H, int T, int d) {
 
 size_t pgrad_ws(int B, int H, int T, int d) {
   (void)d;
-  const size_t nkb = (size_t)(T + saf::pattern_grad_key_block() - 1) / saf::pattern_grad_key_block();
+  const size_t nkb = (size_t)(T + saf::pattern_grad_sub_block() - 1) / saf::pattern_grad_sub_block();
   return pattern_bytes(H, T) + 2 * align_up(sizeof(float) * (size_t)B * H * T) +
-         align_up(sizeof(float) * (size_t)B * H * nkb * T);  // pattern, delta, da / dr partials
+         align_up(sizeof(float) * (size_t)B * H * nkb * T) +  // pattern, delta, da / dr partials
+         align_up(sizeof(double) * (size_t)B * H * saf::pattern_grad_chunks(T) * T);
+}
+
+struct FitLayout {
+  size_t colp, rowp, diagp, entp, state, total;
+};
+FitLayout fit_layout(int H, int T) {
+  const size_t nrt = (T + saf::fit_row_tile() - 1) / saf::fit_row_tile();
+  const size_t nct = (T + saf::fit_col_tile() - 1) / saf::fit_col_tile();
+  FitLayout L;
+  L.colp = 0;
+  L.rowp = L.colp + align_up(sizeof(double) * H * nrt * T);
+  L.diagp = L.rowp + align_up(sizeof(double) * H * nct * T);
+  L.entp = L.diagp + align_up(sizeof(double) * H * nrt * nct * saf::fit_tile_distances());
+  L.state = L.entp + align_up(sizeof(double) * H * nrt * nct);
+  L.total = L.state + align_up(sizeof(double) * H * saf::fit_state_stride(T));
+  return L;
 }
 
 // Point la.pat at the caller's prepared pattern, or prepare one for length T at ws.
@@ -386,6 +403,10 @@ saf_status saf_attn_bwd_pattern(saf_dtype dt, int B, int H, int T, int d, const 
   la.delta_rep = 1;
   la.dap = reinterpret_cast<float*>(base + slab);
   la.drp = reinterpret_cast<float*>(base + 2 * slab);
+  {
+    const size_t nsb = (size_t)(T + saf::pattern_grad_sub_block() - 1) / saf::pattern_grad_sub_block();
+    la.drc = reinterpret_cast<double*>(base + 2 * slab + align_up(sizeof(float) * (size_t)B * H * nsb * T));
+  }
   la.da = da; la.dr = dr;
   if ((st = setup_pattern(la, true, pattern, T, ws, stream, "pattern preparation")) != SAF_OK) return st;
   const bool bf = dt == SAF_BF16;
@@ -395,6 +416,64 @@ saf_status saf_attn_bwd_pattern(saf_dtype dt, int B, int H, int T, int d, const 
   if (e != hipSuccess) return hip_fail(e, "pattern gradient launch");
   e = traced("pattern_grad_reduce", stream, [&] { return saf::launch_pattern_grad_reduce(la, rl, stream); });
   if (e != hipSuccess) return hip_fail(e, "pattern gradient reduction launch");
+  return SAF_OK;
+}
+
+size_t saf_fit_pattern_workspace_size(int H, int T) {
+  if (H < 1 || H > saf::kMaxHeads || T < 0 || T > kMaxT) return SIZE_MAX;
+  if (T == 0) return 0;
+  return fit_layout(H, T).total;
+}
+
+saf_status saf_fit_pattern(int H, int T, const float* ahat, int steps, double lr, float* a,
+                           float* r, double* kl, double* loss, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  g_err[0] = 0;
+  if (H < 1 || T < 0) return fail(SAF_ERR_INVALID_ARG, "need H >= 1 and T >= 0 (got H=%d T=%d)", H, T);
+  if (H > saf::kMaxHeads) return fail(SAF_ERR_UNSUPPORTED, "H=%d exceeds the supported %d heads", H, saf::kMaxHeads);
+  if (T > kMaxT) return fail(SAF_ERR_UNSUPPORTED, "T=%d exceeds the supported %d", T, kMaxT);
+  if (steps < 0 || steps > 1000000) return fail(SAF_ERR_INVALID_ARG, "steps=%d is not in [0, 10^6]", steps);
+  if (!(lr > 0.0) || std::isinf(lr)) return fail(SAF_ERR_INVALID_ARG, "lr must be positive and finite");
+  if (T == 0) return SAF_OK;
+  if (!ahat || !a || !r || !kl) return fail(SAF_ERR_INVALID_ARG, "ahat, a, r and kl are required");
+  if (((uintptr_t)ahat & 3u) || ((uintptr_t)a & 3u) || ((uintptr_t)r & 3u) || ((uintptr_t)kl & 7u) ||
+      ((uintptr_t)loss & 7u))
+    return fail(SAF_ERR_INVALID_ARG, "misaligned pointer");
+  const FitLayout L = fit_layout(H, T);
+  if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
+  if (ws_bytes < L.total) return fail(SAF_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", ws_bytes, L.total);
+
+  saf::FitArgs fa;
+  memset(&fa, 0, sizeof(fa));
+  char* base = reinterpret_cast<char*>(ws);
+  fa.H = H; fa.T = T;
+  fa.ahat = ahat;
+  fa.nrt = (T + saf::fit_row_tile() - 1) / saf::fit_row_tile();
+  fa.nct = (T + saf::fit_col_tile() - 1) / saf::fit_col_tile();
+  fa.colp = reinterpret_cast<double*>(base + L.colp);
+  fa.rowp = reinterpret_cast<double*>(base + L.rowp);
+  fa.diagp = reinterpret_cast<double*>(base + L.diagp);
+  fa.entp = reinterpret_cast<double*>(base + L.entp);
+  fa.state = reinterpret_cast<double*>(base + L.state);
+  fa.stride = saf::fit_state_stride(T);
+  fa.a_out = a; fa.r_out = r; fa.kl = kl; fa.loss = loss;
+  hipError_t e = traced("fit_marginals", stream, [&] { return saf::launch_fit_marginals(fa, stream); });
+  if (e != hipSuccess) return hip_fail(e, "fit marginals launch");
+  e = traced("fit_init", stream, [&] { return saf::launch_fit_init(fa, stream); });
+  if (e != hipSuccess) return hip_fail(e, "fit init launch");
+  for (int s = 1; s <= steps; ++s) {
+    // Adam's bias corrections for step s (beta1 = 0.9, beta2 = 0.999)
+    const double c1 = 1.0 - pow(0.9, (double)s), c2 = 1.0 - pow(0.999, (double)s);
+    e = traced("fit_z", stream, [&] { return saf::launch_fit_z(fa, stream); });
+    if (e != hipSuccess) return hip_fail(e, "fit normaliser launch");
+    e = traced("fit_step", stream, [&] { return saf::launch_fit_step(fa, lr, c1, c2, stream); });
+    if (e != hipSuccess) return hip_fail(e, "fit step launch");
+  }
+  e = traced("fit_z", stream, [&] { return saf::launch_fit_z(fa, stream); });
+  if (e != hipSuccess) return hip_fail(e, "fit normaliser launch");
+  e = traced("fit_final", stream, [&] { return saf::launch_fit_final(fa, stream); });
+  if (e != hipSuccess) return hip_fail(e, "fit final launch");
   return SAF_OK;
 }
 

@@ -52,7 +52,8 @@ struct LayerArgs {
                      // or of replaced heads (delta_rep = 1)
   int delta_rep;
   float* dap;        // pattern gradient workspace: [B*R][T] per-(batch, replaced head) da
-  float* drp;        // [B*R][key blocks][T] per-block dr partials by distance
+  float* drp;        // [B*R][32-key sub-blocks][T] per-wave dr partials by distance
+  double* drc;       // [B*R][chunks of 16 sub-blocks][T] first-stage sums of drp
   float* da;         // [H][pat_len] outputs (rows of replaced heads)
   float* dr;
   void* out;         // forward: o
@@ -81,6 +82,41 @@ struct HeadList {
   uint8_t h[kMaxHeads];
 };
 
+// Compact fit of a, r to target patterns (saf_fit.hip).  Per head, fp64 state of `stride` doubles:
+//   c, e, s [T] (marginals of the target), a, r [T], Adam moments m, v [2T], ea, er [T],
+//   w = s / Z', ln Z' [T], gradient g [2T], scalars {entropy term, max a, max r}.
+constexpr int kStEnt = 0, kStMa = 1, kStMr = 2;
+struct FitArgs {
+  int H, T;
+  const float* ahat;     // [H][T][T]
+  int nrt, nct;          // row / column tiles of the marginal pass
+  double* colp;          // [H][nrt][T] partial column sums
+  double* rowp;          // [H][nct][T] partial row sums
+  double* diagp;         // [H][nrt][nct][tile distances] partial distance sums
+  double* entp;          // [H][nrt][nct] partial sum Ahat ln Ahat
+  double* state;
+  size_t stride;
+  float* a_out;          // [H][T]
+  float* r_out;
+  double* kl;            // [H]
+  double* loss;          // [H] or nullptr
+  __host__ __device__ double* head(int h) const { return state + (size_t)h * stride; }
+  __host__ __device__ double* c(int h) const { return head(h); }
+  __host__ __device__ double* e(int h) const { return head(h) + (size_t)T; }
+  __host__ __device__ double* s(int h) const { return head(h) + 2 * (size_t)T; }
+  __host__ __device__ double* al(int h) const { return head(h) + 3 * (size_t)T; }
+  __host__ __device__ double* rh(int h) const { return head(h) + 4 * (size_t)T; }
+  __host__ __device__ double* m(int h) const { return head(h) + 5 * (size_t)T; }
+  __host__ __device__ double* v(int h) const { return head(h) + 7 * (size_t)T; }
+  __host__ __device__ double* ea(int h) const { return head(h) + 9 * (size_t)T; }
+  __host__ __device__ double* er(int h) const { return head(h) + 10 * (size_t)T; }
+  __host__ __device__ double* w(int h) const { return head(h) + 11 * (size_t)T; }
+  __host__ __device__ double* lz(int h) const { return head(h) + 12 * (size_t)T; }
+  __host__ __device__ double* g(int h) const { return head(h) + 13 * (size_t)T; }
+  __host__ __device__ double* st(int h) const { return head(h) + 15 * (size_t)T; }
+};
+__host__ __device__ inline size_t fit_state_stride(int T) { return ((size_t)15 * T + 4 + 31) / 32 * 32; }
+
 // Each launcher enqueues its kernels on `stream` and returns the first HIP error (hipSuccess if
 // none).  Shapes were validated by the caller.
 hipError_t launch_pattern_prepare(const LayerArgs& a, hipStream_t s);
@@ -90,7 +126,16 @@ hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dq(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pattern(const LayerArgs& a, const HeadList& rl, bool bf16, hipStream_t s);
 hipError_t launch_pattern_grad_reduce(const LayerArgs& a, const HeadList& rl, hipStream_t s);
-int pattern_grad_key_block();  // keys per work item of bwd_pattern (sizes the dr partials)
+int pattern_grad_sub_block();  // keys per dr partial row of bwd_pattern (one per wave)
+int pattern_grad_chunks(int T);  // first-stage chunks of the dr reduction
+int fit_row_tile();
+int fit_col_tile();
+int fit_tile_distances();
+hipError_t launch_fit_marginals(const FitArgs& a, hipStream_t s);
+hipError_t launch_fit_init(const FitArgs& a, hipStream_t s);
+hipError_t launch_fit_z(const FitArgs& a, hipStream_t s);
+hipError_t launch_fit_step(const FitArgs& a, double lr, double c1, double c2, hipStream_t s);
+hipError_t launch_fit_final(const FitArgs& a, hipStream_t s);
 hipError_t launch_calib_lse(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_stats(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s);

@@ -13,13 +13,15 @@
 //                  (lane = key), sweeping the query tiles at or below the diagonal.  G on the
 //                  matrix cores (V of the lane's key in registers, dO rows from LDS), P from the
 //                  prepared pattern, dT.  da: per-lane column sums, written once per key.
-//                  dr: each wave adds dT into two LDS windows indexed by distance, one per lane
-//                  half, so no two lanes of one instruction add to the same address and the order
-//                  of the additions is fixed.  After each query tile the block sums, in a fixed
-//                  order, the window entries of the distances no later tile of the block reaches
-//                  and writes them once to the block's partial row.
-//   pattern_grad_reduce : per (replaced head, position) the fixed-order sum of the partials over
-//                  batch and key blocks -> da, dr (zeros at positions T .. pat_len-1).
+//                  dr: per 32 x 32 subtile, each lane writes its 16 dT values into a per-wave
+//                  LDS buffer at [i - j + 31][i] (row stride 33: conflict-free), then lane x sums
+//                  diagonal x (the subtile's distance (qs - kw) + x - 31).  A 64-lane register
+//                  window keyed by distance carries the sums across the wave's consecutive
+//                  subtiles; after each subtile its lower 32 lanes hold final distances, which
+//                  are written once to the wave's partial row, and the window moves down 32 lanes.
+//   pattern_grad_reduce : fixed-order sums of the partials: first over chunks of 16 sub-blocks
+//                  per (batch, head, position), then over batch and chunks -> da, dr (zeros at
+//                  positions T .. pat_len-1).
 // Everything is summed in a fixed order, so the result is bitwise repeatable.
 #include "saf_device.h"
 #include "saf_internal.h"
@@ -36,9 +38,7 @@ struct PgCfg {
   static constexpr int NS = BQ / 32;                      // 32-query subtiles per tile
   static constexpr int LDP = D + 16 / (int)sizeof(TI);    // padded row of the dO tile
   static constexpr int WIN = BQ + BKV;                    // distance window of r (or er)
-  static constexpr int RING = 256;                        // distance ring per wave and lane half
-  // live distances of one wave span at most BQ + BKV - 1 values between two flushes
-  static_assert(BQ + BKV - 1 <= RING, "distance ring too small");
+  static constexpr int LDK = 33;                          // row stride of the skewed dT buffer
 };
 
 struct PgPrefetch {
@@ -48,12 +48,12 @@ struct PgPrefetch {
 template <typename TI, int D>
 __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList rl) {
   using C = PgCfg<TI, D>;
-  constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, WIN = C::WIN, RING = C::RING;
+  constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, WIN = C::WIN, LDK = C::LDK;
   __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDP];  // dO tile, rows
   __shared__ __attribute__((aligned(16))) float rss[BQ];    // row scale (product form) or lse*log2e
   __shared__ __attribute__((aligned(16))) float dls[BQ];    // delta per query
   __shared__ float rwin[WIN];                               // er (product form) or r*log2e
-  __shared__ float ring[4][2][RING];                        // dT by distance, per wave and lane half
+  __shared__ float skew[4][64 * LDK];                       // per wave: dT at [i - j + 31][i]
 
   const int T = p.T;
   const int R = rl.n;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
   const int kb = x / BRp;  // low key blocks see the most query tiles: heaviest first
   const int b = br / R, h = rl.h[br % R];
   const bool fact = p.pat.flag(h)[0] != 0;
-  const int nkb = (T + BKV - 1) / BKV;
+  const int nsb = (T + 31) / 32;  // 32-key sub-blocks (one per wave)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -83,9 +83,14 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
   const float wscale = fact ? 1.f : kLog2e;
   const float wfill = fact ? 0.f : -INFINITY;
   const float shift = fact ? p.pat.shift(h) : 0.f;
-  float* drp = p.drp + ((size_t)br * nkb + kb) * T;  // this block's partial row, by distance
-
-  for (int e = tid; e < 4 * 2 * RING; e += kNT) (&ring[0][0][0])[e] = 0.f;
+  float* drp = p.drp + ((size_t)br * nsb + (kw >> 5)) * T;  // this wave's partial row, by distance
+  float* sk = skew[w];
+  float win = 0.f;   // lane x: the wave's running sum for distance dbase + x
+  int dbase = 0;     // distance of lane 0 (set by the first visible subtile)
+  bool started = false;
+  // cells [x][row] with key row - x + 31 outside [0, 32) are never written: zero them once, so the
+  // distance sums below need no masks (row 63 stays zero too)
+  for (int e = tid; e < 4 * 64 * LDK; e += kNT) (&skew[0][0])[e] = 0.f;
 
   Frag<TI> vf[D / 16];
 #pragma unroll
@@ -123,23 +128,6 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
     }
     if (tid < WIN) rwin[tid] = pf.rw;
   };
-  // Sum the rings' entries for distances [lo, lo + n) in a fixed order, clear them, and write
-  // the non-negative ones to the partial row (every distance in [0, T - kb0) exactly once).
-  auto flush = [&](int lo, int n) {
-    for (int e = tid; e < n; e += kNT) {
-      const int dd = lo + e;
-      const int slot = dd & (RING - 1);
-      float s = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          s += ring[ww][hh][slot];
-          ring[ww][hh][slot] = 0.f;
-        }
-      if (dd >= 0) drp[dd] = s;
-    }
-  };
 
   const int nqt = (T + BQ - 1) / BQ;
   const int qt0 = kb0 / BQ;
@@ -147,10 +135,7 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
 
   for (int qt = qt0; qt < nqt; ++qt) {
     const int q0 = qt * BQ;
-    __syncthreads();  // the previous tile's readers and ring writers are done
-    // after the tile at q0 - BQ, no later tile of this block reaches a distance below
-    // q0 - kb0 - (BKV - 1): flush the BQ distances that became final
-    if (qt > qt0) flush(q0 - BQ - kb0 - (BKV - 1), BQ);
+    __syncthreads();  // the previous tile's readers are done
     store_tile();
     __syncthreads();
     if (qt + 1 < nqt) load_tile(q0 + BQ);
@@ -159,6 +144,7 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
     for (int s = 0; s < NS; ++s) {
       const int qs = q0 + 32 * s;
       if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
+      const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
       f32x16 gt;
       zero(gt);
 #pragma unroll
@@ -176,24 +162,59 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
           const int q = q0 + qr + e;
           const float rv = rwin[xr + e];
           const float pp = fact ? rv * lv[e] * akey : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
-          const bool valid = kval && q >= kj && q < T;
-          const float dt = valid ? pp * (gt[4 * g + e] - dv[e]) : 0.f;
+          float dt = pp * (gt[4 * g + e] - dv[e]);
+          if (edge) dt = (kval && q >= kj && q < T) ? dt : 0.f;
           col += dt;
-          if (valid) atomicAdd(&ring[w][hi][(q - kj) & (RING - 1)], dt);
+          const int row = 8 * g + 4 * hi + e;  // row within the subtile
+          sk[(row - l32 + 31) * LDK + row] = dt;
         }
       }
+      // distance sums of the subtile: lane x sums skewed row x (rows max(0, x-31) .. min(31, x));
+      // LDS accesses of one wave complete in order, so the stores above are visible here
+      __builtin_amdgcn_wave_barrier();
+      float dsum = 0.f;
+#pragma unroll 8
+      for (int row = 0; row < 32; ++row) dsum += sk[lane * LDK + row];
+      __builtin_amdgcn_wave_barrier();
+      if (!started) {
+        started = true;
+        dbase = qs - kw - 31;
+      }
+      win += dsum;
+      // lanes 0..31 now hold final distances (no later subtile of this wave reaches them)
+      const int dd = dbase + lane;
+      if (lane < 32 && dd >= 0) drp[dd] = win;
+      win = __shfl_down(win, 32);
+      if (lane >= 32) win = 0.f;
+      dbase += 32;
     }
   }
-  __syncthreads();
-  {  // the remaining distances, up to T - 1 - kb0
-    const int lo = (nqt - 1) * BQ - kb0 - (BKV - 1);
-    flush(lo, T - kb0 - lo);
+  {  // the distances still in the window, up to T - 1 - kw
+    const int dd = dbase + lane;
+    if (started && lane < 32 && dd >= 0 && dd < T - kw) drp[dd] = win;
   }
   col += __shfl_xor(col, 32);
   if (hi == 0 && kval) p.dap[(size_t)br * T + kj] = col;
 }
 
-__global__ __launch_bounds__(kNT) void pattern_grad_reduce_kernel(LayerArgs p, HeadList rl, int bkv) {
+constexpr int kSbChunk = 16;  // sub-block partial rows summed per thread by the first reduce stage
+
+// First stage: for (batch x replaced head, chunk of kSbChunk sub-blocks, position x) the sum of the
+// sub-blocks' partials that reach distance x.
+__global__ __launch_bounds__(kNT) void pattern_grad_partial_kernel(LayerArgs p, int nch) {
+  const int T = p.T;
+  const int x = blockIdx.x * kNT + threadIdx.x;
+  const int c = blockIdx.y;
+  const size_t br = blockIdx.z;
+  if (x >= T) return;
+  const int nsb = (T + 31) / 32;
+  const int sbe = min((T - 1 - x) / 32 + 1, (c + 1) * kSbChunk);  // 32 sb <= T-1-x
+  double acc = 0.0;
+  for (int sb = c * kSbChunk; sb < sbe; ++sb) acc += p.drp[(br * nsb + sb) * T + x];
+  p.drc[(br * nch + c) * T + x] = acc;
+}
+
+__global__ __launch_bounds__(kNT) void pattern_grad_reduce_kernel(LayerArgs p, HeadList rl, int nch) {
   const int rr = blockIdx.y, h = rl.h[rr];
   const int x = blockIdx.x * kNT + threadIdx.x;  // position (key or distance)
   if (x >= p.pat_len) return;
@@ -205,13 +226,12 @@ __global__ __launch_bounds__(kNT) void pattern_grad_reduce_kernel(LayerArgs p, H
     dr[x] = 0.f;
     return;
   }
-  const int nkb = (T + bkv - 1) / bkv;
-  const int kbe = (T - 1 - x) / bkv + 1;  // key blocks that reach distance x: kb * bkv <= T-1-x
+  const int che = ((T - 1 - x) / 32) / kSbChunk + 1;  // chunks holding a sub-block that reaches x
   double sa = 0.0, sr = 0.0;
   for (int b = 0; b < p.B; ++b) {
     const size_t br = (size_t)b * R + rr;
     sa += p.dap[br * T + x];
-    for (int kb = 0; kb < kbe; ++kb) sr += p.drp[(br * nkb + kb) * T + x];
+    for (int c = 0; c < che; ++c) sr += p.drc[(br * nch + c) * T + x];
   }
   da[x] = (float)sa;
   dr[x] = (float)sr;
@@ -229,7 +249,8 @@ hipError_t launch_t(const LayerArgs& a, const HeadList& rl, hipStream_t s) {
 
 }  // namespace
 
-int pattern_grad_key_block() { return PgCfg<bf16, 64>::BKV; }
+int pattern_grad_sub_block() { return 32; }
+int pattern_grad_chunks(int T) { return ((T + 31) / 32 + kSbChunk - 1) / kSbChunk; }
 
 hipError_t launch_bwd_pattern(const LayerArgs& a, const HeadList& rl, bool bf16_in, hipStream_t s) {
   static_assert(PgCfg<bf16, 64>::BKV == PgCfg<float, 128>::BKV, "one key block size for all types");
@@ -238,8 +259,15 @@ hipError_t launch_bwd_pattern(const LayerArgs& a, const HeadList& rl, bool bf16_
 }
 
 hipError_t launch_pattern_grad_reduce(const LayerArgs& a, const HeadList& rl, hipStream_t s) {
+  const int nch = pattern_grad_chunks(a.T);
+  if (a.B > 0 && a.T > 0) {
+    const dim3 g1((a.T + kNT - 1) / kNT, nch, a.B * rl.n);
+    hipLaunchKernelGGL(pattern_grad_partial_kernel, g1, dim3(kNT), 0, s, a, nch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((a.pat_len + kNT - 1) / kNT, rl.n);
-  hipLaunchKernelGGL(pattern_grad_reduce_kernel, grid, dim3(kNT), 0, s, a, rl, pattern_grad_key_block());
+  hipLaunchKernelGGL(pattern_grad_reduce_kernel, grid, dim3(kNT), 0, s, a, rl, nch);
   return hipGetLastError();
 }
 

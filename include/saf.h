@@ -152,6 +152,31 @@ saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q
                          size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Compact fit of fixed patterns to target maps.                     [Notes §二.3, Eq.(3)]
+ * For each of H heads, a and r (length T) with P(i,j) = exp(a[j] + r[i-j]) / Z(i) minimising the
+ * row-wise cross-entropy to the target, averaged over rows:
+ *   L = -(1/T) sum_i sum_{j<=i} ahat(i,j) ln P(i,j),
+ * by `steps` Adam updates (step size lr; moment rates 0.9 and 0.999, eps 1e-8, bias corrections)
+ * from a = r = 0 (the uniform causal pattern).  The notes fit each candidate with 400 steps and
+ * accept it when the mean row KL is at most 0.2 nat; neither the step size nor the starting point is
+ * given there (0.1 and zero are this library's reading).
+ *   ahat : [H][T][T] fp32 device, e.g. saf_calibrate's output (rows need not sum exactly to 1;
+ *          entries above the diagonal are not read).
+ *   a, r : [H][T] fp32 device (written): the fitted logits.
+ *   kl   : [H] fp64 device (written): mean row KL(ahat_i || P_i) = L + (1/T) sum ahat ln ahat.
+ *   loss : [H] fp64 device (written) or NULL: L.
+ * The arithmetic is fp64 (the marginals of ahat, the normalisers, the gradient and Adam; the
+ * entropy term of kl takes fp32 logarithms of the entries, an error of at most 2^-21 ln T); a pass
+ * over ahat forms its column, row and distance sums once, then every step costs three length-T
+ * causal convolutions per head.  Workspace: saf_fit_pattern_workspace_size(H, T) bytes, 256-byte
+ * aligned.  T = 0 is a no-op.
+ */
+size_t saf_fit_pattern_workspace_size(int H, int T);
+saf_status saf_fit_pattern(int H, int T, const float* ahat, int steps, double lr, float* a,
+                           float* r, double* kl, double* loss, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
  * Head selection across a whole model.                             [Notes §二.1]
  *   score    : [L][H] host fp64, one score per head of each of L layers (s_var, or s_kl); lower
  *              means the head is easier to replace by a fixed pattern.  NaN is rejected.

@@ -179,7 +179,30 @@ def test_pattern_gradient_without_replaced_heads_is_noop():
 def test_pattern_gradient_workspace():
     B, H, T = 8, 12, 4096
     n = saf.saf_attn_bwd_pattern_workspace_size(B, H, T, 64)
-    # pattern, delta, per-(batch, head) da partials, per-key-block dr partials (128-key blocks)
-    assert n >= saf.saf_pattern_size(H, T) + 2 * B * H * T * 4 + B * H * (T // 128) * T * 4
+    # pattern, delta, per-(batch, head) da partials, dr partials per 32-key sub-block
+    assert n >= saf.saf_pattern_size(H, T) + 2 * B * H * T * 4 + B * H * (T // 32) * T * 4
     assert saf.saf_attn_bwd_pattern_workspace_size(0, H, T, 64) == 0
     assert saf.saf_attn_bwd_pattern_workspace_size(B, H, T, 80) == SIZE_MAX
+
+
+@pytest.mark.parametrize("case,H,T,steps,lr,ptr,n,status", [
+    ("no heads", 0, 64, 10, 0.1, FAKE, 1 << 30, saf.SAF_ERR_INVALID_ARG),
+    ("too many heads", 300, 64, 10, 0.1, FAKE, 1 << 30, saf.SAF_ERR_UNSUPPORTED),
+    ("T too long", 2, 70000, 10, 0.1, FAKE, 1 << 30, saf.SAF_ERR_UNSUPPORTED),
+    ("negative steps", 2, 64, -1, 0.1, FAKE, 1 << 30, saf.SAF_ERR_INVALID_ARG),
+    ("zero lr", 2, 64, 10, 0.0, FAKE, 1 << 30, saf.SAF_ERR_INVALID_ARG),
+    ("NaN lr", 2, 64, 10, float("nan"), FAKE, 1 << 30, saf.SAF_ERR_INVALID_ARG),
+    ("null ahat", 2, 64, 10, 0.1, None, 1 << 30, saf.SAF_ERR_INVALID_ARG),
+    ("short ws", 2, 64, 10, 0.1, FAKE, 1000, saf.SAF_ERR_INVALID_ARG),
+])
+def test_fit_rejects(case, H, T, steps, lr, ptr, n, status):
+    st = saf.saf_fit_pattern(H, T, ptr, steps, lr, FAKE, FAKE, FAKE, None, FAKE, n, None)
+    assert st == status, saf.saf_last_error()
+
+
+def test_fit_workspace():
+    n = saf.saf_fit_pattern_workspace_size(16, 8192)
+    # fp64 state of 15 T values per head plus the partial sums of the marginal pass
+    assert n >= 16 * 15 * 8192 * 8 + 16 * 128 * 8192 * 8
+    assert saf.saf_fit_pattern_workspace_size(16, 0) == 0
+    assert saf.saf_fit_pattern_workspace_size(0, 64) == SIZE_MAX
