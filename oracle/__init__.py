@@ -332,6 +332,47 @@ def layer_bwd(q, k, v, dout, replaced, a, r, scale=None, heads=None, qrows=None,
     return out
 
 
+def layer_fwd_gqa(q, k, v, replaced, a, r, scale=None, heads=None, rows=None):
+    """Forward with grouped key/value heads: q [B, H, T, d], k, v [B, Hkv, T, d]; query head h
+    reads key/value head h // (H // Hkv) ([Notes §二.4]: a replaced head still reads the V it
+    shares).  Returns {(b, h): (o, lse)}."""
+    B, H = q.shape[0], q.shape[1]
+    G = H // k.shape[1]
+    out = {}
+    for b, h in _heads(B, H, heads):
+        hk = h // G
+        if replaced[h]:
+            out[(b, h)] = head_fwd(1, v[b, hk], a=a[h], r=r[h], rows=rows)
+        else:
+            out[(b, h)] = head_fwd(0, v[b, hk], q=q[b, h], k=k[b, hk], scale=scale, rows=rows)
+    return out
+
+
+def layer_bwd_gqa(q, k, v, dout, replaced, a, r, scale=None, batches=None, kv_heads=None,
+                  qrows=None, krows=None):
+    """Backward with grouped key/value heads.  dq per query head; dk, dv per key/value head, the
+    sums over the query heads of its group (a replaced head adds to dv only).  Returns
+    (dq {(b, h)}, dk {(b, hk)}, dv {(b, hk)}) for the listed batches and key/value heads."""
+    B, H = q.shape[0], q.shape[1]
+    Hkv = k.shape[1]
+    G = H // Hkv
+    dq, dk, dv = {}, {}, {}
+    for b in (range(B) if batches is None else batches):
+        for hk in (range(Hkv) if kv_heads is None else kv_heads):
+            sk, sv = None, None
+            for h in range(hk * G, (hk + 1) * G):
+                if replaced[h]:
+                    x = head_bwd(1, v[b, hk], dout[b, h], a=a[h], r=r[h], qrows=qrows, krows=krows)
+                else:
+                    x = head_bwd(0, v[b, hk], dout[b, h], q=q[b, h], k=k[b, hk], scale=scale,
+                                 qrows=qrows, krows=krows)
+                dq[(b, h)] = x[0]
+                sk = x[1] if sk is None else sk + x[1]
+                sv = x[2] if sv is None else sv + x[2]
+            dk[(b, hk)], dv[(b, hk)] = sk, sv
+    return dq, dk, dv
+
+
 def pattern_grad(v, dout, replaced, a, r, heads=None):
     """dL/da, dL/dr of the replaced heads, summed over batch: {h: (da [T], dr [T])}."""
     B, H, T, d = v.shape

@@ -558,6 +558,55 @@ def check_fit_recovers_eq3_and_matches_moments():
     assert abs(kl - want_kl) <= 1e-12
 
 
+# ------------------------------------------------ grouped key/value heads ([Notes §二.4], GQA)
+def check_gqa_identity_mapping():
+    """With one query head per key/value head the grouped layer is the plain mixed layer."""
+    rng = np.random.default_rng(60)
+    B, H, T, d = 2, 3, 9, 4
+    q, k, v, g = (rng.normal(size=(B, H, T, d)) for _ in range(4))
+    a, r = rng.normal(size=(H, T)), rng.normal(size=(H, T))
+    rep = [0, 1, 0]
+    f1, f2 = oracle.layer_fwd(q, k, v, rep, a, r), oracle.layer_fwd_gqa(q, k, v, rep, a, r)
+    for key in f1:
+        assert np.array_equal(f1[key][0], f2[key][0]) and np.array_equal(f1[key][1], f2[key][1])
+    b1 = oracle.layer_bwd(q, k, v, g, rep, a, r)
+    dq, dk, dv = oracle.layer_bwd_gqa(q, k, v, g, rep, a, r)
+    for key in b1:
+        assert np.array_equal(b1[key][0], dq[key]) and np.array_equal(b1[key][1], dk[key])
+        assert np.array_equal(b1[key][2], dv[key])
+
+
+def check_gqa_finite_differences():
+    """dk, dv of a shared key/value head are the derivatives of L = sum_h sum dO_h . O_h through
+    every query head of the group (central differences), including a replaced head's share of dv;
+    a group whose heads are all replaced has dk = 0."""
+    rng = np.random.default_rng(61)
+    B, H, Hkv, T, d, hstep = 1, 4, 2, 6, 3, 1e-6
+    q, g = rng.normal(size=(B, H, T, d)), rng.normal(size=(B, H, T, d))
+    k, v = rng.normal(size=(B, Hkv, T, d)), rng.normal(size=(B, Hkv, T, d))
+    a, r = rng.normal(size=(H, T)), rng.normal(size=(H, T))
+    rep = [0, 1, 1, 1]  # group 0: ordinary + replaced; group 1: replaced only
+
+    def loss():
+        out = oracle.layer_fwd_gqa(q, k, v, rep, a, r)
+        return sum(float((out[(0, h)][0] * g[0, h]).sum()) for h in range(H))
+
+    dq, dk, dv = oracle.layer_bwd_gqa(q, k, v, g, rep, a, r)
+    for arr, grad in ((k, dk), (v, dv)):
+        for hk in range(Hkv):
+            for j in (0, 2, T - 1):
+                for c in range(d):
+                    old = arr[0, hk, j, c]
+                    arr[0, hk, j, c] = old + hstep
+                    lp = loss()
+                    arr[0, hk, j, c] = old - hstep
+                    lm = loss()
+                    arr[0, hk, j, c] = old
+                    fd = (lp - lm) / (2 * hstep)
+                    assert abs(fd - grad[(0, hk)][j, c]) <= 1e-7 * max(1.0, abs(fd))
+    assert np.abs(dk[(0, 1)]).max() == 0.0 and np.abs(dv[(0, 1)]).max() > 0.0
+
+
 ALL_CHECKS = [
     check_pattern_invariants, check_eq3_worked, check_identity_pattern, check_uniform_prefix_mean,
     check_constant_r_and_constant_a, check_ordinary_vs_library, check_two_key_example, check_t1,
@@ -568,4 +617,5 @@ ALL_CHECKS = [
     check_select_brute_force, check_pattern_grad_finite_differences,
     check_pattern_grad_vs_autograd, check_pattern_grad_invariants, check_fit_loss_vs_autograd,
     check_fit_gauge, check_fit_adam_vs_library, check_fit_recovers_eq3_and_matches_moments,
+    check_gqa_identity_mapping, check_gqa_finite_differences,
 ]
