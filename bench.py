@@ -78,12 +78,14 @@ class Layer:
         import synth
         self.saf, self.w, self.rep = saf, w, list(replaced)
         x = synth.layer_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, replaced, w.ar_std,
-                               synth.SEED0 + w.index, backward=True, device=dev)
+                               synth.SEED0 + w.index, backward=True, device=dev, Hkv=w.Hkv or None)
         self.x = x
         B, H, T, d = w.B, w.H, w.T, w.d
-        self.o = torch.empty_like(x.v)
+        self.Hkv = w.kv_heads
+        self.o = torch.empty_like(x.q)
         self.lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-        self.dq, self.dk, self.dv = (torch.empty_like(x.v) for _ in range(3))
+        self.dq = torch.empty_like(x.q)
+        self.dk, self.dv = torch.empty_like(x.k), torch.empty_like(x.v)
         nb = max(saf.saf_attn_bwd_workspace_size(B, H, T, d), 256)
         nf = max(saf.saf_attn_fwd_workspace_size(B, H, T, d), 256)
         self.ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -100,23 +102,23 @@ class Layer:
         torch.cuda.synchronize()
         self.prepare_ms = (time.perf_counter() - t0) * 1e3
 
-    def fwd(self):
+    def fwd(self, stream=None):
         s, w, x = self.saf, self.w, self.x
-        st = s.saf_attn_fwd(self.dt, w.B, w.H, w.T, w.d, x.q.data_ptr(), x.k.data_ptr(),
-                            x.v.data_ptr(), self.mask, x.a.data_ptr(), x.r.data_ptr(),
-                            x.a.shape[1], self.pattern.data_ptr(), 0.0, self.o.data_ptr(),
-                            self.lse.data_ptr(),
-                            self.ws_f.data_ptr(), self.nf, self.stream)
+        st = s.saf_attn_fwd_gqa(self.dt, w.B, w.H, self.Hkv, w.T, w.d, x.q.data_ptr(),
+                                x.k.data_ptr(), x.v.data_ptr(), self.mask, x.a.data_ptr(),
+                                x.r.data_ptr(), x.a.shape[1], self.pattern.data_ptr(), 0.0,
+                                self.o.data_ptr(), self.lse.data_ptr(), self.ws_f.data_ptr(),
+                                self.nf, self.stream if stream is None else stream)
         s._check(st, "saf_attn_fwd")
 
     def bwd(self):
         s, w, x = self.saf, self.w, self.x
-        st = s.saf_attn_bwd(self.dt, w.B, w.H, w.T, w.d, x.q.data_ptr(), x.k.data_ptr(),
-                            x.v.data_ptr(), self.o.data_ptr(), x.dout.data_ptr(),
-                            self.lse.data_ptr(), self.mask, x.a.data_ptr(), x.r.data_ptr(),
-                            x.a.shape[1], self.pattern.data_ptr(), 0.0, self.dq.data_ptr(),
-                            self.dk.data_ptr(),
-                            self.dv.data_ptr(), self.ws_b.data_ptr(), self.nb, self.stream)
+        st = s.saf_attn_bwd_gqa(self.dt, w.B, w.H, self.Hkv, w.T, w.d, x.q.data_ptr(),
+                                x.k.data_ptr(), x.v.data_ptr(), self.o.data_ptr(),
+                                x.dout.data_ptr(), self.lse.data_ptr(), self.mask, x.a.data_ptr(),
+                                x.r.data_ptr(), x.a.shape[1], self.pattern.data_ptr(), 0.0,
+                                self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
+                                self.ws_b.data_ptr(), self.nb, self.stream)
         s._check(st, "saf_attn_bwd")
 
     def step(self):
@@ -233,6 +235,53 @@ def pattern_gradient(torch, saf, layer, steps):
     return {"ms": round(dt * 1e3, 4), "kernels": kernels}
 
 
+def prefill_latency(torch, saf, dev, name="prefill_b1_t4096", reps=50):
+    """Small-batch prefill (B=1, T=4096, forward only), where the pages see launch overhead
+    dominate ([Notes §四]; Appendix D.3): one forward call timed three ways -- back to back on the
+    stream, replayed from a HIP graph that captured it, and one call followed by a synchronize
+    (median).  With the pattern prepared the call is a single kernel launch."""
+    import synth
+    w = synth.WORKLOADS[name]
+    lay = Layer(saf, torch, w, w.replaced(), dev)
+    for _ in range(5):
+        lay.fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        lay.fwd()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / reps
+    singles = []
+    for _ in range(21):
+        t0 = time.perf_counter()
+        lay.fwd()
+        torch.cuda.synchronize()
+        singles.append(time.perf_counter() - t0)
+    singles.sort()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        lay.fwd(stream=cs.cuda_stream)  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
+        lay.fwd(stream=cs.cuda_stream)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph = (time.perf_counter() - t0) / reps
+    flops = total_flops(w.B, w.T, w.d, w.replaced(), False)
+    return {"workload": "%s: B=%d, H=%d, T=%d, d=%d, bf16, fwd" % (w.name, w.B, w.H, w.T, w.d),
+            "eager_ms": round(eager * 1e3, 4), "graph_replay_ms": round(graph * 1e3, 4),
+            "call_and_sync_median_ms": round(singles[len(singles) // 2] * 1e3, 4),
+            "tokens_per_s_graph": round(w.B * w.T / graph, 1),
+            "tflops_graph": round(flops / graph / 1e12, 1)}
+
+
 def fit_timing(torch, saf, ahat, stream, steps=400, lr=0.1, reps=2):
     """Time saf_fit_pattern (400 Adam steps on the row-wise cross-entropy, fp64) on the
     calibration's mean maps, every head fitted.  Per step: three length-T causal convolutions per
@@ -274,15 +323,20 @@ def cpu_baseline(w, replaced, min_seconds=10.0):
     import oracle
     import synth
     x = synth.layer_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, replaced, w.ar_std,
-                           synth.SEED0 + w.index, backward=w.backward)
+                           synth.SEED0 + w.index, backward=w.backward, Hkv=w.Hkv or None)
     oracle.build()
     n_seq, dt = 0, 0.0
     while n_seq < w.B and dt < min_seconds:
         heads = [(n_seq, h) for h in range(w.H)]
         t0 = time.perf_counter()
-        oracle.layer_fwd(x.q, x.k, x.v, replaced, x.a, x.r, heads=heads)
-        if w.backward:
-            oracle.layer_bwd(x.q, x.k, x.v, x.dout, replaced, x.a, x.r, heads=heads)
+        if w.Hkv:
+            oracle.layer_fwd_gqa(x.q, x.k, x.v, replaced, x.a, x.r, heads=heads)
+            if w.backward:
+                oracle.layer_bwd_gqa(x.q, x.k, x.v, x.dout, replaced, x.a, x.r, batches=[n_seq])
+        else:
+            oracle.layer_fwd(x.q, x.k, x.v, replaced, x.a, x.r, heads=heads)
+            if w.backward:
+                oracle.layer_bwd(x.q, x.k, x.v, x.dout, replaced, x.a, x.r, heads=heads)
         dt += time.perf_counter() - t0
         n_seq += 1
     return {
@@ -305,6 +359,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--no-pattern-grad", action="store_true")
+    ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--calibration-workload", default="l1b_t8192",
                     help="workload whose calibration shape (N sequences) is timed")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -373,7 +428,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "T": w.T, "d": w.d,
                    "replaced_heads": [h for h, x in enumerate(replaced) if x],
                    "pass": "fwd+bwd" if w.backward else "fwd",
                    "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"},
@@ -403,6 +458,9 @@ def main():
         if pg is not None:
             pg["step_with_trainable_pattern_ms"] = round(t_step * 1e3 + pg["ms"], 4)
             out["trainable_pattern_gradient"] = pg
+
+    if not args.no_latency:
+        out["prefill_latency_b1"] = prefill_latency(torch, saf, dev)
 
     if not args.no_calibration:
         cw = synth.WORKLOADS[args.calibration_workload]

@@ -75,6 +75,12 @@ _lib.saf_attn_fwd.restype = _i
 _lib.saf_attn_bwd.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                               _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.saf_attn_bwd.restype = _i
+_lib.saf_attn_fwd_gqa.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp,
+                                  ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
+_lib.saf_attn_fwd_gqa.restype = _i
+_lib.saf_attn_bwd_gqa.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _i, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.saf_attn_bwd_gqa.restype = _i
 _lib.saf_calibrate.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
                                _sz, _vp]
 _lib.saf_calibrate.restype = _i
@@ -94,6 +100,8 @@ _lib.saf_select_heads.restype = _i
 # raw entry points, same names as the C ABI
 saf_attn_fwd = _lib.saf_attn_fwd
 saf_attn_bwd = _lib.saf_attn_bwd
+saf_attn_fwd_gqa = _lib.saf_attn_fwd_gqa
+saf_attn_bwd_gqa = _lib.saf_attn_bwd_gqa
 saf_calibrate = _lib.saf_calibrate
 saf_select_heads = _lib.saf_select_heads
 saf_fit_pattern = _lib.saf_fit_pattern
@@ -173,37 +181,42 @@ def prepare_pattern(replaced, a, r):
 
 
 def fwd(q, k, v, replaced, a=None, r=None, scale=None, out=None, lse=None, pattern=None):
-    """Forward of the mixed layer.  q, k, v: [B, H, T, d] (bf16 or fp32, same dtype), replaced:
-    H flags, a, r: [H, pat_len] fp32 on the GPU, pattern: optional prepare_pattern() result.
-    Returns (o, lse)."""
+    """Forward of the mixed layer.  q: [B, H, T, d], k, v: [B, Hkv, T, d] (bf16 or fp32, same
+    dtype; Hkv divides H, Hkv < H for grouped key/value heads), replaced: H flags, a, r:
+    [H, pat_len] fp32 on the GPU, pattern: optional prepare_pattern() result.  Returns (o, lse)."""
     import torch
-    B, H, T, d = v.shape
+    B, Hkv, T, d = v.shape
+    H = q.shape[1] if q is not None else len(replaced)
     dt = _dtype_code(v)
-    o = torch.empty_like(v) if out is None else out
+    o = torch.empty((B, H, T, d), dtype=v.dtype, device=v.device) if out is None else out
     lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device) if lse is None else lse
     ws_n = saf_attn_fwd_workspace_size(B, H, T, d)
     ws = _ws(ws_n, v.device)
     pat_len = a.shape[-1] if a is not None else 0
-    st = saf_attn_fwd(dt, B, H, T, d, _ptr(q), _ptr(k), _ptr(v), _mask(replaced, H), _ptr(a),
-                      _ptr(r), pat_len, _ptr(pattern), 0.0 if scale is None else float(scale),
-                      _ptr(o), _ptr(lse), _ptr(ws), ws_n, _stream(v.device))
+    st = saf_attn_fwd_gqa(dt, B, H, Hkv, T, d, _ptr(q), _ptr(k), _ptr(v), _mask(replaced, H),
+                          _ptr(a), _ptr(r), pat_len, _ptr(pattern),
+                          0.0 if scale is None else float(scale), _ptr(o), _ptr(lse), _ptr(ws),
+                          ws_n, _stream(v.device))
     _check(st, "saf_attn_fwd")
     return o, lse
 
 
 def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None, pattern=None):
-    """Backward of the mixed layer.  Returns (dq, dk, dv); replaced heads get dq = dk = 0."""
+    """Backward of the mixed layer.  Returns (dq [B, H, T, d], dk, dv [B, Hkv, T, d]); replaced
+    heads get dq = 0 and add nothing to dk."""
     import torch
-    B, H, T, d = v.shape
+    B, Hkv, T, d = v.shape
+    H = dout.shape[1]
     dt = _dtype_code(v)
-    dq, dk, dv = torch.empty_like(v), torch.empty_like(v), torch.empty_like(v)
+    dq = torch.empty_like(dout)
+    dk, dv = torch.empty_like(v), torch.empty_like(v)
     ws_n = saf_attn_bwd_workspace_size(B, H, T, d)
     ws = _ws(ws_n, v.device)
     pat_len = a.shape[-1] if a is not None else 0
-    st = saf_attn_bwd(dt, B, H, T, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                      _mask(replaced, H), _ptr(a), _ptr(r), pat_len, _ptr(pattern),
-                      0.0 if scale is None else float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
-                      _ptr(ws), ws_n, _stream(v.device))
+    st = saf_attn_bwd_gqa(dt, B, H, Hkv, T, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                          _ptr(lse), _mask(replaced, H), _ptr(a), _ptr(r), pat_len, _ptr(pattern),
+                          0.0 if scale is None else float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(ws), ws_n, _stream(v.device))
     _check(st, "saf_attn_bwd")
     return dq, dk, dv
 

@@ -48,6 +48,12 @@ saf_status check_shape(int B, int H, int T, int d) {
   return SAF_OK;
 }
 
+saf_status check_groups(int H, int Hkv) {
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0)
+    return fail(SAF_ERR_INVALID_ARG, "Hkv=%d must divide H=%d (query heads per key/value head)", Hkv, H);
+  return SAF_OK;
+}
+
 bool sizes_ok(int B, int H, int T, int d) {
   return B >= 0 && H >= 1 && H <= saf::kMaxHeads && T >= 0 && T <= kMaxT && (d == 64 || d == 128);
 }
@@ -192,6 +198,50 @@ size_t saf_attn_bwd_workspace_size(int B, int H, int T, int d) {
   return bwd_ws(B, H, T, d);
 }
 
+static saf_status fwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
+                           const void* k, const void* v, const uint8_t* replaced, const float* a,
+                           const float* r, int pat_len, const void* pattern, float scale, void* o,
+                           float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
+                           const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, const uint8_t* replaced, const float* a,
+                           const float* r, int pat_len, const void* pattern, float scale, void* dq,
+                           void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
+
+saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
+                        const void* v, const uint8_t* replaced, const float* a, const float* r,
+                        int pat_len, const void* pattern, float scale, void* o, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fwd_impl(dt, B, H, H, T, d, q, k, v, replaced, a, r, pat_len, pattern, scale, o, lse, ws,
+                  ws_bytes, stream);
+}
+
+saf_status saf_attn_fwd_gqa(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
+                            const void* k, const void* v, const uint8_t* replaced, const float* a,
+                            const float* r, int pat_len, const void* pattern, float scale, void* o,
+                            float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fwd_impl(dt, B, H, Hkv, T, d, q, k, v, replaced, a, r, pat_len, pattern, scale, o, lse, ws,
+                  ws_bytes, stream);
+}
+
+saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
+                        const void* v, const void* o, const void* dout, const float* lse,
+                        const uint8_t* replaced, const float* a, const float* r, int pat_len,
+                        const void* pattern, float scale, void* dq, void* dk, void* dv, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(dt, B, H, H, T, d, q, k, v, o, dout, lse, replaced, a, r, pat_len, pattern, scale,
+                  dq, dk, dv, ws, ws_bytes, stream);
+}
+
+saf_status saf_attn_bwd_gqa(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
+                            const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, const uint8_t* replaced, const float* a,
+                            const float* r, int pat_len, const void* pattern, float scale, void* dq,
+                            void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_impl(dt, B, H, Hkv, T, d, q, k, v, o, dout, lse, replaced, a, r, pat_len, pattern,
+                  scale, dq, dk, dv, ws, ws_bytes, stream);
+}
+
 size_t saf_attn_bwd_pattern_workspace_size(int B, int H, int T, int d) {
   if (!sizes_ok(B, H, T, d)) return SIZE_MAX;
   if (B == 0 || T == 0) return 0;
@@ -230,7 +280,7 @@ saf_status saf_pattern_prepare(int H, const uint8_t* replaced, const float* a, c
   if (((uintptr_t)pattern & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "pattern is not 256-byte aligned");
   if (pattern_bytes_given < pattern_bytes(H, pat_len))
     return fail(SAF_ERR_INVALID_ARG, "pattern buffer too small (%zu < %zu bytes)", pattern_bytes_given, pattern_bytes(H, pat_len));
-  la.H = H; la.T = pat_len; la.pat_len = pat_len;
+  la.H = H; la.Hkv = H; la.T = pat_len; la.pat_len = pat_len;
   la.a = a; la.r = r;
   return setup_pattern(la, true, nullptr, pat_len, pattern, stream, "pattern preparation");
 }
@@ -250,14 +300,15 @@ int saf_trace_end(void) {
   return n;
 }
 
-saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
-                        const void* v, const uint8_t* replaced, const float* a, const float* r,
-                        int pat_len, const void* pattern, float scale, void* o, float* lse,
-                        void* ws, size_t ws_bytes, hipStream_t stream) {
+static saf_status fwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
+                    const void* k, const void* v, const uint8_t* replaced, const float* a,
+                    const float* r, int pat_len, const void* pattern, float scale, void* o,
+                    float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   saf_status st = check_shape(B, H, T, d);
   if (st != SAF_OK) return st;
+  if ((st = check_groups(H, Hkv)) != SAF_OK) return st;
   if (B == 0 || T == 0) return SAF_OK;
   saf::LayerArgs la;
   memset(&la, 0, sizeof(la));
@@ -284,6 +335,7 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
   if ((st = check_scale(scale, d, &s)) != SAF_OK) return st;
 
   la.B = B; la.H = H; la.T = T; la.d = d;
+  la.Hkv = Hkv;
   la.pat_len = pat_len;
   la.scale = s;
   la.scale_log2 = s * 1.4426950408889634f;
@@ -298,15 +350,16 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
   return SAF_OK;
 }
 
-saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
-                        const void* v, const void* o, const void* dout, const float* lse,
-                        const uint8_t* replaced, const float* a, const float* r, int pat_len,
-                        const void* pattern, float scale, void* dq, void* dk, void* dv, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
+                    const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    const uint8_t* replaced, const float* a, const float* r, int pat_len,
+                    const void* pattern, float scale, void* dq, void* dk, void* dv, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   saf_status st = check_shape(B, H, T, d);
   if (st != SAF_OK) return st;
+  if ((st = check_groups(H, Hkv)) != SAF_OK) return st;
   if (B == 0 || T == 0) return SAF_OK;
   saf::LayerArgs la;
   memset(&la, 0, sizeof(la));
@@ -332,6 +385,7 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
   if ((st = check_scale(scale, d, &s)) != SAF_OK) return st;
 
   la.B = B; la.H = H; la.T = T; la.d = d;
+  la.Hkv = Hkv;
   la.pat_len = pat_len;
   la.scale = s;
   la.scale_log2 = s * 1.4426950408889634f;
@@ -378,7 +432,7 @@ saf_status saf_attn_bwd_pattern(saf_dtype dt, int B, int H, int T, int d, const 
   if (B == 0 || T == 0) {
     // an empty batch or sequence: the gradient is zero; clear the rows with the reduce kernel
     if (pat_len == 0) return SAF_OK;
-    la.B = 0; la.H = H; la.T = 0; la.pat_len = pat_len;
+    la.B = 0; la.H = H; la.Hkv = H; la.T = 0; la.pat_len = pat_len;
     la.da = da; la.dr = dr;
     hipError_t e = traced("pattern_grad_reduce", stream, [&] { return saf::launch_pattern_grad_reduce(la, rl, stream); });
     return e == hipSuccess ? SAF_OK : hip_fail(e, "pattern gradient reduction launch");
@@ -393,6 +447,7 @@ saf_status saf_attn_bwd_pattern(saf_dtype dt, int B, int H, int T, int d, const 
   if (ws_bytes < need) return fail(SAF_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
 
   la.B = B; la.H = H; la.T = T; la.d = d;
+  la.Hkv = H;
   la.pat_len = pat_len;
   la.v = v; la.o = o; la.dout = dout;
   la.a = a; la.r = r;

@@ -14,13 +14,15 @@
 // Kernels (one stream):
 //   bwd_pre : delta_i = rowsum(dO o O) of ordinary heads (of replaced heads for the pattern
 //             gradient, which reuses this kernel).
-//   bwd_kv  : one work item per (batch, head, 128-key block), both head kinds in one grid, heaviest
-//             (lowest) key blocks first.  4 waves own 32 keys each (lane = key) and sweep the query
-//             tiles at or below the diagonal: S = Q K^T and dP = dO V^T (K, V fragments in
-//             registers, Q and dO rows from LDS), dV^T += dO^T P and dK^T += Q^T dS (Q and dO also
-//             staged transposed, so those operands are single 16-byte LDS reads).  Replaced items
-//             form P from the prepared pattern and accumulate dV only; they also write the zero dQ
-//             and dK rows of their keys.
+//   bwd_kv  : one work item per (batch, key/value head, 128-key block), both head kinds in one
+//             grid, heaviest (lowest) key blocks first.  4 waves own 32 keys each (lane = key) and
+//             sweep the query tiles at or below the diagonal: S = Q K^T and dP = dO V^T (K, V
+//             fragments in registers, Q and dO rows from LDS), dV^T += dO^T P and dK^T += Q^T dS
+//             (Q and dO also staged transposed, so those operands are single 16-byte LDS reads).
+//             Replaced heads form P from the prepared pattern and add to dV only; they also write
+//             the zero dQ rows of their keys.  With grouped heads (several query heads per key /
+//             value head) the item sweeps each query head of its group in turn and dK, dV are the
+//             sums over the group; dK is zero when every head of the group is replaced.
 //   bwd_dq  : one work item per (batch, ordinary head, 128-query block), lane = query: S^T = K Q^T,
 //             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal (K
 //             staged both row-major and transposed).
@@ -75,7 +77,7 @@ struct KvPrefetch {
   float rs, dl, rw;
 };
 
-template <typename TI, int D>
+template <typename TI, int D, bool GROUPED>
 __global__ __launch_bounds__(kNT)
 __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bwd_kv_kernel(LayerArgs p) {
   using C = KvCfg<TI, D>;
@@ -88,44 +90,34 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   __shared__ __attribute__((aligned(16))) float dls[BQ];     // delta per query
   __shared__ float rwin[WIN];                                // replaced: er / r*log2e window
 
-  const int T = p.T, H = p.H;
-  const int BH = p.B * H;
+  const int T = p.T, H = p.H, Hkv = p.Hkv;
+  const int GS = GROUPED ? H / Hkv : 1;  // query heads per key/value head (Hkv = H unless grouped)
+  const int BH = p.B * Hkv;
   const int BHp = (BH + 7) & ~7;
   const int x = blockIdx.x;
   const int bh = x % BHp;
   if (bh >= BH) return;
   const int kb = x / BHp;  // low key blocks see the most query tiles: heaviest first
-  const int b = bh / H, h = bh % H;
-  const bool rep = is_replaced(p.rep, h);
-  const bool fact = rep && p.pat.flag(h)[0] != 0;
+  const int b = bh / Hkv, hk = bh % Hkv;
+  bool any_ord = false;
+  for (int m = 0; m < GS; ++m) any_ord |= !is_replaced(p.rep, hk * GS + m);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int kb0 = kb * BKV;
   const int kw = kb0 + 32 * w;  // the wave's first key
   const int kj = kw + l32;      // the lane's key
-  const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
-  const size_t soff = ((size_t)b * H + h) * (size_t)T;
-  const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
-  const TI* K = reinterpret_cast<const TI*>(p.k) + hoff;
-  const TI* V = reinterpret_cast<const TI*>(p.v) + hoff;
-  const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
-  const float* lse = p.lse + soff;
-  const float* dlt = p.delta + soff;
-  const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
-  const float wscale = fact ? 1.f : kLog2e;
-  const float wfill = fact ? 0.f : -INFINITY;
-  const float shift = fact ? p.pat.shift(h) : 0.f;
+  const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)T * D;
+  const TI* K = reinterpret_cast<const TI*>(p.k) + kvoff;
+  const TI* V = reinterpret_cast<const TI*>(p.v) + kvoff;
   const float c2 = p.scale_log2;
 
   Frag<TI> kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    kf[t] = (!rep && kj < T) ? load8(K + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
-    vf[t] = (!rep && kj < T) ? load8(V + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
+    kf[t] = (any_ord && kj < T) ? load8(K + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
+    vf[t] = (any_ord && kj < T) ? load8(V + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
   }
-  float akey = 0.f;  // replaced: the lane's key preference (ea, or a*log2e)
-  if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
 
   f32x16 dvT[D / 32], dkT[D / 32];
 #pragma unroll
@@ -133,124 +125,156 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
     zero(dvT[c]);
     zero(dkT[c]);
   }
-
-  KvPrefetch<TI, D> pf;
-  auto load_tile = [&](int q0) {
-    pf.g.load(G, q0, T, tid);
-    if (!rep) pf.q.load(Q, q0, T, tid);
-    if (tid < BQ) {
-      const int q = q0 + tid;
-      // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
-      // Rows past the end get weight 0 (their dO rows are zero; an unbounded weight times a zero
-      // row would not be zero).
-      if (q < T) {
-        const float l = lse[q];
-        pf.rs = fact ? expf(shift - l) : l * kLog2e;
-      } else {
-        pf.rs = fact ? 0.f : INFINITY;
-      }
-      pf.dl = (!rep && q < T) ? dlt[q] : 0.f;
-    }
-    if (rep && tid < WIN) {
-      const int dist = q0 - (kb0 + BKV - 1) + tid;
-      pf.rw = (dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
-    }
-  };
-  auto store_tile = [&]() {
-    pf.g.template store_cols<LDT>(GT, tid);
-    if (!rep) {
-      pf.g.template store_rows<LDP>(Gs, tid);
-      pf.q.template store_rows<LDP>(Qs, tid);
-      pf.q.template store_cols<LDT>(QT, tid);
-    }
-    if (tid < BQ) {
-      rss[tid] = pf.rs;
-      dls[tid] = pf.dl;
-    }
-    if (rep && tid < WIN) rwin[tid] = pf.rw;
-  };
+  // Product form: P(i,j) = ea[j] er[i-j] exp(Ma + Mr - lse_i).  With one query head per key/value
+  // head the key's factor ea[j] is applied once to the finished dV row; in a group every replaced
+  // head has its own factor, so it enters each entry.
+  float vs = 1.f;
 
   const int nqt = (T + BQ - 1) / BQ;
   const int qt0 = kb0 / BQ;
-  if (qt0 < nqt) load_tile(qt0 * BQ);
+  for (int m = 0; m < GS; ++m) {
+    const int h = hk * GS + m;
+    const bool rep = is_replaced(p.rep, h);
+    const bool fact = rep && p.pat.flag(h)[0] != 0;
+    const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+    const size_t soff = ((size_t)b * H + h) * (size_t)T;
+    const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
+    const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
+    const float* lse = p.lse + soff;
+    const float* dlt = p.delta + soff;
+    const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
+    const float wscale = fact ? 1.f : kLog2e;
+    const float wfill = fact ? 0.f : -INFINITY;
+    const float shift = fact ? p.pat.shift(h) : 0.f;
+    float akey = 0.f;  // replaced: the lane's key preference (ea, or a*log2e)
+    if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
+    const bool fold = fact && GS > 1;  // the key factor enters each entry
+    if (fact && GS == 1) vs = akey;
 
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int q0 = qt * BQ;
-    __syncthreads();  // the previous tile's readers are done
-    store_tile();
-    __syncthreads();
-    if (qt + 1 < nqt) load_tile(q0 + BQ);
-
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int qs = q0 + 32 * s;
-      if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
-      const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
-      float pr[16], ds[16];
-      if (!rep) {
-        f32x16 st, dpt;
-        zero(st);
-        zero(dpt);
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t]);
-          mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+    KvPrefetch<TI, D> pf;
+    auto load_tile = [&](int q0) {
+      pf.g.load(G, q0, T, tid);
+      if (!rep) pf.q.load(Q, q0, T, tid);
+      if (tid < BQ) {
+        const int q = q0 + tid;
+        // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
+        // Rows past the end get weight 0 (their dO rows are zero; an unbounded weight times a zero
+        // row would not be zero).
+        if (q < T) {
+          const float l = lse[q];
+          pf.rs = fact ? expf(shift - l) : l * kLog2e;
+        } else {
+          pf.rs = fact ? 0.f : INFINITY;
         }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
-          const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-          const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
-            if (edge) {
-              const int q = q0 + qr + e;
-              pp = (q >= kj && q < T && kj < T) ? pp : 0.f;
-            }
-            pr[r] = pp;
-            ds[r] = pp * (dpt[r] - dv[e]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qr = 32 * s + 8 * g + 4 * hi;
-          const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float rv = rwin[xr + e];
-            pr[4 * g + e] = fact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
-          }
-        }
+        pf.dl = (!rep && q < T) ? dlt[q] : 0.f;
       }
-      // dV^T[dcol][key] += dO^T[dcol][q] P[q][key];  dK^T[dim][key] += Q^T[dim][q] dS[q][key]
+      if (rep && tid < WIN) {
+        const int dist = q0 - (kb0 + BKV - 1) + tid;
+        pf.rw = (dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
+      }
+    };
+    auto store_tile = [&]() {
+      pf.g.template store_cols<LDT>(GT, tid);
+      if (!rep) {
+        pf.g.template store_rows<LDP>(Gs, tid);
+        pf.q.template store_rows<LDP>(Qs, tid);
+        pf.q.template store_cols<LDT>(QT, tid);
+      }
+      if (tid < BQ) {
+        rss[tid] = pf.rs;
+        dls[tid] = pf.dl;
+      }
+      if (rep && tid < WIN) rwin[tid] = pf.rw;
+    };
+
+    if (qt0 < nqt) load_tile(qt0 * BQ);
+
+    for (int qt = qt0; qt < nqt; ++qt) {
+      const int q0 = qt * BQ;
+      __syncthreads();  // the previous tile's readers are done
+      store_tile();
+      __syncthreads();
+      if (qt + 1 < nqt) load_tile(q0 + BQ);
+
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-          mma16(dvT[c], tt_frag<TI, LDT>(GT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
+      for (int s = 0; s < NS; ++s) {
+        const int qs = q0 + 32 * s;
+        if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
+        const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
+        float pr[16], ds[16];
         if (!rep) {
-          const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
+          f32x16 st, dpt;
+          zero(st);
+          zero(dpt);
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t) {
+            mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t]);
+            mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
+            const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+            const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
+              if (edge) {
+                const int q = q0 + qr + e;
+                pp = (q >= kj && q < T && kj < T) ? pp : 0.f;
+              }
+              pr[r] = pp;
+              ds[r] = pp * (dpt[r] - dv[e]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int qr = 32 * s + 8 * g + 4 * hi;
+            const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float rv = rwin[xr + e];
+              float pp = fact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
+              if (fold) pp *= akey;
+              pr[4 * g + e] = pp;
+            }
+          }
+        }
+        // dV^T[dcol][key] += dO^T[dcol][q] P[q][key];  dK^T[dim][key] += Q^T[dim][q] dS[q][key]
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
 #pragma unroll
           for (int c = 0; c < D / 32; ++c)
-            mma16(dkT[c], tt_frag<TI, LDT>(QT, 32 * s + 16 * u, 32 * c + l32, hi), sfr);
+            mma16(dvT[c], tt_frag<TI, LDT>(GT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
+          if (!rep) {
+            const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c)
+              mma16(dkT[c], tt_frag<TI, LDT>(QT, 32 * s + 16 * u, 32 * c + l32, hi), sfr);
+          }
         }
       }
+    }
+    if (rep && kj < T) {  // a replaced head's query gradient is zero
+      TI* dQ = reinterpret_cast<TI*>(p.dq) + hoff + (size_t)kj * D;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
     }
   }
 
   if (kj >= T) return;
-  TI* dV = reinterpret_cast<TI*>(p.dv) + hoff + (size_t)kj * D;
-  TI* dK = reinterpret_cast<TI*>(p.dk) + hoff + (size_t)kj * D;
-  const float vs = fact ? akey : 1.f;  // product form: the key's factor ea[kj]
-  const float ks = rep ? 0.f : p.scale;
+  TI* dV = reinterpret_cast<TI*>(p.dv) + kvoff + (size_t)kj * D;
+  TI* dK = reinterpret_cast<TI*>(p.dk) + kvoff + (size_t)kj * D;
+  const float ks = any_ord ? p.scale : 0.f;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
 #pragma unroll
@@ -261,13 +285,6 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
       store4(dK + dc, dkT[c][4 * g] * ks, dkT[c][4 * g + 1] * ks, dkT[c][4 * g + 2] * ks,
              dkT[c][4 * g + 3] * ks);
     }
-  if (rep) {  // a replaced head's query gradient is zero
-    TI* dQ = reinterpret_cast<TI*>(p.dq) + hoff + (size_t)kj * D;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
-  }
 }
 
 // ------------------------------------------------------------------------------------ bwd_dq
@@ -312,10 +329,11 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   const int qw = q0 + 32 * w;
   const int qi = qw + l32;
   const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+  const size_t kvoff = ((size_t)b * p.Hkv + h / (H / p.Hkv)) * (size_t)T * D;
   const size_t soff = ((size_t)b * H + h) * (size_t)T;
   const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
-  const TI* K = reinterpret_cast<const TI*>(p.k) + hoff;
-  const TI* V = reinterpret_cast<const TI*>(p.v) + hoff;
+  const TI* K = reinterpret_cast<const TI*>(p.k) + kvoff;
+  const TI* V = reinterpret_cast<const TI*>(p.v) + kvoff;
   const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
 
   Frag<TI> qf[D / 16], gf[D / 16];
@@ -408,10 +426,13 @@ hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
 
 template <typename TI, int D>
 hipError_t launch_kv_t(const LayerArgs& a, hipStream_t s) {
-  const int BHp = (a.B * a.H + 7) & ~7;
+  const int BHp = (a.B * a.Hkv + 7) & ~7;
   const long long blocks = (long long)BHp * ((a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_kv_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  if (a.Hkv == a.H)
+    hipLaunchKernelGGL((bwd_kv_kernel<TI, D, false>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel<TI, D, true>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 

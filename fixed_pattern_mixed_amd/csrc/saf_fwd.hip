@@ -60,7 +60,8 @@ struct FwdSmem {
 
 struct FwdItem {
   int b, h, q0, T, H;
-  size_t hoff;
+  size_t hoff;   // the query head's [T][D] slice (Q, O)
+  size_t kvoff;  // its key/value head's slice (K, V)
 };
 
 template <typename TI, int D, int KIND>
@@ -76,8 +77,8 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   const int qw = q0 + w * 32;  // the wave's first query
   const int qi = qw + l32;     // the lane's query
   const TI* Q = reinterpret_cast<const TI*>(p.q) + it.hoff;
-  const TI* K = reinterpret_cast<const TI*>(p.k) + it.hoff;
-  const TI* V = reinterpret_cast<const TI*>(p.v) + it.hoff;
+  const TI* K = reinterpret_cast<const TI*>(p.k) + it.kvoff;
+  const TI* V = reinterpret_cast<const TI*>(p.v) + it.kvoff;
   const float* arow = ORD ? nullptr : (FACT ? p.pat.ea(h) : p.a + (size_t)h * p.pat_len);
   const float* rrow = ORD ? nullptr : (FACT ? p.pat.er(h) : p.r + (size_t)h * p.pat_len);
   const float wscale = FACT ? 1.f : kLog2e;    // window values: ea/er, or a, r in log2 units
@@ -254,6 +255,7 @@ void mixed_fwd_kernel(LayerArgs p) {
   it.h = bh % H;
   it.q0 = (nqb - 1 - x / BHp) * kBQ;  // heaviest query blocks first
   it.hoff = ((size_t)it.b * H + it.h) * (size_t)T * D;
+  it.kvoff = ((size_t)it.b * p.Hkv + it.h / (H / p.Hkv)) * (size_t)T * D;
   const FwdSmem<TI> sm{Ks, VT, awin, rwin};
   if (!is_replaced(p.rep, it.h))
     fwd_item<TI, D, kOrdinary>(p, sm, it);

@@ -35,6 +35,7 @@ __host__ __device__ inline int pattern_stride(int P) { return ((3 * P + 64) + 63
 // Per-call description of the mixed layer, passed to kernels by value.
 struct LayerArgs {
   int B, H, T, d;
+  int Hkv;           // key/value heads: query head h reads K, V head h / (H / Hkv) (Hkv = H: MHA)
   int pat_len;
   float scale;       // softmax scale s of ordinary heads
   float scale_log2;  // s * log2(e): scores are exponentiated with exp2

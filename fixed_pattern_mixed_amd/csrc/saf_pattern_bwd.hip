@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
   const bool kval = kj < T;
   const size_t hoff = ((size_t)b * p.H + h) * (size_t)T * D;
   const size_t soff = ((size_t)b * p.H + h) * (size_t)T;
-  const TI* V = reinterpret_cast<const TI*>(p.v) + hoff;
+  const TI* V = reinterpret_cast<const TI*>(p.v) + ((size_t)b * p.Hkv + h / (p.H / p.Hkv)) * (size_t)T * D;
   const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
   const float* lse = p.lse + soff;
   const float* dlt = p.delta + soff;

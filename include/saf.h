@@ -116,6 +116,26 @@ saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
                         size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Grouped key/value heads (GQA): H query heads share Hkv key/value heads, query head h reading
+ * K, V head h / (H / Hkv); Hkv must divide H.                  [Notes §二.4; Paper page Table 26]
+ * A replaced head skips only its queries and keys of the score path: it still reads the V of its
+ * group.  saf_attn_fwd / saf_attn_bwd are these calls with Hkv = H.
+ *   q, o, dout, dq : [B][H][T][d] dt;   k, v, dk, dv : [B][Hkv][T][d] dt.
+ *   dk, dv of a key/value head are the sums over the query heads of its group (replaced heads add
+ *   to dv only; dk is zero when every head of the group is replaced).  Other arguments, the
+ *   workspaces and errors are those of saf_attn_fwd / saf_attn_bwd.
+ */
+saf_status saf_attn_fwd_gqa(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
+                            const void* k, const void* v, const uint8_t* replaced, const float* a,
+                            const float* r, int pat_len, const void* pattern, float scale, void* o,
+                            float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+saf_status saf_attn_bwd_gqa(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
+                            const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, const uint8_t* replaced, const float* a,
+                            const float* r, int pat_len, const void* pattern, float scale, void* dq,
+                            void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Gradient with respect to the replaced heads' pattern, for a pattern that is trained instead of
  * frozen ([Paper page] Table 14, "trainable mean"; saf_attn_bwd treats a and r as frozen).
  * With P(i,j) = exp(a[j] + r[i-j]) / Z(i) on j <= i ([Notes §二.3, Eq.(3)]), G(i,j) = dout_i . v_j

@@ -8,7 +8,10 @@ trained activations (no dataset or checkpoint is used):
   - a 124M-parameter decoder layer: 12 heads of width 64, at 4K and 8K context
     ([Notes §三]; [Paper page] Table 2),
   - one GPU's share of the 1B run at 8K context ([Notes §四.6]; [Paper page] Table 23),
-  - causal prefill at batch 64 and at 16K context ([Paper page] Table 29),
+  - causal prefill at batch 64 and at 16K context ([Paper page] Table 29), and at batch 1, where
+    the pages see launch overhead dominate ([Notes §四], Appendix D.3),
+  - a grouped-query prefill shaped like Qwen3-4B (32 query heads sharing 8 key/value heads of width
+    128; [Notes §二.4] and [Paper page] Table 26 run SAF on that model's GQA layers),
 plus a tiny fp32 case for exact parity.  Q, K, V and dO are N(0, 1); the replaced heads' a and r are
 random preferences in the same position/distance parametrisation as the pages' "structured random"
 control ([Notes §二.2]).  Citation keys as in the oracle package.
@@ -36,10 +39,15 @@ class Workload:
     index: int            # seed offset
     calib_N: int = 0      # > 0: also a calibration over calib_N sequences
     note: str = ""
+    Hkv: int = 0          # key/value heads (grouped-query attention); 0 = H
 
     @property
     def torch_dtype(self):
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def kv_heads(self):
+        return self.Hkv or self.H
 
     def replaced(self, placement: str = "interleaved"):
         return replaced_mask(self.H, self.n_replaced, placement)
@@ -60,6 +68,10 @@ WORKLOADS = {
                  note="causal prefill, batch 64 at 4K, 25% replaced, forward only"),
         Workload("prefill_b2_t16384", 2, 12, 16384, 64, "bf16", 3, 0.5, False, 5,
                  note="causal prefill, batch 2 at 16K, 25% replaced, forward only"),
+        Workload("prefill_b1_t4096", 1, 12, 4096, 64, "bf16", 3, 0.5, False, 6,
+                 note="causal prefill, batch 1 at 4K (launch-bound), 25% replaced, forward only"),
+        Workload("qwen4b_gqa_t4096", 1, 32, 4096, 128, "bf16", 8, 0.5, False, 7, Hkv=8,
+                 note="grouped-query prefill, 32 query heads over 8 key/value heads, 25% replaced"),
     ]
 }
 
@@ -96,15 +108,17 @@ class LayerInputs:
 
 
 def layer_inputs(B, H, T, d, dtype, replaced, ar_std=0.5, seed=SEED0, backward=True,
-                 pat_len=None, device="cpu"):
-    """Draw Q, K, V, dO ~ N(0,1) ([B,H,T,d], then cast to dtype) and a, r ~ N(0, ar_std^2)
-    ([H, pat_len] fp32), in that order, from a CPU generator seeded with `seed`."""
+                 pat_len=None, device="cpu", Hkv=None):
+    """Draw Q, K, V, dO ~ N(0,1) (Q, dO [B,H,T,d]; K, V [B,Hkv,T,d], Hkv = H unless given; then
+    cast to dtype) and a, r ~ N(0, ar_std^2) ([H, pat_len] fp32), in that order, from a CPU
+    generator seeded with `seed`."""
     g = torch.Generator().manual_seed(seed)
     P = T if pat_len is None else pat_len
     shape = (B, H, T, d)
+    kvshape = (B, H if Hkv is None else Hkv, T, d)
     q = torch.randn(shape, generator=g).to(dtype)
-    k = torch.randn(shape, generator=g).to(dtype)
-    v = torch.randn(shape, generator=g).to(dtype)
+    k = torch.randn(kvshape, generator=g).to(dtype)
+    v = torch.randn(kvshape, generator=g).to(dtype)
     dout = torch.randn(shape, generator=g).to(dtype) if backward else None
     a = torch.randn((H, P), generator=g) * ar_std
     r = torch.randn((H, P), generator=g) * ar_std
@@ -119,7 +133,7 @@ def layer_inputs(B, H, T, d, dtype, replaced, ar_std=0.5, seed=SEED0, backward=T
 
 def workload_inputs(w: Workload, placement="interleaved", device="cpu"):
     return layer_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.replaced(placement), w.ar_std,
-                        SEED0 + w.index, w.backward, device=device)
+                        SEED0 + w.index, w.backward, device=device, Hkv=w.Hkv or None)
 
 
 def calib_inputs(N, H, T, d, dtype, seed=SEED0 + 100, device="cpu"):
