@@ -56,14 +56,19 @@ __global__ __launch_bounds__(kNT) void calib_lse_kernel(CalibArgs p) {
     qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
   float m = -INFINITY, l = 0.f;
   const int nkt = (min(T, q0 + kBQ) + kBK - 1) / kBK;
+  Chunks<TI, D, kBK, kNT> kreg;  // the next key tile, in flight while the current one is used
+  kreg.load(K, 0, T, tid);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * kBK;
     __syncthreads();
-    stage_rows<TI, D, kBK, LDP, kNT>(Ks, K, k0, T, tid);
+    kreg.template store<LDP>(Ks, tid);
     __syncthreads();
+    if (kt + 1 < nkt) kreg.load(K, k0 + kBK, T, tid);
     if (k0 > qw + 31) continue;
     float sv[NS][16];
     bool act[NS];
+    // keys past a row's query or past the end exist only in diagonal or last tiles (wave-uniform)
+    const bool edge = (k0 + kBK - 1 > qw) || (k0 + kBK > T) || (qw + 31 >= T);
     float tmax = -INFINITY;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -76,21 +81,29 @@ __global__ __launch_bounds__(kNT) void calib_lse_kernel(CalibArgs p) {
       for (int t = 0; t < D / 16; ++t) mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = ks + crow(r, hi);
-        const float v = (key <= qi && key < T) ? st[r] * p.scale_log2 : -INFINITY;
+        float v = st[r] * p.scale_log2;
+        if (edge) {
+          const int key = ks + crow(r, hi);
+          v = (key <= qi && key < T) ? v : -INFINITY;
+        }
         sv[s][r] = v;
         tmax = fmaxf(tmax, v);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float mnew = fmaxf(m, tmax);
-    const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mnew);
+    // a row with no visible key yet keeps m = -inf: skip its exponentials (they would be exp2(nan))
+    const bool live = mnew != -INFINITY;
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
     float lsum = 0.f;
+    if (live) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (!act[s]) continue;
+      for (int s = 0; s < NS; ++s) {
+        if (!act[s]) continue;
+        // exp2(-inf - m) = 0 for masked entries
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lsum += (sv[s][r] == -INFINITY) ? 0.f : exp2f(sv[s][r] - mnew);
+        for (int r = 0; r < 16; ++r) lsum += __builtin_amdgcn_exp2f(sv[s][r] - mnew);
+      }
     }
     l = l * alpha + lsum;
     m = mnew;
@@ -141,35 +154,55 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
     }
   double ent = 0.0;  // sum over n and this lane's entries of A log2 A (KL score only)
 
-  for (int n = 0; n < N; ++n) {
+  // sequence n + 1's key tile, query fragments and row statistic are loaded while n is used
+  const bool wave_sees = k0 <= qw + 31;  // this wave's queries see some of the tile's keys
+  Chunks<TI, D, kBK, kNT> kreg;
+  Frag<TI> qn[D / 16];
+  float lse_n = 0.f;
+  auto prefetch = [&](int n) {
     const size_t hoff = ((size_t)n * H + h) * (size_t)T * D;
-    const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
-    const TI* K = reinterpret_cast<const TI*>(p.k) + hoff;
-    const float lse2 = qi < T ? p.lse2[((size_t)n * H + h) * T + qi] : 0.f;
+    kreg.load(reinterpret_cast<const TI*>(p.k) + hoff, k0, T, tid);
+    if (wave_sees) {
+      const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t)
+        qn[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+      lse_n = qi < T ? p.lse2[((size_t)n * H + h) * T + qi] : 0.f;
+    }
+  };
+  prefetch(0);
+
+  for (int n = 0; n < N; ++n) {
+    const float lse2 = lse_n;
     const float inv_n = 1.f / (float)(n + 1);
-    __syncthreads();
-    stage_rows<TI, D, kBK, LDP, kNT>(Ks, K, k0, T, tid);
-    __syncthreads();
-    if (k0 > qw + 31) continue;  // this wave's queries see none of the tile's keys
     Frag<TI> qf[D / 16];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+    for (int t = 0; t < D / 16; ++t) qf[t] = qn[t];
+    __syncthreads();
+    kreg.template store<LDP>(Ks, tid);
+    __syncthreads();
+    if (n + 1 < N) prefetch(n + 1);
+    if (!wave_sees) continue;
     float ent_n = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
       if (ks > qw + 31 || ks >= T) continue;
+      // masked entries exist only in diagonal or last tiles (wave-uniform)
+      const bool edge = (ks + 31 > qw) || (ks + 31 >= T) || (qw + 31 >= T);
       f32x16 st;
       zero(st);
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = ks + crow(r, hi);
-        const bool valid = key <= qi && key < T && qi < T;
-        const float x = st[r] * p.scale_log2 - lse2;  // log2 A
-        const float a = valid ? exp2f(x) : 0.f;
+        bool valid = true;
+        if (edge) {
+          const int key = ks + crow(r, hi);
+          valid = key <= qi && key < T && qi < T;
+        }
+        const float x = fmaf(st[r], p.scale_log2, -lse2);  // log2 A
+        const float a = valid ? __builtin_amdgcn_exp2f(x) : 0.f;
         const float dlt = a - mean[s][r];
         mean[s][r] += dlt * inv_n;
         m2[s][r] += dlt * (a - mean[s][r]);
