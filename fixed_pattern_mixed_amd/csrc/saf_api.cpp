@@ -138,7 +138,7 @@ size_t pgrad_ws(int B, int H, int T, int d) {
 }
 
 struct FitLayout {
-  size_t colp, rowp, diagp, entp, state, total;
+  size_t colp, rowp, diagp, entp, state, zpart, gpart, bmax, total;
 };
 FitLayout fit_layout(int H, int T) {
   const size_t nrt = (T + saf::fit_row_tile() - 1) / saf::fit_row_tile();
@@ -149,7 +149,11 @@ FitLayout fit_layout(int H, int T) {
   L.diagp = L.rowp + align_up(sizeof(double) * H * nct * T);
   L.entp = L.diagp + align_up(sizeof(double) * H * nrt * nct * saf::fit_tile_distances());
   L.state = L.entp + align_up(sizeof(double) * H * nrt * nct);
-  L.total = L.state + align_up(sizeof(double) * H * saf::fit_state_stride(T));
+  const size_t ncb = (T + saf::fit_conv_block() - 1) / saf::fit_conv_block();
+  L.zpart = L.state + align_up(sizeof(double) * H * saf::fit_state_stride(T));
+  L.gpart = L.zpart + align_up(sizeof(double) * H * ncb * T);
+  L.bmax = L.gpart + align_up(sizeof(double) * H * ncb * 2 * T);
+  L.total = L.bmax + align_up(sizeof(double) * H * saf::fit_adam_blocks(T) * 2);
   return L;
 }
 
@@ -512,6 +516,10 @@ saf_status saf_fit_pattern(int H, int T, const float* ahat, int steps, double lr
   fa.entp = reinterpret_cast<double*>(base + L.entp);
   fa.state = reinterpret_cast<double*>(base + L.state);
   fa.stride = saf::fit_state_stride(T);
+  fa.ncb = (T + saf::fit_conv_block() - 1) / saf::fit_conv_block();
+  fa.zpart = reinterpret_cast<double*>(base + L.zpart);
+  fa.gpart = reinterpret_cast<double*>(base + L.gpart);
+  fa.bmax = reinterpret_cast<double*>(base + L.bmax);
   fa.a_out = a; fa.r_out = r; fa.kl = kl; fa.loss = loss;
   hipError_t e = traced("fit_marginals", stream, [&] { return saf::launch_fit_marginals(fa, stream); });
   if (e != hipSuccess) return hip_fail(e, "fit marginals launch");

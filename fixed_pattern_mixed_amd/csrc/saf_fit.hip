@@ -18,10 +18,11 @@
 //                     in LDS) for partial column, row and distance sums and sum Ahat ln Ahat.
 //   fit_marg_reduce : fixed-order sums of the partials -> c, s, e, entropy term per head.
 //   fit_init        : a = r = 0 (the uniform causal pattern), Adam moments 0.
-//   fit_z           : Z'(i), w[i] = s[i] / Z'(i), ln Z'(i).
-//   fit_grad        : the two correlation sums -> gradient.
-//   fit_update      : one Adam step (beta1 0.9, beta2 0.999, eps 1e-8, bias corrections), then the
-//                     new maxima and ea, er.
+//   fit_zpart       : partial Z'(i) per block of the summed index.
+//   fit_gpart       : partial correlation sums (w[i] = s[i] / Z'(i) formed from the Z' partials).
+//   fit_adam        : the gradient from the partials and one Adam step (beta1 0.9, beta2 0.999,
+//                     eps 1e-8, bias corrections), elementwise; per-block maxima of a and r.
+//   fit_factors     : the maxima, then ea, er.
 //   fit_final       : the loss, mean row KL = L + (1/T) sum Ahat ln Ahat, fp32 a and r.
 #include "saf_device.h"
 #include "saf_internal.h"
@@ -34,7 +35,7 @@ constexpr int kRT = 64;         // rows of a marginal tile
 constexpr int kCT = 256;        // columns of a marginal tile
 constexpr int kLDT = kCT + 4;   // LDS row stride of the tile (conflict-free row, column and diagonal reads)
 constexpr int kND = kRT + kCT - 1;  // distances a tile spans
-constexpr int kUpd = 1024;      // threads of the update kernel
+constexpr int kUpd = 1024;      // threads of the final (per-head) kernel
 
 __global__ __launch_bounds__(kNT) void fit_marg_kernel(FitArgs p) {
   __shared__ float tile[kRT * kLDT];
@@ -134,118 +135,197 @@ __global__ __launch_bounds__(kNT) void fit_init_kernel(FitArgs p) {
   }
 }
 
-// Z'(i) = sum_{k<=i} ea[k] er[i-k]: thread = row i; key tiles of kNT staged in LDS with the er
-// window they need.
-__global__ __launch_bounds__(kNT) void fit_z_kernel(FitArgs p) {
-  __shared__ double eas[kNT];
-  __shared__ double ers[2 * kNT];
+// The step kernels split positions and the summed index into blocks of kCB = 1024: a block
+// (position block, index block) stages its index block's factors and the shifted factors it needs
+// (a window of 2 kCB values) in LDS; each thread owns 4 consecutive positions and keeps 8 window
+// values in registers, reusing half of them per step, so one broadcast read and four window reads
+// feed 16 (or 32) fp64 multiply-adds.  Partial sums per index block are added in a fixed order by
+// the next kernel.
+constexpr int kCB = 1024;
+
+// Partial Z'(i) over k in index block kc: zpart[kc][i] = sum_{k in kc, k<=i} ea[k] er[i-k], for the
+// rows i of row block rb >= kc.
+__global__ __launch_bounds__(kNT) void fit_zpart_kernel(FitArgs p) {
+  __shared__ __attribute__((aligned(16))) double eas[kCB];
+  __shared__ __attribute__((aligned(16))) double ers[2 * kCB];
+  const int nb = p.ncb;
+  const int rb = blockIdx.x / nb, kc = blockIdx.x % nb;
+  if (kc > rb) return;
   const int h = blockIdx.y, T = p.T, tid = threadIdx.x;
-  const int i0 = blockIdx.x * kNT, i = i0 + tid;
+  const int i0 = rb * kCB, k0 = kc * kCB;
   const double* ea = p.ea(h);
   const double* er = p.er(h);
-  double acc = 0.0;
-  const int last = min(i0 + kNT - 1, T - 1);
-  for (int c0 = 0; c0 <= last; c0 += kNT) {
-    const int db = i0 - c0 - (kNT - 1);  // distance held in ers[0]
-    __syncthreads();
-    eas[tid] = c0 + tid < T ? ea[c0 + tid] : 0.0;
-    for (int x = tid; x < 2 * kNT - 1; x += kNT) {
-      const int dist = db + x;
-      ers[x] = (dist >= 0 && dist < T) ? er[dist] : 0.0;
-    }
-    __syncthreads();
-    if (i < T) {
-      const int base = tid + (kNT - 1);
-#pragma unroll 8
-      for (int kk = 0; kk < kNT; ++kk) acc = fma(eas[kk], ers[base - kk], acc);
+  const int d0 = i0 - k0 - (kCB - 1);  // distance held in ers[0]
+  for (int y = tid; y < kCB; y += kNT) eas[y] = k0 + y < T ? ea[k0 + y] : 0.0;
+  for (int y = tid; y < 2 * kCB; y += kNT) {
+    const int d = d0 + y;
+    ers[y] = (d >= 0 && d < T) ? er[d] : 0.0;  // negative distance: a future key, weight 0
+  }
+  __syncthreads();
+  // row i0 + 4t + u and key k0 + kk + j read ers[4t + u - kk - j + kCB - 1] = W[3 + u - j] with
+  // W = ers[base .. base + 7], base = 4t + kCB - 4 - kk
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  int base = 4 * tid + kCB - 4;
+  double W[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) W[q] = ers[base + q];
+  for (int kk = 0; kk < kCB; kk += 4) {
+    const double e4[4] = {eas[kk], eas[kk + 1], eas[kk + 2], eas[kk + 3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = fma(e4[j], W[3 + u - j], acc[u]);
+    if (kk + 4 < kCB) {  // slide the window down by 4
+      base -= 4;
+#pragma unroll
+      for (int q = 7; q >= 4; --q) W[q] = W[q - 4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) W[q] = ers[base + q];
     }
   }
-  if (i < T) {
-    p.w(h)[i] = p.s(h)[i] / acc;
-    p.lz(h)[i] = log(acc);
+  double* zp = p.zpart + ((size_t)h * nb + kc) * T;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = i0 + 4 * tid + u;
+    if (i < T) zp[i] = acc[u];
   }
 }
 
-// For position x: colS = sum_{i>=x} er[i-x] w[i], diagS = sum_{i>=x} ea[i-x] w[i]; the gradient
-// (1/T)(ea[x] colS - c[x]) for a[x] and (1/T)(er[x] diagS - e[x]) for r[x].
-__global__ __launch_bounds__(kNT) void fit_grad_kernel(FitArgs p) {
-  __shared__ double ws[kNT];
-  __shared__ double ers[2 * kNT];
-  __shared__ double eas[2 * kNT];
+// Z'(i) from the partials (fixed order)
+__device__ __forceinline__ double z_of(const FitArgs& p, int h, int i) {
+  double z = 0.0;
+  const int rb = i / kCB;
+  for (int kc = 0; kc <= rb; ++kc) z += p.zpart[((size_t)h * p.ncb + kc) * p.T + i];
+  return z;
+}
+
+// Partial correlation sums over i in index block ic for the positions x of block xb <= ic:
+// cs = sum er[i-x] w[i], ds = sum ea[i-x] w[i], with w[i] = s[i] / Z'(i).
+__global__ __launch_bounds__(kNT) void fit_gpart_kernel(FitArgs p) {
+  __shared__ __attribute__((aligned(16))) double ws[kCB];
+  __shared__ __attribute__((aligned(16))) double ers[2 * kCB];
+  __shared__ __attribute__((aligned(16))) double eas[2 * kCB];
+  const int nb = p.ncb;
+  const int xb = blockIdx.x / nb, ic = blockIdx.x % nb;
+  if (ic < xb) return;
   const int h = blockIdx.y, T = p.T, tid = threadIdx.x;
-  const int x0 = blockIdx.x * kNT, x = x0 + tid;
+  const int x0 = xb * kCB, i0 = ic * kCB;
   const double* ea = p.ea(h);
   const double* er = p.er(h);
-  const double* w = p.w(h);
-  double cs = 0.0, ds = 0.0;
-  for (int c0 = x0; c0 < T; c0 += kNT) {
-    const int db = c0 - x0 - (kNT - 1);  // offset i - x held in the windows' slot 0
-    __syncthreads();
-    ws[tid] = c0 + tid < T ? w[c0 + tid] : 0.0;
-    for (int y = tid; y < 2 * kNT - 1; y += kNT) {
-      const int off = db + y;
-      const bool ok = off >= 0 && off < T;
-      ers[y] = ok ? er[off] : 0.0;
-      eas[y] = ok ? ea[off] : 0.0;
-    }
-    __syncthreads();
-    if (x < T) {
-      const int base = (kNT - 1) - tid;  // window slot of offset (c0 + ii) - x is base + ii
-#pragma unroll 8
-      for (int ii = 0; ii < kNT; ++ii) {
-        const double wi = ws[ii];
-        cs = fma(ers[base + ii], wi, cs);
-        ds = fma(eas[base + ii], wi, ds);
+  const int o0 = i0 - x0 - (kCB - 1);  // offset i - x held in the windows' slot 0
+  for (int y = tid; y < kCB; y += kNT) {
+    const int i = i0 + y;
+    ws[y] = i < T ? p.s(h)[i] / z_of(p, h, i) : 0.0;
+  }
+  for (int y = tid; y < 2 * kCB; y += kNT) {
+    const int o = o0 + y;
+    const bool ok = o >= 0 && o < T;
+    ers[y] = ok ? er[o] : 0.0;
+    eas[y] = ok ? ea[o] : 0.0;
+  }
+  __syncthreads();
+  // position x0 + 4t + u and index i0 + ii + j read slot ii + j - 4t - u + kCB - 1 = base + 3 + j - u
+  // with base = ii - 4t + kCB - 4
+  double cs[4] = {0.0, 0.0, 0.0, 0.0}, ds[4] = {0.0, 0.0, 0.0, 0.0};
+  int base = kCB - 4 - 4 * tid;
+  double Wr[8], Wa[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    Wr[q] = ers[base + q];
+    Wa[q] = eas[base + q];
+  }
+  for (int ii = 0; ii < kCB; ii += 4) {
+    const double w4[4] = {ws[ii], ws[ii + 1], ws[ii + 2], ws[ii + 3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        cs[u] = fma(Wr[3 + j - u], w4[j], cs[u]);
+        ds[u] = fma(Wa[3 + j - u], w4[j], ds[u]);
+      }
+    if (ii + 4 < kCB) {  // slide the windows up by 4
+      base += 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        Wr[q] = Wr[q + 4];
+        Wa[q] = Wa[q + 4];
+      }
+#pragma unroll
+      for (int q = 4; q < 8; ++q) {
+        Wr[q] = ers[base + q];
+        Wa[q] = eas[base + q];
       }
     }
   }
-  if (x < T) {
-    const double invT = 1.0 / (double)T;
-    p.g(h)[x] = (ea[x] * cs - p.c(h)[x]) * invT;
-    p.g(h)[T + x] = (er[x] * ds - p.e(h)[x]) * invT;
+  double* gp = p.gpart + ((size_t)h * nb + ic) * 2 * (size_t)T;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int x = x0 + 4 * tid + u;
+    if (x < T) {
+      gp[x] = cs[u];
+      gp[T + x] = ds[u];
+    }
   }
 }
 
-__device__ double block_max(double v, double* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double m = red[0];
-  for (int k = 1; k < kUpd / 64; ++k) m = fmax(m, red[k]);
-  return m;
-}
-
-// One Adam step on (a, r) of head blockIdx.x, then the new maxima and the factors ea, er.
-__global__ __launch_bounds__(kUpd) void fit_update_kernel(FitArgs p, double lr, double c1, double c2) {
-  __shared__ double red[kUpd / 64];
-  const int h = blockIdx.x, T = p.T;
-  double* al = p.al(h);
-  double* rh = p.rh(h);
-  double* m = p.m(h);
-  double* v = p.v(h);
-  const double* g = p.g(h);
+// One Adam step, elementwise over the 2T parameters of every head (a then r); each block also
+// writes the maxima of the new a and r over its elements.
+__global__ __launch_bounds__(kNT) void fit_adam_kernel(FitArgs p, double lr, double c1, double c2) {
+  __shared__ double ra[kNT / 64], rr[kNT / 64];
+  const int h = blockIdx.y, T = p.T;
+  const int x = blockIdx.x * kNT + threadIdx.x;
   const double b1 = 0.9, b2 = 0.999, eps = 1e-8;
   double ma = -INFINITY, mr = -INFINITY;
-  for (int x = threadIdx.x; x < 2 * T; x += kUpd) {
-    const double gx = g[x];
+  if (x < 2 * T) {
+    // gradient: (1/T)(ea[y] cs[y] - c[y]) for a[y], (1/T)(er[y] ds[y] - e[y]) for r[y]
+    const int y = x < T ? x : x - T;
+    double sum = 0.0;
+    for (int ic = y / kCB; ic < p.ncb; ++ic) sum += p.gpart[((size_t)h * p.ncb + ic) * 2 * (size_t)T + x];
+    const double invT = 1.0 / (double)T;
+    const double gx = x < T ? (p.ea(h)[y] * sum - p.c(h)[y]) * invT : (p.er(h)[y] * sum - p.e(h)[y]) * invT;
+    double* m = p.m(h);
+    double* v = p.v(h);
     const double mx = b1 * m[x] + (1.0 - b1) * gx;
     const double vx = b2 * v[x] + (1.0 - b2) * gx * gx;
     m[x] = mx;
     v[x] = vx;
-    double* wgt = x < T ? &al[x] : &rh[x - T];
+    double* wgt = x < T ? &p.al(h)[y] : &p.rh(h)[y];
     const double nw = *wgt - lr * (mx / c1) / (sqrt(vx / c2) + eps);
     *wgt = nw;
-    if (x < T) ma = fmax(ma, nw); else mr = fmax(mr, nw);
+    if (x < T) ma = nw; else mr = nw;
   }
-  ma = block_max(ma, red);
-  mr = block_max(mr, red);
-  for (int x = threadIdx.x; x < T; x += kUpd) {
-    p.ea(h)[x] = exp(al[x] - ma);
-    p.er(h)[x] = exp(rh[x] - mr);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    ma = fmax(ma, __shfl_xor(ma, o));
+    mr = fmax(mr, __shfl_xor(mr, o));
   }
+  if ((threadIdx.x & 63) == 0) {
+    ra[threadIdx.x >> 6] = ma;
+    rr[threadIdx.x >> 6] = mr;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
+    double* bm = p.bmax + ((size_t)h * gridDim.x + blockIdx.x) * 2;
+    bm[0] = fmax(fmax(ra[0], ra[1]), fmax(ra[2], ra[3]));
+    bm[1] = fmax(fmax(rr[0], rr[1]), fmax(rr[2], rr[3]));
+  }
+}
+
+// The maxima of a and r from the Adam blocks' maxima, then ea = exp(a - max a), er = exp(r - max r).
+__global__ __launch_bounds__(kNT) void fit_factors_kernel(FitArgs p, int nblk) {
+  const int h = blockIdx.y, T = p.T;
+  const int x = blockIdx.x * kNT + threadIdx.x;
+  double ma = -INFINITY, mr = -INFINITY;
+  const double* bm = p.bmax + (size_t)h * nblk * 2;
+  for (int k = 0; k < nblk; ++k) {
+    ma = fmax(ma, bm[2 * k]);
+    mr = fmax(mr, bm[2 * k + 1]);
+  }
+  if (x < T) {
+    p.ea(h)[x] = exp(p.al(h)[x] - ma);
+    p.er(h)[x] = exp(p.rh(h)[x] - mr);
+  }
+  if (x == 0) {
     p.st(h)[kStMa] = ma;
     p.st(h)[kStMr] = mr;
   }
@@ -259,7 +339,7 @@ __global__ __launch_bounds__(kUpd) void fit_final_kernel(FitArgs p) {
   const double shift = st[kStMa] + st[kStMr];
   double acc = 0.0;
   for (int x = threadIdx.x; x < T; x += kUpd) {
-    acc += p.s(h)[x] * (p.lz(h)[x] + shift) - p.al(h)[x] * p.c(h)[x] - p.rh(h)[x] * p.e(h)[x];
+    acc += p.s(h)[x] * (log(z_of(p, h, x)) + shift) - p.al(h)[x] * p.c(h)[x] - p.rh(h)[x] * p.e(h)[x];
     p.a_out[(size_t)h * T + x] = (float)p.al(h)[x];
     p.r_out[(size_t)h * T + x] = (float)p.rh(h)[x];
   }
@@ -279,6 +359,8 @@ __global__ __launch_bounds__(kUpd) void fit_final_kernel(FitArgs p) {
 }  // namespace
 
 int fit_row_tile() { return kRT; }
+int fit_conv_block() { return kCB; }
+int fit_adam_blocks(int T) { return (2 * T + kNT - 1) / kNT; }
 int fit_col_tile() { return kCT; }
 int fit_tile_distances() { return kND; }
 
@@ -296,15 +378,19 @@ hipError_t launch_fit_init(const FitArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fit_z(const FitArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(fit_z_kernel, dim3((a.T + kNT - 1) / kNT, a.H), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(fit_zpart_kernel, dim3(a.ncb * a.ncb, a.H), dim3(kNT), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fit_step(const FitArgs& a, double lr, double c1, double c2, hipStream_t s) {
-  hipLaunchKernelGGL(fit_grad_kernel, dim3((a.T + kNT - 1) / kNT, a.H), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(fit_gpart_kernel, dim3(a.ncb * a.ncb, a.H), dim3(kNT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fit_update_kernel, dim3(a.H), dim3(kUpd), 0, s, a, lr, c1, c2);
+  const int nblk = fit_adam_blocks(a.T);
+  hipLaunchKernelGGL(fit_adam_kernel, dim3(nblk, a.H), dim3(kNT), 0, s, a, lr, c1, c2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fit_factors_kernel, dim3((a.T + kNT - 1) / kNT, a.H), dim3(kNT), 0, s, a, nblk);
   return hipGetLastError();
 }
 

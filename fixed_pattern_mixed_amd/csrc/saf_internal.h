@@ -97,6 +97,10 @@ struct FitArgs {
   double* entp;          // [H][nrt][nct] partial sum Ahat ln Ahat
   double* state;
   size_t stride;
+  int ncb;               // blocks of 1024 positions (the step kernels' split of T)
+  double* zpart;         // [H][ncb][T] partial row normalisers Z'
+  double* gpart;         // [H][ncb][2T] partial correlation sums of the gradient
+  double* bmax;          // [H][Adam blocks][2] per-block maxima of a and r
   float* a_out;          // [H][T]
   float* r_out;
   double* kl;            // [H]
@@ -130,6 +134,8 @@ hipError_t launch_pattern_grad_reduce(const LayerArgs& a, const HeadList& rl, hi
 int pattern_grad_sub_block();  // keys per dr partial row of bwd_pattern (one per wave)
 int pattern_grad_chunks(int T);  // first-stage chunks of the dr reduction
 int fit_row_tile();
+int fit_conv_block();
+int fit_adam_blocks(int T);
 int fit_col_tile();
 int fit_tile_distances();
 hipError_t launch_fit_marginals(const FitArgs& a, hipStream_t s);
