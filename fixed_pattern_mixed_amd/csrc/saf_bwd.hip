@@ -196,6 +196,61 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
       __syncthreads();
       if (qt + 1 < nqt) load_tile(q0 + BQ);
 
+      // Ordinary head, both subtiles below the diagonal and inside the sequence (most tiles):
+      // straight-line code without masks, ordered so that subtile 1's score product is in flight
+      // during subtile 0's exponentials and its dP product during subtile 0's dV / dK products.
+      if (NS == 2 && !rep && q0 >= kw + 31 && q0 + BQ <= T && kw + 31 < T) {
+        auto grad_entries = [&](const f32x16& st, const f32x16& dpt, int s, float* pr, float* ds) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int qr = 32 * s + 8 * g + 4 * hi;
+            const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+            const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              const float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
+              pr[r] = pp;
+              ds[r] = pp * (dpt[r] - dv[e]);
+            }
+          }
+        };
+        auto grad_products = [&](int s, const float* pr, const float* ds) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
+            const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c) {
+              mma16(dvT[c], tt_frag<TI, LDT>(GT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
+              mma16(dkT[c], tt_frag<TI, LDT>(QT, 32 * s + 16 * u, 32 * c + l32, hi), sfr);
+            }
+          }
+        };
+        f32x16 st0, dp0, st1, dp1;
+        zero(st0);
+        zero(dp0);
+        zero(st1);
+        zero(dp1);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          mma16(st0, load8(Qs + l32 * LDP + 16 * t + 8 * hi), kf[t]);
+          mma16(dp0, load8(Gs + l32 * LDP + 16 * t + 8 * hi), vf[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) mma16(st1, load8(Qs + (32 + l32) * LDP + 16 * t + 8 * hi), kf[t]);
+        float pr[16], ds[16];
+        grad_entries(st0, dp0, 0, pr, ds);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+        grad_products(0, pr, ds);
+        grad_entries(st1, dp1, 1, pr, ds);
+        grad_products(1, pr, ds);
+        continue;
+      }
+
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int qs = q0 + 32 * s;
