@@ -117,6 +117,44 @@ hipError_t traced(const char* name, hipStream_t s, F&& fn) {
   return hipSuccess;
 }
 
+// A second stream per (host thread, device), created on first use and kept, on which the
+// backward's query-block kernel runs beside the key-block kernel: both depend only on the
+// preprocess and write disjoint outputs, so the hardware can fill one kernel's tail with the other's
+// blocks.  The fork and join are event record / wait pairs on the caller's stream, which a graph
+// capture of that stream records as dependencies.  Default stream priority.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+thread_local SideStream g_side[kMaxDevices];
+
+// The side stream of the current device, or nullptr (then everything runs on the caller's stream).
+SideStream* side_stream() {
+#ifdef SAF_SERIAL_BWD
+  return nullptr;
+#else
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f) hipEventDestroy(f);
+      hipStreamDestroy(s);
+      return nullptr;
+    }
+    ss.s = s;
+    ss.fork = f;
+    ss.join = j;
+  }
+  return &ss;
+#endif
+}
+
 size_t pattern_bytes(int H, int P) {
   return align_up(sizeof(float) * (size_t)saf::pattern_stride(P) * H);
 }
@@ -402,9 +440,19 @@ static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
   const bool bf = dt == SAF_BF16;
   hipError_t e = traced("bwd_pre", stream, [&] { return saf::launch_bwd_pre(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  SideStream* side = any_ord ? side_stream() : nullptr;
+  if (side) {  // fork: the query-block kernel on the side stream after the preprocess
+    if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return hip_fail(e, "backward fork");
+    if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return hip_fail(e, "backward fork");
+    e = traced("bwd_dq", side->s, [&] { return saf::launch_bwd_dq(la, bf, side->s); });
+    if (e != hipSuccess) return hip_fail(e, "backward query-block launch");
+  }
   e = traced("bwd_kv", stream, [&] { return saf::launch_bwd_kv(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward key-block launch");
-  if (any_ord) {
+  if (side) {  // join
+    if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return hip_fail(e, "backward join");
+    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return hip_fail(e, "backward join");
+  } else if (any_ord) {
     e = traced("bwd_dq", stream, [&] { return saf::launch_bwd_dq(la, bf, stream); });
     if (e != hipSuccess) return hip_fail(e, "backward query-block launch");
   }

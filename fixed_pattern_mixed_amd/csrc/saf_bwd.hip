@@ -230,21 +230,19 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
           }
         };
         f32x16 st0, dp0, st1, dp1;
-        zero(st0);
-        zero(dp0);
-        zero(st1);
-        zero(dp1);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          mma16(st0, load8(Qs + l32 * LDP + 16 * t + 8 * hi), kf[t]);
-          mma16(dp0, load8(Gs + l32 * LDP + 16 * t + 8 * hi), vf[t]);
+          mma16(st0, load8(Qs + l32 * LDP + 16 * t + 8 * hi), kf[t], t == 0);
+          mma16(dp0, load8(Gs + l32 * LDP + 16 * t + 8 * hi), vf[t], t == 0);
         }
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) mma16(st1, load8(Qs + (32 + l32) * LDP + 16 * t + 8 * hi), kf[t]);
+        for (int t = 0; t < D / 16; ++t)
+          mma16(st1, load8(Qs + (32 + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
         float pr[16], ds[16];
         grad_entries(st0, dp0, 0, pr, ds);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+        for (int t = 0; t < D / 16; ++t)
+          mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
         grad_products(0, pr, ds);
         grad_entries(st1, dp1, 1, pr, ds);
         grad_products(1, pr, ds);
@@ -259,12 +257,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         float pr[16], ds[16];
         if (!rep) {
           f32x16 st, dpt;
-          zero(st);
-          zero(dpt);
 #pragma unroll
           for (int t = 0; t < D / 16; ++t) {
-            mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t]);
-            mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+            mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
+            mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
           }
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -430,12 +426,10 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
       const int ks = k0 + 32 * s;
       if (ks > qw + 31 || ks >= T) break;  // wave-uniform: the rest of the tile is masked out
       f32x16 st, dpt;
-      zero(st);
-      zero(dpt);
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
-        mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t]);
+        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+        mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], t == 0);
       }
       const bool edge = (ks + 31 > qw) || (ks + 31 >= T);
       float ds[16];

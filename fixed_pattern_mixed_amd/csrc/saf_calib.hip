@@ -76,9 +76,9 @@ __global__ __launch_bounds__(kNT) void calib_lse_kernel(CalibArgs p) {
       act[s] = ks <= qw + 31 && ks < T;
       if (!act[s]) continue;
       f32x16 st;
-      zero(st);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
+      for (int t = 0; t < D / 16; ++t)
+        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float v = st[r] * p.scale_log2;
@@ -191,9 +191,9 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
       // masked entries exist only in diagonal or last tiles (wave-uniform)
       const bool edge = (ks + 31 > qw) || (ks + 31 >= T) || (qw + 31 >= T);
       f32x16 st;
-      zero(st);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
+      for (int t = 0; t < D / 16; ++t)
+        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         bool valid = true;

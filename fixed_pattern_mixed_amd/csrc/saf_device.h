@@ -50,6 +50,19 @@ __device__ __forceinline__ void mma16(f32x16& acc, const Frag<float>& a, const F
   for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[e], b.v[e], acc, 0, 0, 0);
 }
 
+// The same, starting a fresh accumulation when `first` (a compile-time constant after unrolling):
+// the zero accumulator is then the instruction's inline constant, not 16 register moves.
+__device__ __forceinline__ void mma16(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b, bool first) {
+  const f32x16 z = {};
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, first ? z : acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16& acc, const Frag<float>& a, const Frag<float>& b, bool first) {
+  const f32x16 z = {};
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[0], b.v[0], first ? z : acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 1; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
 __device__ __forceinline__ void zero(f32x16& x) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) x[r] = 0.f;

@@ -149,10 +149,9 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
       float pv[16];
       if (ORD) {
         f32x16 st;
-        zero(st);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-          mma16(st, load8(sm.Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t]);
+          mma16(st, load8(sm.Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
         float tmax = -INFINITY;
         if ((ks + 31 > qw) || (ks + 31 >= T)) {  // subtile crosses the diagonal or the end
 #pragma unroll

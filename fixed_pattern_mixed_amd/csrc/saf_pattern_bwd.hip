@@ -146,9 +146,9 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
       if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
       const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
       f32x16 gt;
-      zero(gt);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) mma16(gt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+      for (int t = 0; t < D / 16; ++t)
+        mma16(gt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g

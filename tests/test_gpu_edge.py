@@ -162,3 +162,36 @@ def test_wide_range_pattern_uses_exponential_form(dtype):
     heads = [(0, h) for h in range(H)]
     check_fwd(x, o, lse, heads, None, TOL[dtype], "wide")
     check_bwd(x, dq, dk, dv, heads, None, None, TOL[dtype], "wide")
+
+
+def test_graph_capture_of_forward_and_backward_replays_exactly():
+    """fwd + bwd captured into a HIP graph (the backward forks its query-block kernel onto a side
+    stream and joins back) replay to the bits of the eager calls, with eager work between replays."""
+    saf = _saf()
+    B, H, T, d = 2, 4, 300, 64
+    rep = [0, 1, 0, 1]
+    g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=17, device="cuda")
+    pat = saf.prepare_pattern(rep, g.a, g.r)
+    o0, l0 = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)
+    d0 = saf.bwd(g.q, g.k, g.v, o0, g.dout, l0, rep, g.a, g.r, pattern=pat)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):  # warm up on the capture stream
+        o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)
+        dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, pattern=pat)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cs):
+        o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)
+        dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, pattern=pat)
+    for it in range(3):
+        for t in (o, lse, dq, dk, dv):
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o0) and torch.equal(lse, l0), it
+        assert torch.equal(dq, d0[0]) and torch.equal(dk, d0[1]) and torch.equal(dv, d0[2]), it
+        saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)  # eager work between replays
+        torch.cuda.synchronize()
