@@ -6,8 +6,8 @@
 //   replaced head: O = P V, P(i,j) = exp(a[j] + r[i-j]) / Z(i) on j <= i         [Notes §二.3, Eq.(3)]
 // The fused kernel the pages describe runs ordinary heads as online-softmax tiles and rebuilds the
 // fixed heads' causal tiles in registers from the two preference vectors and Z before the product
-// with the current V ([Notes §二.4, Fig. 2]).  Here a work item is one (batch, head, 128-query
-// block); its 4 waves own 32 queries each and sweep the key tiles at or below the diagonal.  The
+// with the current V ([Notes §二.4, Fig. 2]).  Here a work item is one (batch, head, 256-query
+// block); its 8 waves own 32 queries each and sweep the key tiles at or below the diagonal.  The
 // next key tile is loaded into registers while the current one is multiplied, then written to LDS.
 // Each kind of item runs its own copy of the tile loop (no per-tile branching on the head kind).
 //
@@ -34,8 +34,12 @@
 namespace saf {
 namespace {
 
-constexpr int kBQ = 128;  // queries per work item
-constexpr int kNT = 256;  // threads per block (4 waves)
+#ifndef SAF_FWD_WAVES
+#define SAF_FWD_WAVES 8  // 8 waves share each staged key/value tile (fewer loads per query)
+#endif
+constexpr int kWaves = SAF_FWD_WAVES;
+constexpr int kBQ = 32 * kWaves;  // queries per work item (32 per wave)
+constexpr int kNT = 64 * kWaves;  // threads per block
 
 enum Kind { kOrdinary = 0, kProduct = 1, kExponential = 2 };
 
