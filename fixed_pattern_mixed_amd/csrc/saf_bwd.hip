@@ -61,9 +61,14 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(LayerArgs p) {
 }
 
 // ------------------------------------------------------------------------------------ bwd_kv
+#ifndef SAF_KV_WAVES
+#define SAF_KV_WAVES 4
+#endif
+constexpr int kKvNT = 64 * SAF_KV_WAVES;  // threads of a key-block work item (32 keys per wave)
+
 template <typename TI, int D>
 struct KvCfg {
-  static constexpr int BKV = 128;                         // keys per work item (4 waves x 32)
+  static constexpr int BKV = 32 * SAF_KV_WAVES;           // keys per work item
   static constexpr int BQ = sizeof(TI) == 2 ? 64 : 32;    // queries per staged tile
   static constexpr int NS = BQ / 32;                      // 32-query subtiles per tile
   static constexpr int LDP = D + 16 / (int)sizeof(TI);    // padded row of the Q / dO tiles
@@ -73,12 +78,12 @@ struct KvCfg {
 
 template <typename TI, int D>
 struct KvPrefetch {
-  Blocks4<TI, D, KvCfg<TI, D>::BQ, kNT> q, g;
+  Blocks4<TI, D, KvCfg<TI, D>::BQ, kKvNT> q, g;
   float rs, dl, rw;
 };
 
 template <typename TI, int D, bool GROUPED>
-__global__ __launch_bounds__(kNT)
+__global__ __launch_bounds__(kKvNT)
 __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bwd_kv_kernel(LayerArgs p) {
   using C = KvCfg<TI, D>;
   constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, LDT = C::LDT, WIN = C::WIN;
@@ -198,7 +203,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
 
       // Ordinary head, both subtiles below the diagonal and inside the sequence (most tiles):
       // straight-line code without masks, ordered so that subtile 1's score product is in flight
-      // during subtile 0's exponentials and its dP product during subtile 0's dV / dK products.
+      // during subtile 0's exponentials (and, at d = 128, its dP product during subtile 0's dV /
+      // dK products).
       if (NS == 2 && !rep && q0 >= kw + 31 && q0 + BQ <= T && kw + 31 < T) {
         auto grad_entries = [&](const f32x16& st, const f32x16& dpt, int s, float* pr, float* ds) {
 #pragma unroll
@@ -240,10 +246,19 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
           mma16(st1, load8(Qs + (32 + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
         float pr[16], ds[16];
         grad_entries(st0, dp0, 0, pr, ds);
+        if constexpr (D == 64) {
+          // 256-register budget (two waves per SIMD): subtile 0's products first keeps the
+          // live set smaller (measured faster at d = 64)
+          grad_products(0, pr, ds);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-          mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
-        grad_products(0, pr, ds);
+          for (int t = 0; t < D / 16; ++t)
+            mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
+        } else {
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t)
+            mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
+          grad_products(0, pr, ds);
+        }
         grad_entries(st1, dp1, 1, pr, ds);
         grad_products(1, pr, ds);
         continue;
@@ -479,9 +494,9 @@ hipError_t launch_kv_t(const LayerArgs& a, hipStream_t s) {
   const long long blocks = (long long)BHp * ((a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.Hkv == a.H)
-    hipLaunchKernelGGL((bwd_kv_kernel<TI, D, false>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<TI, D, false>), dim3((unsigned)blocks), dim3(kKvNT), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_kv_kernel<TI, D, true>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<TI, D, true>), dim3((unsigned)blocks), dim3(kKvNT), 0, s, a);
   return hipGetLastError();
 }
 
