@@ -448,6 +448,12 @@ def main():
             var[label] = {"ms_per_step": round(tv * 1e3, 4), "tflops": round(fv / tv / 1e12, 1),
                           "pct_bf16_peak": round(100 * fv / tv / 1e12 / PEAK_BF16_TFLOPS, 2)}
             del lv
+        if w.backward:  # the same layer with the backward's two kernels overlapped on two streams
+            saf.saf_set_backward_overlap(1)
+            to = time_steps(torch, layer, max(5, args.steps // 3), 2)
+            saf.saf_set_backward_overlap(0)
+            var["backward_overlap"] = {"ms_per_step": round(to * 1e3, 4),
+                                       "tokens_per_s": round(tokens / to, 1)}
         var["mixed_speedup_vs_all_ordinary"] = round(var["all_ordinary"]["ms_per_step"] / (t_step * 1e3), 4)
         var["replaced_vs_ordinary_time_per_head"] = round(
             var["all_replaced"]["ms_per_step"] / var["all_ordinary"]["ms_per_step"], 4)

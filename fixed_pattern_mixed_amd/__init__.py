@@ -94,6 +94,8 @@ _lib.saf_fit_pattern_workspace_size.restype = _sz
 _lib.saf_fit_pattern.argtypes = [_i, _i, _vp, _i, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _sz,
                                  _vp]
 _lib.saf_fit_pattern.restype = _i
+_lib.saf_set_backward_overlap.argtypes = [_i]
+_lib.saf_set_backward_overlap.restype = _i
 _lib.saf_select_heads.argtypes = [_i, _i, _vp, _vp, ctypes.c_double, _vp, ctypes.POINTER(_i)]
 _lib.saf_select_heads.restype = _i
 
@@ -104,6 +106,7 @@ saf_attn_fwd_gqa = _lib.saf_attn_fwd_gqa
 saf_attn_bwd_gqa = _lib.saf_attn_bwd_gqa
 saf_calibrate = _lib.saf_calibrate
 saf_select_heads = _lib.saf_select_heads
+saf_set_backward_overlap = _lib.saf_set_backward_overlap
 saf_fit_pattern = _lib.saf_fit_pattern
 saf_fit_pattern_workspace_size = _lib.saf_fit_pattern_workspace_size
 saf_attn_bwd_pattern = _lib.saf_attn_bwd_pattern

@@ -128,12 +128,11 @@ struct SideStream {
 };
 constexpr int kMaxDevices = 64;
 thread_local SideStream g_side[kMaxDevices];
+thread_local bool g_overlap = false;  // saf_set_backward_overlap
 
 // The side stream of the current device, or nullptr (then everything runs on the caller's stream).
 SideStream* side_stream() {
-#ifdef SAF_SERIAL_BWD
-  return nullptr;
-#else
+  if (!g_overlap) return nullptr;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   SideStream& ss = g_side[dev];
@@ -152,7 +151,6 @@ SideStream* side_stream() {
     ss.join = j;
   }
   return &ss;
-#endif
 }
 
 size_t pattern_bytes(int H, int P) {
@@ -325,6 +323,12 @@ saf_status saf_pattern_prepare(int H, const uint8_t* replaced, const float* a, c
   la.H = H; la.Hkv = H; la.T = pat_len; la.pat_len = pat_len;
   la.a = a; la.r = r;
   return setup_pattern(la, true, nullptr, pat_len, pattern, stream, "pattern preparation");
+}
+
+saf_status saf_set_backward_overlap(int enable) {
+  g_err[0] = 0;
+  g_overlap = enable != 0;
+  return SAF_OK;
 }
 
 saf_status saf_trace_begin(saf_kernel_event* ev, int capacity) {

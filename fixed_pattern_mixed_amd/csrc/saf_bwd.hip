@@ -436,6 +436,32 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
     store_tile();
     __syncthreads();
     if (kt + 1 < nkt) load_tile(k0 + BK);
+    // d = 64, both key subtiles below the diagonal and inside the sequence: the same work without
+    // masks or exits in one basic block (measured faster at d = 64; at d = 128 the register budget
+    // does not allow it)
+    if (D == 64 && NS == 2 && k0 + BK - 1 <= qw && k0 + BK <= T && qw + 31 < T) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        f32x16 st, dpt;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+          mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], t == 0);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ds[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2)) * (dpt[r] - dl);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const Frag<TI> sf = to_frag<TI>(&ds[8 * u]);
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c)
+            mma16(dqT[c], tt_frag<TI, LDT>(KT, 32 * s + 16 * u, 32 * c + l32, hi), sf);
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;

@@ -218,6 +218,18 @@ saf_status saf_select_heads(int L, int H, const double* score, const uint8_t* ac
 const char* saf_last_error(void);
 
 /*
+ * Overlap inside the backward (off by default; per host thread).  When enabled, saf_attn_bwd and
+ * saf_attn_bwd_gqa run the query-block kernel on a second stream of the current device (created on
+ * first use, kept for the thread's life, default priority) beside the key-block kernel: both depend
+ * only on the preprocess and write disjoint outputs.  The fork and join are event record / wait
+ * pairs on the caller's stream (a graph capture of that stream records them), so the call keeps its
+ * stream semantics and its results are bitwise the same.  Faster where the two kernels leave each
+ * other's tails idle (e.g. half the heads replaced at 8K context); per-kernel durations from
+ * saf_trace_* then overlap.
+ */
+saf_status saf_set_backward_overlap(int enable);
+
+/*
  * Per-kernel timing (off by default), for profiling a layer from the host.
  * saf_trace_begin(ev, capacity): until saf_trace_end(), every kernel that a call made on this
  * thread launches is bracketed by hipEventRecord(ev[i].start) / hipEventRecord(ev[i].stop) on that

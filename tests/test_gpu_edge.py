@@ -164,10 +164,13 @@ def test_wide_range_pattern_uses_exponential_form(dtype):
     check_bwd(x, dq, dk, dv, heads, None, None, TOL[dtype], "wide")
 
 
-def test_graph_capture_of_forward_and_backward_replays_exactly():
-    """fwd + bwd captured into a HIP graph (the backward forks its query-block kernel onto a side
-    stream and joins back) replay to the bits of the eager calls, with eager work between replays."""
+@pytest.mark.parametrize("overlap", [0, 1])
+def test_graph_capture_of_forward_and_backward_replays_exactly(overlap):
+    """fwd + bwd captured into a HIP graph (with overlap on, the backward forks its query-block
+    kernel onto a side stream and joins back) replay to the bits of the eager calls, with eager work
+    between replays."""
     saf = _saf()
+    saf.saf_set_backward_overlap(overlap)
     B, H, T, d = 2, 4, 300, 64
     rep = [0, 1, 0, 1]
     g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=17, device="cuda")
@@ -195,3 +198,21 @@ def test_graph_capture_of_forward_and_backward_replays_exactly():
         assert torch.equal(dq, d0[0]) and torch.equal(dk, d0[1]) and torch.equal(dv, d0[2]), it
         saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)  # eager work between replays
         torch.cuda.synchronize()
+    saf.saf_set_backward_overlap(0)
+
+
+def test_backward_overlap_gives_the_same_bits():
+    saf = _saf()
+    B, H, T, d = 2, 6, 700, 64
+    rep = [0, 1, 0, 0, 1, 0]
+    g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=19, device="cuda")
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    serial = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
+    saf.saf_set_backward_overlap(1)
+    try:
+        over = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
+        torch.cuda.synchronize()
+    finally:
+        saf.saf_set_backward_overlap(0)
+    for x, y in zip(serial, over):
+        assert torch.equal(x, y)
