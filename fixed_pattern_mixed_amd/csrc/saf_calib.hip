@@ -25,8 +25,8 @@
 namespace saf {
 namespace {
 
-constexpr int kNT = 256;
-constexpr int kBQ = kCalibQTile;  // 128
+constexpr int kNT = 64 * kCalibWaves;
+constexpr int kBQ = kCalibQTile;  // 32 queries per wave
 constexpr int kBK = kCalibKTile;  // 64
 
 template <typename TI, int D>

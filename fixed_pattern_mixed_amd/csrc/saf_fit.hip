@@ -19,7 +19,8 @@
 //   fit_marg_reduce : fixed-order sums of the partials -> c, s, e, entropy term per head.
 //   fit_init        : a = r = 0 (the uniform causal pattern), Adam moments 0.
 //   fit_zpart       : partial Z'(i) per block of the summed index.
-//   fit_gpart       : partial correlation sums (w[i] = s[i] / Z'(i) formed from the Z' partials).
+//   fit_w           : w[i] = s[i] / Z'(i) from the Z' partials.
+//   fit_gpart       : partial correlation sums.
 //   fit_adam        : the gradient from the partials and one Adam step (beta1 0.9, beta2 0.999,
 //                     eps 1e-8, bias corrections), elementwise; per-block maxima of a and r.
 //   fit_factors     : the maxima, then ea, er.
@@ -199,8 +200,14 @@ __device__ __forceinline__ double z_of(const FitArgs& p, int h, int i) {
   return z;
 }
 
+// w[i] = s[i] / Z'(i), once per step (the correlation blocks read it)
+__global__ __launch_bounds__(kNT) void fit_w_kernel(FitArgs p) {
+  const int h = blockIdx.y, i = blockIdx.x * kNT + threadIdx.x;
+  if (i < p.T) p.w(h)[i] = p.s(h)[i] / z_of(p, h, i);
+}
+
 // Partial correlation sums over i in index block ic for the positions x of block xb <= ic:
-// cs = sum er[i-x] w[i], ds = sum ea[i-x] w[i], with w[i] = s[i] / Z'(i).
+// cs = sum er[i-x] w[i], ds = sum ea[i-x] w[i].
 __global__ __launch_bounds__(kNT) void fit_gpart_kernel(FitArgs p) {
   __shared__ __attribute__((aligned(16))) double ws[kCB];
   __shared__ __attribute__((aligned(16))) double ers[2 * kCB];
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(kNT) void fit_gpart_kernel(FitArgs p) {
   const int o0 = i0 - x0 - (kCB - 1);  // offset i - x held in the windows' slot 0
   for (int y = tid; y < kCB; y += kNT) {
     const int i = i0 + y;
-    ws[y] = i < T ? p.s(h)[i] / z_of(p, h, i) : 0.0;
+    ws[y] = i < T ? p.w(h)[i] : 0.0;
   }
   for (int y = tid; y < 2 * kCB; y += kNT) {
     const int o = o0 + y;
@@ -383,8 +390,11 @@ hipError_t launch_fit_z(const FitArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fit_step(const FitArgs& a, double lr, double c1, double c2, hipStream_t s) {
-  hipLaunchKernelGGL(fit_gpart_kernel, dim3(a.ncb * a.ncb, a.H), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(fit_w_kernel, dim3((a.T + kNT - 1) / kNT, a.H), dim3(kNT), 0, s, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fit_gpart_kernel, dim3(a.ncb * a.ncb, a.H), dim3(kNT), 0, s, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nblk = fit_adam_blocks(a.T);
   hipLaunchKernelGGL(fit_adam_kernel, dim3(nblk, a.H), dim3(kNT), 0, s, a, lr, c1, c2);

@@ -148,7 +148,11 @@ hipError_t launch_calib_stats(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s);
 
 // Tile geometry shared by the host (workspace sizing) and the kernels.
-constexpr int kCalibQTile = 128;  // queries per calibration statistics tile
+#ifndef SAF_CALIB_WAVES
+#define SAF_CALIB_WAVES 4
+#endif
+constexpr int kCalibWaves = SAF_CALIB_WAVES;     // waves per calibration work item (32 queries each)
+constexpr int kCalibQTile = 32 * kCalibWaves;    // queries per calibration statistics tile
 constexpr int kCalibKTile = 64;   // keys per calibration statistics tile
 
 __host__ __device__ inline bool is_replaced(const uint64_t* rep, int h) { return (rep[h >> 6] >> (h & 63)) & 1ull; }
