@@ -6,9 +6,10 @@
 //   replaced head: O = P V, P(i,j) = exp(a[j] + r[i-j]) / Z(i) on j <= i         [Notes §二.3, Eq.(3)]
 // The fused kernel the pages describe runs ordinary heads as online-softmax tiles and rebuilds the
 // fixed heads' causal tiles in registers from the two preference vectors and Z before the product
-// with the current V ([Notes §二.4, Fig. 2]).  Here a work item is one (batch, head, 256-query
-// block); its 8 waves own 32 queries each and sweep the key tiles at or below the diagonal.  The
-// next key tile is loaded into registers while the current one is multiplied, then written to LDS.
+// with the current V ([Notes §二.4, Fig. 2]).  Here a work item is one (batch, head, query block);
+// its 8 (or, for small grids, 4 or 2) waves own 32 queries each and sweep the key tiles at or below
+// the diagonal.  The next key tile is loaded into registers while the current one is multiplied,
+// then written to LDS.
 // Each kind of item runs its own copy of the tile loop (no per-tile branching on the head kind).
 //
 //   ordinary: S^T = K Q^T on the matrix cores (lane = query, registers = keys); base-2 online
@@ -34,24 +35,23 @@
 namespace saf {
 namespace {
 
-#ifndef SAF_FWD_WAVES
-#define SAF_FWD_WAVES 8  // 8 waves share each staged key/value tile (fewer loads per query)
-#endif
-constexpr int kWaves = SAF_FWD_WAVES;
-constexpr int kBQ = 32 * kWaves;  // queries per work item (32 per wave)
-constexpr int kNT = 64 * kWaves;  // threads per block
+// A work item is W waves x 32 queries.  Wide items (W = 8) share each staged key/value tile among
+// more queries; narrow ones (W = 4, 2) make more items, so that a small grid (batch 1) still fills
+// the chip and its heaviest item, which bounds the launch, is shorter.  The launcher picks W.
 
 enum Kind { kOrdinary = 0, kProduct = 1, kExponential = 2 };
 
-template <typename TI, int D>
+template <typename TI, int D, int W>
 struct FwdCfg {
+  static constexpr int BQ = 32 * W;                      // queries per work item
+  static constexpr int NT = 64 * W;                      // threads per block
   static constexpr bool BF = sizeof(TI) == 2;
   static constexpr int BK = BF ? SAF_FWD_BK : 32;        // keys per staged tile
   static constexpr int NS = BK / 32;                     // 32-key subtiles per tile
   static constexpr int LDP = D + 16 / (int)sizeof(TI);   // padded LDS row (elements)
   static constexpr int LDT = BK + 16 / (int)sizeof(TI);  // padded row of the transposed V tile
-  static constexpr int WIN = BK + kBQ;                   // distance window
-  static constexpr int WPT = (WIN + kNT - 1) / kNT;      // window values per thread
+  static constexpr int WIN = BK + BQ;                    // distance window
+  static constexpr int WPT = (WIN + NT - 1) / NT;        // window values per thread
 };
 
 template <typename TI>
@@ -68,11 +68,11 @@ struct FwdItem {
   size_t kvoff;  // its key/value head's slice (K, V)
 };
 
-template <typename TI, int D, int KIND>
+template <typename TI, int D, int KIND, int W>
 __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& sm,
                                          const FwdItem& it) {
-  using C = FwdCfg<TI, D>;
-  constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP;
+  using C = FwdCfg<TI, D, W>;
+  constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP, kBQ = C::BQ, kNT = C::NT;
   constexpr int LDT = C::LDT, WIN = C::WIN, WPT = C::WPT;
   constexpr bool ORD = KIND == kOrdinary, FACT = KIND == kProduct;
   const int T = it.T, h = it.h, q0 = it.q0;
@@ -235,10 +235,10 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   if (hi == 0) p.lse[((size_t)it.b * it.H + h) * T + qi] = lse;
 }
 
-template <typename TI, int D>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? SAF_FWD_W64 : 2)))
+template <typename TI, int D, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? SAF_FWD_W64 : 2)))
 void mixed_fwd_kernel(LayerArgs p) {
-  using C = FwdCfg<TI, D>;
+  using C = FwdCfg<TI, D, W>;
   __shared__ __attribute__((aligned(16))) TI Ks[C::BK * C::LDP];
   __shared__ __attribute__((aligned(16))) TI VT[D * C::LDT];
   __shared__ __attribute__((aligned(16))) float awin[C::BK];
@@ -247,7 +247,7 @@ void mixed_fwd_kernel(LayerArgs p) {
   const int T = p.T, H = p.H;
   const int BH = p.B * H;
   const int BHp = (BH + 7) & ~7;  // pad so that blockIdx % 8 (the XCD) depends on (b, h) only
-  const int nqb = (T + kBQ - 1) / kBQ;
+  const int nqb = (T + C::BQ - 1) / C::BQ;
   const int x = blockIdx.x;
   const int bh = x % BHp;
   if (bh >= BH) return;
@@ -256,27 +256,49 @@ void mixed_fwd_kernel(LayerArgs p) {
   it.H = H;
   it.b = bh / H;
   it.h = bh % H;
-  it.q0 = (nqb - 1 - x / BHp) * kBQ;  // heaviest query blocks first
+  it.q0 = (nqb - 1 - x / BHp) * C::BQ;  // heaviest query blocks first
   it.hoff = ((size_t)it.b * H + it.h) * (size_t)T * D;
   it.kvoff = ((size_t)it.b * p.Hkv + it.h / (H / p.Hkv)) * (size_t)T * D;
   const FwdSmem<TI> sm{Ks, VT, awin, rwin};
   if (!is_replaced(p.rep, it.h))
-    fwd_item<TI, D, kOrdinary>(p, sm, it);
+    fwd_item<TI, D, kOrdinary, W>(p, sm, it);
   else if (p.pat.flag(it.h)[0] != 0)
-    fwd_item<TI, D, kProduct>(p, sm, it);
+    fwd_item<TI, D, kProduct, W>(p, sm, it);
   else
-    fwd_item<TI, D, kExponential>(p, sm, it);
+    fwd_item<TI, D, kExponential, W>(p, sm, it);
+}
+
+template <typename TI, int D, int W>
+hipError_t launch_fwd_w(const LayerArgs& a, hipStream_t s) {
+  const int BHp = (a.B * a.H + 7) & ~7;
+  const int nqb = (a.T + 32 * W - 1) / (32 * W);
+  const long long blocks = (long long)BHp * nqb;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mixed_fwd_kernel<TI, D, W>), dim3((unsigned)blocks), dim3(64 * W), 0, s, a);
+  return hipGetLastError();
+}
+
+// The widest work item whose grid still gives every compute unit (256 of them) one item: wider items
+// share each staged key/value tile among more queries, but a grid smaller than the chip leaves units
+// idle, so small batches are cut finer.
+#ifndef SAF_FWD_FORCE_W
+#define SAF_FWD_FORCE_W 0
+#endif
+int fwd_waves(const LayerArgs& a) {
+  if (SAF_FWD_FORCE_W) return SAF_FWD_FORCE_W;
+  const long long bh = (long long)a.B * a.H;
+  for (int W = 8; W > 2; W /= 2)
+    if (bh * ((a.T + 32 * W - 1) / (32 * W)) >= 256) return W;
+  return 2;
 }
 
 template <typename TI, int D>
 hipError_t launch_fwd_t(const LayerArgs& a, hipStream_t s) {
-  const int BH = a.B * a.H;
-  const int BHp = (BH + 7) & ~7;
-  const int nqb = (a.T + kBQ - 1) / kBQ;
-  const long long blocks = (long long)BHp * nqb;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((mixed_fwd_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
-  return hipGetLastError();
+  switch (fwd_waves(a)) {
+    case 8: return launch_fwd_w<TI, D, 8>(a, s);
+    case 4: return launch_fwd_w<TI, D, 4>(a, s);
+    default: return launch_fwd_w<TI, D, 2>(a, s);
+  }
 }
 
 }  // namespace

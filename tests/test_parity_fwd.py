@@ -42,7 +42,42 @@ def test_forward_small_full_compare(B, H, T, d, dtype, R, placement, std):
     check_fwd(x, o, lse, heads, None, TOL[dtype], "small")
 
 
-FULL = ["l124m_t4096", "l124m_t8192", "l1b_t8192", "prefill_b64_t4096", "prefill_b2_t16384"]
+# The forward cuts a (batch, head) into work items of 8, 4 or 2 waves (256, 128 or 64 queries): the
+# widest whose grid still has 256 items.  The shapes below reach each width with a ragged last block.
+def _waves(B, H, T):
+    for w in (8, 4):
+        if B * H * -(-T // (32 * w)) >= 256:
+            return w
+    return 2
+
+
+WIDTHS = [
+    # B, H, T, d, dtype, n_replaced
+    (8, 8, 1000, 64, torch.bfloat16, 2),
+    (8, 8, 1000, 128, torch.float32, 2),
+    (2, 4, 4000, 64, torch.bfloat16, 1),
+    (2, 4, 4000, 128, torch.float32, 2),
+    (1, 4, 2000, 64, torch.bfloat16, 1),
+]
+
+
+@pytest.mark.parametrize("B,H,T,d,dtype,R", WIDTHS,
+                         ids=["W%d-B%dH%dT%dd%d-%s" % (_waves(c[0], c[1], c[2]), c[0], c[1], c[2], c[3], str(c[4])[6:]) for c in WIDTHS])
+def test_forward_each_work_item_width(B, H, T, d, dtype, R):
+    saf = _saf()
+    rep = synth.replaced_mask(H, R, "interleaved")
+    x = synth.layer_inputs(B, H, T, d, dtype, rep, ar_std=0.5, seed=T + d, backward=False)
+    g = synth.layer_inputs(B, H, T, d, dtype, rep, ar_std=0.5, seed=T + d, backward=False,
+                           device="cuda")
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    torch.cuda.synchronize()
+    rows = sample_rows(T, 48, seed=d)
+    heads = pick_heads(B, rep, n_each=2)
+    check_fwd(x, o, lse, heads, rows, TOL[dtype], "W%d" % _waves(B, H, T))
+
+
+FULL = ["l124m_t4096", "l124m_t8192", "l1b_t8192", "prefill_b64_t4096", "prefill_b2_t16384",
+        "prefill_b1_t4096"]
 
 
 @pytest.mark.parametrize("name", FULL)
