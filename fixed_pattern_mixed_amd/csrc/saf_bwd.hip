@@ -156,29 +156,21 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
     const bool fold = fact && GS > 1;  // the key factor enters each entry
     if (fact && GS == 1) vs = akey;
 
+    // The prefetch registers hold raw values (loads from clamped, always valid addresses): any
+    // arithmetic on a loaded value, or a select between it and a constant, would make the wave wait
+    // for the load there and then.  Masks and conversions are applied when the tile is stored.
     KvPrefetch<TI, D> pf;
     auto load_tile = [&](int q0) {
       pf.g.load(G, q0, T, tid);
       if (!rep) pf.q.load(Q, q0, T, tid);
       if (tid < BQ) {
-        const int q = q0 + tid;
-        // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
-        // Rows past the end get weight 0 (their dO rows are zero; an unbounded weight times a zero
-        // row would not be zero).
-        if (q < T) {
-          const float l = lse[q];
-          pf.rs = fact ? expf(shift - l) : l * kLog2e;
-        } else {
-          pf.rs = fact ? 0.f : INFINITY;
-        }
-        pf.dl = (!rep && q < T) ? dlt[q] : 0.f;
+        const int q = min(q0 + tid, T - 1);
+        pf.rs = lse[q];
+        pf.dl = dlt[q];  // (unused for a replaced head)
       }
-      if (rep && tid < WIN) {
-        const int dist = q0 - (kb0 + BKV - 1) + tid;
-        pf.rw = (dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
-      }
+      if (rep && tid < WIN) pf.rw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int q0) {
       pf.g.template store_cols<LDT>(GT, tid);
       if (!rep) {
         pf.g.template store_rows<LDP>(Gs, tid);
@@ -186,10 +178,17 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         pf.q.template store_cols<LDT>(QT, tid);
       }
       if (tid < BQ) {
-        rss[tid] = pf.rs;
-        dls[tid] = pf.dl;
+        // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
+        // Rows past the end get weight 0 (their dO rows are zero; an unbounded weight times a zero
+        // row would not be zero).
+        const bool in = q0 + tid < T;
+        rss[tid] = in ? (fact ? expf(shift - pf.rs) : pf.rs * kLog2e) : (fact ? 0.f : INFINITY);
+        dls[tid] = (!rep && in) ? pf.dl : 0.f;
       }
-      if (rep && tid < WIN) rwin[tid] = pf.rw;
+      if (rep && tid < WIN) {
+        const int dist = q0 - (kb0 + BKV - 1) + tid;
+        rwin[tid] = (dist >= 0 && dist < T) ? pf.rw * wscale : wfill;
+      }
     };
 
     if (qt0 < nqt) load_tile(qt0 * BQ);
@@ -197,7 +196,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
     for (int qt = qt0; qt < nqt; ++qt) {
       const int q0 = qt * BQ;
       __syncthreads();  // the previous tile's readers are done
-      store_tile();
+      store_tile(q0);
       __syncthreads();
       if (qt + 1 < nqt) load_tile(q0 + BQ);
 

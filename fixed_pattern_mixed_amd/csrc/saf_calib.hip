@@ -163,11 +163,13 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
     const size_t hoff = ((size_t)n * H + h) * (size_t)T * D;
     kreg.load(reinterpret_cast<const TI*>(p.k) + hoff, k0, T, tid);
     if (wave_sees) {
+      // rows past the end read row T-1 (always valid; a select with a constant would wait for the
+      // load): their entries are masked out
+      const int qc = min(qi, T - 1);
       const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t)
-        qn[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
-      lse_n = qi < T ? p.lse2[((size_t)n * H + h) * T + qi] : 0.f;
+      for (int t = 0; t < D / 16; ++t) qn[t] = load8(Q + (size_t)qc * D + 16 * t + 8 * hi);
+      lse_n = p.lse2[((size_t)n * H + h) * T + qc];
     }
   };
   prefetch(0);

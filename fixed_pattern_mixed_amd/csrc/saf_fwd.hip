@@ -95,30 +95,32 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   Chunks<TI, D, BK, kNT> kreg;
   Blocks4<TI, D, BK, kNT> vreg;
   float awr = 0.f, rwr[WPT];
+  // Window values are loaded raw from clamped (always valid) addresses and masked / scaled when
+  // stored: arithmetic on a value right after its load would make the wave wait for it there.
   auto load_tile = [&](int k0) {
     vreg.load(V, k0, T, tid);
     if (ORD) {
       kreg.load(K, k0, T, tid);
     } else {
       const int d0 = q0 - k0 - (BK - 1);
-      if (tid < BK) awr = (k0 + tid < T) ? arow[k0 + tid] * wscale : wfill;
+      if (tid < BK) awr = arow[min(k0 + tid, T - 1)];
 #pragma unroll
-      for (int j = 0; j < WPT; ++j) {
-        const int x = tid + j * kNT;
-        const int dist = d0 + x;
-        rwr[j] = (x < WIN && dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
-      }
+      for (int j = 0; j < WPT; ++j) rwr[j] = rrow[min(max(d0 + tid + j * kNT, 0), T - 1)];
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int k0) {
     vreg.template store_cols<LDT>(sm.VT, tid);
     if (ORD) {
       kreg.template store<LDP>(sm.Ks, tid);
     } else {
-      if (tid < BK) sm.awin[tid] = awr;
+      const int d0 = q0 - k0 - (BK - 1);
+      if (tid < BK) sm.awin[tid] = (k0 + tid < T) ? awr * wscale : wfill;
 #pragma unroll
-      for (int j = 0; j < WPT; ++j)
-        if (tid + j * kNT < WIN) sm.rwin[tid + j * kNT] = rwr[j];
+      for (int j = 0; j < WPT; ++j) {
+        const int x = tid + j * kNT;
+        const int dist = d0 + x;
+        if (x < WIN) sm.rwin[x] = (dist >= 0 && dist < T) ? rwr[j] * wscale : wfill;
+      }
     }
   };
 
@@ -138,7 +140,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   const float c2 = p.scale_log2;
 
   load_tile(0);
-  store_tile();
+  store_tile(0);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -211,7 +213,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
 
     __syncthreads();
     if (kt + 1 < nkt) {
-      store_tile();
+      store_tile(k0 + BK);
       __syncthreads();
     }
   }

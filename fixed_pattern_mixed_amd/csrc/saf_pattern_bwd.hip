@@ -102,31 +102,28 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
 
   Chunks<TI, D, BQ, kNT> gch;
   PgPrefetch pf;
+  // Raw loads from clamped (always valid) addresses; masks and conversions are applied when the
+  // tile is stored (arithmetic on a value right after its load would make the wave wait for it).
   auto load_tile = [&](int q0) {
     gch.load(G, q0, T, tid);
     if (tid < BQ) {
-      const int q = q0 + tid;
-      if (q < T) {
-        const float l = lse[q];
-        pf.rs = fact ? expf(shift - l) : l * kLog2e;
-        pf.dl = dlt[q];
-      } else {
-        pf.rs = fact ? 0.f : INFINITY;  // rows past the end get weight 0
-        pf.dl = 0.f;
-      }
+      const int q = min(q0 + tid, T - 1);
+      pf.rs = lse[q];
+      pf.dl = dlt[q];
+    }
+    if (tid < WIN) pf.rw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
+  };
+  auto store_tile = [&](int q0) {
+    gch.template store<LDP>(Gs, tid);
+    if (tid < BQ) {
+      const bool in = q0 + tid < T;  // rows past the end get weight 0
+      rss[tid] = in ? (fact ? expf(shift - pf.rs) : pf.rs * kLog2e) : (fact ? 0.f : INFINITY);
+      dls[tid] = in ? pf.dl : 0.f;
     }
     if (tid < WIN) {
       const int dist = q0 - (kb0 + BKV - 1) + tid;
-      pf.rw = (dist >= 0 && dist < T) ? rrow[dist] * wscale : wfill;
+      rwin[tid] = (dist >= 0 && dist < T) ? pf.rw * wscale : wfill;
     }
-  };
-  auto store_tile = [&]() {
-    gch.template store<LDP>(Gs, tid);
-    if (tid < BQ) {
-      rss[tid] = pf.rs;
-      dls[tid] = pf.dl;
-    }
-    if (tid < WIN) rwin[tid] = pf.rw;
   };
 
   const int nqt = (T + BQ - 1) / BQ;
@@ -136,7 +133,7 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
   for (int qt = qt0; qt < nqt; ++qt) {
     const int q0 = qt * BQ;
     __syncthreads();  // the previous tile's readers are done
-    store_tile();
+    store_tile(q0);
     __syncthreads();
     if (qt + 1 < nqt) load_tile(q0 + BQ);
 
