@@ -29,10 +29,16 @@ constexpr int kNT = 64 * kCalibWaves;
 constexpr int kBQ = kCalibQTile;  // 32 queries per wave
 constexpr int kBK = kCalibKTile;  // 64
 
-template <typename TI, int D>
-__global__ __launch_bounds__(kNT) void calib_lse_kernel(CalibArgs p) {
+// calib_lse: a work item is W waves x 32 queries sharing each staged key tile (wider items re-read
+// K less often).
+#ifndef SAF_LSE_WAVES
+#define SAF_LSE_WAVES 8
+#endif
+template <typename TI, int D, int W>
+__global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
   constexpr int NS = kBK / 32;
   constexpr int LDP = D + 16 / (int)sizeof(TI);
+  constexpr int kNT = 64 * W, kBQ = 32 * W;
   __shared__ __attribute__((aligned(16))) TI Ks[kBK * LDP];
 
   const int T = p.T;
@@ -295,10 +301,11 @@ __global__ __launch_bounds__(kNT) void calib_reduce_kernel(CalibArgs p) {
 
 template <typename TI, int D>
 hipError_t launch_lse_t(const CalibArgs& a, hipStream_t s) {
+  constexpr int W = SAF_LSE_WAVES;
   const int NHp = (a.N * a.H + 7) & ~7;
-  const long long blocks = (long long)NHp * ((a.T + kBQ - 1) / kBQ);
+  const long long blocks = (long long)NHp * ((a.T + 32 * W - 1) / (32 * W));
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((calib_lse_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL((calib_lse_kernel<TI, D, W>), dim3((unsigned)blocks), dim3(64 * W), 0, s, a);
   return hipGetLastError();
 }
 

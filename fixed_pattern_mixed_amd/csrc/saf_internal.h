@@ -153,7 +153,10 @@ hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s);
 #endif
 constexpr int kCalibWaves = SAF_CALIB_WAVES;     // waves per calibration work item (32 queries each)
 constexpr int kCalibQTile = 32 * kCalibWaves;    // queries per calibration statistics tile
-constexpr int kCalibKTile = 64;   // keys per calibration statistics tile
+#ifndef SAF_CALIB_KTILE
+#define SAF_CALIB_KTILE 64
+#endif
+constexpr int kCalibKTile = SAF_CALIB_KTILE;  // keys per calibration statistics tile
 
 __host__ __device__ inline bool is_replaced(const uint64_t* rep, int h) { return (rep[h >> 6] >> (h & 63)) & 1ull; }
 
