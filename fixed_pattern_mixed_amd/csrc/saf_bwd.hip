@@ -92,7 +92,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   __shared__ __attribute__((aligned(16))) TI QT[D * LDT];    // Q tile transposed [dim][query]
   __shared__ __attribute__((aligned(16))) TI GT[D * LDT];    // dO tile transposed [dcol][query]
   __shared__ __attribute__((aligned(16))) float rss[BQ];     // row statistic per query
-  __shared__ __attribute__((aligned(16))) float dls[BQ];     // delta per query
+  __shared__ __attribute__((aligned(16))) float dls[BQ];     // -delta per query
   __shared__ float rwin[WIN];                                // replaced: er / r*log2e window
 
   const int T = p.T, H = p.H, Hkv = p.Hkv;
@@ -183,7 +183,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         // row would not be zero).
         const bool in = q0 + tid < T;
         rss[tid] = in ? (fact ? expf(shift - pf.rs) : pf.rs * kLog2e) : (fact ? 0.f : INFINITY);
-        dls[tid] = (!rep && in) ? pf.dl : 0.f;
+        dls[tid] = (!rep && in) ? -pf.dl : 0.f;  // -delta: the initial value of the dP product
       }
       if (rep && tid < WIN) {
         const int dist = q0 - (kb0 + BKV - 1) + tid;
@@ -204,21 +204,32 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
       // straight-line code without masks, ordered so that subtile 1's score product is in flight
       // during subtile 0's exponentials (and, at d = 128, its dP product during subtile 0's dV /
       // dK products).
+      // The dP product of a subtile starts from -delta of its queries (read from LDS into the
+      // accumulator), so that it yields dP - delta and dS = P o (dP - delta) is one multiply.
+      auto neg_delta = [&](int s) {
+        f32x16 c;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 d4 = *reinterpret_cast<const float4*>(dls + 32 * s + 8 * g + 4 * hi);
+          c[4 * g] = d4.x;
+          c[4 * g + 1] = d4.y;
+          c[4 * g + 2] = d4.z;
+          c[4 * g + 3] = d4.w;
+        }
+        return c;
+      };
       if (NS == 2 && !rep && q0 >= kw + 31 && q0 + BQ <= T && kw + 31 < T) {
         auto grad_entries = [&](const f32x16& st, const f32x16& dpt, int s, float* pr, float* ds) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int qr = 32 * s + 8 * g + 4 * hi;
-            const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-            const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
+            const float4 l4 = *reinterpret_cast<const float4*>(rss + 32 * s + 8 * g + 4 * hi);
             const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
               const float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
               pr[r] = pp;
-              ds[r] = pp * (dpt[r] - dv[e]);
+              ds[r] = pp * dpt[r];
             }
           }
         };
@@ -234,11 +245,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
             }
           }
         };
-        f32x16 st0, dp0, st1, dp1;
+        f32x16 st0, dp0 = neg_delta(0), st1, dp1 = neg_delta(1);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
           mma16(st0, load8(Qs + l32 * LDP + 16 * t + 8 * hi), kf[t], t == 0);
-          mma16(dp0, load8(Gs + l32 * LDP + 16 * t + 8 * hi), vf[t], t == 0);
+          mma16(dp0, load8(Gs + l32 * LDP + 16 * t + 8 * hi), vf[t]);
         }
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
@@ -251,11 +262,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
           grad_products(0, pr, ds);
 #pragma unroll
           for (int t = 0; t < D / 16; ++t)
-            mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
+            mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t]);
         } else {
 #pragma unroll
           for (int t = 0; t < D / 16; ++t)
-            mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
+            mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t]);
           grad_products(0, pr, ds);
         }
         grad_entries(st1, dp1, 1, pr, ds);
@@ -270,19 +281,17 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
         float pr[16], ds[16];
         if (!rep) {
-          f32x16 st, dpt;
+          f32x16 st, dpt = neg_delta(s);
 #pragma unroll
           for (int t = 0; t < D / 16; ++t) {
             mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
-            mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
+            mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
           }
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
             const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-            const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
             const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
@@ -292,7 +301,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
                 pp = (q >= kj && q < T && kj < T) ? pp : 0.f;
               }
               pr[r] = pp;
-              ds[r] = pp * (dpt[r] - dv[e]);
+              ds[r] = pp * dpt[r];
             }
           }
         } else {

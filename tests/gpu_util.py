@@ -91,7 +91,10 @@ def check_bwd(x, dq, dk, dv, heads, qrows, krows, tol, what=""):
             assert np.all(gq == 0.0) and np.all(gk == 0.0), "%s replaced dq/dk must be 0" % what
         else:
             for name, g, r in (("dq", gq, rq), ("dk", gk, rk)):
-                e = norm_err(g, r)
+                # At T = 1 an ordinary head's dq and dk vanish by cancellation (P = 1, so
+                # dS = dP - delta = 0 exactly); the GPU's dP - delta is a rounding residue, and a
+                # reference of exact zeros has no relative scale: compare on the inputs' unit scale.
+                e = norm_err(g, r, floor=1.0 if np.abs(r).max() == 0.0 else 0.0)
                 assert e <= tol, "%s %s[b=%d,h=%d] normwise error %.3e > %.1e" % (what, name, b, h, e, tol)
                 worst = max(worst, e)
         e = norm_err(gv, rv)
