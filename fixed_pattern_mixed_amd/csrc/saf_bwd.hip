@@ -419,6 +419,14 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   const float lse2 = qi < T ? p.lse[soff + qi] * kLog2e : 0.f;
   const float dl = qi < T ? p.delta[soff + qi] : 0.f;
   const float c2 = p.scale_log2;
+  // d = 64: every dP^T product of the sweep starts from -delta of the lane's query (kept in
+  // registers for the whole item), so that it yields dP - delta and dS = P o (dP - delta) is one
+  // multiply.  (At d = 128 the 16 registers do not fit the budget: there dP starts from zero.)
+  constexpr bool kNegd = D == 64;
+  const float dsub = kNegd ? 0.f : dl;
+  f32x16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = kNegd ? -dl : 0.f;
 
   f32x16 dqT[D / 32];
 #pragma unroll
@@ -450,16 +458,16 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
     if (D == 64 && NS == 2 && k0 + BK - 1 <= qw && k0 + BK <= T && qw + 31 < T) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        f32x16 st, dpt;
+        f32x16 st, dpt = negd;
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
           mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
-          mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], t == 0);
+          mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], !kNegd && t == 0);
         }
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          ds[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2)) * (dpt[r] - dl);
+          ds[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2)) * (dpt[r] - dsub);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const Frag<TI> sf = to_frag<TI>(&ds[8 * u]);
@@ -474,11 +482,11 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
       if (ks > qw + 31 || ks >= T) break;  // wave-uniform: the rest of the tile is masked out
-      f32x16 st, dpt;
+      f32x16 st, dpt = negd;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
-        mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], t == 0);
+        mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], !kNegd && t == 0);
       }
       const bool edge = (ks + 31 > qw) || (ks + 31 >= T);
       float ds[16];
@@ -489,7 +497,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
           const int key = ks + crow(r, hi);
           pp = (key <= qi && key < T) ? pp : 0.f;
         }
-        ds[r] = pp * (dpt[r] - dl);
+        ds[r] = pp * (dpt[r] - dsub);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
         tmax = fmaxf(tmax, v);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = half_max(tmax);
     const float mnew = fmaxf(m, tmax);
     // a row with no visible key yet keeps m = -inf: skip its exponentials (they would be exp2(nan))
     const bool live = mnew != -INFINITY;

@@ -156,6 +156,14 @@ __device__ __forceinline__ Frag<TI> col_frag(const TI* tile, int row0, int col0,
   return col_frag_impl<LDP>(tile, row0, col0, lane);
 }
 
+// max(x[lane], x[lane ^ 32]) with one cross-half lane swap (v_permlane32_swap: the two results of
+// swapping lanes 32..63 of one copy with lanes 0..31 of another hold, in every lane, x[lane] and
+// x[lane ^ 32]); no LDS round trip as with a shuffle.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Sum of a fragment's eight values (bf16: two-way dot products with 1, fp32 accumulation).
 __device__ __forceinline__ float frag_sum(const Frag<bf16>& f) {
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;

@@ -173,7 +173,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
             tmax = fmaxf(tmax, st[r]);
           }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c2;
+        tmax = half_max(tmax) * c2;
         // lazy maximum: keep the running one while the subtile stays within 2^8 of it
         const float mnew = (tmax > m + 8.f) ? tmax : m;
         if (__any(mnew != m)) {
