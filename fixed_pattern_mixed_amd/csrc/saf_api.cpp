@@ -89,6 +89,40 @@ saf_status fill_mask(const uint8_t* replaced, int H, uint64_t* rep, bool* any_re
   return SAF_OK;
 }
 
+// Slice order of the work items (LayerArgs::qord, kvord; SlotOrder describes why).  cost[h] is a
+// head's class key (larger = more expensive); heads are listed by descending key, ties in index
+// order.  More distinct keys than kMaxClasses collapse into one class (order kept).
+static void fill_slot_order(saf::SlotOrder& o, const int* cost, int n) {
+  int m = 0, ncls = 0;
+  int keys[saf::kMaxHeads + 1];
+  for (int h = 0; h < n; ++h) keys[h] = cost[h];
+  int prev = INT32_MAX;
+  o.cls[0] = 0;
+  while (m < n) {
+    int best = INT32_MIN;
+    for (int h = 0; h < n; ++h)
+      if (keys[h] < prev && keys[h] > best) best = keys[h];
+    for (int h = 0; h < n; ++h)
+      if (keys[h] == best) o.head[m++] = (uint8_t)h;
+    if (ncls < saf::kMaxClasses) ++ncls;
+    o.cls[ncls] = (int16_t)m;
+    prev = best;
+  }
+  o.ncls = ncls;
+}
+
+void fill_order(saf::LayerArgs& la, const uint8_t* replaced) {
+  int cost[saf::kMaxHeads];
+  for (int h = 0; h < la.H; ++h) cost[h] = replaced[h] ? 0 : 1;
+  fill_slot_order(la.qord, cost, la.H);
+  const int G = la.H / la.Hkv;
+  for (int hk = 0; hk < la.Hkv; ++hk) {
+    cost[hk] = 0;
+    for (int m = 0; m < G; ++m) cost[hk] += !replaced[hk * G + m];
+  }
+  fill_slot_order(la.kvord, cost, la.Hkv);
+}
+
 // ---- optional per-kernel event tracing (saf_trace_begin / saf_trace_end)
 struct Trace {
   saf_kernel_event* ev = nullptr;
@@ -382,6 +416,7 @@ static saf_status fwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
 
   la.B = B; la.H = H; la.T = T; la.d = d;
   la.Hkv = Hkv;
+  fill_order(la, replaced);
   la.pat_len = pat_len;
   la.scale = s;
   la.scale_log2 = s * 1.4426950408889634f;
@@ -432,6 +467,7 @@ static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
 
   la.B = B; la.H = H; la.T = T; la.d = d;
   la.Hkv = Hkv;
+  fill_order(la, replaced);
   la.pat_len = pat_len;
   la.scale = s;
   la.scale_log2 = s * 1.4426950408889634f;

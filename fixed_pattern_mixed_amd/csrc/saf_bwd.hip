@@ -103,7 +103,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   const int bh = x % BHp;
   if (bh >= BH) return;
   const int kb = x / BHp;  // low key blocks see the most query tiles: heaviest first
-  const int b = bh / Hkv, hk = bh % Hkv;
+  int b, hk;
+  p.kvord.slice(bh, p.B, b, hk);
   bool any_ord = false;
   for (int m = 0; m < GS; ++m) any_ord |= !is_replaced(p.rep, hk * GS + m);
 
@@ -394,7 +395,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   const int bh = x % BHp;
   if (bh >= BH) return;
   const int qb = nqb - 1 - x / BHp;  // heaviest query blocks first
-  const int b = bh / H, h = bh % H;
+  int b, h;
+  p.qord.slice(bh, p.B, b, h);
   if (is_replaced(p.rep, h)) return;  // replaced heads: zero dQ rows come from bwd_kv
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

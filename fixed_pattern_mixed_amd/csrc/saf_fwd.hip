@@ -248,7 +248,7 @@ void mixed_fwd_kernel(LayerArgs p) {
 
   const int T = p.T, H = p.H;
   const int BH = p.B * H;
-  const int BHp = (BH + 7) & ~7;  // pad so that blockIdx % 8 (the XCD) depends on (b, h) only
+  const int BHp = (BH + 7) & ~7;  // pad so that blockIdx % 8 (the XCD) depends on the slice only
   const int nqb = (T + C::BQ - 1) / C::BQ;
   const int x = blockIdx.x;
   const int bh = x % BHp;
@@ -256,8 +256,7 @@ void mixed_fwd_kernel(LayerArgs p) {
   FwdItem it;
   it.T = T;
   it.H = H;
-  it.b = bh / H;
-  it.h = bh % H;
+  p.qord.slice(bh, p.B, it.b, it.h);
   it.q0 = (nqb - 1 - x / BHp) * C::BQ;  // heaviest query blocks first
   it.hoff = ((size_t)it.b * H + it.h) * (size_t)T * D;
   it.kvoff = ((size_t)it.b * p.Hkv + it.h / (H / p.Hkv)) * (size_t)T * D;

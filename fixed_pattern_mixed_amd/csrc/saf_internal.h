@@ -33,6 +33,34 @@ struct PatternView {
 __host__ __device__ inline int pattern_stride(int P) { return ((3 * P + 64) + 63) / 64 * 64; }
 
 // Per-call description of the mixed layer, passed to kernels by value.
+// Order of the (batch, head) slices over a grid's slots.  blockIdx % 8 picks the XCD a workgroup is
+// dispatched to, and the grids take the slice slot from blockIdx modulo the (padded) slice count,
+// so slot j runs on XCD j % 8.  Heads are grouped in cost classes (most expensive first: ordinary
+// before replaced heads; key/value heads by the number of ordinary query heads in their group) and
+// a class's B x n slices fill consecutive slots batch-major, so every XCD gets its share of each
+// class.  With heads in their natural order a regular placement of replaced heads (every fourth
+// head, say) would put all of them on two XCDs, whose cheap items finish early while the others
+// still hold every ordinary one.
+constexpr int kMaxClasses = 16;
+struct SlotOrder {
+  uint8_t head[kMaxHeads];        // heads, class by class
+  int16_t cls[kMaxClasses + 1];   // class c holds head[cls[c] .. cls[c+1])
+  int ncls;
+  __host__ __device__ void slice(int j, int B, int& b, int& h) const {
+    for (int c = 0; c < ncls; ++c) {
+      const int n = cls[c + 1] - cls[c];
+      if (j < B * cls[c + 1]) {
+        const int k = j - B * cls[c];
+        b = k / n;
+        h = head[cls[c] + k % n];
+        return;
+      }
+    }
+    b = B;  // past the last slice (not reached for j < B x heads)
+    h = 0;
+  }
+};
+
 struct LayerArgs {
   int B, H, T, d;
   int Hkv;           // key/value heads: query head h reads K, V head h / (H / Hkv) (Hkv = H: MHA)
@@ -40,6 +68,8 @@ struct LayerArgs {
   float scale;       // softmax scale s of ordinary heads
   float scale_log2;  // s * log2(e): scores are exponentiated with exp2
   uint64_t rep[kMaxHeads / 64];  // bit h set = head h is replaced
+  // Work-item order of the (batch, head) slices, for query heads and for key/value heads.
+  SlotOrder qord, kvord;
   const void* q;
   const void* k;
   const void* v;
