@@ -363,9 +363,13 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
 }
 
 // ------------------------------------------------------------------------------------ bwd_dq
+#ifndef SAF_DQ_WAVES
+#define SAF_DQ_WAVES 4
+#endif
 template <typename TI, int D>
 struct DqCfg {
-  static constexpr int BQ = 128;                          // queries per work item (4 waves x 32)
+  static constexpr int NT = 64 * SAF_DQ_WAVES;            // threads per block
+  static constexpr int BQ = 32 * SAF_DQ_WAVES;            // queries per work item (32 per wave)
   static constexpr int BK = sizeof(TI) == 2 ? 64 : 32;    // keys per staged tile
   static constexpr int NS = BK / 32;
   static constexpr int LDP = D + 16 / (int)sizeof(TI);
@@ -374,12 +378,12 @@ struct DqCfg {
 
 template <typename TI, int D>
 struct DqPrefetch {
-  Blocks4<TI, D, DqCfg<TI, D>::BK, kNT> k;
-  Chunks<TI, D, DqCfg<TI, D>::BK, kNT> v;
+  Blocks4<TI, D, DqCfg<TI, D>::BK, DqCfg<TI, D>::NT> k;
+  Chunks<TI, D, DqCfg<TI, D>::BK, DqCfg<TI, D>::NT> v;
 };
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kNT)
+__global__ __launch_bounds__(64 * SAF_DQ_WAVES)
 __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel(LayerArgs p) {
   using C = DqCfg<TI, D>;
   constexpr int BQ = C::BQ, BK = C::BK, NS = C::NS, LDP = C::LDP, LDT = C::LDT;
@@ -549,7 +553,7 @@ hipError_t launch_dq_t(const LayerArgs& a, hipStream_t s) {
   const int BHp = (a.B * a.H + 7) & ~7;
   const long long blocks = (long long)BHp * ((a.T + DqCfg<TI, D>::BQ - 1) / DqCfg<TI, D>::BQ);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_dq_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<TI, D>), dim3((unsigned)blocks), dim3(DqCfg<TI, D>::NT), 0, s, a);
   return hipGetLastError();
 }
 
