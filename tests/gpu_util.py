@@ -58,11 +58,13 @@ def check_fwd(x, o, lse, heads, rows, tol, what=""):
     """Compare o / lse of the listed (b, h) slices and rows with the oracle."""
     worst = 0.0
     rows = np.arange(x.v.shape[2], dtype=np.int32) if rows is None else rows
+    G = len(x.replaced) // x.v.shape[1]  # query heads per key/value head (1 unless grouped)
     for b, h in heads:
+        hk = h // G
         if x.replaced[h]:
-            ro, rl = oracle.head_fwd(1, x.v[b, h], a=x.a[h], r=x.r[h], rows=rows)
+            ro, rl = oracle.head_fwd(1, x.v[b, hk], a=x.a[h], r=x.r[h], rows=rows)
         else:
-            ro, rl = oracle.head_fwd(0, x.v[b, h], q=x.q[b, h], k=x.k[b, h], rows=rows)
+            ro, rl = oracle.head_fwd(0, x.v[b, hk], q=x.q[b, h], k=x.k[b, hk], rows=rows)
         idx = torch.as_tensor(rows, dtype=torch.long, device=o.device)
         e = norm_err(cpu64(o[b, h].index_select(0, idx)), ro)
         el = norm_err(cpu64(lse[b, h].index_select(0, idx)), rl, floor=1.0)
