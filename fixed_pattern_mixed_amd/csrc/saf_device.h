@@ -111,51 +111,6 @@ __device__ __forceinline__ Frag<float> to_frag<float>(const float* x) {
   return f;
 }
 
-// Column gather from a row-major LDS tile: slot e takes row (row0 + perm_row(e, hi)), column col.
-template <typename TI, int LDP>
-__device__ __forceinline__ Frag<TI> gather_col(const TI* tile, int row0, int col, int hi) {
-  Frag<TI> f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = tile[(row0 + perm_row(e, hi)) * LDP + col];
-  return f;
-}
-
-// Column fragment of a row-major LDS tile (row stride LDP elements): slot e holds
-// tile[row0 + perm_row(e, lane/32)][col0 + lane%32], i.e. the k16-step operand of a product that
-// contracts over the tile's rows.
-//   bf16: two transposing LDS reads (ds_read_b64_tr_b16).  Within each 16-lane group the hardware
-//         gathers the 64-bit row segments the 16 lanes address (lane j: row j/4, columns 4*(j%4)..)
-//         into columns: lane i receives rows 0..3 of column i.  One read covers slots 0..3 (rows
-//         row0 + 4*hi + 0..3), the second slots 4..7 (rows row0 + 8 + 4*hi + 0..3).
-//   fp32: eight scalar LDS reads.
-typedef short v4i16 __attribute__((__vector_size__(8)));
-typedef short v8i16 __attribute__((__vector_size__(16)));
-
-template <int LDP>
-__device__ __forceinline__ Frag<bf16> col_frag_impl(const bf16* tile, int row0, int col0, int lane) {
-  const int j = lane & 15, g = (lane >> 4) & 1, hi = lane >> 5;
-  const bf16* p0 = tile + (row0 + 4 * hi + (j >> 2)) * LDP + col0 + 16 * g + 4 * (j & 3);
-  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
-  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 8 * LDP));
-  const v8i16 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  Frag<bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, c);
-  return f;
-}
-template <int LDP>
-__device__ __forceinline__ Frag<float> col_frag_impl(const float* tile, int row0, int col0, int lane) {
-  const int hi = lane >> 5, col = col0 + (lane & 31);
-  Frag<float> f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = tile[(row0 + perm_row(e, hi)) * LDP + col];
-  return f;
-}
-template <typename TI, int LDP>
-__device__ __forceinline__ Frag<TI> col_frag(const TI* tile, int row0, int col0, int lane) {
-  return col_frag_impl<LDP>(tile, row0, col0, lane);
-}
-
 // max(x[lane], x[lane ^ 32]) with one cross-half lane swap (v_permlane32_swap: the two results of
 // swapping lanes 32..63 of one copy with lanes 0..31 of another hold, in every lane, x[lane] and
 // x[lane ^ 32]); no LDS round trip as with a shuffle.
@@ -355,23 +310,6 @@ struct Chunks {
   }
 };
 
-// Copy rows [row0, row0+ROWS) of a [T][D] global matrix into a padded LDS tile (row stride LDP
-// elements); rows >= T are filled with zeros.  All NT threads of the block take part.
-template <typename TI, int D, int ROWS, int LDP, int NT>
-__device__ __forceinline__ void stage_rows(TI* lds, const TI* g, int row0, int T, int tid) {
-  constexpr int EPC = 16 / sizeof(TI);  // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;          // chunks per row
-  static_assert((LDP * sizeof(TI)) % 16 == 0, "LDS rows must stay 16-byte aligned");
-#pragma unroll
-  for (int c = tid; c < ROWS * CPR; c += NT) {
-    const int rr = c / CPR, cc = c % CPR;
-    const int row = row0 + rr;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (row < T) val = *reinterpret_cast<const uint4*>(g + (size_t)row * D + cc * EPC);
-    *reinterpret_cast<uint4*>(lds + rr * LDP + cc * EPC) = val;
-  }
-}
-
 // Store 4 consecutive fp32 values as the tensor's element type.
 __device__ __forceinline__ void store4(bf16* p, float x0, float x1, float x2, float x3) {
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -381,12 +319,6 @@ __device__ __forceinline__ void store4(bf16* p, float x0, float x1, float x2, fl
 }
 __device__ __forceinline__ void store4(float* p, float x0, float x1, float x2, float x3) {
   *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
 }
 
 }  // namespace saf
