@@ -142,11 +142,23 @@ __global__ __launch_bounds__(kNT) void fit_init_kernel(FitArgs p) {
 // values in registers, reusing half of them per step, so one broadcast read and four window reads
 // feed 16 (or 32) fp64 multiply-adds.  Partial sums per index block are added in a fixed order by
 // the next kernel.
-constexpr int kCB = 1024;
+#ifndef SAF_FIT_CB
+#define SAF_FIT_CB 1024
+#endif
+constexpr int kCB = SAF_FIT_CB;
+constexpr int kSNT = kCB / 4;  // threads of a step block: 4 positions each
+// The gradient kernel's windows are stored with one pad double after every 64 slots: its window
+// reads are 32 bytes apart per lane (4 positions per thread), which without padding puts lanes 8
+// apart on the same LDS banks.  Chosen by measurement over paddings of 1-4 doubles every 8-512
+// (fit of 16 maps at T = 8192: 133 ms unpadded, 87 ms with this one; the LDS bank-conflict counters
+// had shown that kernel waiting on LDS issue 70% of its cycles).  The Z' kernel, with one window,
+// is faster unpadded.
+__device__ __forceinline__ int wslot(int s) { return s + (s >> 6); }
+constexpr int kWin = 2 * kCB + 2 * kCB / 64;  // padded window of 2 kCB slots
 
 // Partial Z'(i) over k in index block kc: zpart[kc][i] = sum_{k in kc, k<=i} ea[k] er[i-k], for the
 // rows i of row block rb >= kc.
-__global__ __launch_bounds__(kNT) void fit_zpart_kernel(FitArgs p) {
+__global__ __launch_bounds__(kSNT) void fit_zpart_kernel(FitArgs p) {
   __shared__ __attribute__((aligned(16))) double eas[kCB];
   __shared__ __attribute__((aligned(16))) double ers[2 * kCB];
   const int nb = p.ncb;
@@ -157,8 +169,8 @@ __global__ __launch_bounds__(kNT) void fit_zpart_kernel(FitArgs p) {
   const double* ea = p.ea(h);
   const double* er = p.er(h);
   const int d0 = i0 - k0 - (kCB - 1);  // distance held in ers[0]
-  for (int y = tid; y < kCB; y += kNT) eas[y] = k0 + y < T ? ea[k0 + y] : 0.0;
-  for (int y = tid; y < 2 * kCB; y += kNT) {
+  for (int y = tid; y < kCB; y += kSNT) eas[y] = k0 + y < T ? ea[k0 + y] : 0.0;
+  for (int y = tid; y < 2 * kCB; y += kSNT) {
     const int d = d0 + y;
     ers[y] = (d >= 0 && d < T) ? er[d] : 0.0;  // negative distance: a future key, weight 0
   }
@@ -208,10 +220,10 @@ __global__ __launch_bounds__(kNT) void fit_w_kernel(FitArgs p) {
 
 // Partial correlation sums over i in index block ic for the positions x of block xb <= ic:
 // cs = sum er[i-x] w[i], ds = sum ea[i-x] w[i].
-__global__ __launch_bounds__(kNT) void fit_gpart_kernel(FitArgs p) {
+__global__ __launch_bounds__(kSNT) void fit_gpart_kernel(FitArgs p) {
   __shared__ __attribute__((aligned(16))) double ws[kCB];
-  __shared__ __attribute__((aligned(16))) double ers[2 * kCB];
-  __shared__ __attribute__((aligned(16))) double eas[2 * kCB];
+  __shared__ __attribute__((aligned(16))) double ers[kWin];
+  __shared__ __attribute__((aligned(16))) double eas[kWin];
   const int nb = p.ncb;
   const int xb = blockIdx.x / nb, ic = blockIdx.x % nb;
   if (ic < xb) return;
@@ -220,15 +232,15 @@ __global__ __launch_bounds__(kNT) void fit_gpart_kernel(FitArgs p) {
   const double* ea = p.ea(h);
   const double* er = p.er(h);
   const int o0 = i0 - x0 - (kCB - 1);  // offset i - x held in the windows' slot 0
-  for (int y = tid; y < kCB; y += kNT) {
+  for (int y = tid; y < kCB; y += kSNT) {
     const int i = i0 + y;
     ws[y] = i < T ? p.w(h)[i] : 0.0;
   }
-  for (int y = tid; y < 2 * kCB; y += kNT) {
+  for (int y = tid; y < 2 * kCB; y += kSNT) {
     const int o = o0 + y;
     const bool ok = o >= 0 && o < T;
-    ers[y] = ok ? er[o] : 0.0;
-    eas[y] = ok ? ea[o] : 0.0;
+    ers[wslot(y)] = ok ? er[o] : 0.0;
+    eas[wslot(y)] = ok ? ea[o] : 0.0;
   }
   __syncthreads();
   // position x0 + 4t + u and index i0 + ii + j read slot ii + j - 4t - u + kCB - 1 = base + 3 + j - u
@@ -238,8 +250,8 @@ __global__ __launch_bounds__(kNT) void fit_gpart_kernel(FitArgs p) {
   double Wr[8], Wa[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    Wr[q] = ers[base + q];
-    Wa[q] = eas[base + q];
+    Wr[q] = ers[wslot(base + q)];
+    Wa[q] = eas[wslot(base + q)];
   }
   for (int ii = 0; ii < kCB; ii += 4) {
     const double w4[4] = {ws[ii], ws[ii + 1], ws[ii + 2], ws[ii + 3]};
@@ -259,8 +271,8 @@ __global__ __launch_bounds__(kNT) void fit_gpart_kernel(FitArgs p) {
       }
 #pragma unroll
       for (int q = 4; q < 8; ++q) {
-        Wr[q] = ers[base + q];
-        Wa[q] = eas[base + q];
+        Wr[q] = ers[wslot(base + q)];
+        Wa[q] = eas[wslot(base + q)];
       }
     }
   }
@@ -385,7 +397,7 @@ hipError_t launch_fit_init(const FitArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fit_z(const FitArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(fit_zpart_kernel, dim3(a.ncb * a.ncb, a.H), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(fit_zpart_kernel, dim3(a.ncb * a.ncb, a.H), dim3(kSNT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -393,7 +405,7 @@ hipError_t launch_fit_step(const FitArgs& a, double lr, double c1, double c2, hi
   hipLaunchKernelGGL(fit_w_kernel, dim3((a.T + kNT - 1) / kNT, a.H), dim3(kNT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fit_gpart_kernel, dim3(a.ncb * a.ncb, a.H), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(fit_gpart_kernel, dim3(a.ncb * a.ncb, a.H), dim3(kSNT), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nblk = fit_adam_blocks(a.T);
