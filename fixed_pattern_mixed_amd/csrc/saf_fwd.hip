@@ -136,8 +136,27 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) zero(oacc[c]);
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // running maximum of the row (log2 units) and row sum
   const float c2 = p.scale_log2;
+
+  // probabilities 2^(s*log2(e)*x - mx) of a subtile's (masked) scores as operand fragments;
+  // returns the lane's sum of them as rounded for the product
+  auto probs_at = [&](const f32x16& x, float mx, Frag<TI> (&pf)[2]) {
+    float pv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(x[r], c2, -mx));
+    pf[0] = to_frag<TI>(&pv[0]);
+    pf[1] = to_frag<TI>(&pv[8]);
+    return frag_sum(pf[0]) + frag_sum(pf[1]);
+  };
+  // O^T += V^T P^T over subtile s
+  auto accumulate = [&](int s, const Frag<TI> (&pf)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        mma16(oacc[c], tt_frag<TI, LDT>(sm.VT, 32 * s + 16 * u, 32 * c + l32, hi), pf[u]);
+  };
 
   load_tile(0);
   store_tile(0);
@@ -152,42 +171,43 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
       if (ks > qw + 31 || ks >= T) break;  // wave-uniform: the rest of the tile is masked out
-      float pv[16];
       if (ORD) {
         f32x16 st;
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
           mma16(st, load8(sm.Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
-        float tmax = -INFINITY;
         if ((ks + 31 > qw) || (ks + 31 >= T)) {  // subtile crosses the diagonal or the end
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = ks + crow(r, hi);
-            pv[r] = (key <= qi && key < T) ? st[r] : -INFINITY;
-            tmax = fmaxf(tmax, pv[r]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            pv[r] = st[r];
-            tmax = fmaxf(tmax, st[r]);
+            st[r] = (key <= qi && key < T) ? st[r] : -INFINITY;
           }
         }
-        tmax = half_max(tmax) * c2;
-        // lazy maximum: keep the running one while the subtile stays within 2^8 of it
-        const float mnew = (tmax > m + 8.f) ? tmax : m;
-        if (__any(mnew != m)) {
-          const float alpha = exp2f(m - mnew);
+        // Lazy maximum: the probabilities are taken with the running maximum m and kept while
+        // none exceeds 2^8, which the lane's sum of them (at most 256 then) shows without a
+        // maximum over the subtile.  Otherwise (rare after the first subtile, and always on it,
+        // where m is still -inf and the sum inf or NaN) m moves to the row maximum, O and l are
+        // rescaled and the subtile is redone.
+        Frag<TI> pf[2];
+        float ls = probs_at(st, m, pf);
+        if (__any(!(ls <= 256.f))) {
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
+          const float mnew = fmaxf(m, half_max(tmax) * c2);
+          const float alpha = exp2f(m - mnew);  // 0 on the first subtile (m = -inf)
           l *= alpha;
 #pragma unroll
           for (int c = 0; c < D / 32; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
           m = mnew;
+          ls = probs_at(st, m, pf);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(pv[r], c2, -m));
+        l += ls;
+        accumulate(s, pf);
       } else {
+        float pv[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int kk = 32 * s + 8 * g + 4 * hi;    // tile-relative first key of the run
@@ -200,14 +220,9 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
             pv[4 * g + e] = FACT ? av[e] * rv : __builtin_amdgcn_exp2f(av[e] + rv - lz2_q);
           }
         }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const Frag<TI> pfr = to_frag<TI>(&pv[8 * u]);
-        l += frag_sum(pfr);
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-          mma16(oacc[c], tt_frag<TI, LDT>(sm.VT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
+        Frag<TI> pf[2] = {to_frag<TI>(&pv[0]), to_frag<TI>(&pv[8])};
+        l += frag_sum(pf[0]) + frag_sum(pf[1]);
+        accumulate(s, pf);
       }
     }
 
