@@ -252,8 +252,11 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   if (hi == 0) p.lse[((size_t)it.b * it.H + h) * T + qi] = lse;
 }
 
+// Narrow items (W < 8) are launched only for grids of at most a few blocks per compute unit, where
+// occupancy cannot be high anyway: they get 256 registers (their staging registers, 4x those of a
+// wide item, would spill at 128).
 template <typename TI, int D, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? SAF_FWD_W64 : 2)))
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 && W == 8 ? SAF_FWD_W64 : 2)))
 void mixed_fwd_kernel(LayerArgs p) {
   using C = FwdCfg<TI, D, W>;
   __shared__ __attribute__((aligned(16))) TI Ks[C::BK * C::LDP];
