@@ -118,13 +118,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   const TI* V = reinterpret_cast<const TI*>(p.v) + kvoff;
   const float c2 = p.scale_log2;
 
-  // K is held scaled by s*log2(e) (bf16: one more rounding of k, below that of the probabilities
-  // entering the products), and every score product starts from -lse (log2 units) of its queries,
-  // so that it yields the exponent of P with no arithmetic per entry.
   Frag<TI> kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    kf[t] = (any_ord && kj < T) ? scale_frag(load8(K + (size_t)kj * D + 16 * t + 8 * hi), c2) : zero_frag<TI>();
+    kf[t] = (any_ord && kj < T) ? load8(K + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
     vf[t] = (any_ord && kj < T) ? load8(V + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
   }
 
@@ -182,12 +179,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         pf.q.template store_cols<LDT>(QT, tid);
       }
       if (tid < BQ) {
-        // ordinary: -lse in log2 units (the initial value of the score product); exponential
-        // form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).  Rows past the end get
-        // weight 0 (their dO rows are zero; an unbounded weight times a zero row would not be zero).
+        // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
+        // Rows past the end get weight 0 (their dO rows are zero; an unbounded weight times a zero
+        // row would not be zero).
         const bool in = q0 + tid < T;
-        const float l2 = pf.rs * kLog2e;
-        rss[tid] = fact ? (in ? expf(shift - pf.rs) : 0.f) : rep ? (in ? l2 : INFINITY) : (in ? -l2 : -INFINITY);
+        rss[tid] = in ? (fact ? expf(shift - pf.rs) : pf.rs * kLog2e) : (fact ? 0.f : INFINITY);
         dls[tid] = (!rep && in) ? -pf.dl : 0.f;  // -delta: the initial value of the dP product
       }
       if (rep && tid < WIN) {
@@ -211,12 +207,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
       // dK products).
       // The dP product of a subtile starts from -delta of its queries (read from LDS into the
       // accumulator), so that it yields dP - delta and dS = P o (dP - delta) is one multiply.
-      // (The score product likewise starts from -lse.)
-      auto row_init = [&](const float* src, int s) {
+      auto neg_delta = [&](int s) {
         f32x16 c;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 d4 = *reinterpret_cast<const float4*>(src + 32 * s + 8 * g + 4 * hi);
+          const float4 d4 = *reinterpret_cast<const float4*>(dls + 32 * s + 8 * g + 4 * hi);
           c[4 * g] = d4.x;
           c[4 * g + 1] = d4.y;
           c[4 * g + 2] = d4.z;
@@ -224,15 +219,19 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         }
         return c;
       };
-      auto neg_delta = [&](int s) { return row_init(dls, s); };
-      auto neg_lse = [&](int s) { return row_init(rss, s); };
       if (NS == 2 && !rep && q0 >= kw + 31 && q0 + BQ <= T && kw + 31 < T) {
-        auto grad_entries = [&](const f32x16& st, const f32x16& dpt, float* pr, float* ds) {
+        auto grad_entries = [&](const f32x16& st, const f32x16& dpt, int s, float* pr, float* ds) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pp = __builtin_amdgcn_exp2f(st[r]);
-            pr[r] = pp;
-            ds[r] = pp * dpt[r];
+          for (int g = 0; g < 4; ++g) {
+            const float4 l4 = *reinterpret_cast<const float4*>(rss + 32 * s + 8 * g + 4 * hi);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              const float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
+              pr[r] = pp;
+              ds[r] = pp * dpt[r];
+            }
           }
         };
         auto grad_products = [&](int s, const float* pr, const float* ds) {
@@ -247,16 +246,17 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
             }
           }
         };
-        f32x16 st0 = neg_lse(0), dp0 = neg_delta(0), st1 = neg_lse(1), dp1 = neg_delta(1);
+        f32x16 st0, dp0 = neg_delta(0), st1, dp1 = neg_delta(1);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          mma16(st0, load8(Qs + l32 * LDP + 16 * t + 8 * hi), kf[t]);
+          mma16(st0, load8(Qs + l32 * LDP + 16 * t + 8 * hi), kf[t], t == 0);
           mma16(dp0, load8(Gs + l32 * LDP + 16 * t + 8 * hi), vf[t]);
         }
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) mma16(st1, load8(Qs + (32 + l32) * LDP + 16 * t + 8 * hi), kf[t]);
+        for (int t = 0; t < D / 16; ++t)
+          mma16(st1, load8(Qs + (32 + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
         float pr[16], ds[16];
-        grad_entries(st0, dp0, pr, ds);
+        grad_entries(st0, dp0, 0, pr, ds);
         if constexpr (D == 64) {
           // 256-register budget (two waves per SIMD): subtile 0's products first keeps the
           // live set smaller (measured faster at d = 64)
@@ -270,7 +270,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
             mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t]);
           grad_products(0, pr, ds);
         }
-        grad_entries(st1, dp1, pr, ds);
+        grad_entries(st1, dp1, 1, pr, ds);
         grad_products(1, pr, ds);
         continue;
       }
@@ -282,21 +282,28 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
         float pr[16], ds[16];
         if (!rep) {
-          f32x16 st = neg_lse(s), dpt = neg_delta(s);
+          f32x16 st, dpt = neg_delta(s);
 #pragma unroll
           for (int t = 0; t < D / 16; ++t) {
-            mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t]);
+            mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
             mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
           }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pp = __builtin_amdgcn_exp2f(st[r]);
-            if (edge) {
-              const int q = q0 + 32 * s + crow(r, hi);
-              pp = (q >= kj && q < T && kj < T) ? pp : 0.f;
+          for (int g = 0; g < 4; ++g) {
+            const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
+            const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
+              if (edge) {
+                const int q = q0 + qr + e;
+                pp = (q >= kj && q < T && kj < T) ? pp : 0.f;
+              }
+              pr[r] = pp;
+              ds[r] = pp * dpt[r];
             }
-            pr[r] = pp;
-            ds[r] = pp * dpt[r];
           }
         } else {
 #pragma unroll
@@ -409,31 +416,23 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   const TI* V = reinterpret_cast<const TI*>(p.v) + kvoff;
   const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
 
-  const float c2 = p.scale_log2;
-  // d = 64: every dP^T product of the sweep starts from -delta of the lane's query and every score
-  // product from -lse (log2 units), with Q held scaled by s*log2(e) (bf16: one more rounding of q,
-  // below that of the probabilities entering the products); both start values stay in registers
-  // for the whole item, so that the products yield dP - delta and the exponent of P, and
-  // dS = P o (dP - delta) is one multiply after the exponential.  (At d = 128 the 32 registers do
-  // not fit the budget: there both products start from zero.)
-  constexpr bool kInit = D == 64;
   Frag<TI> qf[D / 16], gf[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    const Frag<TI> q = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
-    qf[t] = kInit ? scale_frag(q, c2) : q;
+    qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
     gf[t] = qi < T ? load8(G + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
   }
   const float lse2 = qi < T ? p.lse[soff + qi] * kLog2e : 0.f;
   const float dl = qi < T ? p.delta[soff + qi] : 0.f;
-  const float dsub = kInit ? 0.f : dl;
-  const float sc2 = kInit ? 1.f : c2, lsub = kInit ? 0.f : lse2;
-  f32x16 negd, negl;
+  const float c2 = p.scale_log2;
+  // d = 64: every dP^T product of the sweep starts from -delta of the lane's query (kept in
+  // registers for the whole item), so that it yields dP - delta and dS = P o (dP - delta) is one
+  // multiply.  (At d = 128 the 16 registers do not fit the budget: there dP starts from zero.)
+  constexpr bool kNegd = D == 64;
+  const float dsub = kNegd ? 0.f : dl;
+  f32x16 negd;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    negd[r] = kInit ? -dl : 0.f;
-    negl[r] = kInit ? -lse2 : 0.f;
-  }
+  for (int r = 0; r < 16; ++r) negd[r] = kNegd ? -dl : 0.f;
 
   f32x16 dqT[D / 32];
 #pragma unroll
@@ -465,16 +464,16 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
     if (D == 64 && NS == 2 && k0 + BK - 1 <= qw && k0 + BK <= T && qw + 31 < T) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        f32x16 st = negl, dpt = negd;
+        f32x16 st, dpt = negd;
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], !kInit && t == 0);
-          mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], !kInit && t == 0);
+          mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+          mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], !kNegd && t == 0);
         }
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          ds[r] = __builtin_amdgcn_exp2f(kInit ? st[r] : fmaf(st[r], c2, -lse2)) * (dpt[r] - dsub);
+          ds[r] = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2)) * (dpt[r] - dsub);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const Frag<TI> sf = to_frag<TI>(&ds[8 * u]);
@@ -489,17 +488,17 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
       if (ks > qw + 31 || ks >= T) break;  // wave-uniform: the rest of the tile is masked out
-      f32x16 st = negl, dpt = negd;
+      f32x16 st, dpt = negd;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], !kInit && t == 0);
-        mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], !kInit && t == 0);
+        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+        mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], !kNegd && t == 0);
       }
       const bool edge = (ks + 31 > qw) || (ks + 31 >= T);
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pp = __builtin_amdgcn_exp2f(fmaf(st[r], sc2, -lsub));
+        float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
         if (edge) {
           const int key = ks + crow(r, hi);
           pp = (key <= qi && key < T) ? pp : 0.f;

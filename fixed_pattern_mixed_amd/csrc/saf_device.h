@@ -90,20 +90,6 @@ __device__ __forceinline__ Frag<TI> zero_frag() {
   return f;
 }
 
-// fragment scaled by c (bf16: the product rounded to nearest even)
-__device__ __forceinline__ Frag<bf16> scale_frag(const Frag<bf16>& f, float c) {
-  Frag<bf16> g;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) g.v[e] = (bf16)((float)f.v[e] * c);
-  return g;
-}
-__device__ __forceinline__ Frag<float> scale_frag(const Frag<float>& f, float c) {
-  Frag<float> g;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) g.v[e] = f.v[e] * c;
-  return g;
-}
-
 // fp32 values -> operand fragment (bf16: round to nearest even)
 __device__ __forceinline__ Frag<bf16> to_frag_bf16(const float* x) {
   Frag<bf16> f;
