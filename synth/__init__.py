@@ -131,6 +131,43 @@ def layer_inputs(B, H, T, d, dtype, replaced, ar_std=0.5, seed=SEED0, backward=T
     return out
 
 
+def score_range_inputs(T, d, dtype, trend, seed=SEED0 + 300, device="cpu"):
+    """One batch entry, two heads (head 0 ordinary, head 1 replaced) whose ordinary scores span a
+    wide range with a set shape along the keys.  Every query is 8u plus small noise and key j is
+    c_j u plus small noise, for one random unit vector u, so that with the 1/sqrt(d) scale of
+    d = 64 the score of key j is about c_j:
+      rising:  c_j = 150 j / (T-1)   (the row maximum moves with almost every 32 keys)
+      falling: c_j = 150 (T-1-j) / (T-1)   (the first key dominates every row)
+      spiky:   c_j = 120 at j = 5, 42, 79, ... (j % 37 == 5), else 0   (isolated jumps of about
+               173 in log2 units, past the fp32 exponent range)
+    V, dO ~ N(0, 1); a, r ~ N(0, 0.25)."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(d, generator=g, dtype=torch.float64)
+    u /= u.norm()
+    j = torch.arange(T, dtype=torch.float64)
+    if trend == "rising":
+        c = 150.0 * j / max(T - 1, 1)
+    elif trend == "falling":
+        c = 150.0 * (T - 1 - j) / max(T - 1, 1)
+    elif trend == "spiky":
+        c = torch.where(j % 37 == 5, torch.full_like(j, 120.0), torch.zeros_like(j))
+    else:
+        raise ValueError(trend)
+    shape = (1, 2, T, d)
+    q = 8.0 * u.expand(shape).clone() + 0.05 * torch.randn(shape, generator=g, dtype=torch.float64)
+    k = c[None, None, :, None] * u + 0.05 * torch.randn(shape, generator=g, dtype=torch.float64)
+    v = torch.randn(shape, generator=g)
+    dout = torch.randn(shape, generator=g)
+    a = torch.randn((2, T), generator=g) * 0.5
+    r = torch.randn((2, T), generator=g) * 0.5
+    out = LayerInputs(q.to(dtype), k.to(dtype), v.to(dtype), dout.to(dtype), a.float(), r.float(),
+                      [False, True])
+    if device != "cpu":
+        for name in ("q", "k", "v", "dout", "a", "r"):
+            setattr(out, name, getattr(out, name).to(device))
+    return out
+
+
 def workload_inputs(w: Workload, placement="interleaved", device="cpu"):
     return layer_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, w.replaced(placement), w.ar_std,
                         SEED0 + w.index, w.backward, device=device, Hkv=w.Hkv or None)

@@ -1,11 +1,13 @@
-"""Edge cases of the mixed layer on the GPU: what replaced heads must never read, degenerate
-patterns, a pattern longer than the input, repeatability, and a non-default stream."""
+"""Edge cases of the mixed layer on the GPU: wide score ranges for the online softmax, what replaced
+heads must never read, degenerate patterns, a pattern longer than the input, repeatability, and a
+non-default stream."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
-from gpu_util import TOL, check_bwd, check_fwd
+from gpu_util import TOL, check_bwd, check_fwd, norm_err
 
 pytestmark = pytest.mark.gpu
 
@@ -13,6 +15,47 @@ pytestmark = pytest.mark.gpu
 def _saf():
     import fixed_pattern_mixed_amd as saf
     return saf
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("trend", ["rising", "falling", "spiky"])
+def test_wide_score_ranges(dtype, trend):
+    """Ordinary scores over a range of ~200 log2 units: the forward's lazily updated row maximum
+    moves on almost every subtile (rising), is set by the first key (falling), or meets jumps whose
+    probabilities overflow fp32 before the rescale (spiky); forward and backward must still match
+    the oracle's softmax.
+
+    With rows this peaked, dS = P o (dP - delta) nearly cancels (dP is close to delta where P is
+    close to 1), so dQ and dK are small against the terms that form them, and any rounding of those
+    terms (on the bf16 path: delta from the bf16 output O, P and dS rounded for the products) shows
+    up magnified in a max-relative comparison.  dQ and dK are therefore compared on the scale of
+    the uncancelled terms: |error| against max of s (P o (|dP| + |delta|)) |K| (and its transpose
+    with |Q|), with P from the oracle; the forward and dV keep the usual comparison."""
+    saf = _saf()
+    T = 300
+    x = synth.score_range_inputs(T, 64, dtype, trend)
+    g = synth.score_range_inputs(T, 64, dtype, trend, device="cuda")
+    o, lse = saf.fwd(g.q, g.k, g.v, g.replaced, g.a, g.r)
+    dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, g.replaced, g.a, g.r)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    tol = TOL[dtype]
+    check_fwd(x, o, lse, [(0, 0), (0, 1)], None, tol, trend)
+    check_bwd(x, dq, dk, dv, [(0, 1)], None, None, tol, trend)  # the replaced head
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    Q, K, V, G = f64(x.q[0, 0]), f64(x.k[0, 0]), f64(x.v[0, 0]), f64(x.dout[0, 0])
+    rq, rk, rv = oracle.head_bwd(0, x.v[0, 0], x.dout[0, 0], q=x.q[0, 0], k=x.k[0, 0])
+    P = oracle.head_pattern(0, T, q=x.q[0, 0], k=x.k[0, 0])
+    dP = G @ V.T
+    delta = (P * dP).sum(axis=1, keepdims=True)
+    W = P * (np.abs(dP) + np.abs(delta))
+    sc = 1.0 / np.sqrt(Q.shape[1])
+    for name, got, ref, bound in (("dq", dq, rq, sc * W @ np.abs(K)), ("dk", dk, rk, sc * W.T @ np.abs(Q))):
+        e = float(np.abs(f64(got[0, 0]) - ref).max() / bound.max())
+        assert e <= tol, "%s %s error %.3e of the uncancelled scale > %.1e" % (trend, name, e, tol)
+    e = norm_err(f64(dv[0, 0]), rv)
+    assert e <= tol, "%s dv error %.3e > %.1e" % (trend, e, tol)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
