@@ -53,6 +53,28 @@ def test_calibrate_full_compare(N, H, T, d, dtype):
         assert abs(gk[h] - rk[h]) <= TOL[dtype] * rk[h] + 1e-6, (h, gk[h], rk[h])
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_calibrate_wide_score_ranges(dtype):
+    """Three sequences whose scores span ~200 log2 units with different shapes along the keys (row
+    maximum moving with the keys, set by the first key, isolated jumps past the fp32 exponent
+    range): the row statistics and the streamed mean / variance must match the oracle."""
+    saf = _saf()
+    T = 300
+    xs = [synth.score_range_inputs(T, 64, dtype, t) for t in ("rising", "falling", "spiky")]
+    q = torch.cat([x.q[:, :1] for x in xs])  # [3, 1, T, d]: the ordinary head of each
+    k = torch.cat([x.k[:, :1] for x in xs])
+    ahat, svar, skl = saf.calibrate(q.cuda(), k.cuda(), kl=True)
+    torch.cuda.synchronize()
+    ga, gs, gk = cpu64(ahat), cpu64(svar), cpu64(skl)
+    assert np.isfinite(ga).all() and np.isfinite(gs).all() and np.isfinite(gk).all()
+    ra, dev = oracle.head_calibrate(q[:, 0], k[:, 0])
+    rs = dev.sum() / (2 * T * T)
+    rk = oracle.kl_score(q, k)
+    assert norm_err(ga[0], ra) <= TOL[dtype], norm_err(ga[0], ra)
+    assert abs(gs[0] - rs) / rs <= TOL[dtype], (gs[0], rs)
+    assert abs(gk[0] - rk[0]) <= TOL[dtype] * rk[0] + 1e-6, (gk[0], rk[0])
+
+
 def test_kl_score_identical_sequences_and_uniform_maps():
     """N copies of one sequence, or Q = 0 (every map uniform): s_var = 0 and s_kl = 0 up to
     rounding, at a size that spans many tiles (T = 1000, ragged)."""
