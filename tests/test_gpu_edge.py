@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL, check_bwd, check_fwd, norm_err
+from gpu_util import TOL, check_bwd, check_fwd, norm_err, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,33 @@ def test_wide_score_ranges(dtype, trend):
         assert e <= tol, "%s %s error %.3e of the uncancelled scale > %.1e" % (trend, name, e, tol)
     e = norm_err(f64(dv[0, 0]), rv)
     assert e <= tol, "%s dv error %.3e > %.1e" % (trend, e, tol)
+
+
+def test_maximum_length():
+    """T = 65536, the largest length the library takes, one ordinary and one replaced head (bf16,
+    d = 64): forward rows, dQ rows of the ordinary head and dV rows of the replaced head, sampled
+    (always including the first and the last position), against the oracle."""
+    saf = _saf()
+    T = 65536
+    rep = [False, True]
+    x = synth.layer_inputs(1, 2, T, 64, torch.bfloat16, rep, ar_std=0.5, seed=65)
+    g = synth.layer_inputs(1, 2, T, 64, torch.bfloat16, rep, ar_std=0.5, seed=65, device="cuda")
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
+    torch.cuda.synchronize()
+    rows = sample_rows(T, 24, seed=7)
+    check_fwd(x, o, lse, [(0, 0), (0, 1)], rows, TOL[torch.bfloat16], "T=65536")
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    idx = torch.as_tensor(rows, dtype=torch.long, device="cuda")
+    rq, _, _ = oracle.head_bwd(0, x.v[0, 0], x.dout[0, 0], q=x.q[0, 0], k=x.k[0, 0], qrows=rows,
+                               want_dk=False, want_dv=False)
+    e = norm_err(f64(dq[0, 0].index_select(0, idx)), rq)
+    assert e <= TOL[torch.bfloat16], ("dq", e)
+    _, _, rv = oracle.head_bwd(1, x.v[0, 1], x.dout[0, 1], a=x.a[1], r=x.r[1], krows=rows,
+                               want_dq=False, want_dk=False)
+    e = norm_err(f64(dv[0, 1].index_select(0, idx)), rv)
+    assert e <= TOL[torch.bfloat16], ("replaced dv", e)
+    assert torch.count_nonzero(dq[0, 1]) == 0 and torch.count_nonzero(dk[0, 1]) == 0
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
