@@ -19,6 +19,8 @@
 //                  row-wise forward-KL selector; its terms summed over a row are KL(A^(n)_i || Ahat_i)).
 //   calib_reduce : per head, the fixed-order fp64 sum of the partials -> s_var, and the KL score
 //                  sum / (N T) (deterministic).
+#include <type_traits>
+
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -202,20 +204,27 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
 #pragma unroll
       for (int t = 0; t < D / 16; ++t)
         mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+      // one copy of the update per case, so that interior tiles carry no per-entry mask
+      auto update = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        bool valid = true;
-        if (edge) {
-          const int key = ks + crow(r, hi);
-          valid = key <= qi && key < T && qi < T;
+        for (int r = 0; r < 16; ++r) {
+          bool valid = true;
+          if constexpr (decltype(masked)::value) {
+            const int key = ks + crow(r, hi);
+            valid = key <= qi && key < T && qi < T;
+          }
+          const float x = fmaf(st[r], p.scale_log2, -lse2);  // log2 A
+          const float a = valid ? __builtin_amdgcn_exp2f(x) : 0.f;
+          const float dlt = a - mean[s][r];
+          mean[s][r] += dlt * inv_n;
+          m2[s][r] += dlt * (a - mean[s][r]);
+          if (KL) ent_n += valid ? a * x : 0.f;
         }
-        const float x = fmaf(st[r], p.scale_log2, -lse2);  // log2 A
-        const float a = valid ? __builtin_amdgcn_exp2f(x) : 0.f;
-        const float dlt = a - mean[s][r];
-        mean[s][r] += dlt * inv_n;
-        m2[s][r] += dlt * (a - mean[s][r]);
-        if (KL) ent_n += valid ? a * x : 0.f;
-      }
+      };
+      if (edge)
+        update(std::true_type{});
+      else
+        update(std::false_type{});
     }
     if (KL) ent += (double)ent_n;
   }
