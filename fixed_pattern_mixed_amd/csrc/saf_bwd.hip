@@ -29,6 +29,8 @@
 // Every output element is written by exactly one work item and summed in a fixed order, so the
 // backward is bitwise repeatable.  S and dP are formed twice (once per kernel): seven products per
 // entry of an ordinary head instead of five, traded for having no atomic traffic.
+#include <type_traits>
+
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -496,15 +498,22 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
       }
       const bool edge = (ks + 31 > qw) || (ks + 31 >= T);
       float ds[16];
+      // one copy per case, so that subtiles below the diagonal carry no per-entry mask select
+      auto entries = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
-        if (edge) {
-          const int key = ks + crow(r, hi);
-          pp = (key <= qi && key < T) ? pp : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lse2));
+          if constexpr (decltype(masked)::value) {
+            const int key = ks + crow(r, hi);
+            pp = (key <= qi && key < T) ? pp : 0.f;
+          }
+          ds[r] = pp * (dpt[r] - dsub);
         }
-        ds[r] = pp * (dpt[r] - dsub);
-      }
+      };
+      if (edge)
+        entries(std::true_type{});
+      else
+        entries(std::false_type{});
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const Frag<TI> sf = to_frag<TI>(&ds[8 * u]);
