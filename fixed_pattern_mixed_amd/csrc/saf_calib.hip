@@ -73,11 +73,16 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
     __syncthreads();
     if (kt + 1 < nkt) kreg.load(K, k0 + kBK, T, tid);
     if (k0 > qw + 31) continue;
-    float sv[NS][16];
+    float sv[NS][16];  // the tile's scores (masked entries -inf), unscaled
     bool act[NS];
     // keys past a row's query or past the end exist only in diagonal or last tiles (wave-uniform)
     const bool edge = (k0 + kBK - 1 > qw) || (k0 + kBK > T) || (qw + 31 >= T);
-    float tmax = -INFINITY;
+    const float c2 = p.scale_log2;
+    // Lazy reference maximum: the row sum is taken relative to the current m, which any finite
+    // value serves (lse = m + log2 of the sum), as long as no term overflows.  The sum shows that:
+    // it is finite and at most 2^64 unless a term exceeds 2^64 (or m is still -inf, first tile).
+    // Only then is the tile's maximum formed and the sum rescaled and redone.
+    float lsum = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
@@ -87,34 +92,48 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
 #pragma unroll
       for (int t = 0; t < D / 16; ++t)
         mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+      // one copy per case (masking and sum together, so that the branch stays a branch)
+      auto add_terms = [&](auto masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = st[r] * p.scale_log2;
-        if (edge) {
-          const int key = ks + crow(r, hi);
-          v = (key <= qi && key < T) ? v : -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          float v = st[r];
+          if constexpr (decltype(masked)::value) {
+            const int key = ks + crow(r, hi);
+            v = (key <= qi && key < T) ? v : -INFINITY;
+          }
+          sv[s][r] = v;
+          lsum += __builtin_amdgcn_exp2f(fmaf(v, c2, -m));
         }
-        sv[s][r] = v;
-        tmax = fmaxf(tmax, v);
+      };
+      if (edge)
+        add_terms(std::true_type{});
+      else
+        add_terms(std::false_type{});
+    }
+    if (__any(!(lsum <= 0x1p64f))) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        if (act[s]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sv[s][r]);
+        }
+      const float mnew = fmaxf(m, half_max(tmax) * c2);
+      if (mnew == -INFINITY) {
+        lsum = 0.f;  // a row with no visible key yet (only rows past the end): nothing to add
+      } else {
+        l *= (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        lsum = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          if (act[s]) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lsum += __builtin_amdgcn_exp2f(fmaf(sv[s][r], c2, -m));
+          }
       }
     }
-    tmax = half_max(tmax);
-    const float mnew = fmaxf(m, tmax);
-    // a row with no visible key yet keeps m = -inf: skip its exponentials (they would be exp2(nan))
-    const bool live = mnew != -INFINITY;
-    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
-    float lsum = 0.f;
-    if (live) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (!act[s]) continue;
-        // exp2(-inf - m) = 0 for masked entries
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lsum += __builtin_amdgcn_exp2f(sv[s][r] - mnew);
-      }
-    }
-    l = l * alpha + lsum;
-    m = mnew;
+    l += lsum;
   }
   const float lt = l + __shfl_xor(l, 32);
   if (qi < T && hi == 0) p.lse2[(size_t)nh * T + qi] = m + log2f(lt);
