@@ -290,23 +290,31 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
             mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
             mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
           }
+          // one copy per case; the mask is one select per entry (bitwise conditions: a
+          // short-circuit chain would branch per entry)
+          auto entries = [&](auto masked) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
-            const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            for (int g = 0; g < 4; ++g) {
+              const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
+              const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
-              if (edge) {
-                const int q = q0 + qr + e;
-                pp = (q >= kj && q < T && kj < T) ? pp : 0.f;
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
+                if constexpr (decltype(masked)::value) {
+                  const int q = q0 + qr + e;
+                  pp = ((q >= kj) & (q < T) & (kj < T)) ? pp : 0.f;
+                }
+                pr[r] = pp;
+                ds[r] = pp * dpt[r];
               }
-              pr[r] = pp;
-              ds[r] = pp * dpt[r];
             }
-          }
+          };
+          if (edge)
+            entries(std::true_type{});
+          else
+            entries(std::false_type{});
         } else {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
