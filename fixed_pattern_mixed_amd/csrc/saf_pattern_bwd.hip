@@ -23,6 +23,8 @@
 //                  per (batch, head, position), then over batch and chunks -> da, dr (zeros at
 //                  positions T .. pat_len-1).
 // Everything is summed in a fixed order, so the result is bitwise repeatable.
+#include <type_traits>
+
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -146,25 +148,37 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
 #pragma unroll
       for (int t = 0; t < D / 16; ++t)
         mma16(gt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
+      // one copy of the entry loop per (form, edge) case: both are uniform over the subtile, and
+      // tested per entry they would branch per entry; the mask is one select (bitwise conditions)
+      auto entries = [&](auto fact_c, auto edge_c) {
+        constexpr bool kFact = decltype(fact_c)::value, kEdge = decltype(edge_c)::value;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
-        const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-        const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-        const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
+        for (int g = 0; g < 4; ++g) {
+          const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
+          const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+          const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+          const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = q0 + qr + e;
-          const float rv = rwin[xr + e];
-          const float pp = fact ? rv * lv[e] * akey : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
-          float dt = pp * (gt[4 * g + e] - dv[e]);
-          if (edge) dt = (kval && q >= kj && q < T) ? dt : 0.f;
-          col += dt;
-          const int row = 8 * g + 4 * hi + e;  // row within the subtile
-          sk[(row - l32 + 31) * LDK + row] = dt;
+          for (int e = 0; e < 4; ++e) {
+            const int q = q0 + qr + e;
+            const float rv = rwin[xr + e];
+            const float pp = kFact ? rv * lv[e] * akey : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
+            float dt = pp * (gt[4 * g + e] - dv[e]);
+            if constexpr (kEdge) dt = (kval & (q >= kj) & (q < T)) ? dt : 0.f;
+            col += dt;
+            const int row = 8 * g + 4 * hi + e;  // row within the subtile
+            sk[(row - l32 + 31) * LDK + row] = dt;
+          }
         }
+      };
+      if (fact) {
+        if (edge) entries(std::true_type{}, std::true_type{});
+        else entries(std::true_type{}, std::false_type{});
+      } else {
+        if (edge) entries(std::false_type{}, std::true_type{});
+        else entries(std::false_type{}, std::false_type{});
       }
       // distance sums of the subtile: lane x sums skewed row x (rows max(0, x-31) .. min(31, x));
       // LDS accesses of one wave complete in order, so the stores above are visible here
