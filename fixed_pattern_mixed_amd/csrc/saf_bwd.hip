@@ -316,20 +316,28 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
           else
             entries(std::false_type{});
         } else {
+          // one copy per form (uniform over the head): selecting per entry would evaluate both
+          auto rep_entries = [&](auto fact_c) {
+            constexpr bool kFact = decltype(fact_c)::value;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int qr = 32 * s + 8 * g + 4 * hi;
-            const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
+            for (int g = 0; g < 4; ++g) {
+              const int qr = 32 * s + 8 * g + 4 * hi;
+              const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+              const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float rv = rwin[xr + e];
-              float pp = fact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
-              if (fold) pp *= akey;
-              pr[4 * g + e] = pp;
+              for (int e = 0; e < 4; ++e) {
+                const float rv = rwin[xr + e];
+                float pp = kFact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
+                if (kFact && fold) pp *= akey;
+                pr[4 * g + e] = pp;
+              }
             }
-          }
+          };
+          if (fact)
+            rep_entries(std::true_type{});
+          else
+            rep_entries(std::false_type{});
         }
         // dV^T[dcol][key] += dO^T[dcol][q] P[q][key];  dK^T[dim][key] += Q^T[dim][q] dS[q][key]
 #pragma unroll
