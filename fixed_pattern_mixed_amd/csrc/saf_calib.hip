@@ -6,8 +6,9 @@
 // with A^(n) = softmax_causal(s Q^(n) K^(n)T) the head's map on sequence n.  The N maps are never
 // stored: at the 1B shape they would be N*H*T^2 values (137 GB in fp32).
 //
-//   calib_lse    : per (sequence, head, 128-query block) the base-2 log-sum-exp of the scaled
-//                  causal scores of every row (an online max / sum over key tiles).
+//   calib_lse    : per (sequence, head, 256-query block) the base-2 log-sum-exp of the scaled
+//                  causal scores of every row (an online sum over key tiles relative to a lazily
+//                  updated reference maximum).
 //   calib_stats  : per (head, 128-query tile I, 64-key tile J): for n = 1..N re-form the score tile
 //                  on the matrix cores, A = exp2(s' S - lse2), and update a per-element running mean
 //                  and sum of squared deviations (Welford) held in registers.  The tile then writes
