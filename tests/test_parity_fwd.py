@@ -57,7 +57,10 @@ WIDTHS = [
     (8, 8, 1000, 128, torch.float32, 2),
     (2, 4, 4000, 64, torch.bfloat16, 1),
     (2, 4, 4000, 128, torch.float32, 2),
+    (2, 4, 4000, 128, torch.bfloat16, 1),
     (1, 4, 2000, 64, torch.bfloat16, 1),
+    (1, 4, 2000, 128, torch.bfloat16, 2),
+    (1, 3, 1500, 64, torch.float32, 1),
 ]
 
 
