@@ -80,7 +80,9 @@ struct KvCfg {
 
 template <typename TI, int D>
 struct KvPrefetch {
-  Blocks4<TI, D, KvCfg<TI, D>::BQ, kKvNT> q, g;
+  // bf16 stages rows only (16-byte chunks); fp32 also writes transposed copies (4x4 blocks)
+  std::conditional_t<sizeof(TI) == 2, Chunks<TI, D, KvCfg<TI, D>::BQ, kKvNT>,
+                     Blocks4<TI, D, KvCfg<TI, D>::BQ, kKvNT>> q, g;
   float rs, dl, rw;
 };
 
@@ -91,8 +93,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, LDT = C::LDT, WIN = C::WIN;
   __shared__ __attribute__((aligned(16))) TI Qs[BQ * LDP];   // Q tile, rows
   __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDP];   // dO tile, rows
-  __shared__ __attribute__((aligned(16))) TI QT[D * LDT];    // Q tile transposed [dim][query]
-  __shared__ __attribute__((aligned(16))) TI GT[D * LDT];    // dO tile transposed [dcol][query]
+  // bf16 reads the transposed fragments from the row tiles (gfx950 transposing LDS read); fp32
+  // keeps transposed copies
+  constexpr bool kTr = sizeof(TI) == 2;
+  __shared__ __attribute__((aligned(16))) TI QT[kTr ? 8 : D * LDT];  // Q tile transposed [dim][query]
+  __shared__ __attribute__((aligned(16))) TI GT[kTr ? 8 : D * LDT];  // dO tile transposed [dcol][query]
   __shared__ __attribute__((aligned(16))) float rss[BQ];     // row statistic per query
   __shared__ __attribute__((aligned(16))) float dls[BQ];     // -delta per query
   __shared__ float rwin[WIN];                                // replaced: er / r*log2e window
@@ -174,11 +179,16 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
       if (rep && tid < WIN) pf.rw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
     };
     auto store_tile = [&](int q0) {
-      pf.g.template store_cols<LDT>(GT, tid);
-      if (!rep) {
+      if constexpr (kTr) {
         pf.g.template store_rows<LDP>(Gs, tid);
-        pf.q.template store_rows<LDP>(Qs, tid);
-        pf.q.template store_cols<LDT>(QT, tid);
+        if (!rep) pf.q.template store_rows<LDP>(Qs, tid);
+      } else {
+        pf.g.template store_cols<LDT>(GT, tid);
+        if (!rep) {
+          pf.g.template store_rows<LDP>(Gs, tid);
+          pf.q.template store_rows<LDP>(Qs, tid);
+          pf.q.template store_cols<LDT>(QT, tid);
+        }
       }
       if (tid < BQ) {
         // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
@@ -192,6 +202,20 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         const int dist = q0 - (kb0 + BKV - 1) + tid;
         rwin[tid] = (dist >= 0 && dist < T) ? pf.rw * wscale : wfill;
       }
+    };
+
+    // dO^T and Q^T fragments: rows row0 + perm_row(e, hi) (queries), column 32 c + l32
+    auto gt_frag = [&](int row0, int c) {
+      if constexpr (kTr)
+        return tr_frag<LDP>(Gs, row0, 32 * c, lane);
+      else
+        return tt_frag<TI, LDT>(GT, row0, 32 * c + l32, hi);
+    };
+    auto qt_frag = [&](int row0, int c) {
+      if constexpr (kTr)
+        return tr_frag<LDP>(Qs, row0, 32 * c, lane);
+      else
+        return tt_frag<TI, LDT>(QT, row0, 32 * c + l32, hi);
     };
 
     if (qt0 < nqt) load_tile(qt0 * BQ);
@@ -243,8 +267,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
             const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
 #pragma unroll
             for (int c = 0; c < D / 32; ++c) {
-              mma16(dvT[c], tt_frag<TI, LDT>(GT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
-              mma16(dkT[c], tt_frag<TI, LDT>(QT, 32 * s + 16 * u, 32 * c + l32, hi), sfr);
+              mma16(dvT[c], gt_frag(32 * s + 16 * u, c), pfr);
+              mma16(dkT[c], qt_frag(32 * s + 16 * u, c), sfr);
             }
           }
         };
@@ -345,12 +369,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
           const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
 #pragma unroll
           for (int c = 0; c < D / 32; ++c)
-            mma16(dvT[c], tt_frag<TI, LDT>(GT, 32 * s + 16 * u, 32 * c + l32, hi), pfr);
+            mma16(dvT[c], gt_frag(32 * s + 16 * u, c), pfr);
           if (!rep) {
             const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
 #pragma unroll
             for (int c = 0; c < D / 32; ++c)
-              mma16(dkT[c], tt_frag<TI, LDT>(QT, 32 * s + 16 * u, 32 * c + l32, hi), sfr);
+              mma16(dkT[c], qt_frag(32 * s + 16 * u, c), sfr);
           }
         }
       }
@@ -396,7 +420,8 @@ struct DqCfg {
 
 template <typename TI, int D>
 struct DqPrefetch {
-  Blocks4<TI, D, DqCfg<TI, D>::BK, DqCfg<TI, D>::NT> k;
+  std::conditional_t<sizeof(TI) == 2, Chunks<TI, D, DqCfg<TI, D>::BK, DqCfg<TI, D>::NT>,
+                     Blocks4<TI, D, DqCfg<TI, D>::BK, DqCfg<TI, D>::NT>> k;
   Chunks<TI, D, DqCfg<TI, D>::BK, DqCfg<TI, D>::NT> v;
 };
 
@@ -406,7 +431,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   using C = DqCfg<TI, D>;
   constexpr int BQ = C::BQ, BK = C::BK, NS = C::NS, LDP = C::LDP, LDT = C::LDT;
   __shared__ __attribute__((aligned(16))) TI Ks[BK * LDP];   // K tile, rows
-  __shared__ __attribute__((aligned(16))) TI KT[D * LDT];    // K tile transposed [dim][key]
+  constexpr bool kTr = sizeof(TI) == 2;  // bf16: K^T fragments by transposing LDS reads of Ks
+  __shared__ __attribute__((aligned(16))) TI KT[kTr ? 8 : D * LDT];  // K tile transposed [dim][key]
   __shared__ __attribute__((aligned(16))) TI Vs[BK * LDP];   // V tile, rows
 
   const int T = p.T, H = p.H;
@@ -463,8 +489,15 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   };
   auto store_tile = [&]() {
     pf.k.template store_rows<LDP>(Ks, tid);
-    pf.k.template store_cols<LDT>(KT, tid);
+    if constexpr (!kTr) pf.k.template store_cols<LDT>(KT, tid);
     pf.v.template store<LDP>(Vs, tid);
+  };
+  // K^T fragment: rows row0 + perm_row(e, hi) (keys), column 32 c + l32
+  auto kt_frag = [&](int row0, int c) {
+    if constexpr (kTr)
+      return tr_frag<LDP>(Ks, row0, 32 * c, lane);
+    else
+      return tt_frag<TI, LDT>(KT, row0, 32 * c + l32, hi);
   };
 
   const int kend = min(T, q0 + BQ);
@@ -497,7 +530,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
           const Frag<TI> sf = to_frag<TI>(&ds[8 * u]);
 #pragma unroll
           for (int c = 0; c < D / 32; ++c)
-            mma16(dqT[c], tt_frag<TI, LDT>(KT, 32 * s + 16 * u, 32 * c + l32, hi), sf);
+            mma16(dqT[c], kt_frag(32 * s + 16 * u, c), sf);
         }
       }
       continue;
@@ -535,7 +568,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
         const Frag<TI> sf = to_frag<TI>(&ds[8 * u]);
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
-          mma16(dqT[c], tt_frag<TI, LDT>(KT, 32 * s + 16 * u, 32 * c + l32, hi), sf);
+          mma16(dqT[c], kt_frag(32 * s + 16 * u, c), sf);
       }
     }
   }

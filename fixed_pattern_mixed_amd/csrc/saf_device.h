@@ -155,6 +155,26 @@ __device__ __forceinline__ Frag<TI> tt_frag(const TI* tt, int row0, int col, int
   return load8(tt + col * LDT + ((row0 + 8 * hi) ^ tswz(col)));
 }
 
+// The same fragment read from the row-major bf16 tile (row stride LDP) with the transposing LDS read
+// of gfx950 (ds_read_b64_tr_b16).  Within each group of 16 lanes that instruction gives lane i, as
+// its element j, element i % 4 of the 8 bytes addressed by lane 4j + i / 4.  Here lane 4j + a of a
+// group addresses columns 4a..4a+3 (of the group's 16) in row j of a 4-row block, so lane i receives
+// column i of the four rows.  Two such reads (rows +0..3 and +8..11 from the lane half's base) give
+// slot e the row row0 + perm_row(e, hi) and the column col0 + (lane & 31), the order of tt_frag.
+template <int LDP>
+__device__ __forceinline__ Frag<bf16> tr_frag(const bf16* rows, int row0, int col0, int lane) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
+  typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+  const int i = lane & 15;
+  const int r = row0 + 4 * (lane >> 5) + (i >> 2);
+  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+  const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rows + r * LDP + c));
+  const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rows + (r + 8) * LDP + c));
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
 // 4 consecutive elements of one row (bf16: 8 bytes, fp32: 16 bytes)
 template <typename TI>
 struct Quad;
@@ -308,6 +328,8 @@ struct Chunks {
       *reinterpret_cast<uint4*>(lds + (idx / CPR) * LDP + (idx % CPR) * EPC) = v[c];
     }
   }
+  template <int LDP>
+  __device__ __forceinline__ void store_rows(TI* lds, int tid) const { store<LDP>(lds, tid); }
 };
 
 // Store 4 consecutive fp32 values as the tensor's element type.

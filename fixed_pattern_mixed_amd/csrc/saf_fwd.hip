@@ -22,6 +22,8 @@
 //             of its entries at the end; where the prepared pattern flags the product form as
 //             inaccurate, the entry is exp(a[j] + r[i-j] - log Z(i)) instead.  Windows hold 0 (or
 //             -inf) at future and out-of-range positions, so no per-entry mask is evaluated.
+#include <type_traits>
+
 #include "saf_device.h"
 #include "saf_internal.h"
 
@@ -57,7 +59,8 @@ struct FwdCfg {
 template <typename TI>
 struct FwdSmem {
   TI* Ks;       // [BK][LDP]   K tile (ordinary items)
-  TI* VT;       // [D][LDT]    V tile transposed, key-permuted, swizzled
+  TI* VT;       // V tile: bf16 [BK][LDP] rows (read transposed by the LDS); fp32 [D][LDT]
+                //   transposed, key-permuted, swizzled
   float* awin;  // [BK]        ea (or a*log2e) of the tile's keys
   float* rwin;  // [WIN]       er (or r*log2e) of the tile's distance window
 };
@@ -93,7 +96,8 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
 
   // ---- staging: global -> registers (next tile) -> LDS
   Chunks<TI, D, BK, kNT> kreg;
-  Blocks4<TI, D, BK, kNT> vreg;
+  // bf16 stages V as rows (16-byte chunks); fp32 writes it transposed (4x4 blocks)
+  std::conditional_t<C::BF, Chunks<TI, D, BK, kNT>, Blocks4<TI, D, BK, kNT>> vreg;
   float awr = 0.f, rwr[WPT];
   // Window values are loaded raw from clamped (always valid) addresses and masked / scaled when
   // stored: arithmetic on a value right after its load would make the wave wait for it there.
@@ -109,7 +113,10 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
     }
   };
   auto store_tile = [&](int k0) {
-    vreg.template store_cols<LDT>(sm.VT, tid);
+    if constexpr (C::BF)
+      vreg.template store<LDP>(sm.VT, tid);
+    else
+      vreg.template store_cols<LDT>(sm.VT, tid);
     if (ORD) {
       kreg.template store<LDP>(sm.Ks, tid);
     } else {
@@ -155,7 +162,10 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
-        mma16(oacc[c], tt_frag<TI, LDT>(sm.VT, 32 * s + 16 * u, 32 * c + l32, hi), pf[u]);
+        if constexpr (C::BF)
+          mma16(oacc[c], tr_frag<LDP>(sm.VT, 32 * s + 16 * u, 32 * c, lane), pf[u]);
+        else
+          mma16(oacc[c], tt_frag<TI, LDT>(sm.VT, 32 * s + 16 * u, 32 * c + l32, hi), pf[u]);
   };
 
   load_tile(0);
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D == 64 
 void mixed_fwd_kernel(LayerArgs p) {
   using C = FwdCfg<TI, D, W>;
   __shared__ __attribute__((aligned(16))) TI Ks[C::BK * C::LDP];
-  __shared__ __attribute__((aligned(16))) TI VT[D * C::LDT];
+  __shared__ __attribute__((aligned(16))) TI VT[C::BF ? C::BK * C::LDP : D * C::LDT];
   __shared__ __attribute__((aligned(16))) float awin[C::BK];
   __shared__ float rwin[C::WIN];
 
