@@ -406,12 +406,15 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
 
 // ------------------------------------------------------------------------------------ bwd_dq
 #ifndef SAF_DQ_WAVES
-#define SAF_DQ_WAVES 4
+#define SAF_DQ_WAVES 0  // 0: by shape (below)
 #endif
 template <typename TI, int D>
 struct DqCfg {
-  static constexpr int NT = 64 * SAF_DQ_WAVES;            // threads per block
-  static constexpr int BQ = 32 * SAF_DQ_WAVES;            // queries per work item (32 per wave)
+  // waves per work item: 8 for bf16 at d = 128 (each staged K/V tile serves twice the queries; the
+  // wave fits the 256 registers that two waves per SIMD allow), 4 otherwise
+  static constexpr int W = SAF_DQ_WAVES ? SAF_DQ_WAVES : (sizeof(TI) == 2 && D == 128 ? 8 : 4);
+  static constexpr int NT = 64 * W;                       // threads per block
+  static constexpr int BQ = 32 * W;                       // queries per work item (32 per wave)
   static constexpr int BK = sizeof(TI) == 2 ? 64 : 32;    // keys per staged tile
   static constexpr int NS = BK / 32;
   static constexpr int LDP = D + 16 / (int)sizeof(TI);
@@ -426,7 +429,7 @@ struct DqPrefetch {
 };
 
 template <typename TI, int D>
-__global__ __launch_bounds__(64 * SAF_DQ_WAVES)
+__global__ __launch_bounds__((DqCfg<TI, D>::NT))
 __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel(LayerArgs p) {
   using C = DqCfg<TI, D>;
   constexpr int BQ = C::BQ, BK = C::BK, NS = C::NS, LDP = C::LDP, LDT = C::LDT;
