@@ -28,7 +28,7 @@
 #include "saf_internal.h"
 
 #ifndef SAF_FWD_BK
-#define SAF_FWD_BK 64
+#define SAF_FWD_BK 128
 #endif
 #ifndef SAF_FWD_W64
 #define SAF_FWD_W64 4  // minimum waves per SIMD requested for d = 64 (fits in 128 VGPRs)
