@@ -18,14 +18,16 @@
 //             grid, heaviest (lowest) key blocks first.  4 waves own 32 keys each (lane = key) and
 //             sweep the query tiles at or below the diagonal: S = Q K^T and dP = dO V^T (K, V
 //             fragments in registers, Q and dO rows from LDS), dV^T += dO^T P and dK^T += Q^T dS
-//             (Q and dO also staged transposed, so those operands are single 16-byte LDS reads).
+//             (bf16: the Q^T and dO^T fragments come from the row tiles through the transposing
+//             LDS read; fp32: Q and dO are also staged transposed).
 //             Replaced heads form P from the prepared pattern and add to dV only; they also write
 //             the zero dQ rows of their keys.  With grouped heads (several query heads per key /
 //             value head) the item sweeps each query head of its group in turn and dK, dV are the
 //             sums over the group; dK is zero when every head of the group is replaced.
-//   bwd_dq  : one work item per (batch, ordinary head, 128-query block), lane = query: S^T = K Q^T,
-//             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal (K
-//             staged both row-major and transposed).
+//   bwd_dq  : one work item per (batch, ordinary head, 32-query block per wave), lane = query: S^T = K Q^T,
+//             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal
+//             (bf16: K^T fragments by transposing reads of the K row tile; fp32: K is also staged
+//             transposed).  8 waves per item for bf16 at d = 128, else 4.
 // Every output element is written by exactly one work item and summed in a fixed order, so the
 // backward is bitwise repeatable.  S and dP are formed twice (once per kernel): seven products per
 // entry of an ordinary head instead of five, traded for having no atomic traffic.

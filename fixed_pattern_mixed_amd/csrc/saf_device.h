@@ -139,7 +139,8 @@ __device__ __forceinline__ float frag_sum(const Frag<float>& f) {
 }
 
 // ---- Transposed, permuted LDS tiles ---------------------------------------------------------------
-// A tile that a product contracts over its rows (keys or queries) is also kept transposed in LDS,
+// fp32 tiles that a product contracts over their rows (keys or queries) are also kept transposed
+// in LDS (bf16 tiles are read transposed from their rows instead: tr_frag below),
 // TT[col][tpos(row)] with row stride LDT, where inside each 16-row group row k = 8a + 4h + b is
 // placed at 8h + 4a + b (bits 2 and 3 swapped).  Slot e of lane half hi in a k16 step then reads
 // row 16u + perm_row(e, hi) at position 16u + 8*hi + e: the 8 values of a fragment are contiguous

@@ -15,8 +15,8 @@
 //   ordinary: S^T = K Q^T on the matrix cores (lane = query, registers = keys); base-2 online
 //             softmax with a lazily updated running maximum (the accumulator is rescaled only when
 //             the subtile maximum exceeds the running one by more than 2^8); O^T += V^T P^T, where
-//             the V tile is staged transposed (and key-permuted) so that a V^T fragment is one
-//             16-byte LDS read.
+//             a V^T fragment is two transposing LDS reads of the V row tile (bf16) or one 16-byte
+//             read of a transposed, key-permuted copy (fp32).
 //   replaced: no Q, no K, no QK^T and no running maximum: each entry is ea[j] * er[i-j] (one
 //             multiply) from LDS windows of the prepared pattern, and the row is divided by the sum
 //             of its entries at the end; where the prepared pattern flags the product form as
