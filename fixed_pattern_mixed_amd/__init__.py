@@ -170,11 +170,50 @@ def _ws(nbytes, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _expect(t, name, shape, dtype, device):
+    """Raise ValueError unless t has exactly this shape, dtype and device.  The C ABI takes plain
+    pointers and cannot check sizes: a tensor of another shape or element size would be read or
+    written out of its bounds."""
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _expect_pattern(a, r, H, T, device):
+    """a, r: fp32 [H, pat_len] with pat_len >= T on the device (rows of replaced heads are read)."""
+    import torch
+    if a is None or r is None:
+        raise ValueError("a and r are required when a head is replaced")
+    if a.dim() != 2 or a.shape[0] != H or a.shape[1] < T:
+        raise ValueError("a has shape %s, expected [%d, pat_len >= %d]" % (tuple(a.shape), H, T))
+    _expect(a, "a", (H, a.shape[1]), torch.float32, device)
+    _expect(r, "r", tuple(a.shape), torch.float32, device)
+
+
+def _expect_prepared(pattern, H, pat_len, device):
+    import torch
+    if pattern is None:
+        return
+    need = saf_pattern_size(H, pat_len)
+    if pattern.dtype != torch.uint8 or pattern.dim() != 1 or pattern.numel() < need:
+        raise ValueError("pattern must be a uint8 buffer of at least %d bytes (prepare_pattern)" % need)
+    if pattern.device != device:
+        raise ValueError("pattern is on %s, expected %s" % (pattern.device, device))
+
+
 def prepare_pattern(replaced, a, r):
     """Prepared pattern of the replaced heads (a, r: [H, pat_len] fp32 on the GPU), to pass as
     `pattern=` to fwd / bwd with the same replaced, a and r.  Returns a uint8 device tensor."""
     import torch
+    if a is None or a.dim() != 2:
+        raise ValueError("a must be [H, pat_len]")
     H, P = a.shape
+    _expect_pattern(a, r, H, P, a.device)
     n = saf_pattern_size(H, P)
     buf = torch.empty(max(n, 1), dtype=torch.uint8, device=a.device)
     st = saf_pattern_prepare(H, _mask(replaced, H), _ptr(a), _ptr(r), P, _ptr(buf), n,
@@ -186,11 +225,24 @@ def prepare_pattern(replaced, a, r):
 def fwd(q, k, v, replaced, a=None, r=None, scale=None, out=None, lse=None, pattern=None):
     """Forward of the mixed layer.  q: [B, H, T, d], k, v: [B, Hkv, T, d] (bf16 or fp32, same
     dtype; Hkv divides H, Hkv < H for grouped key/value heads), replaced: H flags, a, r:
-    [H, pat_len] fp32 on the GPU, pattern: optional prepare_pattern() result.  Returns (o, lse)."""
+    [H, pat_len] fp32 on the GPU, pattern: optional prepare_pattern() result.  Returns (o, lse).
+    q and k may be None when every head is replaced (they are never read then)."""
     import torch
+    if v is None or v.dim() != 4:
+        raise ValueError("v must be [B, Hkv, T, d]")
     B, Hkv, T, d = v.shape
     H = q.shape[1] if q is not None else len(replaced)
     dt = _dtype_code(v)
+    if any(not x for x in replaced) or q is not None:
+        _expect(q, "q", (B, H, T, d), v.dtype, v.device)
+        _expect(k, "k", (B, Hkv, T, d), v.dtype, v.device)
+    if any(replaced):
+        _expect_pattern(a, r, H, T, v.device)
+        _expect_prepared(pattern, H, a.shape[1], v.device)
+    if out is not None:
+        _expect(out, "out", (B, H, T, d), v.dtype, v.device)
+    if lse is not None:
+        _expect(lse, "lse", (B, H, T), torch.float32, v.device)
     o = torch.empty((B, H, T, d), dtype=v.dtype, device=v.device) if out is None else out
     lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device) if lse is None else lse
     ws_n = saf_attn_fwd_workspace_size(B, H, T, d)
@@ -208,9 +260,21 @@ def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None, pattern=Non
     """Backward of the mixed layer.  Returns (dq [B, H, T, d], dk, dv [B, Hkv, T, d]); replaced
     heads get dq = 0 and add nothing to dk."""
     import torch
+    if v is None or v.dim() != 4 or dout is None or dout.dim() != 4:
+        raise ValueError("v must be [B, Hkv, T, d] and dout [B, H, T, d]")
     B, Hkv, T, d = v.shape
     H = dout.shape[1]
     dt = _dtype_code(v)
+    _expect(dout, "dout", (B, H, T, d), v.dtype, v.device)
+    if any(not x for x in replaced) or q is not None:
+        _expect(q, "q", (B, H, T, d), v.dtype, v.device)
+        _expect(k, "k", (B, Hkv, T, d), v.dtype, v.device)
+    if any(not x for x in replaced) or o is not None:
+        _expect(o, "o", (B, H, T, d), v.dtype, v.device)
+    _expect(lse, "lse", (B, H, T), torch.float32, v.device)
+    if any(replaced):
+        _expect_pattern(a, r, H, T, v.device)
+        _expect_prepared(pattern, H, a.shape[1], v.device)
     dq = torch.empty_like(dout)
     dk, dv = torch.empty_like(v), torch.empty_like(v)
     ws_n = saf_attn_bwd_workspace_size(B, H, T, d)
@@ -228,9 +292,20 @@ def bwd_pattern(v, o, dout, lse, replaced, a, r, pattern=None, da=None, dr=None)
     """Gradient of a trained pattern: returns (da, dr) [H, pat_len] fp32; rows of replaced heads
     written (summed over the batch), rows of ordinary heads zero (fresh tensors) or untouched."""
     import torch
+    if v is None or v.dim() != 4:
+        raise ValueError("v must be [B, H, T, d]")
     B, H, T, d = v.shape
     dt = _dtype_code(v)
+    _expect(o, "o", (B, H, T, d), v.dtype, v.device)
+    _expect(dout, "dout", (B, H, T, d), v.dtype, v.device)
+    _expect(lse, "lse", (B, H, T), torch.float32, v.device)
+    _expect_pattern(a, r, H, T, v.device)
     pat_len = a.shape[-1]
+    _expect_prepared(pattern, H, pat_len, v.device)
+    if da is not None:
+        _expect(da, "da", (H, pat_len), torch.float32, v.device)
+    if dr is not None:
+        _expect(dr, "dr", (H, pat_len), torch.float32, v.device)
     da = torch.zeros_like(a) if da is None else da
     dr = torch.zeros_like(r) if dr is None else dr
     ws_n = saf_attn_bwd_pattern_workspace_size(B, H, T, d)
@@ -246,8 +321,11 @@ def calibrate(q, k, scale=None, kl=False):
     """Calibration statistics over N sequences: q, k [N, H, T, d].  Returns (ahat [H, T, T] fp32,
     svar [H] fp64), plus skl [H] fp64 (the forward-KL score) when kl is True."""
     import torch
+    if q is None or q.dim() != 4:
+        raise ValueError("q must be [N, H, T, d]")
     N, H, T, d = q.shape
     dt = _dtype_code(q)
+    _expect(k, "k", (N, H, T, d), q.dtype, q.device)
     ahat = torch.empty((H, T, T), dtype=torch.float32, device=q.device)
     svar = torch.empty((H,), dtype=torch.float64, device=q.device)
     skl = torch.empty((H,), dtype=torch.float64, device=q.device) if kl else None
@@ -264,6 +342,10 @@ def fit_pattern(ahat, steps=400, lr=0.1):
     """Compact fit of target maps ahat [H, T, T] fp32 (GPU).  Returns (a [H, T], r [H, T] fp32,
     kl [H] fp64 mean row KL, loss [H] fp64)."""
     import torch
+    if ahat is None or ahat.dim() != 3 or ahat.shape[1] != ahat.shape[2]:
+        raise ValueError("ahat must be [H, T, T]")
+    if ahat.dtype != torch.float32:
+        raise ValueError("ahat has dtype %s, expected torch.float32" % ahat.dtype)
     H, T, _ = ahat.shape
     a = torch.empty((H, T), dtype=torch.float32, device=ahat.device)
     r = torch.empty_like(a)

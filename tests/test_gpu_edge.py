@@ -1,13 +1,12 @@
 """Edge cases of the mixed layer on the GPU: wide score ranges for the online softmax, what replaced
 heads must never read, degenerate patterns, a pattern longer than the input, repeatability, and a
 non-default stream."""
-import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from gpu_util import TOL, check_bwd, check_fwd, norm_err, sample_rows
+from gpu_util import TOL, Worst, check_bwd, check_fwd, dq_uncancelled_scale, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -23,14 +22,9 @@ def test_wide_score_ranges(dtype, trend):
     """Ordinary scores over a range of ~200 log2 units: the forward's lazily updated row maximum
     moves on almost every subtile (rising), is set by the first key (falling), or meets jumps whose
     probabilities overflow fp32 before the rescale (spiky); forward and backward must still match
-    the oracle's softmax.
-
-    With rows this peaked, dS = P o (dP - delta) nearly cancels (dP is close to delta where P is
-    close to 1), so dQ and dK are small against the terms that form them, and any rounding of those
-    terms (on the bf16 path: delta from the bf16 output O, P and dS rounded for the products) shows
-    up magnified in a max-relative comparison.  dQ and dK are therefore compared on the scale of
-    the uncancelled terms: |error| against max of s (P o (|dP| + |delta|)) |K| (and its transpose
-    with |Q|), with P from the oracle; the forward and dV keep the usual comparison."""
+    the oracle's softmax.  With rows this peaked, dS = P o (dP - delta) nearly cancels wherever P
+    is close to 1, so many dQ and dK rows are judged on their uncancelled terms (gpu_util notes),
+    and many dV rows sum terms that underflow fp32 (the flush floor)."""
     saf = _saf()
     T = 300
     x = synth.score_range_inputs(T, 64, dtype, trend)
@@ -42,20 +36,7 @@ def test_wide_score_ranges(dtype, trend):
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
     tol = TOL[dtype]
     check_fwd(x, o, lse, [(0, 0), (0, 1)], None, tol, trend)
-    check_bwd(x, dq, dk, dv, [(0, 1)], None, None, tol, trend)  # the replaced head
-    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
-    Q, K, V, G = f64(x.q[0, 0]), f64(x.k[0, 0]), f64(x.v[0, 0]), f64(x.dout[0, 0])
-    rq, rk, rv = oracle.head_bwd(0, x.v[0, 0], x.dout[0, 0], q=x.q[0, 0], k=x.k[0, 0])
-    P = oracle.head_pattern(0, T, q=x.q[0, 0], k=x.k[0, 0])
-    dP = G @ V.T
-    delta = (P * dP).sum(axis=1, keepdims=True)
-    W = P * (np.abs(dP) + np.abs(delta))
-    sc = 1.0 / np.sqrt(Q.shape[1])
-    for name, got, ref, bound in (("dq", dq, rq, sc * W @ np.abs(K)), ("dk", dk, rk, sc * W.T @ np.abs(Q))):
-        e = float(np.abs(f64(got[0, 0]) - ref).max() / bound.max())
-        assert e <= tol, "%s %s error %.3e of the uncancelled scale > %.1e" % (trend, name, e, tol)
-    e = norm_err(f64(dv[0, 0]), rv)
-    assert e <= tol, "%s dv error %.3e > %.1e" % (trend, e, tol)
+    check_bwd(x, dq, dk, dv, [(0, 0), (0, 1)], None, None, tol, trend)
 
 
 def test_maximum_length():
@@ -70,18 +51,19 @@ def test_maximum_length():
     o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
     dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
     torch.cuda.synchronize()
-    rows = sample_rows(T, 24, seed=7)
+    rows = sample_rows(T, 64, seed=7)
     check_fwd(x, o, lse, [(0, 0), (0, 1)], rows, TOL[torch.bfloat16], "T=65536")
     f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
     idx = torch.as_tensor(rows, dtype=torch.long, device="cuda")
     rq, _, _ = oracle.head_bwd(0, x.v[0, 0], x.dout[0, 0], q=x.q[0, 0], k=x.k[0, 0], qrows=rows,
                                want_dk=False, want_dv=False)
-    e = norm_err(f64(dq[0, 0].index_select(0, idx)), rq)
-    assert e <= TOL[torch.bfloat16], ("dq", e)
+    wr = Worst("T=65536")
+    wr.add(f64(dq[0, 0].index_select(0, idx)), rq, TOL[torch.bfloat16], "dq", T=T, rows=rows,
+           rounding=lambda r: dq_uncancelled_scale(x.q[0, 0], x.k[0, 0], x.v[0, 0], x.dout[0, 0], r))
     _, _, rv = oracle.head_bwd(1, x.v[0, 1], x.dout[0, 1], a=x.a[1], r=x.r[1], krows=rows,
                                want_dq=False, want_dk=False)
-    e = norm_err(f64(dv[0, 1].index_select(0, idx)), rv)
-    assert e <= TOL[torch.bfloat16], ("replaced dv", e)
+    wr.add(f64(dv[0, 1].index_select(0, idx)), rv, TOL[torch.bfloat16], "replaced dv", T=T)
+    wr.report()
     assert torch.count_nonzero(dq[0, 1]) == 0 and torch.count_nonzero(dk[0, 1]) == 0
 
 

@@ -1,10 +1,9 @@
-"""Backward of the mixed layer on the GPU (through the C ABI) against the fp64 oracle."""
-import numpy as np
+"""Backward of the mixed layer on the GPU (through the C ABI) against the fp64 oracle, row by row."""
 import pytest
 import torch
 
 import synth
-from gpu_util import TOL, check_bwd, pick_heads, sample_rows
+from gpu_util import TOL, Worst, all_heads, check_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -36,28 +35,28 @@ def test_backward_small_full_compare(B, H, T, d, dtype, R, placement, std):
     o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
     dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
     torch.cuda.synchronize()
-    heads = [(b, h) for b in range(B) for h in range(H)]
-    check_bwd(x, dq, dk, dv, heads, None, None, TOL[dtype], "small")
+    check_bwd(x, dq, dk, dv, all_heads(B, H), None, None, TOL[dtype], "small")
 
 
+# Every fwd+bwd workload of the benchmark table, in the launch configuration the benchmark times
+# (inputs resident on the GPU, the pattern prepared once and passed in), compared in full: every
+# dQ row and every dK / dV row of every slice.
 FULL = ["l124m_t4096", "l124m_t8192", "l1b_t8192"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_backward_full_size_sampled(name):
+def test_backward_full_size_full_compare(name):
     saf = _saf()
     w = synth.WORKLOADS[name]
     x = synth.workload_inputs(w)
     print("workload", name, flush=True)
     q, k, v, g, a, r = (t.to("cuda") for t in (x.q, x.k, x.v, x.dout, x.a, x.r))
-    o, lse = saf.fwd(q, k, v, x.replaced, a, r)
-    dq, dk, dv = saf.bwd(q, k, v, o, g, lse, x.replaced, a, r)
+    pat = saf.prepare_pattern(x.replaced, a, r)
+    o, lse = saf.fwd(q, k, v, x.replaced, a, r, pattern=pat)
+    dq, dk, dv = saf.bwd(q, k, v, o, g, lse, x.replaced, a, r, pattern=pat)
     torch.cuda.synchronize()
-    rows = sample_rows(w.T, 24, seed=w.index + 7)
-    heads = pick_heads(w.B, x.replaced, n_each=1)
-    check_bwd(x, dq, dk, dv, heads, rows, rows, TOL[w.torch_dtype], name)
-    # every replaced head of every batch entry: dq and dk are exactly zero
-    for h, isrep in enumerate(x.replaced):
-        if isrep:
-            assert torch.count_nonzero(dq[:, h]) == 0 and torch.count_nonzero(dk[:, h]) == 0
-    assert torch.isfinite(dq.float()).all() and torch.isfinite(dv.float()).all()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    del q, k, v, g, o, lse
+    wr = Worst("bwd full " + name)
+    check_bwd(x, dq, dk, dv, all_heads(w.B, w.H), None, None, TOL[w.torch_dtype], name, worst=wr)
+    wr.report(workload=name)

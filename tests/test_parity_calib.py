@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL, cpu64, norm_err, sample_rows
+from gpu_util import TOL, Worst, cpu64
 
 pytestmark = pytest.mark.gpu
 
@@ -41,10 +41,11 @@ def test_calibrate_full_compare(N, H, T, d, dtype):
     assert torch.equal(ahat, ahat2) and torch.equal(svar, svar2)
     ga, gs, gk = cpu64(ahat), cpu64(svar), cpu64(skl)
     rk = oracle.kl_score(q, k)
+    wr = Worst("calib small N%dH%dT%dd%d" % (N, H, T, d))
     for h in range(H):
         ra, dev = oracle.head_calibrate(q[:, h], k[:, h])
         rs = dev.sum() / ((N - 1) * T * T)
-        assert norm_err(ga[h], ra) <= TOL[dtype], (h, norm_err(ga[h], ra))
+        wr.add(ga[h], ra, TOL[dtype], "ahat[h=%d]" % h)
         assert np.all(ga[h][np.triu_indices(T, 1)] == 0.0)
         if rs == 0.0:
             assert abs(gs[h]) <= 1e-12
@@ -70,7 +71,7 @@ def test_calibrate_wide_score_ranges(dtype):
     ra, dev = oracle.head_calibrate(q[:, 0], k[:, 0])
     rs = dev.sum() / (2 * T * T)
     rk = oracle.kl_score(q, k)
-    assert norm_err(ga[0], ra) <= TOL[dtype], norm_err(ga[0], ra)
+    Worst("calib wide").add(ga[0], ra, TOL[dtype], "ahat")
     assert abs(gs[0] - rs) / rs <= TOL[dtype], (gs[0], rs)
     assert abs(gk[0] - rk[0]) <= TOL[dtype] * rk[0] + 1e-6, (gk[0], rk[0])
 
@@ -110,24 +111,38 @@ def test_mean_optimality_identity_on_gpu_outputs():
         assert abs(lhs - rhs) <= 1e-5 * lhs
 
 
-def test_calibrate_full_size_sampled():
-    """The 1B-shaped calibration (N=32, H=16, T=8192, d=128, bf16): sampled rows of Ahat against
-    the oracle, and properties that hold at any size (rows sum to 1, zeros above the diagonal,
-    0 <= s_var)."""
+def test_calibrate_full_size():
+    """The 1B-shaped calibration (N=32, H=16, T=8192, d=128, bf16): for the first and the last head,
+    every row of Ahat, s_var and the KL score against the oracle (rows formed in chunks, the
+    deviation sums added up for s_var); for every head the properties that hold at any size (rows
+    sum to 1, zeros above the diagonal, s_var and s_kl finite and >= 0)."""
     saf = _saf()
     w = synth.WORKLOADS["l1b_t8192"]
     N, H, T, d = w.calib_N, w.H, w.T, w.d
     q, k = synth.calib_inputs(N, H, T, d, torch.bfloat16)
+    print("workload l1b_t8192 calibration", flush=True)
     ahat, svar, skl = saf.calibrate(q.cuda(), k.cuda(), kl=True)
     torch.cuda.synchronize()
-    rows = sample_rows(T, 12, seed=9)
-    idx = torch.as_tensor(rows, dtype=torch.long, device="cuda")
-    for h in (0, H - 1):
-        ra, _ = oracle.head_calibrate(q[:, h], k[:, h], rows=rows)
-        got = cpu64(ahat[h].index_select(0, idx))
-        assert norm_err(got, ra) <= TOL[torch.bfloat16]
     sums = ahat.double().sum(-1)
     assert torch.allclose(sums, torch.ones_like(sums), atol=1e-4)
-    assert torch.count_nonzero(torch.triu(ahat[0], 1)) == 0
-    assert torch.isfinite(svar).all() and (svar >= 0).all()
-    assert torch.isfinite(skl).all() and (skl >= 0).all()
+    for h in range(H):
+        assert torch.count_nonzero(torch.triu(ahat[h], 1)) == 0
+    gs, gk = cpu64(svar), cpu64(skl)
+    assert np.isfinite(gs).all() and (gs >= 0).all() and np.isfinite(gk).all() and (gk >= 0).all()
+    wr = Worst("calib full l1b_t8192")
+    tol = TOL[torch.bfloat16]
+    for h in (0, H - 1):
+        ga = ahat[h].cpu()
+        dev_sum = 0.0
+        for r0 in range(0, T, 1024):
+            rows = np.arange(r0, min(T, r0 + 1024), dtype=np.int32)
+            ra, dev = oracle.head_calibrate(q[:, h], k[:, h], rows=rows)
+            dev_sum += float(dev.sum())
+            wr.add(ga[r0:r0 + len(rows)].double().numpy(), ra, tol, "ahat[h=%d]" % h)
+        rs = dev_sum / ((N - 1) * T * T)
+        rk = float(oracle.head_kl_score(q[:, h], k[:, h]).sum()) / (N * T)
+        print("head %d: s_var gpu %.6e oracle %.6e; s_kl gpu %.6e oracle %.6e"
+              % (h, gs[h], rs, gk[h], rk), flush=True)
+        assert abs(gs[h] - rs) <= tol * rs, (h, gs[h], rs)
+        assert abs(gk[h] - rk) <= tol * rk, (h, gk[h], rk)
+    wr.report(workload="l1b_t8192 calibration", svar_heads=[0, H - 1])

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL, TOL_LSE, cpu64, norm_err, sample_rows
+from gpu_util import TOL, TOL_LSE, Worst, cpu64, dq_uncancelled_scale, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -29,28 +29,35 @@ def _compare(x, rep, o, lse, dq, dk, dv, tol, tol_lse, batches=None, kv_heads=No
     ridx = slice(None) if rows is None else rows
     ref = oracle.layer_fwd_gqa(x.q, x.k, x.v, rep, x.a, x.r, heads=heads, rows=rows)
     go, gl = cpu64(o), cpu64(lse)
+    wr = Worst("gqa " + what)
     for (b, h), (ro, rl) in ref.items():
-        assert norm_err(go[b, h][ridx], ro) <= tol, (what, "o", b, h, norm_err(go[b, h][ridx], ro))
-        assert np.abs(gl[b, h][ridx] - rl).max() <= tol_lse, (what, "lse", b, h)
+        wr.add(go[b, h][ridx], ro, tol, "o[b=%d,h=%d]" % (b, h), T=x.v.shape[2])
+        wr.add_lse(gl[b, h][ridx], rl, tol_lse, "lse[b=%d,h=%d]" % (b, h))
     if dq is None:
+        wr.report()
         return
     rq, rk, rv = oracle.layer_bwd_gqa(x.q, x.k, x.v, x.dout, rep, x.a, x.r, batches=batches,
                                       kv_heads=kv_heads, qrows=rows, krows=rows)
     gq, gk, gv = cpu64(dq), cpu64(dk), cpu64(dv)
     for (b, h), ref_q in rq.items():
-        # an ordinary head at T = 1 has dq = 0 exactly (P = 1, dS = dP - delta = 0); the GPU's
-        # dP and delta round differently, so compare on the inputs' unit scale there
-        fl = 1.0 if np.abs(ref_q).max() == 0.0 else 0.0
-        err = norm_err(gq[b, h][ridx], ref_q, floor=fl)
-        assert err <= tol, (what, "dq", b, h, err)
+        if rep[h]:
+            assert np.all(gq[b, h][ridx] == 0.0), (what, "dq", b, h)
+        else:
+            # rows of exact zeros in the reference (row 0, where P = 1 and dS = 0) are measured
+            # on the inputs' unit scale, rows with few keys that fail their own scale against
+            # their uncancelled terms (gpu_util notes)
+            T = x.v.shape[2]
+            rws = np.arange(T, dtype=np.int32) if rows is None else rows
+            args = (x.q[b, h], x.k[b, h // G], x.v[b, h // G], x.dout[b, h])
+            wr.add(gq[b, h][ridx], ref_q, tol, "dq[b=%d,h=%d]" % (b, h), T=T, rows=rws,
+                   rounding=lambda r, a=args: dq_uncancelled_scale(*a, r))
     for (b, hk), ref_k in rk.items():
         if all(rep[h] for h in range(hk * G, (hk + 1) * G)):  # every head replaced: exactly zero
             assert np.all(gk[b, hk][ridx] == 0.0), (what, "dk", b, hk)
         else:
-            fl = 1.0 if np.abs(ref_k).max() == 0.0 else 0.0
-            err = norm_err(gk[b, hk][ridx], ref_k, floor=fl)
-            assert err <= tol, (what, "dk", b, hk, err)
-        assert norm_err(gv[b, hk][ridx], rv[(b, hk)]) <= tol, (what, "dv", b, hk)
+            wr.add(gk[b, hk][ridx], ref_k, tol, "dk[b=%d,hk=%d]" % (b, hk), T=x.v.shape[2])
+        wr.add(gv[b, hk][ridx], rv[(b, hk)], tol, "dv[b=%d,hk=%d]" % (b, hk), T=x.v.shape[2])
+    wr.report()
 
 
 SMALL = [
@@ -96,6 +103,30 @@ def test_gqa_with_one_query_head_per_group_is_the_plain_layer():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_plain_backward_export_matches_the_grouped_one(dtype):
+    """saf_attn_bwd (no grouping argument), called directly through the C ABI, writes the bits of
+    saf_attn_bwd_gqa with Hkv = H (what the binding calls), for a layer with both head kinds."""
+    saf = _saf()
+    B, H, T, d = 2, 4, 300, 128 if dtype == torch.float32 else 64
+    rep = [0, 1, 0, 1]
+    g = synth.layer_inputs(B, H, T, d, dtype, rep, seed=6, device="cuda")
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    dq1, dk1, dv1 = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
+    dq2, dk2, dv2 = (torch.full_like(g.q, float("nan")) for _ in range(3))
+    n = saf.saf_attn_bwd_workspace_size(B, H, T, d)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    code = saf.SAF_BF16 if dtype == torch.bfloat16 else saf.SAF_F32
+    st = saf.saf_attn_bwd(code, B, H, T, d, g.q.data_ptr(), g.k.data_ptr(), g.v.data_ptr(),
+                          o.data_ptr(), g.dout.data_ptr(), lse.data_ptr(), saf._mask(rep, H),
+                          g.a.data_ptr(), g.r.data_ptr(), T, None, 0.0, dq2.data_ptr(),
+                          dk2.data_ptr(), dv2.data_ptr(), ws.data_ptr(), n,
+                          torch.cuda.current_stream().cuda_stream)
+    assert st == saf.SAF_OK, saf.saf_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+
+
 def test_gqa_rejects_groups_that_do_not_divide():
     saf = _saf()
     rep = (ctypes.c_uint8 * 6)(*[0] * 6)
@@ -119,7 +150,7 @@ def test_gqa_full_size_sampled():
     o, lse = saf.fwd(q, k, v, rep, a, r)
     dq, dk, dv = saf.bwd(q, k, v, o, gd, lse, rep, a, r)
     torch.cuda.synchronize()
-    rows = sample_rows(w.T, 16, seed=3)
+    rows = sample_rows(w.T, 64, seed=3)
     _compare(x, rep, o, lse, None, None, None, TOL[torch.bfloat16], TOL_LSE[torch.bfloat16],
              batches=[0], kv_heads=[0, w.Hkv - 1], rows=rows, what="full fwd")
     _compare(x, rep, o, lse, dq, dk, dv, TOL[torch.bfloat16], TOL_LSE[torch.bfloat16],
