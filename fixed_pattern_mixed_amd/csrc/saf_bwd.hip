@@ -19,7 +19,8 @@
 //             sweep the query tiles at or below the diagonal: S = Q K^T and dP = dO V^T (K, V
 //             fragments in registers, Q and dO rows from LDS), dV^T += dO^T P and dK^T += Q^T dS
 //             (bf16: the Q^T and dO^T fragments come from the row tiles through the transposing
-//             LDS read; fp32: Q and dO are also staged transposed).
+//             LDS read, the tiles stored swizzled so that both reads are free of bank conflicts;
+//             fp32: Q and dO are also staged transposed).
 //             Replaced heads form P from the prepared pattern and add to dV only; they also write
 //             the zero dQ rows of their keys.  With grouped heads (several query heads per key /
 //             value head) the item sweeps each query head of its group in turn and dK, dV are the
@@ -93,11 +94,13 @@ __global__ __launch_bounds__(kKvNT)
 __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bwd_kv_kernel(LayerArgs p) {
   using C = KvCfg<TI, D>;
   constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, LDT = C::LDT, WIN = C::WIN;
-  __shared__ __attribute__((aligned(16))) TI Qs[BQ * LDP];   // Q tile, rows
-  __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDP];   // dO tile, rows
-  // bf16 reads the transposed fragments from the row tiles (gfx950 transposing LDS read); fp32
-  // keeps transposed copies
+  // bf16 reads the transposed fragments from the row tiles (gfx950 transposing LDS read), which
+  // are stored swizzled (tile_off) so that both reads are free of bank conflicts; fp32 keeps
+  // padded rows and transposed copies
   constexpr bool kTr = sizeof(TI) == 2;
+  constexpr int LDQ = kTr ? TileGeom<D>::LDR : LDP;
+  __shared__ __attribute__((aligned(16))) TI Qs[BQ * LDQ];   // Q tile, rows
+  __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDQ];   // dO tile, rows
   __shared__ __attribute__((aligned(16))) TI QT[kTr ? 8 : D * LDT];  // Q tile transposed [dim][query]
   __shared__ __attribute__((aligned(16))) TI GT[kTr ? 8 : D * LDT];  // dO tile transposed [dcol][query]
   __shared__ __attribute__((aligned(16))) float rss[BQ];     // row statistic per query
@@ -133,6 +136,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
     kf[t] = (any_ord && kj < T) ? load8(K + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
     vf[t] = (any_ord && kj < T) ? load8(V + (size_t)kj * D + 16 * t + 8 * hi) : zero_frag<TI>();
   }
+
+  const TileLane<D, true> tl(lane);  // lane bases of the swizzled Q / dO tiles (bf16)
 
   f32x16 dvT[D / 32], dkT[D / 32];
 #pragma unroll
@@ -182,8 +187,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
     };
     auto store_tile = [&](int q0) {
       if constexpr (kTr) {
-        pf.g.template store_rows<LDP>(Gs, tid);
-        if (!rep) pf.q.template store_rows<LDP>(Qs, tid);
+        pf.g.template store_tile<true>(Gs, tid);
+        if (!rep) pf.q.template store_tile<true>(Qs, tid);
       } else {
         pf.g.template store_cols<LDT>(GT, tid);
         if (!rep) {
@@ -209,15 +214,28 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
     // dO^T and Q^T fragments: rows row0 + perm_row(e, hi) (queries), column 32 c + l32
     auto gt_frag = [&](int row0, int c) {
       if constexpr (kTr)
-        return tr_frag<LDP>(Gs, row0, 32 * c, lane);
+        return tile_tr_frag<D, true>(Gs, row0, c, tl);
       else
         return tt_frag<TI, LDT>(GT, row0, 32 * c + l32, hi);
     };
     auto qt_frag = [&](int row0, int c) {
       if constexpr (kTr)
-        return tr_frag<LDP>(Qs, row0, 32 * c, lane);
+        return tile_tr_frag<D, true>(Qs, row0, c, tl);
       else
         return tt_frag<TI, LDT>(QT, row0, 32 * c + l32, hi);
+    };
+    // Q and dO row fragments (lane = query row row_base + l32, columns 16t + 8hi ..)
+    auto q_row = [&](int row_base, int t) {
+      if constexpr (kTr)
+        return tile_row_frag<D, true>(Qs, row_base, t, tl);
+      else
+        return load8(Qs + (row_base + l32) * LDP + 16 * t + 8 * hi);
+    };
+    auto g_row = [&](int row_base, int t) {
+      if constexpr (kTr)
+        return tile_row_frag<D, true>(Gs, row_base, t, tl);
+      else
+        return load8(Gs + (row_base + l32) * LDP + 16 * t + 8 * hi);
     };
 
     if (qt0 < nqt) load_tile(qt0 * BQ);
@@ -277,12 +295,12 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
         f32x16 st0, dp0 = neg_delta(0), st1, dp1 = neg_delta(1);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          mma16(st0, load8(Qs + l32 * LDP + 16 * t + 8 * hi), kf[t], t == 0);
-          mma16(dp0, load8(Gs + l32 * LDP + 16 * t + 8 * hi), vf[t]);
+          mma16(st0, q_row(0, t), kf[t], t == 0);
+          mma16(dp0, g_row(0, t), vf[t]);
         }
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
-          mma16(st1, load8(Qs + (32 + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
+          mma16(st1, q_row(32, t), kf[t], t == 0);
         float pr[16], ds[16];
         grad_entries(st0, dp0, 0, pr, ds);
         if constexpr (D == 64) {
@@ -291,11 +309,11 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
           grad_products(0, pr, ds);
 #pragma unroll
           for (int t = 0; t < D / 16; ++t)
-            mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+            mma16(dp1, g_row(32, t), vf[t]);
         } else {
 #pragma unroll
           for (int t = 0; t < D / 16; ++t)
-            mma16(dp1, load8(Gs + (32 + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+            mma16(dp1, g_row(32, t), vf[t]);
           grad_products(0, pr, ds);
         }
         grad_entries(st1, dp1, 1, pr, ds);
@@ -313,8 +331,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
           f32x16 st, dpt = neg_delta(s);
 #pragma unroll
           for (int t = 0; t < D / 16; ++t) {
-            mma16(st, load8(Qs + (32 * s + l32) * LDP + 16 * t + 8 * hi), kf[t], t == 0);
-            mma16(dpt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t]);
+            mma16(st, q_row(32 * s, t), kf[t], t == 0);
+            mma16(dpt, g_row(32 * s, t), vf[t]);
           }
           // one copy per case; the mask is one select per entry (bitwise conditions: a
           // short-circuit chain would branch per entry)
@@ -435,8 +453,10 @@ __global__ __launch_bounds__((DqCfg<TI, D>::NT))
 __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel(LayerArgs p) {
   using C = DqCfg<TI, D>;
   constexpr int BQ = C::BQ, BK = C::BK, NS = C::NS, LDP = C::LDP, LDT = C::LDT;
-  __shared__ __attribute__((aligned(16))) TI Ks[BK * LDP];   // K tile, rows
-  constexpr bool kTr = sizeof(TI) == 2;  // bf16: K^T fragments by transposing LDS reads of Ks
+  // bf16: K^T fragments by transposing LDS reads of the K row tile, stored swizzled (tile_off)
+  constexpr bool kTr = sizeof(TI) == 2;
+  constexpr int LDK = kTr ? TileGeom<D>::LDR : LDP;
+  __shared__ __attribute__((aligned(16))) TI Ks[BK * LDK];   // K tile, rows
   __shared__ __attribute__((aligned(16))) TI KT[kTr ? 8 : D * LDT];  // K tile transposed [dim][key]
   __shared__ __attribute__((aligned(16))) TI Vs[BK * LDP];   // V tile, rows
 
@@ -493,16 +513,28 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
     pf.v.load(V, k0, T, tid);
   };
   auto store_tile = [&]() {
-    pf.k.template store_rows<LDP>(Ks, tid);
-    if constexpr (!kTr) pf.k.template store_cols<LDT>(KT, tid);
+    if constexpr (kTr) {
+      pf.k.template store_tile<true>(Ks, tid);
+    } else {
+      pf.k.template store_rows<LDP>(Ks, tid);
+      pf.k.template store_cols<LDT>(KT, tid);
+    }
     pf.v.template store<LDP>(Vs, tid);
   };
+  const TileLane<D, true> tl(lane);  // lane bases of the swizzled K tile (bf16)
   // K^T fragment: rows row0 + perm_row(e, hi) (keys), column 32 c + l32
   auto kt_frag = [&](int row0, int c) {
     if constexpr (kTr)
-      return tr_frag<LDP>(Ks, row0, 32 * c, lane);
+      return tile_tr_frag<D, true>(Ks, row0, c, tl);
     else
       return tt_frag<TI, LDT>(KT, row0, 32 * c + l32, hi);
+  };
+  // K row fragment (lane = key row row_base + l32, columns 16t + 8hi ..)
+  auto k_row = [&](int row_base, int t) {
+    if constexpr (kTr)
+      return tile_row_frag<D, true>(Ks, row_base, t, tl);
+    else
+      return load8(Ks + (row_base + l32) * LDP + 16 * t + 8 * hi);
   };
 
   const int kend = min(T, q0 + BQ);
@@ -523,7 +555,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
         f32x16 st, dpt = negd;
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+          mma16(st, k_row(32 * s, t), qf[t], t == 0);
           mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], !kNegd && t == 0);
         }
         float ds[16];
@@ -547,7 +579,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
       f32x16 st, dpt = negd;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+        mma16(st, k_row(32 * s, t), qf[t], t == 0);
         mma16(dpt, load8(Vs + (32 * s + l32) * LDP + 16 * t + 8 * hi), gf[t], !kNegd && t == 0);
       }
       const bool edge = (ks + 31 > qw) || (ks + 31 >= T);

@@ -140,7 +140,7 @@ __device__ __forceinline__ float frag_sum(const Frag<float>& f) {
 
 // ---- Transposed, permuted LDS tiles ---------------------------------------------------------------
 // fp32 tiles that a product contracts over their rows (keys or queries) are also kept transposed
-// in LDS (bf16 tiles are read transposed from their rows instead: tr_frag below),
+// in LDS (bf16 tiles are read transposed from their rows instead: tile_tr_frag below),
 // TT[col][tpos(row)] with row stride LDT, where inside each 16-row group row k = 8a + 4h + b is
 // placed at 8h + 4a + b (bits 2 and 3 swapped).  Slot e of lane half hi in a k16 step then reads
 // row 16u + perm_row(e, hi) at position 16u + 8*hi + e: the 8 values of a fragment are contiguous
@@ -156,21 +156,72 @@ __device__ __forceinline__ Frag<TI> tt_frag(const TI* tt, int row0, int col, int
   return load8(tt + col * LDT + ((row0 + 8 * hi) ^ tswz(col)));
 }
 
-// The same fragment read from the row-major bf16 tile (row stride LDP) with the transposing LDS read
+// ---- bf16 row tiles read with the transposing LDS read -------------------------------------------
+// LDS serves 64 banks of 4 bytes per clock; the transposing read is served 32 lanes per pass (here
+// 4 rows r0..r0+3, r0 = 0 mod 4, x 32 columns = 16 banks per row), the 16-byte read 16 lanes per
+// pass (16 consecutive rows x one 16-byte chunk); both measured with in-bounds probes on gfx950.
+// With the rows padded to D + 8 elements, the four rows of a transposing read overlap in the banks
+// (4-way at D = 128: half the read rate).  Tiles read that way are stored with row stride
+// LDR = D + 32 elements (48 or 80 dwords: 16 x an odd number, modulo the 64-bank line), so the four
+// rows of a pass cover four disjoint 16-bank segments.  A tile that is also read as rows (16
+// consecutive rows of one chunk, which the padding puts four apart on the same segment) has the
+// low two bits of its chunk index XORed with (r >> 2) & 3 ("swizzled"), which separates those
+// four rows inside their segment and leaves the transposing read's segments as they are.
+// Every address is then a per-lane base plus a compile-time offset.
+template <int D>
+struct TileGeom {
+  static_assert(D == 64 || D == 128, "head width");
+  static constexpr int LDR = D + 32;
+};
+// element offset of (row r, column c); SW = low chunk bits swizzled
+template <int D, bool SW>
+__host__ __device__ __forceinline__ int tile_off(int r, int c) {
+  int ch = c >> 3;
+  if (SW) ch = (ch & ~3) | ((ch & 3) ^ ((r >> 2) & 3));
+  return r * TileGeom<D>::LDR + 8 * ch + (c & 7);
+}
+
+// Per-lane bases of the two reads (row bases and column groups at multiples of 16 rows / 32 cols):
+//   row read of fragment step t (row base + l32, columns 16t + 8hi .. +7):  32 (t >> 1) + rb(t & 1)
+//   transposing read s (rows +0..3 / +8..11 of base + 4hi, columns 32 cc + ..):  32 cc + tb(s)
+// Rows are multiples of 32 elements long, so bit 4 of an offset comes from the chunk position
+// alone: the odd fragment step (logical chunk bit 1) and the second transposing read (rows + 8,
+// which flips bit 1 of (r >> 2) & 3) move the swizzled position by exactly that bit.  One base per
+// read kind is kept; the other is one XOR away.
+template <int D, bool SW>
+struct TileLane {
+  int rb0, tb0;
+  __device__ __forceinline__ explicit TileLane(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5, i = lane & 15;
+    rb0 = tile_off<D, SW>(l32, 8 * hi);
+    tb0 = tile_off<D, SW>(4 * hi + (i >> 2), 16 * ((lane >> 4) & 1) + 4 * (i & 3));
+  }
+  __device__ __forceinline__ int rb(int p) const { return p ? rb0 ^ 16 : rb0; }
+  __device__ __forceinline__ int tb(int s) const {
+    return s ? (SW ? tb0 ^ 16 : tb0) + 8 * TileGeom<D>::LDR : tb0;
+  }
+};
+
+// A-operand row fragment (row row_base + l32, columns 16t + 8hi .. +7); row_base = 0 mod 16
+template <int D, bool SW>
+__device__ __forceinline__ Frag<bf16> tile_row_frag(const bf16* tile, int row_base, int t,
+                                                    const TileLane<D, SW>& L) {
+  return load8(tile + row_base * TileGeom<D>::LDR + 32 * (t >> 1) + L.rb(t & 1));
+}
+// Transposed fragment (the order of tt_frag), read from the row tile with the transposing LDS read
 // of gfx950 (ds_read_b64_tr_b16).  Within each group of 16 lanes that instruction gives lane i, as
 // its element j, element i % 4 of the 8 bytes addressed by lane 4j + i / 4.  Here lane 4j + a of a
 // group addresses columns 4a..4a+3 (of the group's 16) in row j of a 4-row block, so lane i receives
 // column i of the four rows.  Two such reads (rows +0..3 and +8..11 from the lane half's base) give
-// slot e the row row0 + perm_row(e, hi) and the column col0 + (lane & 31), the order of tt_frag.
-template <int LDP>
-__device__ __forceinline__ Frag<bf16> tr_frag(const bf16* rows, int row0, int col0, int lane) {
+// slot e the row row0 + perm_row(e, hi) and the column 32 cc + (lane & 31).  row0 = 0 mod 16.
+template <int D, bool SW>
+__device__ __forceinline__ Frag<bf16> tile_tr_frag(const bf16* tile, int row0, int cc,
+                                                   const TileLane<D, SW>& L) {
   typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
   typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
-  const int i = lane & 15;
-  const int r = row0 + 4 * (lane >> 5) + (i >> 2);
-  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-  const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rows + r * LDP + c));
-  const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rows + (r + 8) * LDP + c));
+  const bf16* base = tile + row0 * TileGeom<D>::LDR + 32 * cc;
+  const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + L.tb(0)));
+  const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + L.tb(1)));
   Frag<bf16> f;
   f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return f;
@@ -331,6 +382,16 @@ struct Chunks {
   }
   template <int LDP>
   __device__ __forceinline__ void store_rows(TI* lds, int tid) const { store<LDP>(lds, tid); }
+  // into a [ROWS][LDR] bf16 tile of the transposing read (tile_off)
+  template <bool SW>
+  __device__ __forceinline__ void store_tile(TI* lds, int tid) const {
+    static_assert(EPC == 8, "tiles of the transposing read are bf16");
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      *reinterpret_cast<uint4*>(lds + tile_off<D, SW>(idx / CPR, 8 * (idx % CPR))) = v[c];
+    }
+  }
 };
 
 // Store 4 consecutive fp32 values as the tensor's element type.

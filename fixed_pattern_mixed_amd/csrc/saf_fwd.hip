@@ -15,8 +15,9 @@
 //   ordinary: S^T = K Q^T on the matrix cores (lane = query, registers = keys); base-2 online
 //             softmax with a lazily updated running maximum (the accumulator is rescaled only when
 //             the subtile maximum exceeds the running one by more than 2^8); O^T += V^T P^T, where
-//             a V^T fragment is two transposing LDS reads of the V row tile (bf16) or one 16-byte
-//             read of a transposed, key-permuted copy (fp32).
+//             a V^T fragment is two transposing LDS reads of the V row tile (bf16; its rows are
+//             padded so that those reads are free of bank conflicts) or one 16-byte read of a
+//             transposed, key-permuted copy (fp32).
 //   replaced: no Q, no K, no QK^T and no running maximum: each entry is ea[j] * er[i-j] (one
 //             multiply) from LDS windows of the prepared pattern, and the row is divided by the sum
 //             of its entries at the end; where the prepared pattern flags the product form as
@@ -52,6 +53,7 @@ struct FwdCfg {
   static constexpr int NS = BK / 32;                     // 32-key subtiles per tile
   static constexpr int LDP = D + 16 / (int)sizeof(TI);   // padded LDS row (elements)
   static constexpr int LDT = BK + 16 / (int)sizeof(TI);  // padded row of the transposed V tile
+  static constexpr int VT_ELEMS = BF ? BK * TileGeom<D>::LDR : D * LDT;  // V tile (below)
   static constexpr int WIN = BK + BQ;                    // distance window
   static constexpr int WPT = (WIN + NT - 1) / NT;        // window values per thread
 };
@@ -59,8 +61,8 @@ struct FwdCfg {
 template <typename TI>
 struct FwdSmem {
   TI* Ks;       // [BK][LDP]   K tile (ordinary items)
-  TI* VT;       // V tile: bf16 [BK][LDP] rows (read transposed by the LDS); fp32 [D][LDT]
-                //   transposed, key-permuted, swizzled
+  TI* VT;       // V tile: bf16 [BK][D + 32] rows (tile_off, unswizzled: read only transposed, by
+                //   the LDS); fp32 [D][LDT] transposed, key-permuted, swizzled
   float* awin;  // [BK]        ea (or a*log2e) of the tile's keys
   float* rwin;  // [WIN]       er (or r*log2e) of the tile's distance window
 };
@@ -114,7 +116,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   };
   auto store_tile = [&](int k0) {
     if constexpr (C::BF)
-      vreg.template store<LDP>(sm.VT, tid);
+      vreg.template store_tile<false>(sm.VT, tid);
     else
       vreg.template store_cols<LDT>(sm.VT, tid);
     if (ORD) {
@@ -140,6 +142,8 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   const float lz_q = (KIND == kExponential && qi < T) ? p.pat.lz(h)[qi] : 0.f;
   const float lz2_q = lz_q * kLog2e;
 
+  const TileLane<D, false> vtl(lane);  // lane bases of the V tile's transposing reads (bf16)
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) zero(oacc[c]);
@@ -163,7 +167,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
         if constexpr (C::BF)
-          mma16(oacc[c], tr_frag<LDP>(sm.VT, 32 * s + 16 * u, 32 * c, lane), pf[u]);
+          mma16(oacc[c], tile_tr_frag<D, false>(sm.VT, 32 * s + 16 * u, c, vtl), pf[u]);
         else
           mma16(oacc[c], tt_frag<TI, LDT>(sm.VT, 32 * s + 16 * u, 32 * c + l32, hi), pf[u]);
   };
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D == 64 
 void mixed_fwd_kernel(LayerArgs p) {
   using C = FwdCfg<TI, D, W>;
   __shared__ __attribute__((aligned(16))) TI Ks[C::BK * C::LDP];
-  __shared__ __attribute__((aligned(16))) TI VT[C::BF ? C::BK * C::LDP : D * C::LDT];
+  __shared__ __attribute__((aligned(16))) TI VT[C::VT_ELEMS];
   __shared__ __attribute__((aligned(16))) float awin[C::BK];
   __shared__ float rwin[C::WIN];
 

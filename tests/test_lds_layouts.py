@@ -3,11 +3,17 @@
 The matrix-core operand order: slot e of lane l in a k16 step carries contraction index
 16u + perm_row(e, l // 32), the row order of an output block (register r of C holds row
 8(r // 4) + 4(l // 32) + r % 4).  A fragment of a tile that a product contracts over its rows is
-read from the row-major tile with the transposing LDS read, whose lane rule (measured on the GPU
-with an in-bounds probe of two address patterns) is: within each group of 16 lanes, lane i
-receives as element j the element i % 4 of the 8 bytes addressed by lane 4j + i // 4.  These
-tests check that the addresses the kernels give each lane (tr_frag) then deliver exactly the
-operand order above, for every lane and slot, and that every read stays inside the tile."""
+read from the row tile with the transposing LDS read, whose lane rule (measured on the GPU with an
+in-bounds probe of two address patterns) is: within each group of 16 lanes, lane i receives as
+element j the element i % 4 of the 8 bytes addressed by lane 4j + i // 4.
+
+Tiles read that way have rows of D + 32 elements, and tiles also read as rows (16-byte A-operand
+fragments) have the low two bits of each 16-byte chunk index XORed with (r >> 2) & 3
+(saf_device.h: tile_off, TileLane).  These tests check, for every lane and slot, that the
+addresses the kernels issue deliver exactly the operand order above, that every access stays
+inside the tile and is aligned, that the one-XOR second bases equal the direct formula, and that
+both reads are free of bank conflicts under the LDS model measured with probes on the GPU: 64
+banks of 4 bytes; the transposing read served 32 lanes per pass, the 16-byte read 16 lanes."""
 import itertools
 
 import pytest
@@ -31,16 +37,63 @@ def tr_read(addr_of_lane, mem):
     return out
 
 
-def tr_frag_addresses(row0, col0, ldp):
-    """The two per-lane element addresses tr_frag issues (row-major tile, row stride ldp)."""
+def ldr(d):
+    return d + 32
+
+
+def tile_off(d, sw, r, c):
+    ch = c >> 3
+    if sw:
+        ch = (ch & ~3) | ((ch & 3) ^ ((r >> 2) & 3))
+    return r * ldr(d) + 8 * ch + (c & 7)
+
+
+def lane_bases(d, sw, lane):
+    """TileLane: (rb0, tb0) and the derived second bases rb(1), tb(1)."""
+    l32, hi, i = lane & 31, lane >> 5, lane & 15
+    rb0 = tile_off(d, sw, l32, 8 * hi)
+    tb0 = tile_off(d, sw, 4 * hi + (i >> 2), 16 * ((lane >> 4) & 1) + 4 * (i & 3))
+    rb1 = rb0 ^ 16
+    tb1 = (tb0 ^ 16 if sw else tb0) + 8 * ldr(d)
+    return rb0, rb1, tb0, tb1
+
+
+def tr_addresses(d, sw, row0, cc):
+    """Per-lane element addresses of tile_tr_frag's two reads."""
     lo, hi = [], []
     for lane in range(64):
-        i = lane & 15
-        r = row0 + 4 * (lane >> 5) + (i >> 2)
-        c = col0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3)
-        lo.append(r * ldp + c)
-        hi.append((r + 8) * ldp + c)
+        _, _, tb0, tb1 = lane_bases(d, sw, lane)
+        lo.append(row0 * ldr(d) + 32 * cc + tb0)
+        hi.append(row0 * ldr(d) + 32 * cc + tb1)
     return lo, hi
+
+
+def row_addresses(d, sw, row_base, t):
+    """Per-lane element addresses of tile_row_frag (8 consecutive elements each)."""
+    out = []
+    for lane in range(64):
+        rb0, rb1, _, _ = lane_bases(d, sw, lane)
+        out.append(row_base * ldr(d) + 32 * (t >> 1) + (rb1 if t & 1 else rb0))
+    return out
+
+
+def tile_mem(rows, d, sw):
+    mem = [None] * (rows * ldr(d))
+    for r, c in itertools.product(range(rows), range(d)):
+        mem[tile_off(d, sw, r, c)] = (r, c)  # each element names its own row and column
+    return mem
+
+
+def banks_max(addrs, nbytes, lanes_per_pass):
+    worst = 0
+    for p0 in range(0, 64, lanes_per_pass):
+        cnt = [0] * 64
+        for l in range(p0, p0 + lanes_per_pass):
+            dw = 2 * addrs[l] // 4
+            for k in range(nbytes // 4):
+                cnt[(dw + k) % 64] += 1
+        worst = max(worst, max(cnt))
+    return worst
 
 
 def test_probe_patterns_follow_the_rule():
@@ -53,31 +106,93 @@ def test_probe_patterns_follow_the_rule():
     assert b[16] == [4, 260, 516, 772] and b[63] == [207, 463, 719, 975]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("sw", [False, True])
+def test_second_bases_equal_the_direct_formula(d, sw):
+    """rb(1) and tb(1), one XOR from the first bases, are the offsets tile_off gives directly."""
+    for lane in range(64):
+        l32, hi, i = lane & 31, lane >> 5, lane & 15
+        _, rb1, _, tb1 = lane_bases(d, sw, lane)
+        if sw:  # rb1 is only used on swizzled tiles (the forward's V tile is never read as rows)
+            assert rb1 == tile_off(d, sw, l32, 16 + 8 * hi)
+        assert tb1 == tile_off(d, sw, 4 * hi + (i >> 2) + 8, 16 * ((lane >> 4) & 1) + 4 * (i & 3))
+
+
 @pytest.mark.parametrize("rows,d", [(64, 64), (64, 128), (128, 64), (128, 128)])
-def test_tr_frag_gives_the_operand_order(rows, d):
-    ldp = d + 8  # padded bf16 row of the kernels' tiles
-    mem = [None] * (rows * ldp)
-    for r, c in itertools.product(range(rows), range(d)):
-        mem[r * ldp + c] = (r, c)  # each element names its own row and column
+@pytest.mark.parametrize("sw", [False, True])
+def test_transposing_read_gives_the_operand_order(rows, d, sw):
+    mem = tile_mem(rows, d, sw)
     for row0 in range(0, rows, 16):
-        for col0 in range(0, d, 32):
-            lo, hi = tr_frag_addresses(row0, col0, ldp)
-            for a in lo + hi:  # every 8-byte read inside the tile, 8-byte aligned
-                assert 0 <= a and a + 3 < rows * ldp and (2 * a) % 8 == 0
-                assert a % ldp + 3 < d  # never into the row padding
+        for cc in range(d // 32):
+            lo, hi = tr_addresses(d, sw, row0, cc)
+            for a in lo + hi:  # every 8-byte read inside the tile, 8-byte aligned, never padding
+                assert 0 <= a and a + 3 < rows * ldr(d) and (2 * a) % 8 == 0
+                assert a % ldr(d) + 3 < d
             vlo, vhi = tr_read(lo, mem), tr_read(hi, mem)
             for lane in range(64):
                 frag = vlo[lane] + vhi[lane]
                 for e in range(8):
-                    assert frag[e] == (row0 + perm_row(e, lane >> 5), col0 + (lane & 31))
+                    assert frag[e] == (row0 + perm_row(e, lane >> 5), 32 * cc + (lane & 31))
+
+
+@pytest.mark.parametrize("rows,d", [(64, 64), (64, 128), (128, 128)])
+def test_row_read_gives_the_a_operand(rows, d):
+    """Lane l reads row row_base + l % 32, columns 16t + 8(l // 32) .. +7, contiguous."""
+    mem = tile_mem(rows, d, True)
+    for row_base in range(0, rows, 32):
+        for t in range(d // 16):
+            for lane, a in enumerate(row_addresses(d, True, row_base, t)):
+                assert a % 8 == 0 and 0 <= a and a + 7 < rows * ldr(d)
+                want = [(row_base + (lane & 31), 16 * t + 8 * (lane >> 5) + k) for k in range(8)]
+                assert mem[a:a + 8] == want
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_reads_are_free_of_bank_conflicts(d):
+    for row0, cc in itertools.product(range(0, 64, 16), range(d // 32)):
+        for sw in (False, True):
+            for addrs in tr_addresses(d, sw, row0, cc):
+                assert banks_max(addrs, 8, 32) == 1
+    for row_base, t in itertools.product((0, 32), range(d // 16)):
+        assert banks_max(row_addresses(d, True, row_base, t), 16, 16) == 1
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_padded_rows_of_d_plus_8_conflict(d):
+    """The layout these replace (rows of D + 8 elements): its transposing reads were 2-way (D = 64)
+    and 4-way (D = 128) conflicted, half the measured read rate at D = 128."""
+    ld = d + 8
+    addrs = []
+    for lane in range(64):
+        i = lane & 15
+        r = 4 * (lane >> 5) + (i >> 2)
+        c = 16 * ((lane >> 4) & 1) + 4 * (i & 3)
+        addrs.append(r * ld + c)
+    assert banks_max(addrs, 8, 32) == (2 if d == 64 else 4)
+
+
+@pytest.mark.parametrize("d,rows,nt", [(64, 64, 256), (128, 64, 256), (128, 128, 512), (64, 128, 512)])
+def test_staging_writes_cover_the_tile_once(d, rows, nt):
+    """Chunks::store_tile: chunk idx of the tile (row idx / (d/8), chunk idx % (d/8)) lands at
+    tile_off; every element of every row is written exactly once, inside the tile."""
+    cpr = d // 8
+    seen = set()
+    for sw in (False, True):
+        seen.clear()
+        for idx in range(rows * cpr):
+            r, ch = idx // cpr, idx % cpr
+            a = tile_off(d, sw, r, 8 * ch)
+            assert a % 8 == 0 and a + 7 < rows * ldr(d) and a % ldr(d) + 7 < d
+            for k in range(8):
+                assert a + k not in seen
+                seen.add(a + k)
+        assert len(seen) == rows * d
 
 
 def test_a_planted_address_mistake_is_caught():
     """Swapping the two 4-row reads (a plausible slip) breaks the order the test checks."""
-    ldp, rows, d = 72, 64, 64
-    mem = [None] * (rows * ldp)
-    for r, c in itertools.product(range(rows), range(d)):
-        mem[r * ldp + c] = (r, c)
-    lo, hi = tr_frag_addresses(0, 0, ldp)
+    d, rows = 64, 64
+    mem = tile_mem(rows, d, True)
+    lo, hi = tr_addresses(d, True, 0, 0)
     frag = tr_read(hi, mem)[0] + tr_read(lo, mem)[0]
     assert [frag[e] for e in range(8)] != [(perm_row(e, 0), 0) for e in range(8)]
