@@ -75,6 +75,9 @@ _lib.saf_attn_fwd.restype = _i
 _lib.saf_attn_bwd.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                               _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.saf_attn_bwd.restype = _i
+_lib.saf_attn_bwd_noalloc.argtypes = [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _i, _vp, ctypes.c_float, _vp, _vp, _vp, _vp]
+_lib.saf_attn_bwd_noalloc.restype = _i
 _lib.saf_attn_fwd_gqa.argtypes = [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp,
                                   ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
 _lib.saf_attn_fwd_gqa.restype = _i
@@ -104,6 +107,7 @@ saf_attn_fwd = _lib.saf_attn_fwd
 saf_attn_bwd = _lib.saf_attn_bwd
 saf_attn_fwd_gqa = _lib.saf_attn_fwd_gqa
 saf_attn_bwd_gqa = _lib.saf_attn_bwd_gqa
+saf_attn_bwd_noalloc = _lib.saf_attn_bwd_noalloc
 saf_calibrate = _lib.saf_calibrate
 saf_select_heads = _lib.saf_select_heads
 saf_set_backward_overlap = _lib.saf_set_backward_overlap

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include <initializer_list>
@@ -187,6 +188,35 @@ SideStream* side_stream() {
   return &ss;
 }
 
+// ---- Library-owned workspace of saf_attn_bwd_noalloc (for callers that cannot allocate) ----------
+// One array per device (each GPU the library runs on holds its own copy until the process ends).
+// Host code never uses the array's name as an address: on the host it is only a stand-in for the
+// symbol, and a kernel given it would fault.  The device address is looked up once per device
+// with hipGetSymbolAddress (the device current) and kept.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` in *out (looked up on the first call on a device).
+saf_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "no-allocation backward: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SAF_ERR_UNSUPPORTED, "device %d is beyond the %d devices this library serves", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "no-allocation backward: hipGetSymbolAddress");
+    if (!ptr) return fail(SAF_ERR_HIP, "no-allocation backward: hipGetSymbolAddress gave no address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAF_OK;
+}
+
 size_t pattern_bytes(int H, int P) {
   return align_up(sizeof(float) * (size_t)saf::pattern_stride(P) * H);
 }
@@ -280,7 +310,8 @@ static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
                            const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const uint8_t* replaced, const float* a,
                            const float* r, int pat_len, const void* pattern, float scale, void* dq,
-                           void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
+                           void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream,
+                           bool allow_side = true, bool lib_ws = false);
 
 saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
                         const void* v, const uint8_t* replaced, const float* a, const float* r,
@@ -314,6 +345,16 @@ saf_status saf_attn_bwd_gqa(saf_dtype dt, int B, int H, int Hkv, int T, int d, c
                             void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
   return bwd_impl(dt, B, H, Hkv, T, d, q, k, v, o, dout, lse, replaced, a, r, pat_len, pattern,
                   scale, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+saf_status saf_attn_bwd_noalloc(saf_dtype dt, int B, int H, int T, int d, const void* q,
+                                const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, const uint8_t* replaced, const float* a,
+                                const float* r, int pat_len, const void* pattern, float scale,
+                                void* dq, void* dk, void* dv, hipStream_t stream) {
+  // the library's device array as the workspace; no side stream (it would be created on first use)
+  return bwd_impl(dt, B, H, H, T, d, q, k, v, o, dout, lse, replaced, a, r, pat_len, pattern, scale,
+                  dq, dk, dv, nullptr, 0, stream, /*allow_side=*/false, /*lib_ws=*/true);
 }
 
 size_t saf_attn_bwd_pattern_workspace_size(int B, int H, int T, int d) {
@@ -435,7 +476,7 @@ static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
                     const void* k, const void* v, const void* o, const void* dout, const float* lse,
                     const uint8_t* replaced, const float* a, const float* r, int pat_len,
                     const void* pattern, float scale, void* dq, void* dk, void* dv, void* ws,
-                    size_t ws_bytes, hipStream_t stream) {
+                    size_t ws_bytes, hipStream_t stream, bool allow_side, bool lib_ws) {
   g_err[0] = 0;
   if (dt != SAF_F32 && dt != SAF_BF16) return fail(SAF_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   saf_status st = check_shape(B, H, T, d);
@@ -459,11 +500,23 @@ static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
   if (any_rep && pattern && ((uintptr_t)pattern & (kAlign - 1)) != 0)
     return fail(SAF_ERR_INVALID_ARG, "pattern is not 256-byte aligned");
   const size_t need = bwd_ws(B, H, T, d);
-  if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL");
-  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
-  if (ws_bytes < need) return fail(SAF_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  if (lib_ws) {  // saf_attn_bwd_noalloc: the library's device array
+    if (need > kScratchBytes)
+      return fail(SAF_ERR_UNSUPPORTED,
+                  "saf_attn_bwd_noalloc: B=%d H=%d T=%d needs %zu workspace bytes, more than its "
+                  "%zu-byte device array (call saf_attn_bwd with a workspace instead)",
+                  B, H, T, need, kScratchBytes);
+  } else {
+    if (!ws) return fail(SAF_ERR_INVALID_ARG, "ws is NULL");
+    if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(SAF_ERR_INVALID_ARG, "ws is not 256-byte aligned");
+    if (ws_bytes < need) return fail(SAF_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", ws_bytes, need);
+  }
   float s;
   if ((st = check_scale(scale, d, &s)) != SAF_OK) return st;
+  if (lib_ws) {  // every argument checked: look up this device's array
+    if ((st = scratch_address(&ws)) != SAF_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
 
   la.B = B; la.H = H; la.T = T; la.d = d;
   la.Hkv = Hkv;
@@ -480,7 +533,7 @@ static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
   const bool bf = dt == SAF_BF16;
   hipError_t e = traced("bwd_pre", stream, [&] { return saf::launch_bwd_pre(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-  SideStream* side = any_ord ? side_stream() : nullptr;
+  SideStream* side = (any_ord && allow_side) ? side_stream() : nullptr;
   if (side) {  // fork: the query-block kernel on the side stream after the preprocess
     if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return hip_fail(e, "backward fork");
     if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return hip_fail(e, "backward fork");

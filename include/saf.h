@@ -136,6 +136,25 @@ saf_status saf_attn_bwd_gqa(saf_dtype dt, int B, int H, int Hkv, int T, int d, c
                             void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * saf_attn_bwd without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Arguments,
+ * results and errors are those of saf_attn_bwd (Hkv = H).  The workspace (the delta rows, and the
+ * prepared pattern when `pattern` is NULL) lives in a device array owned by the library, 16 MiB
+ * per device, allocated when the library is loaded and held until the process ends; the call
+ * itself allocates nothing.  Shapes whose saf_attn_bwd_workspace_size exceeds 16 MiB (B*H*T*4
+ * bytes of delta plus, without a prepared pattern, about 12*H*T bytes) return SAF_ERR_UNSUPPORTED
+ * with nothing enqueued.  The backward-overlap option is not used on this path (its side stream
+ * would be created on first use).  Every call on a device uses that device's one array: calls
+ * that may run at the same time on one device (other streams, other threads) race and must be
+ * ordered by the caller.  Each call writes every part of the array it reads.
+ */
+saf_status saf_attn_bwd_noalloc(saf_dtype dt, int B, int H, int T, int d, const void* q,
+                                const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, const uint8_t* replaced, const float* a,
+                                const float* r, int pat_len, const void* pattern, float scale,
+                                void* dq, void* dk, void* dv, hipStream_t stream);
+
+/*
  * Gradient with respect to the replaced heads' pattern, for a pattern that is trained instead of
  * frozen ([Paper page] Table 14, "trainable mean"; saf_attn_bwd treats a and r as frozen).
  * With P(i,j) = exp(a[j] + r[i-j]) / Z(i) on j <= i ([Notes §二.3, Eq.(3)]), G(i,j) = dout_i . v_j
