@@ -6,12 +6,17 @@ mixed forward (ordinary and replaced heads in one grid) followed by the mixed ba
 preprocess, key-block kernel, query-block dQ kernel).  Forward-only workloads (prefill) time the
 forward alone.  Prints ONE JSON line.
 
-The default workload is the 124M-shaped layer of the pages' main update benchmark: B=8, H=12
-heads of width 64, T=4096, bf16, 3 of 12 heads replaced ([Notes §三]; [Paper page] Table 2).
+The headline workload is the largest fwd+bwd configuration that fits one GPU: one GPU's share of
+the pages' 1B-model run, B=2, H=16 heads of width 128, T=8192, bf16, 4 of 16 heads replaced
+([Notes §四.6]; [Paper page] Table 23).  The same line carries, under "configs", the other layer
+shapes the pages time: the 124M-shaped layer at 4K (B=8, 3 of 12 heads replaced) and 8K (B=4, 6 of
+12 replaced), fwd+bwd ([Paper page] Table 2), and causal prefill at B=64, T=4096 and B=2, T=16384,
+forward only ([Paper page] Table 29), each also with all heads ordinary and all replaced.
 Algorithmic flops per (batch, head) over the T(T+1)/2 causal entries: ordinary forward 4d,
 ordinary backward 10d, replaced forward 2d, replaced backward 2d per entry.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-variants]
+                  [--no-configs]
 
 [Notes] = "When Can Attention Heads Be Statically Defined?：中文精读笔记";
 [Paper page] = "When Can Attention Heads Be Statically Defined?".
@@ -72,13 +77,15 @@ def total_flops(B, T, d, replaced, backward):
 
 
 class Layer:
-    """Preallocated buffers and raw C-ABI calls for one layer shape (no allocation per step)."""
+    """Preallocated buffers and raw C-ABI calls for one layer shape (no allocation per step).
+    draw_on="cuda" draws the synthetic inputs on the GPU (same distributions, no host work)."""
 
-    def __init__(self, saf, torch, w, replaced, dev):
+    def __init__(self, saf, torch, w, replaced, dev, draw_on=None):
         import synth
         self.saf, self.w, self.rep = saf, w, list(replaced)
         x = synth.layer_inputs(w.B, w.H, w.T, w.d, w.torch_dtype, replaced, w.ar_std,
-                               synth.SEED0 + w.index, backward=True, device=dev, Hkv=w.Hkv or None)
+                               synth.SEED0 + w.index, backward=True, device=dev, Hkv=w.Hkv or None,
+                               draw_on=draw_on)
         self.x = x
         B, H, T, d = w.B, w.H, w.T, w.d
         self.Hkv = w.kv_heads
@@ -125,6 +132,22 @@ class Layer:
         self.fwd()
         if self.w.backward:
             self.bwd()
+
+
+def spin_up(torch, seconds=0.3):
+    """Bring the GPU out of its idle clocks before anything is timed: a plain bf16 matrix product
+    loop for `seconds` (not part of the hot path; the W warm-up steps and K timed steps follow).
+    Without it the first few milliseconds of timing run at ramping clocks."""
+    a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            b = a @ a
+        torch.cuda.synchronize()
+        n += 8
+    del a, b
+    return round((time.perf_counter() - t0) * 1e3, 1)
 
 
 def time_steps(torch, layer, steps, warmup, trace=None):
@@ -317,6 +340,18 @@ def fit_timing(torch, saf, ahat, stream, steps=400, lr=0.1, reps=2):
             "accepted_at_0.2_nat": sum(1 for x in klh if x <= 0.2)}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo, as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, replaced, min_seconds=10.0):
     """The fp64 oracle, as it stands, on whole sequences of the same workload (all heads, full T),
     one after another until at least min_seconds of CPU work (or the whole batch) is done."""
@@ -343,10 +378,62 @@ def cpu_baseline(w, replaced, min_seconds=10.0):
         "value": round(n_seq * w.T / dt, 1),
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": "%d of %d sequences (all %d heads, full T=%d, %s) in %.1f s"
                   % (n_seq, w.B, w.H, w.T, "fwd+bwd" if w.backward else "fwd", dt),
     }
+
+
+def variants_of(torch, saf, w, dev, steps, layer_ms=None, draw_on=None):
+    """The layer with all heads ordinary and with all heads replaced (same shape): ordinary-tile
+    efficiency, replaced vs ordinary time per head, and the mixed layer's speedup over all-ordinary
+    (the analogue of the pages' speedup over ordinary attention)."""
+    var = {}
+    for label, rr in (("all_ordinary", [0] * w.H), ("all_replaced", [1] * w.H)):
+        lv = Layer(saf, torch, w, rr, dev, draw_on=draw_on)
+        tv = time_steps(torch, lv, steps, 2)
+        fv = total_flops(w.B, w.T, w.d, rr, w.backward)
+        var[label] = {"ms_per_step": round(tv * 1e3, 4), "tflops": round(fv / tv / 1e12, 1),
+                      "pct_bf16_peak": round(100 * fv / tv / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        del lv
+    if layer_ms is not None:
+        var["mixed_speedup_vs_all_ordinary"] = round(var["all_ordinary"]["ms_per_step"] / layer_ms, 4)
+    var["replaced_vs_ordinary_time_per_head"] = round(
+        var["all_replaced"]["ms_per_step"] / var["all_ordinary"]["ms_per_step"], 4)
+    return var
+
+
+def config_line(torch, saf, name, dev, steps):
+    """One more workload of the pages' tables, timed like the headline (inputs drawn on the GPU):
+    tokens/s, TFLOP/s, % of peak, per-kernel times and the all-ordinary / all-replaced variants."""
+    import synth
+    w = synth.WORKLOADS[name]
+    rep = w.replaced()
+    lay = Layer(saf, torch, w, rep, dev, draw_on="cuda")
+    trace = saf.KernelTrace(capacity=4 * (steps + 1))
+    t = time_steps(torch, lay, steps, 3, trace)
+    kf = kernel_flops(w.B, w.T, w.d, rep)
+    kernels = {}
+    for kname, st in trace.summary().items():
+        ent = {"avg_ms": round(st["avg_ms"], 4)}
+        if kf.get(kname):
+            ent["tflops"] = round(kf[kname] / (st["avg_ms"] * 1e-3) / 1e12, 1)
+        kernels[kname] = ent
+    trace.close()
+    del lay
+    fl = total_flops(w.B, w.T, w.d, rep, w.backward)
+    return {"workload": "%s: B=%d, H=%d, T=%d, d=%d, bf16, %d replaced, %s"
+                        % (w.name, w.B, w.H, w.T, w.d, w.n_replaced, "fwd+bwd" if w.backward else "fwd"),
+            "ms_per_step": round(t * 1e3, 4), "tokens_per_s": round(w.B * w.T / t, 1),
+            "tflops": round(fl / t / 1e12, 1),
+            "pct_bf16_peak": round(100 * fl / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "kernels": kernels,
+            "variants": variants_of(torch, saf, w, dev, steps, layer_ms=t * 1e3, draw_on="cuda")}
+
+
+CONFIGS = ["l124m_t4096", "l124m_t8192", "prefill_b64_t4096", "prefill_b2_t16384"]
 
 
 def main():
@@ -354,7 +441,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="l124m_t4096")
+    ap.add_argument("--workload", default="l1b_t8192")
+    ap.add_argument("--configs", default=",".join(CONFIGS),
+                    help="comma-separated further workloads timed into the line's configs object")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
@@ -394,6 +484,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     replaced = w.replaced()
     layer = Layer(saf, torch, w, replaced, dev)
+    spin_ms = spin_up(torch)
     trace = saf.KernelTrace(capacity=4 * (args.steps + 1))
     t_step = time_steps(torch, layer, args.steps, args.warmup, trace)
     tokens = w.B * w.T
@@ -436,28 +527,23 @@ def main():
         "pct_bf16_peak": round(100 * flops / t_step / 1e12 / PEAK_BF16_TFLOPS, 2),
         "kernels": kernels,
         "pattern_prepare_ms": round(layer.prepare_ms, 3),
+        "gpu_spin_up_ms": spin_ms,
         "roofline": roofline,
     }
 
     if not args.no_variants:
-        var = {}
-        for label, rr in (("all_ordinary", [0] * w.H), ("all_replaced", [1] * w.H)):
-            lv = Layer(saf, torch, w, rr, dev)
-            tv = time_steps(torch, lv, max(5, args.steps // 3), 2)
-            fv = total_flops(w.B, w.T, w.d, rr, w.backward)
-            var[label] = {"ms_per_step": round(tv * 1e3, 4), "tflops": round(fv / tv / 1e12, 1),
-                          "pct_bf16_peak": round(100 * fv / tv / 1e12 / PEAK_BF16_TFLOPS, 2)}
-            del lv
+        var = variants_of(torch, saf, w, dev, max(5, args.steps // 3), layer_ms=t_step * 1e3)
         if w.backward:  # the same layer with the backward's two kernels overlapped on two streams
             saf.saf_set_backward_overlap(1)
             to = time_steps(torch, layer, max(5, args.steps // 3), 2)
             saf.saf_set_backward_overlap(0)
             var["backward_overlap"] = {"ms_per_step": round(to * 1e3, 4),
                                        "tokens_per_s": round(tokens / to, 1)}
-        var["mixed_speedup_vs_all_ordinary"] = round(var["all_ordinary"]["ms_per_step"] / (t_step * 1e3), 4)
-        var["replaced_vs_ordinary_time_per_head"] = round(
-            var["all_replaced"]["ms_per_step"] / var["all_ordinary"]["ms_per_step"], 4)
         out["variants"] = var
+
+    if not args.no_configs and args.configs:
+        out["configs"] = {name: config_line(torch, saf, name, dev, max(5, args.steps // 2))
+                          for name in args.configs.split(",") if name and name != w.name}
 
     if not args.no_pattern_grad:
         pg = pattern_gradient(torch, saf, layer, max(5, args.steps // 3))

@@ -108,20 +108,23 @@ class LayerInputs:
 
 
 def layer_inputs(B, H, T, d, dtype, replaced, ar_std=0.5, seed=SEED0, backward=True,
-                 pat_len=None, device="cpu", Hkv=None):
+                 pat_len=None, device="cpu", Hkv=None, draw_on=None):
     """Draw Q, K, V, dO ~ N(0,1) (Q, dO [B,H,T,d]; K, V [B,Hkv,T,d], Hkv = H unless given; then
     cast to dtype) and a, r ~ N(0, ar_std^2) ([H, pat_len] fp32), in that order, from a CPU
-    generator seeded with `seed`."""
-    g = torch.Generator().manual_seed(seed)
+    generator seeded with `seed` (the values the oracle checks see).  draw_on="cuda" draws them
+    with a generator on the GPU instead: the same distributions, other values, and no host work
+    (for timing runs of large shapes)."""
+    gdev = "cpu" if draw_on is None else draw_on
+    g = torch.Generator(device=gdev).manual_seed(seed)
     P = T if pat_len is None else pat_len
     shape = (B, H, T, d)
     kvshape = (B, H if Hkv is None else Hkv, T, d)
-    q = torch.randn(shape, generator=g).to(dtype)
-    k = torch.randn(kvshape, generator=g).to(dtype)
-    v = torch.randn(kvshape, generator=g).to(dtype)
-    dout = torch.randn(shape, generator=g).to(dtype) if backward else None
-    a = torch.randn((H, P), generator=g) * ar_std
-    r = torch.randn((H, P), generator=g) * ar_std
+    q = torch.randn(shape, generator=g, device=gdev).to(dtype)
+    k = torch.randn(kvshape, generator=g, device=gdev).to(dtype)
+    v = torch.randn(kvshape, generator=g, device=gdev).to(dtype)
+    dout = torch.randn(shape, generator=g, device=gdev).to(dtype) if backward else None
+    a = torch.randn((H, P), generator=g, device=gdev) * ar_std
+    r = torch.randn((H, P), generator=g, device=gdev) * ar_std
     out = LayerInputs(q, k, v, dout, a.float(), r.float(), list(replaced))
     if device != "cpu":
         for name in ("q", "k", "v", "dout", "a", "r"):
