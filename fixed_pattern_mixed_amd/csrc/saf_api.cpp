@@ -712,12 +712,15 @@ saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q
   ca.svar = svar;
   ca.skl = skl;
   const size_t tiles = calib_tiles(T, &ca.n_qt, &ca.n_kt);
+  ca.n_ag = saf::calib_groups(ca.n_qt);
   ca.klp = reinterpret_cast<double*>(reinterpret_cast<char*>(ca.m2) + align_up(sizeof(double) * (size_t)H * tiles));
   const bool bf = dt == SAF_BF16;
   hipError_t e = traced("calib_lse", stream, [&] { return saf::launch_calib_lse(ca, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "calibration statistics launch");
   e = traced("calib_stats", stream, [&] { return saf::launch_calib_stats(ca, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "calibration tile launch");
+  e = traced("calib_zero", stream, [&] { return saf::launch_calib_zero(ca, stream); });
+  if (e != hipSuccess) return hip_fail(e, "calibration zero-fill launch");
   e = traced("calib_reduce", stream, [&] { return saf::launch_calib_reduce(ca, stream); });
   if (e != hipSuccess) return hip_fail(e, "calibration reduction launch");
   return SAF_OK;

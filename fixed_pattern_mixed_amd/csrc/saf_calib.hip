@@ -8,16 +8,22 @@
 //
 //   calib_lse    : per (sequence, head, 256-query block) the base-2 log-sum-exp of the scaled
 //                  causal scores of every row (an online sum over key tiles relative to a lazily
-//                  updated reference maximum).
-//   calib_stats  : per (head, 128-query tile I, 64-key tile J): for n = 1..N re-form the score tile
-//                  on the matrix cores, A = exp2(s' S - lse2), and update a per-element running mean
-//                  and sum of squared deviations (Welford) held in registers.  The tile then writes
-//                  its block of Ahat and one fp64 partial sum of squared deviations.  Tiles above
-//                  the diagonal write zeros.
+//                  updated reference maximum).  The query blocks of one (sequence, head) run one
+//                  after another on one XCD (blockIdx % 8), so each key tile leaves HBM once per
+//                  slice and the later blocks find it in that XCD's L2.
+//   calib_stats  : per (head, 128-query tile I, 64-key tile J) on or below the diagonal: for
+//                  n = 1..N re-form the score tile on the matrix cores, A = exp2(s' S - lse2), and
+//                  update a per-element running mean and sum of squared deviations (Welford) held
+//                  in registers.  The tile then writes its block of Ahat and one fp64 partial sum
+//                  of squared deviations.  Tiles are scheduled in groups of 8 x 16 (1024 queries x
+//                  1024 keys), a group's 128 tiles together on one XCD: they sweep n side by side,
+//                  so each sequence's 8 query tiles and 16 key tiles of the group are read from HBM
+//                  once and shared through that XCD's L2.
 //                  With the forward-KL score requested, the tile also sums A log A over the N
 //                  sequences and subtracts N Ahat log Ahat of the finished mean: per entry this is
 //                  sum_n A^(n) log(A^(n) / Ahat), since sum_n A^(n) = N Ahat ([Notes §二.1] names a
 //                  row-wise forward-KL selector; its terms summed over a row are KL(A^(n)_i || Ahat_i)).
+//   calib_zero   : the zeros of Ahat right of the diagonal tiles (a plain fill, no memset node).
 //   calib_reduce : per head, the fixed-order fp64 sum of the partials -> s_var, and the KL score
 //                  sum / (N T) (deterministic).
 #include <type_traits>
@@ -46,12 +52,13 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
 
   const int T = p.T;
   const int NH = p.N * p.H;
-  const int NHp = (NH + 7) & ~7;
   const int nqb = (T + kBQ - 1) / kBQ;
+  // slice nh runs on XCD nh % 8, its query blocks consecutively there (heaviest first)
   const int x = blockIdx.x;
-  const int nh = x % NHp;
+  const int k = x >> 3;
+  const int nh = (k / nqb) * 8 + (x & 7);
   if (nh >= NH) return;
-  const int qb = nqb - 1 - x / NHp;
+  const int qb = nqb - 1 - k % nqb;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int q0 = qb * kBQ, qw = q0 + 32 * w, qi = qw + l32;
@@ -149,28 +156,31 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
 
   const int T = p.T, H = p.H, N = p.N;
   const int tiles = p.n_qt * p.n_kt;
+  // Block x runs on XCD c = x % 8; that XCD's k-th block (k = x / 8) is tile k % 128 of group
+  // slot k / 128, the group g = slot * 8 + c of the list of groups on or below the diagonal
+  // (head-major, then group rows gi, then group columns gj <= gi).
+  constexpr int GT = kCalibGroupQ * kCalibGroupK;
   const int x = blockIdx.x;
-  const int h = x / tiles;
-  const int tile = x % tiles;
-  const int I = tile / p.n_kt, J = tile % p.n_kt;
+  const int kx = x >> 3;
+  const int g = (kx / GT) * 8 + (x & 7);
+  if (g >= H * p.n_ag) return;
+  const int h = g / p.n_ag;
+  const int rg = g % p.n_ag;  // gi (gi + 1) / 2 + gj
+  int gi = (int)((sqrtf(8.f * (float)rg + 1.f) - 1.f) * 0.5f);
+  while ((gi + 1) * (gi + 2) / 2 <= rg) ++gi;
+  while (gi * (gi + 1) / 2 > rg) --gi;
+  const int gj = rg - gi * (gi + 1) / 2;
+  const int t = kx % GT;
+  const int I = gi * kCalibGroupQ + t / kCalibGroupK, J = gj * kCalibGroupK + t % kCalibGroupK;
+  if (I >= p.n_qt || J >= p.n_kt) return;
+  const int tile = I * p.n_kt + J;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int q0 = I * kBQ, k0 = J * kBK;
   const int qw = q0 + 32 * w, qi = qw + l32;
   float* A = p.ahat + (size_t)h * T * T;
   const bool vec4 = (T & 3) == 0;
-
-  if (k0 > q0 + kBQ - 1) {  // entirely above the diagonal: zeros
-    for (int e = tid; e < kBQ * kBK; e += kNT) {
-      const int qq = q0 + e / kBK, kk = k0 + e % kBK;
-      if (qq < T && kk < T) A[(size_t)qq * T + kk] = 0.f;
-    }
-    if (tid == 0) {
-      p.m2[(size_t)h * tiles + tile] = 0.0;
-      if (KL) p.klp[(size_t)h * tiles + tile] = 0.0;
-    }
-    return;
-  }
+  if (k0 > q0 + kBQ - 1) return;  // entirely above the diagonal: calib_zero writes its zeros
 
   float mean[NS][16], m2[NS][16];
 #pragma unroll
@@ -301,6 +311,33 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
   }
 }
 
+// Zeros of Ahat right of the diagonal tiles: in the rows of query tile I, the columns from
+// kBQ (I + 1) on (the key tiles J with J kBK > I kBQ + kBQ - 1, which calib_stats skips).  One block
+// per (head, query tile).
+__global__ __launch_bounds__(kNT) void calib_zero_kernel(CalibArgs p) {
+  const int T = p.T;
+  const int h = blockIdx.x / p.n_qt, I = blockIdx.x % p.n_qt;
+  const int c0 = (I + 1) * kBQ;
+  if (c0 >= T) return;
+  const int r0 = I * kBQ, nr = min(kBQ, T - r0);
+  float* A = p.ahat + (size_t)h * T * T + (size_t)r0 * T;
+  if ((T & 3) == 0) {  // rows and c0 are 16-byte aligned
+    const int w4 = (T - c0) >> 2;
+    const long long n = (long long)nr * w4;
+    for (long long e = threadIdx.x; e < n; e += kNT) {
+      const int r = (int)(e / w4), c = c0 + 4 * (int)(e % w4);
+      *reinterpret_cast<float4*>(A + (size_t)r * T + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+    const int w1 = T - c0;
+    const long long n = (long long)nr * w1;
+    for (long long e = threadIdx.x; e < n; e += kNT) {
+      const int r = (int)(e / w1), c = c0 + (int)(e % w1);
+      A[(size_t)r * T + c] = 0.f;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kNT) void calib_reduce_kernel(CalibArgs p) {
   __shared__ double red[kNT], redk[kNT];
   const int h = blockIdx.x;
@@ -308,6 +345,8 @@ __global__ __launch_bounds__(kNT) void calib_reduce_kernel(CalibArgs p) {
   const bool kl = p.skl != nullptr;
   double acc = 0.0, acck = 0.0;
   for (int i = threadIdx.x; i < tiles; i += kNT) {
+    const int I = i / p.n_kt, J = i % p.n_kt;
+    if (J * kBK > I * kBQ + kBQ - 1) continue;  // above the diagonal: no partial (all zeros)
     acc += p.m2[(size_t)h * tiles + i];
     if (kl) acck += p.klp[(size_t)h * tiles + i];
   }
@@ -331,7 +370,7 @@ __global__ __launch_bounds__(kNT) void calib_reduce_kernel(CalibArgs p) {
 template <typename TI, int D>
 hipError_t launch_lse_t(const CalibArgs& a, hipStream_t s) {
   constexpr int W = SAF_LSE_WAVES;
-  const int NHp = (a.N * a.H + 7) & ~7;
+  const int NHp = (a.N * a.H + 7) & ~7;  // slices per XCD x 8
   const long long blocks = (long long)NHp * ((a.T + 32 * W - 1) / (32 * W));
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((calib_lse_kernel<TI, D, W>), dim3((unsigned)blocks), dim3(64 * W), 0, s, a);
@@ -340,7 +379,8 @@ hipError_t launch_lse_t(const CalibArgs& a, hipStream_t s) {
 
 template <typename TI, int D>
 hipError_t launch_stats_t(const CalibArgs& a, hipStream_t s) {
-  const long long blocks = (long long)a.H * a.n_qt * a.n_kt;
+  const long long groups = (long long)a.H * a.n_ag;
+  const long long blocks = (groups + 7) / 8 * 8 * (kCalibGroupQ * kCalibGroupK);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.skl)
     hipLaunchKernelGGL((calib_stats_kernel<TI, D, true>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
@@ -358,6 +398,12 @@ hipError_t launch_calib_lse(const CalibArgs& a, bool bf16_in, hipStream_t s) {
 hipError_t launch_calib_stats(const CalibArgs& a, bool bf16_in, hipStream_t s) {
   if (bf16_in) return a.d == 64 ? launch_stats_t<bf16, 64>(a, s) : launch_stats_t<bf16, 128>(a, s);
   return a.d == 64 ? launch_stats_t<float, 64>(a, s) : launch_stats_t<float, 128>(a, s);
+}
+hipError_t launch_calib_zero(const CalibArgs& a, hipStream_t s) {
+  const long long blocks = (long long)a.H * a.n_qt;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(calib_zero_kernel, dim3((unsigned)blocks), dim3(kNT), 0, s, a);
+  return hipGetLastError();
 }
 hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(calib_reduce_kernel, dim3(a.H), dim3(kNT), 0, s, a);

@@ -105,6 +105,7 @@ struct CalibArgs {
   double* svar;      // [H]
   double* skl;       // [H] or nullptr: forward-KL score
   int n_qt, n_kt;    // query / key tile counts of the statistics grid
+  int n_ag;          // statistics tile groups on or below the diagonal, per head (calib_groups)
 };
 
 // The replaced heads of a call, in head order (kernels map a compact index to the head).
@@ -175,6 +176,7 @@ hipError_t launch_fit_step(const FitArgs& a, double lr, double c1, double c2, hi
 hipError_t launch_fit_final(const FitArgs& a, hipStream_t s);
 hipError_t launch_calib_lse(const CalibArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_calib_stats(const CalibArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_calib_zero(const CalibArgs& a, hipStream_t s);
 hipError_t launch_calib_reduce(const CalibArgs& a, hipStream_t s);
 
 // Tile geometry shared by the host (workspace sizing) and the kernels.
@@ -187,6 +189,16 @@ constexpr int kCalibQTile = 32 * kCalibWaves;    // queries per calibration stat
 #define SAF_CALIB_KTILE 64
 #endif
 constexpr int kCalibKTile = SAF_CALIB_KTILE;  // keys per calibration statistics tile
+// Statistics tiles are scheduled in square groups of kCalibGroupQ x kCalibGroupK tiles (1024 queries x
+// 1024 keys), one group per XCD at a time (see calib_stats).
+constexpr int kCalibGroupQ = 8;
+constexpr int kCalibGroupK = kCalibGroupQ * kCalibQTile / kCalibKTile;
+static_assert(kCalibGroupK * kCalibKTile == kCalibGroupQ * kCalibQTile, "square tile groups");
+// groups of one head on or below the diagonal: gi(gi+1)/2 summed over the nqt / kCalibGroupQ rows
+__host__ __device__ inline int calib_groups(int n_qt) {
+  const int gi = (n_qt + kCalibGroupQ - 1) / kCalibGroupQ;
+  return gi * (gi + 1) / 2;
+}
 
 __host__ __device__ inline bool is_replaced(const uint64_t* rep, int h) { return (rep[h >> 6] >> (h & 63)) & 1ull; }
 
