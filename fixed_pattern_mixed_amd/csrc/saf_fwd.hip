@@ -149,6 +149,10 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   for (int c = 0; c < D / 32; ++c) zero(oacc[c]);
   float m = -INFINITY, l = 0.f;  // running maximum of the row (log2 units) and row sum
   const float c2 = p.scale_log2;
+  int k_base = 0;  // first key of the tile being multiplied
+  // bf16 at d = 128 has the registers for a second score block (two waves per SIMD either way);
+  // at d = 64 the items run four waves per SIMD in 128 registers, which it would not fit
+  constexpr bool kPipe = C::BF && D == 128 && W == 8;
 
   // probabilities 2^(s*log2(e)*x - mx) of a subtile's (masked) scores as operand fragments;
   // returns the lane's sum of them as rounded for the product
@@ -172,14 +176,90 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
           mma16(oacc[c], tt_frag<TI, LDT>(sm.VT, 32 * s + 16 * u, 32 * c + l32, hi), pf[u]);
   };
 
+  // Ordinary subtile s: the score product S^T = K Q^T into st ...
+  auto score = [&](int s, f32x16& st) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      mma16(st, load8(sm.Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+  };
+  // ... then (masked where it crosses the diagonal or the end) the probabilities and O^T += V^T P^T.
+  // Lazy maximum: the probabilities are taken with the running maximum m and kept while none
+  // exceeds 2^8, which the lane's sum of them (at most 256 then) shows without a maximum over the
+  // subtile.  Otherwise (rare after the first subtile, and always on it, where m is still -inf and
+  // the sum inf or NaN) m moves to the row maximum, O and l are rescaled and the subtile is redone.
+  auto finish = [&](int s, f32x16& st, bool masked) {
+    if (masked) {
+      const int ks = k_base + 32 * s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = ks + crow(r, hi);
+        st[r] = (key <= qi && key < T) ? st[r] : -INFINITY;
+      }
+    }
+    Frag<TI> pf[2];
+    float ls = probs_at(st, m, pf);
+    if (__any(!(ls <= 256.f))) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
+      const float mnew = fmaxf(m, half_max(tmax) * c2);
+      const float alpha = exp2f(m - mnew);  // 0 on the first subtile (m = -inf)
+      l *= alpha;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
+      m = mnew;
+      ls = probs_at(st, m, pf);
+    }
+    l += ls;
+    accumulate(s, pf);
+  };
+
+  // Scheduling groups of one pipelined block: 8 P V products (two transposing LDS reads each) and 8
+  // score products (one 16-byte LDS read each), each followed by three vector instructions.
+  auto interleave_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // vector
+    }
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  };
+
   load_tile(0);
   store_tile(0);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BK;
+    k_base = k0;
     if (kt + 1 < nkt) load_tile(k0 + BK);
 
+    if (kPipe && ORD && k0 + BK - 1 <= qw && k0 + BK <= T) {
+      // Every subtile of the tile is visible to all of the wave's queries (most tiles): no masks,
+      // and subtile s+1's score product is issued before subtile s's softmax and P V product, so
+      // that the matrix cores form the next scores while the vector units turn the current ones
+      // into probabilities (one wave overlaps the two; the straight-line code keeps them in one
+      // basic block for the scheduler).
+      f32x16 sc[2];
+      score(0, sc[0]);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s + 1 < NS) score(s + 1, sc[(s + 1) & 1]);
+        // From here to the softmax's branch the block holds subtile s-1's P V product, subtile
+        // s+1's score product and subtile s's probabilities, none waiting on another: interleave
+        // each matrix instruction (and the LDS reads of its operand) with vector work.
+        if (s >= 1) interleave_block();
+        finish(s, sc[s & 1], false);
+      }
+    } else {
     // 32-key subtiles visible to this wave, one at a time: scores -> probabilities -> O^T += V^T P^T
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -187,39 +267,8 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
       if (ks > qw + 31 || ks >= T) break;  // wave-uniform: the rest of the tile is masked out
       if (ORD) {
         f32x16 st;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-          mma16(st, load8(sm.Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
-        if ((ks + 31 > qw) || (ks + 31 >= T)) {  // subtile crosses the diagonal or the end
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = ks + crow(r, hi);
-            st[r] = (key <= qi && key < T) ? st[r] : -INFINITY;
-          }
-        }
-        // Lazy maximum: the probabilities are taken with the running maximum m and kept while
-        // none exceeds 2^8, which the lane's sum of them (at most 256 then) shows without a
-        // maximum over the subtile.  Otherwise (rare after the first subtile, and always on it,
-        // where m is still -inf and the sum inf or NaN) m moves to the row maximum, O and l are
-        // rescaled and the subtile is redone.
-        Frag<TI> pf[2];
-        float ls = probs_at(st, m, pf);
-        if (__any(!(ls <= 256.f))) {
-          float tmax = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[r]);
-          const float mnew = fmaxf(m, half_max(tmax) * c2);
-          const float alpha = exp2f(m - mnew);  // 0 on the first subtile (m = -inf)
-          l *= alpha;
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
-          m = mnew;
-          ls = probs_at(st, m, pf);
-        }
-        l += ls;
-        accumulate(s, pf);
+        score(s, st);
+        finish(s, st, (ks + 31 > qw) || (ks + 31 >= T));
       } else {
         float pv[16];
 #pragma unroll
@@ -238,6 +287,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
         l += frag_sum(pf[0]) + frag_sum(pf[1]);
         accumulate(s, pf);
       }
+    }
     }
 
     __syncthreads();
