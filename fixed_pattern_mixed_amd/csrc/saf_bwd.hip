@@ -25,6 +25,9 @@
 //             the zero dQ rows of their keys.  With grouped heads (several query heads per key /
 //             value head) the item sweeps each query head of its group in turn and dK, dV are the
 //             sums over the group; dK is zero when every head of the group is replaced.
+//             bf16 at d = 128 runs the wide variant instead: 8 waves, two per SIMD, K and V staged
+//             transposed in LDS rather than held in registers, two waves per 32 keys (one per
+//             32-query half of a tile), Q / dO tiles double-buffered.
 //   bwd_dq  : one work item per (batch, ordinary head, 32-query block per wave), lane = query: S^T = K Q^T,
 //             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal
 //             (bf16: K^T fragments by transposing reads of the K row tile; fp32: K is also staged
@@ -424,6 +427,287 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
     }
 }
 
+// ----------------------------------------------------------------------------- bwd_kv, wide
+// bf16 at d = 128.  Holding a wave's K and V fragments (64 registers) next to its dK, dV accumulators
+// (128) leaves one wave per SIMD, which then waits on every dependency of its own chain.  Here the
+// item's K and V blocks are staged once, transposed, in LDS (kt_off tiles; their fragments are
+// transposing reads, the fast LDS read), so a wave fits the 256 registers of two waves per SIMD:
+// 8 waves, where waves w and w + 4 own the same 32 keys and take the two 32-query halves of each
+// 64-query tile; their partial dK, dV are added through LDS at the end (a fixed order: the sums
+// stay bitwise repeatable).  Q and dO tiles are double-buffered (one barrier per tile).
+namespace wide {
+constexpr int NW = 8, NT = 64 * NW, D = 128, BKV = 128, BQ = 64, WIN = BQ + BKV;
+constexpr int TILE = BQ * TileGeom<D>::LDR;  // elements of one Q or dO tile
+constexpr int OFF_KT = 0, OFF_VT = OFF_KT + kKT * kKT * 2, OFF_Q = OFF_VT + kKT * kKT * 2;
+constexpr int OFF_G = OFF_Q + 2 * TILE * 2, OFF_RS = OFF_G + 2 * TILE * 2;
+constexpr int OFF_DL = OFF_RS + 2 * BQ * 4, OFF_RW = OFF_DL + 2 * BQ * 4;
+constexpr int SMEM = OFF_RW + 2 * WIN * 4;
+constexpr int RED = 2 * 4 * 16 * 64 * 16;  // partial sums: [dV | dK][key group][16 float4][lane]
+static_assert(RED <= SMEM && SMEM <= 160 * 1024, "LDS budget");
+static_assert(BKV == kKT && D == kKT, "one transposed tile per key block");
+}  // namespace wide
+
+template <bool GROUPED>
+__global__ __launch_bounds__(wide::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_kv_wide_kernel(LayerArgs p) {
+  using namespace wide;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  bf16* KTs = reinterpret_cast<bf16*>(smem + OFF_KT);  // K^T [dim][key] (kt_off)
+  bf16* VTs = reinterpret_cast<bf16*>(smem + OFF_VT);  // V^T
+  bf16* Qs = reinterpret_cast<bf16*>(smem + OFF_Q);    // [2][TILE] Q tiles (tile_off, swizzled)
+  bf16* Gs = reinterpret_cast<bf16*>(smem + OFF_G);    // [2][TILE] dO tiles
+  float* rss = reinterpret_cast<float*>(smem + OFF_RS);  // [2][BQ] row statistic per query
+  float* dls = reinterpret_cast<float*>(smem + OFF_DL);  // [2][BQ] -delta per query
+  float* rwin = reinterpret_cast<float*>(smem + OFF_RW);  // [2][WIN] replaced: distance window
+
+  const int T = p.T, H = p.H, Hkv = p.Hkv;
+  const int GS = GROUPED ? H / Hkv : 1;
+  const int BH = p.B * Hkv;
+  const int BHp = (BH + 7) & ~7;
+  const int x = blockIdx.x;
+  const int bh = x % BHp;
+  if (bh >= BH) return;
+  const int kb = x / BHp;  // low key blocks see the most query tiles: heaviest first
+  int b, hk;
+  p.kvord.slice(bh, p.B, b, hk);
+  bool any_ord = false;
+  for (int m = 0; m < GS; ++m) any_ord |= !is_replaced(p.rep, hk * GS + m);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kg = w & 3, qh = w >> 2;  // the wave's key group (32 keys) and query half
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int kb0 = kb * BKV;
+  const int kw = kb0 + 32 * kg;  // the wave's first key
+  const int kj = kw + l32;       // the lane's key
+  const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)T * D;
+  const bf16* K = reinterpret_cast<const bf16*>(p.k) + kvoff;
+  const bf16* V = reinterpret_cast<const bf16*>(p.v) + kvoff;
+  const float c2 = p.scale_log2;
+
+  // K^T, V^T: thread chunk idx = key idx % 128, dimensions 8 (idx / 128) .. +7; keys past the end
+  // are zero
+  if (any_ord) {
+#pragma unroll
+    for (int c = 0; c < BKV * D / 8 / NT; ++c) {
+      const int idx = tid + c * NT;
+      const int key = idx & (BKV - 1), d0 = 8 * (idx >> 7);
+      const bool in = kb0 + key < T;
+      const size_t src = (size_t)(kb0 + key) * D + d0;
+      const bf16x8 kv = in ? *reinterpret_cast<const bf16x8*>(K + src) : bf16x8{};
+      const bf16x8 vv = in ? *reinterpret_cast<const bf16x8*>(V + src) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        KTs[kt_off(d0 + e, key)] = kv[e];
+        VTs[kt_off(d0 + e, key)] = vv[e];
+      }
+    }
+  }
+
+  const TileLane<D, true> tl(lane);  // lane bases of the swizzled Q / dO tiles
+  const KtLane ktl(lane, kg);        // lane base of the K^T / V^T fragments of the wave's keys
+
+  f32x16 dvT[D / 32], dkT[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    zero(dvT[c]);
+    zero(dkT[c]);
+  }
+  float vs = 1.f;  // product form, one query head per key/value head: ea[j] applied to the dV row
+
+  const int nqt = (T + BQ - 1) / BQ;
+  const int qt0 = kb0 / BQ;
+  for (int m = 0; m < GS; ++m) {
+    const int h = hk * GS + m;
+    const bool rep = is_replaced(p.rep, h);
+    const bool fact = rep && p.pat.flag(h)[0] != 0;
+    const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+    const size_t soff = ((size_t)b * H + h) * (size_t)T;
+    const bf16* Q = reinterpret_cast<const bf16*>(p.q) + hoff;
+    const bf16* G = reinterpret_cast<const bf16*>(p.dout) + hoff;
+    const float* lse = p.lse + soff;
+    const float* dlt = p.delta + soff;
+    const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
+    const float wscale = fact ? 1.f : kLog2e;
+    const float wfill = fact ? 0.f : -INFINITY;
+    const float shift = fact ? p.pat.shift(h) : 0.f;
+    float akey = 0.f;  // replaced: the lane's key preference (ea, or a*log2e)
+    if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
+    const bool fold = fact && GS > 1;  // the key factor enters each entry
+    if (fact && GS == 1) vs = akey;
+
+    // prefetch registers hold raw loads (clamped addresses); masks and conversions at the store
+    Chunks<bf16, D, BQ, NT> pq, pg;
+    float prs = 0.f, pdl = 0.f, prw = 0.f;
+    auto load_tile = [&](int q0) {
+      pg.load(G, q0, T, tid);
+      if (!rep) pq.load(Q, q0, T, tid);
+      if (tid < BQ) {
+        const int q = min(q0 + tid, T - 1);
+        prs = lse[q];
+        pdl = dlt[q];
+      }
+      if (rep && tid < WIN) prw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
+    };
+    auto store_tile = [&](int buf, int q0) {
+      pg.template store_tile<true>(Gs + buf * TILE, tid);
+      if (!rep) pq.template store_tile<true>(Qs + buf * TILE, tid);
+      if (tid < BQ) {
+        // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse);
+        // rows past the end get weight 0
+        const bool in = q0 + tid < T;
+        rss[buf * BQ + tid] = in ? (fact ? expf(shift - prs) : prs * kLog2e) : (fact ? 0.f : INFINITY);
+        dls[buf * BQ + tid] = (!rep && in) ? -pdl : 0.f;
+      }
+      if (rep && tid < WIN) {
+        const int dist = q0 - (kb0 + BKV - 1) + tid;
+        rwin[buf * WIN + tid] = (dist >= 0 && dist < T) ? prw * wscale : wfill;
+      }
+    };
+
+    load_tile(qt0 * BQ);
+    store_tile(0, qt0 * BQ);
+    if (qt0 + 1 < nqt) load_tile((qt0 + 1) * BQ);
+    __syncthreads();  // also orders the K^T / V^T stores before the first reads
+
+    for (int qt = qt0; qt < nqt; ++qt) {
+      const int buf = (qt - qt0) & 1;
+      const int q0 = qt * BQ;
+      const int qs = q0 + 32 * qh;  // the wave's first query
+      const bf16* Qb = Qs + buf * TILE;
+      const bf16* Gb = Gs + buf * TILE;
+      const float* rsb = rss + buf * BQ + 32 * qh;
+      const float* dlb = dls + buf * BQ + 32 * qh;
+      if (qs + 31 >= kw && qs < T && kw < T) {  // wave-uniform: something visible
+        // P (and dS = P o (dP - delta)) of the subtile as operand fragments of its two k16 steps:
+        // only fragments, not 32 fp32 entries, are live where the head kinds' branches meet
+        Frag<bf16> pf[2], sf[2];
+        if (!rep) {
+          // S = Q K^T and dP = dO V^T (-delta is added per entry: as the products' initial value it
+          // would hold 16 more registers through them)
+          f32x16 st, dpt;
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t) {
+            mma16(st, tile_row_frag<D, true>(Qb, 32 * qh, t, tl), kt_frag(KTs, t, ktl), t == 0);
+            mma16(dpt, tile_row_frag<D, true>(Gb, 32 * qh, t, tl), kt_frag(VTs, t, ktl), t == 0);
+          }
+          const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
+          auto entries = [&](auto masked) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              float pr[8], ds[8];
+#pragma unroll
+              for (int g2 = 0; g2 < 2; ++g2) {
+                const int g = 2 * u + g2;
+                const float4 l4 = *reinterpret_cast<const float4*>(rsb + 8 * g + 4 * hi);
+                const float4 n4 = *reinterpret_cast<const float4*>(dlb + 8 * g + 4 * hi);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, nd[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int r = 4 * g + e;
+                  float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
+                  if constexpr (decltype(masked)::value) {
+                    const int q = qs + 8 * g + 4 * hi + e;
+                    pp = ((q >= kj) & (q < T) & (kj < T)) ? pp : 0.f;
+                  }
+                  pr[4 * g2 + e] = pp;
+                  ds[4 * g2 + e] = pp * (dpt[r] + nd[e]);
+                }
+              }
+              pf[u] = to_frag<bf16>(pr);
+              sf[u] = to_frag<bf16>(ds);
+            }
+          };
+          if (edge)
+            entries(std::true_type{});
+          else
+            entries(std::false_type{});
+        } else {
+          const float* rwb = rwin + buf * WIN;
+          auto rep_entries = [&](auto fact_c) {
+            constexpr bool kFact = decltype(fact_c)::value;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              float pr[8];
+#pragma unroll
+              for (int g2 = 0; g2 < 2; ++g2) {
+                const int g = 2 * u + g2;
+                const int qr = 32 * qh + 8 * g + 4 * hi;  // tile row of register group g
+                const float4 l4 = *reinterpret_cast<const float4*>(rsb + 8 * g + 4 * hi);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float rv = rwb[xr + e];
+                  float pp = kFact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
+                  if (kFact && fold) pp *= akey;
+                  pr[4 * g2 + e] = pp;
+                }
+              }
+              pf[u] = to_frag<bf16>(pr);
+            }
+          };
+          if (fact)
+            rep_entries(std::true_type{});
+          else
+            rep_entries(std::false_type{});
+        }
+        // dV^T[dcol][key] += dO^T[dcol][q] P[q][key];  dK^T[dim][key] += Q^T[dim][q] dS[q][key]
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c)
+            mma16(dvT[c], tile_tr_frag<D, true>(Gb, 32 * qh + 16 * u, c, tl), pf[u]);
+          if (!rep) {
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c)
+              mma16(dkT[c], tile_tr_frag<D, true>(Qb, 32 * qh + 16 * u, c, tl), sf[u]);
+          }
+        }
+      }
+      if (qt + 1 < nqt) {
+        store_tile(buf ^ 1, q0 + BQ);  // that buffer's readers passed the previous barrier
+        if (qt + 2 < nqt) load_tile(q0 + 2 * BQ);
+      }
+      __syncthreads();
+    }
+    if (rep && qh == 0 && kj < T) {  // a replaced head's query gradient is zero
+      bf16* dQ = reinterpret_cast<bf16*>(p.dq) + hoff + (size_t)kj * D;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
+    }
+  }
+
+  // The two query halves' partial sums: half 1 hands over its dV, half 0 its dK (the tiles are no
+  // longer read: the sweep ended with a barrier); each half then finishes one of the two.
+  float4* red = reinterpret_cast<float4*>(smem);
+  {
+    const f32x16* give = qh ? dvT : dkT;
+    float4* dst = red + ((qh ? 0 : 4) + kg) * 16 * 64 + lane;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        dst[(4 * c + g) * 64] = make_float4(give[c][4 * g], give[c][4 * g + 1], give[c][4 * g + 2],
+                                            give[c][4 * g + 3]);
+  }
+  __syncthreads();
+  if (kj >= T) return;
+  f32x16* keep = qh ? dkT : dvT;
+  const float4* src = red + ((qh ? 4 : 0) + kg) * 16 * 64 + lane;
+  const float sc = qh ? (any_ord ? p.scale : 0.f) : vs;
+  bf16* out = reinterpret_cast<bf16*>(qh ? p.dk : p.dv) + kvoff + (size_t)kj * D;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 o = src[(4 * c + g) * 64];
+      store4(out + 32 * c + 8 * g + 4 * hi, (keep[c][4 * g] + o.x) * sc, (keep[c][4 * g + 1] + o.y) * sc,
+             (keep[c][4 * g + 2] + o.z) * sc, (keep[c][4 * g + 3] + o.w) * sc);
+    }
+}
+
 // ------------------------------------------------------------------------------------ bwd_dq
 #ifndef SAF_DQ_WAVES
 #define SAF_DQ_WAVES 0  // 0: by shape (below)
@@ -631,9 +915,21 @@ hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef SAF_KV_WIDE
+#define SAF_KV_WIDE 1  // bf16 at d = 128: the 8-wave kernel (0: the 4-wave one)
+#endif
 template <typename TI, int D>
 hipError_t launch_kv_t(const LayerArgs& a, hipStream_t s) {
   const int BHp = (a.B * a.Hkv + 7) & ~7;
+  if constexpr (sizeof(TI) == 2 && D == 128 && SAF_KV_WIDE) {
+    const long long blocks = (long long)BHp * ((a.T + wide::BKV - 1) / wide::BKV);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (a.Hkv == a.H)
+      hipLaunchKernelGGL((bwd_kv_wide_kernel<false>), dim3((unsigned)blocks), dim3(wide::NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_kv_wide_kernel<true>), dim3((unsigned)blocks), dim3(wide::NT), 0, s, a);
+    return hipGetLastError();
+  }
   const long long blocks = (long long)BHp * ((a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.Hkv == a.H)

@@ -227,6 +227,37 @@ __device__ __forceinline__ Frag<bf16> tile_tr_frag(const bf16* tile, int row0, i
   return f;
 }
 
+// ---- [dimension][key] tiles: a key block stored transposed ------------------------------------
+// A 128 x 128 bf16 tile (row = dimension, column = key) with unpadded rows; the 32-column block of an
+// element is XORed with the low two bits of its row, so that the four rows a transposing read
+// serves in one pass fall on four disjoint 16-bank segments.
+constexpr int kKT = 128;
+__host__ __device__ __forceinline__ int kt_off(int r, int c) {
+  return r * kKT + ((((c >> 5) ^ r) & 3) << 5) + (c & 31);
+}
+// B-operand fragment of column 32 cb + (lane & 31) over contraction rows 16 t + 8 hi + e, in natural
+// order (the order of a row fragment of the other operand), by two transposing reads: lane 4j + a of
+// a 16-lane group addresses row 8 hi + j, columns 4a .. 4a+3 of the group's 16, so lane i receives
+// column i of rows 8 hi + 0..3 (first read) and, 4 rows on, 8 hi + 4..7 (second).  Rows 16 t + 4 s
+// further on keep the XOR (a multiple of 4 rows), so both reads are the lane's base plus a constant.
+struct KtLane {
+  int base;
+  __device__ __forceinline__ KtLane(int lane, int cb) {
+    const int hi = lane >> 5, i = lane & 15;
+    base = kt_off(8 * hi + (i >> 2), 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (i & 3));
+  }
+};
+__device__ __forceinline__ Frag<bf16> kt_frag(const bf16* tile, int t, const KtLane& L) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
+  typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+  const bf16* base = tile + L.base + 16 * t * kKT;
+  const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)base);
+  const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 4 * kKT));
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
 // 4 consecutive elements of one row (bf16: 8 bytes, fp32: 16 bytes)
 template <typename TI>
 struct Quad;

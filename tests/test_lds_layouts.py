@@ -196,3 +196,80 @@ def test_a_planted_address_mistake_is_caught():
     lo, hi = tr_addresses(d, True, 0, 0)
     frag = tr_read(hi, mem)[0] + tr_read(lo, mem)[0]
     assert [frag[e] for e in range(8)] != [(perm_row(e, 0), 0) for e in range(8)]
+
+
+# ---- [dimension][key] tiles (saf_device.h: kt_off, KtLane, kt_frag) -------------------------------
+KKT = 128
+
+
+def kt_off(r, c):
+    return r * KKT + ((((c >> 5) ^ r) & 3) << 5) + (c & 31)
+
+
+def kt_base(lane, cb):
+    hi, i = lane >> 5, lane & 15
+    return kt_off(8 * hi + (i >> 2), 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (i & 3))
+
+
+def kt_addresses(cb, t):
+    """Per-lane element addresses of kt_frag's two reads (rows +0..3 and +4..7 of 16t + 8hi)."""
+    lo = [kt_base(l, cb) + 16 * t * KKT for l in range(64)]
+    return lo, [a + 4 * KKT for a in lo]
+
+
+def kt_mem():
+    mem = [None] * (KKT * KKT)
+    for r, c in itertools.product(range(KKT), range(KKT)):
+        assert mem[kt_off(r, c)] is None  # one slot per element: the XOR is a bijection per row
+        mem[kt_off(r, c)] = (r, c)
+    return mem
+
+
+def test_kt_read_gives_the_natural_b_operand():
+    """Slot e of lane l: contraction row 16t + 8(l // 32) + e (the order of a row fragment of the
+    other operand), column 32 cb + l % 32."""
+    mem = kt_mem()
+    for cb, t in itertools.product(range(4), range(8)):
+        lo, hi = kt_addresses(cb, t)
+        for a in lo + hi:
+            assert 0 <= a and a + 3 < KKT * KKT and (2 * a) % 8 == 0
+        vlo, vhi = tr_read(lo, mem), tr_read(hi, mem)
+        for lane in range(64):
+            frag = vlo[lane] + vhi[lane]
+            assert frag == [(16 * t + 8 * (lane >> 5) + e, 32 * cb + (lane & 31)) for e in range(8)]
+
+
+def test_kt_read_is_free_of_bank_conflicts():
+    for cb, t in itertools.product(range(4), range(8)):
+        for addrs in kt_addresses(cb, t):
+            assert banks_max(addrs, 8, 32) == 1
+
+
+def test_kt_staging_writes():
+    """The staging of a key block: thread chunk idx -> key idx % 128, dimensions 8 (idx // 128) ..
+    +7, one 2-byte store each.  Every element is written once; a wave's 64 stores of one dimension
+    touch each 4-byte word at most twice (its two halves), so no two lanes meet on a bank with
+    different words."""
+    seen = set()
+    for idx in range(KKT * KKT // 8):
+        key, d0 = idx & 127, 8 * (idx >> 7)
+        for e in range(8):
+            a = kt_off(d0 + e, key)
+            assert a not in seen
+            seen.add(a)
+    assert len(seen) == KKT * KKT
+    for w0, e in itertools.product(range(0, KKT * KKT // 8, 64), range(8)):
+        words = {}
+        for idx in range(w0, w0 + 64):
+            a = kt_off(8 * (idx >> 7) + e, idx & 127)
+            words.setdefault((a // 2) % 64, set()).add(a // 2)
+        assert all(len(v) == 1 for v in words.values())
+
+
+def test_kt_without_the_xor_conflicts():
+    """Unpadded rows without the XOR: the four rows of a pass share one 16-bank segment."""
+    addrs = []
+    for lane in range(64):
+        hi, i = lane >> 5, lane & 15
+        addrs.append((8 * hi + (i >> 2)) * KKT + 16 * ((lane >> 4) & 1) + 4 * (i & 3))
+    assert banks_max(addrs, 8, 32) == 4
