@@ -393,10 +393,13 @@ def variants_of(torch, saf, w, dev, steps, layer_ms=None, draw_on=None):
     var = {}
     for label, rr in (("all_ordinary", [0] * w.H), ("all_replaced", [1] * w.H)):
         lv = Layer(saf, torch, w, rr, dev, draw_on=draw_on)
-        tv = time_steps(torch, lv, steps, 2)
+        trace = saf.KernelTrace(capacity=4 * (steps + 1))
+        tv = time_steps(torch, lv, steps, 2, trace)
         fv = total_flops(w.B, w.T, w.d, rr, w.backward)
         var[label] = {"ms_per_step": round(tv * 1e3, 4), "tflops": round(fv / tv / 1e12, 1),
-                      "pct_bf16_peak": round(100 * fv / tv / 1e12 / PEAK_BF16_TFLOPS, 2)}
+                      "pct_bf16_peak": round(100 * fv / tv / 1e12 / PEAK_BF16_TFLOPS, 2),
+                      "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in trace.summary().items()}}
+        trace.close()
         del lv
     if layer_ms is not None:
         var["mixed_speedup_vs_all_ordinary"] = round(var["all_ordinary"]["ms_per_step"] / layer_ms, 4)

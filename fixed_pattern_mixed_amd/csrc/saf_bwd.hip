@@ -82,6 +82,7 @@ struct KvCfg {
   static constexpr int LDP = D + 16 / (int)sizeof(TI);    // padded row of the Q / dO tiles
   static constexpr int LDT = BQ + 16 / (int)sizeof(TI);   // padded row of the transposed tiles
   static constexpr int WIN = BQ + BKV;                    // distance window of replaced items
+  static constexpr int WINP = win_pad(WIN);               // one of its 4 copies (win_store)
 };
 
 template <typename TI, int D>
@@ -108,7 +109,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   __shared__ __attribute__((aligned(16))) TI GT[kTr ? 8 : D * LDT];  // dO tile transposed [dcol][query]
   __shared__ __attribute__((aligned(16))) float rss[BQ];     // row statistic per query
   __shared__ __attribute__((aligned(16))) float dls[BQ];     // -delta per query
-  __shared__ float rwin[WIN];                                // replaced: er / r*log2e window
+  __shared__ __attribute__((aligned(16))) float rwin[4 * C::WINP];  // replaced: er / r*log2e window
 
   const int T = p.T, H = p.H, Hkv = p.Hkv;
   const int GS = GROUPED ? H / Hkv : 1;  // query heads per key/value head (Hkv = H unless grouped)
@@ -210,7 +211,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
       }
       if (rep && tid < WIN) {
         const int dist = q0 - (kb0 + BKV - 1) + tid;
-        rwin[tid] = (dist >= 0 && dist < T) ? pf.rw * wscale : wfill;
+        win_store(rwin, C::WINP, tid, (dist >= 0 && dist < T) ? pf.rw * wscale : wfill);
       }
     };
 
@@ -371,10 +372,13 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
               const int qr = 32 * s + 8 * g + 4 * hi;
               const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
               const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-              const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
+              // window entries xr .. xr+3 of distances (q0 + qr + e) - kj; xr = 3 - l32 mod 4
+              const int xr = qr + (kb0 + BKV - 1) - kj;
+              const float4 r4 = win_read4(win_base(rwin, C::WINP, (3 - l32) & 3), xr);
+              const float rw4[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float rv = rwin[xr + e];
+                const float rv = rw4[e];
                 float pp = kFact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
                 if (kFact && fold) pp *= akey;
                 pr[4 * g + e] = pp;
@@ -441,7 +445,8 @@ constexpr int TILE = BQ * TileGeom<D>::LDR;  // elements of one Q or dO tile
 constexpr int OFF_KT = 0, OFF_VT = OFF_KT + kKT * kKT * 2, OFF_Q = OFF_VT + kKT * kKT * 2;
 constexpr int OFF_G = OFF_Q + 2 * TILE * 2, OFF_RS = OFF_G + 2 * TILE * 2;
 constexpr int OFF_DL = OFF_RS + 2 * BQ * 4, OFF_RW = OFF_DL + 2 * BQ * 4;
-constexpr int SMEM = OFF_RW + 2 * WIN * 4;
+constexpr int WINP = win_pad(WIN);  // one of the 4 copies of a distance window (win_store)
+constexpr int SMEM = OFF_RW + 2 * 4 * WINP * 4;
 constexpr int RED = 2 * 4 * 16 * 64 * 16;  // partial sums: [dV | dK][key group][16 float4][lane]
 static_assert(RED <= SMEM && SMEM <= 160 * 1024, "LDS budget");
 static_assert(BKV == kKT && D == kKT, "one transposed tile per key block");
@@ -516,166 +521,274 @@ void bwd_kv_wide_kernel(LayerArgs p) {
 
   const int nqt = (T + BQ - 1) / BQ;
   const int qt0 = kb0 / BQ;
-  for (int m = 0; m < GS; ++m) {
-    const int h = hk * GS + m;
-    const bool rep = is_replaced(p.rep, h);
-    const bool fact = rep && p.pat.flag(h)[0] != 0;
-    const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
-    const size_t soff = ((size_t)b * H + h) * (size_t)T;
-    const bf16* Q = reinterpret_cast<const bf16*>(p.q) + hoff;
-    const bf16* G = reinterpret_cast<const bf16*>(p.dout) + hoff;
-    const float* lse = p.lse + soff;
-    const float* dlt = p.delta + soff;
-    const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
-    const float wscale = fact ? 1.f : kLog2e;
-    const float wfill = fact ? 0.f : -INFINITY;
-    const float shift = fact ? p.pat.shift(h) : 0.f;
-    float akey = 0.f;  // replaced: the lane's key preference (ea, or a*log2e)
-    if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
-    const bool fold = fact && GS > 1;  // the key factor enters each entry
-    if (fact && GS == 1) vs = akey;
+  if (!any_ord) {
+    // Every query head of the item is replaced: P comes from the pattern, the only product is dV,
+    // and there is no K^T / V^T to keep, so tiles are 128 queries tall (each wave: its 32 keys x
+    // two 32-query subtiles per tile), which halves the staging, barriers and statistics per product.
+    constexpr int BQR = 2 * BQ, WINR = BQR + BKV, WINRP = win_pad(WINR), TILER = BQR * TileGeom<D>::LDR;
+    constexpr int OFF_GR = 0, OFF_RSR = OFF_GR + 2 * TILER * 2, OFF_RWR = OFF_RSR + 2 * BQR * 4;
+    static_assert(OFF_RWR + 2 * 4 * WINRP * 4 <= SMEM, "LDS budget of the replaced-only sweep");
+    bf16* Gr = reinterpret_cast<bf16*>(smem + OFF_GR);       // [2][TILER] dO tiles
+    float* rsr = reinterpret_cast<float*>(smem + OFF_RSR);   // [2][BQR] row scale per query
+    float* rwr = reinterpret_cast<float*>(smem + OFF_RWR);   // [2][4][WINRP] distance window
+    const int nqr = (T + BQR - 1) / BQR;
+    const int qr0 = kb0 / BQR;
+    for (int m = 0; m < GS; ++m) {
+      const int h = hk * GS + m;
+      const bool fact = p.pat.flag(h)[0] != 0;
+      const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+      const size_t soff = ((size_t)b * H + h) * (size_t)T;
+      const bf16* G = reinterpret_cast<const bf16*>(p.dout) + hoff;
+      const float* lse = p.lse + soff;
+      const float* rrow = fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len;
+      const float wscale = fact ? 1.f : kLog2e;
+      const float wfill = fact ? 0.f : -INFINITY;
+      const float shift = fact ? p.pat.shift(h) : 0.f;
+      float akey = 0.f;
+      if (kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
+      const bool fold = fact && GS > 1;
+      if (fact && GS == 1) vs = akey;
 
-    // prefetch registers hold raw loads (clamped addresses); masks and conversions at the store
-    Chunks<bf16, D, BQ, NT> pq, pg;
-    float prs = 0.f, pdl = 0.f, prw = 0.f;
-    auto load_tile = [&](int q0) {
-      pg.load(G, q0, T, tid);
-      if (!rep) pq.load(Q, q0, T, tid);
-      if (tid < BQ) {
-        const int q = min(q0 + tid, T - 1);
-        prs = lse[q];
-        pdl = dlt[q];
-      }
-      if (rep && tid < WIN) prw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
-    };
-    auto store_tile = [&](int buf, int q0) {
-      pg.template store_tile<true>(Gs + buf * TILE, tid);
-      if (!rep) pq.template store_tile<true>(Qs + buf * TILE, tid);
-      if (tid < BQ) {
-        // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse);
-        // rows past the end get weight 0
-        const bool in = q0 + tid < T;
-        rss[buf * BQ + tid] = in ? (fact ? expf(shift - prs) : prs * kLog2e) : (fact ? 0.f : INFINITY);
-        dls[buf * BQ + tid] = (!rep && in) ? -pdl : 0.f;
-      }
-      if (rep && tid < WIN) {
-        const int dist = q0 - (kb0 + BKV - 1) + tid;
-        rwin[buf * WIN + tid] = (dist >= 0 && dist < T) ? prw * wscale : wfill;
-      }
-    };
-
-    load_tile(qt0 * BQ);
-    store_tile(0, qt0 * BQ);
-    if (qt0 + 1 < nqt) load_tile((qt0 + 1) * BQ);
-    __syncthreads();  // also orders the K^T / V^T stores before the first reads
-
-    for (int qt = qt0; qt < nqt; ++qt) {
-      const int buf = (qt - qt0) & 1;
-      const int q0 = qt * BQ;
-      const int qs = q0 + 32 * qh;  // the wave's first query
-      const bf16* Qb = Qs + buf * TILE;
-      const bf16* Gb = Gs + buf * TILE;
-      const float* rsb = rss + buf * BQ + 32 * qh;
-      const float* dlb = dls + buf * BQ + 32 * qh;
-      if (qs + 31 >= kw && qs < T && kw < T) {  // wave-uniform: something visible
-        // P (and dS = P o (dP - delta)) of the subtile as operand fragments of its two k16 steps:
-        // only fragments, not 32 fp32 entries, are live where the head kinds' branches meet
-        Frag<bf16> pf[2], sf[2];
-        if (!rep) {
-          // S = Q K^T and dP = dO V^T (-delta is added per entry: as the products' initial value it
-          // would hold 16 more registers through them)
-          f32x16 st, dpt;
-#pragma unroll
-          for (int t = 0; t < D / 16; ++t) {
-            mma16(st, tile_row_frag<D, true>(Qb, 32 * qh, t, tl), kt_frag(KTs, t, ktl), t == 0);
-            mma16(dpt, tile_row_frag<D, true>(Gb, 32 * qh, t, tl), kt_frag(VTs, t, ktl), t == 0);
-          }
-          const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
-          auto entries = [&](auto masked) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              float pr[8], ds[8];
-#pragma unroll
-              for (int g2 = 0; g2 < 2; ++g2) {
-                const int g = 2 * u + g2;
-                const float4 l4 = *reinterpret_cast<const float4*>(rsb + 8 * g + 4 * hi);
-                const float4 n4 = *reinterpret_cast<const float4*>(dlb + 8 * g + 4 * hi);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, nd[4] = {n4.x, n4.y, n4.z, n4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int r = 4 * g + e;
-                  float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
-                  if constexpr (decltype(masked)::value) {
-                    const int q = qs + 8 * g + 4 * hi + e;
-                    pp = ((q >= kj) & (q < T) & (kj < T)) ? pp : 0.f;
-                  }
-                  pr[4 * g2 + e] = pp;
-                  ds[4 * g2 + e] = pp * (dpt[r] + nd[e]);
-                }
-              }
-              pf[u] = to_frag<bf16>(pr);
-              sf[u] = to_frag<bf16>(ds);
-            }
-          };
-          if (edge)
-            entries(std::true_type{});
-          else
-            entries(std::false_type{});
-        } else {
-          const float* rwb = rwin + buf * WIN;
-          auto rep_entries = [&](auto fact_c) {
-            constexpr bool kFact = decltype(fact_c)::value;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              float pr[8];
-#pragma unroll
-              for (int g2 = 0; g2 < 2; ++g2) {
-                const int g = 2 * u + g2;
-                const int qr = 32 * qh + 8 * g + 4 * hi;  // tile row of register group g
-                const float4 l4 = *reinterpret_cast<const float4*>(rsb + 8 * g + 4 * hi);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float rv = rwb[xr + e];
-                  float pp = kFact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
-                  if (kFact && fold) pp *= akey;
-                  pr[4 * g2 + e] = pp;
-                }
-              }
-              pf[u] = to_frag<bf16>(pr);
-            }
-          };
-          if (fact)
-            rep_entries(std::true_type{});
-          else
-            rep_entries(std::false_type{});
+      Chunks<bf16, D, BQR, NT> pg;
+      float prs = 0.f, prw = 0.f;
+      auto load_tile = [&](int q0) {
+        pg.load(G, q0, T, tid);
+        if (tid < BQR) prs = lse[min(q0 + tid, T - 1)];
+        if (tid < WINR) prw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
+      };
+      auto store_tile = [&](int buf, int q0) {
+        pg.template store_tile<true>(Gr + buf * TILER, tid);
+        if (tid < BQR) {
+          const bool in = q0 + tid < T;
+          rsr[buf * BQR + tid] = in ? (fact ? expf(shift - prs) : prs * kLog2e) : (fact ? 0.f : INFINITY);
         }
-        // dV^T[dcol][key] += dO^T[dcol][q] P[q][key];  dK^T[dim][key] += Q^T[dim][q] dS[q][key]
+        if (tid < WINR) {
+          const int dist = q0 - (kb0 + BKV - 1) + tid;
+          win_store(rwr + buf * 4 * WINRP, WINRP, tid, (dist >= 0 && dist < T) ? prw * wscale : wfill);
+        }
+      };
+      load_tile(qr0 * BQR);
+      store_tile(0, qr0 * BQR);
+      if (qr0 + 1 < nqr) load_tile((qr0 + 1) * BQR);
+      __syncthreads();
+      for (int qt = qr0; qt < nqr; ++qt) {
+        const int buf = (qt - qr0) & 1;
+        const int q0 = qt * BQR;
+        const bf16* Gb = Gr + buf * TILER;
+        const float* rwb = win_base(rwr + buf * 4 * WINRP, WINRP, (3 - l32) & 3);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int sub = 0; sub < 2; ++sub) {
+          const int row0 = 64 * qh + 32 * sub;  // tile row of the subtile
+          const int qs = q0 + row0;
+          if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
+          const float* rsb = rsr + buf * BQR + row0;
+          auto rep_entries = [&](auto fact_c, int u) {
+            constexpr bool kFact = decltype(fact_c)::value;
+            float pr[8];
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c)
-            mma16(dvT[c], tile_tr_frag<D, true>(Gb, 32 * qh + 16 * u, c, tl), pf[u]);
-          if (!rep) {
+            for (int g2 = 0; g2 < 2; ++g2) {
+              const int g = 2 * u + g2;
+              const float4 l4 = *reinterpret_cast<const float4*>(rsb + 8 * g + 4 * hi);
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+              const int xr = row0 + 8 * g + 4 * hi + (kb0 + BKV - 1) - kj;  // = 3 - l32 mod 4
+              const float4 r4 = win_read4(rwb, xr);
+              const float rw4[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float rv = rw4[e];
+                float pp = kFact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
+                if (kFact && fold) pp *= akey;
+                pr[4 * g2 + e] = pp;
+              }
+            }
+            return to_frag<bf16>(pr);
+          };
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const Frag<bf16> pfr = fact ? rep_entries(std::true_type{}, u) : rep_entries(std::false_type{}, u);
 #pragma unroll
             for (int c = 0; c < D / 32; ++c)
-              mma16(dkT[c], tile_tr_frag<D, true>(Qb, 32 * qh + 16 * u, c, tl), sf[u]);
+              mma16(dvT[c], tile_tr_frag<D, true>(Gb, row0 + 16 * u, c, tl), pfr);
           }
         }
+        if (qt + 1 < nqr) {
+          store_tile(buf ^ 1, q0 + BQR);
+          if (qt + 2 < nqr) load_tile(q0 + 2 * BQR);
+        }
+        __syncthreads();
       }
-      if (qt + 1 < nqt) {
-        store_tile(buf ^ 1, q0 + BQ);  // that buffer's readers passed the previous barrier
-        if (qt + 2 < nqt) load_tile(q0 + 2 * BQ);
+      if (qh == 0 && kj < T) {  // a replaced head's query gradient is zero
+        bf16* dQ = reinterpret_cast<bf16*>(p.dq) + hoff + (size_t)kj * D;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
       }
-      __syncthreads();
     }
-    if (rep && qh == 0 && kj < T) {  // a replaced head's query gradient is zero
-      bf16* dQ = reinterpret_cast<bf16*>(p.dq) + hoff + (size_t)kj * D;
+  } else {
+    for (int m = 0; m < GS; ++m) {
+      const int h = hk * GS + m;
+      const bool rep = is_replaced(p.rep, h);
+      const bool fact = rep && p.pat.flag(h)[0] != 0;
+      const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+      const size_t soff = ((size_t)b * H + h) * (size_t)T;
+      const bf16* Q = reinterpret_cast<const bf16*>(p.q) + hoff;
+      const bf16* G = reinterpret_cast<const bf16*>(p.dout) + hoff;
+      const float* lse = p.lse + soff;
+      const float* dlt = p.delta + soff;
+      const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
+      const float wscale = fact ? 1.f : kLog2e;
+      const float wfill = fact ? 0.f : -INFINITY;
+      const float shift = fact ? p.pat.shift(h) : 0.f;
+      float akey = 0.f;  // replaced: the lane's key preference (ea, or a*log2e)
+      if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
+      const bool fold = fact && GS > 1;  // the key factor enters each entry
+      if (fact && GS == 1) vs = akey;
+
+      // prefetch registers hold raw loads (clamped addresses); masks and conversions at the store
+      Chunks<bf16, D, BQ, NT> pq, pg;
+      float prs = 0.f, pdl = 0.f, prw = 0.f;
+      auto load_tile = [&](int q0) {
+        pg.load(G, q0, T, tid);
+        if (!rep) pq.load(Q, q0, T, tid);
+        if (tid < BQ) {
+          const int q = min(q0 + tid, T - 1);
+          prs = lse[q];
+          pdl = dlt[q];
+        }
+        if (rep && tid < WIN) prw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
+      };
+      auto store_tile = [&](int buf, int q0) {
+        pg.template store_tile<true>(Gs + buf * TILE, tid);
+        if (!rep) pq.template store_tile<true>(Qs + buf * TILE, tid);
+        if (tid < BQ) {
+          // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse);
+          // rows past the end get weight 0
+          const bool in = q0 + tid < T;
+          rss[buf * BQ + tid] = in ? (fact ? expf(shift - prs) : prs * kLog2e) : (fact ? 0.f : INFINITY);
+          dls[buf * BQ + tid] = (!rep && in) ? -pdl : 0.f;
+        }
+        if (rep && tid < WIN) {
+          const int dist = q0 - (kb0 + BKV - 1) + tid;
+          win_store(rwin + buf * 4 * WINP, WINP, tid, (dist >= 0 && dist < T) ? prw * wscale : wfill);
+        }
+      };
+
+      load_tile(qt0 * BQ);
+      store_tile(0, qt0 * BQ);
+      if (qt0 + 1 < nqt) load_tile((qt0 + 1) * BQ);
+      __syncthreads();  // also orders the K^T / V^T stores before the first reads
+
+      for (int qt = qt0; qt < nqt; ++qt) {
+        const int buf = (qt - qt0) & 1;
+        const int q0 = qt * BQ;
+        const int qs = q0 + 32 * qh;  // the wave's first query
+        const bf16* Qb = Qs + buf * TILE;
+        const bf16* Gb = Gs + buf * TILE;
+        const float* rsb = rss + buf * BQ + 32 * qh;
+        const float* dlb = dls + buf * BQ + 32 * qh;
+        if (qs + 31 >= kw && qs < T && kw < T) {  // wave-uniform: something visible
+          // P (and dS = P o (dP - delta)) of the subtile as operand fragments of its two k16 steps:
+          // only fragments, not 32 fp32 entries, are live where the head kinds' branches meet
+          Frag<bf16> pf[2], sf[2];
+          if (!rep) {
+            // S = Q K^T and dP = dO V^T (-delta is added per entry: as the products' initial value it
+            // would hold 16 more registers through them)
+            f32x16 st, dpt;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c)
+            for (int t = 0; t < D / 16; ++t) {
+              mma16(st, tile_row_frag<D, true>(Qb, 32 * qh, t, tl), kt_frag(KTs, t, ktl), t == 0);
+              mma16(dpt, tile_row_frag<D, true>(Gb, 32 * qh, t, tl), kt_frag(VTs, t, ktl), t == 0);
+            }
+            const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
+            auto entries = [&](auto masked) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
+              for (int u = 0; u < 2; ++u) {
+                float pr[8], ds[8];
+#pragma unroll
+                for (int g2 = 0; g2 < 2; ++g2) {
+                  const int g = 2 * u + g2;
+                  const float4 l4 = *reinterpret_cast<const float4*>(rsb + 8 * g + 4 * hi);
+                  const float4 n4 = *reinterpret_cast<const float4*>(dlb + 8 * g + 4 * hi);
+                  const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, nd[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e;
+                    float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
+                    if constexpr (decltype(masked)::value) {
+                      const int q = qs + 8 * g + 4 * hi + e;
+                      pp = ((q >= kj) & (q < T) & (kj < T)) ? pp : 0.f;
+                    }
+                    pr[4 * g2 + e] = pp;
+                    ds[4 * g2 + e] = pp * (dpt[r] + nd[e]);
+                  }
+                }
+                pf[u] = to_frag<bf16>(pr);
+                sf[u] = to_frag<bf16>(ds);
+              }
+            };
+            if (edge)
+              entries(std::true_type{});
+            else
+              entries(std::false_type{});
+          } else {
+            const float* rwb = win_base(rwin + buf * 4 * WINP, WINP, (3 - l32) & 3);
+            auto rep_entries = [&](auto fact_c) {
+              constexpr bool kFact = decltype(fact_c)::value;
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                float pr[8];
+#pragma unroll
+                for (int g2 = 0; g2 < 2; ++g2) {
+                  const int g = 2 * u + g2;
+                  const int qr = 32 * qh + 8 * g + 4 * hi;  // tile row of register group g
+                  const float4 l4 = *reinterpret_cast<const float4*>(rsb + 8 * g + 4 * hi);
+                  const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                  const int xr = qr + (kb0 + BKV - 1) - kj;  // = 3 - l32 mod 4
+                  const float4 r4 = win_read4(rwb, xr);
+                  const float rw4[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    const float rv = rw4[e];
+                    float pp = kFact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
+                    if (kFact && fold) pp *= akey;
+                    pr[4 * g2 + e] = pp;
+                  }
+                }
+                pf[u] = to_frag<bf16>(pr);
+              }
+            };
+            if (fact)
+              rep_entries(std::true_type{});
+            else
+              rep_entries(std::false_type{});
+          }
+          // dV^T[dcol][key] += dO^T[dcol][q] P[q][key];  dK^T[dim][key] += Q^T[dim][q] dS[q][key]
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c)
+              mma16(dvT[c], tile_tr_frag<D, true>(Gb, 32 * qh + 16 * u, c, tl), pf[u]);
+            if (!rep) {
+#pragma unroll
+              for (int c = 0; c < D / 32; ++c)
+                mma16(dkT[c], tile_tr_frag<D, true>(Qb, 32 * qh + 16 * u, c, tl), sf[u]);
+            }
+          }
+        }
+        if (qt + 1 < nqt) {
+          store_tile(buf ^ 1, q0 + BQ);  // that buffer's readers passed the previous barrier
+          if (qt + 2 < nqt) load_tile(q0 + 2 * BQ);
+        }
+        __syncthreads();
+      }
+      if (rep && qh == 0 && kj < T) {  // a replaced head's query gradient is zero
+        bf16* dQ = reinterpret_cast<bf16*>(p.dq) + hoff + (size_t)kj * D;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
+      }
     }
   }
 

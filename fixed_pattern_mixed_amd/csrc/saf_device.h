@@ -258,6 +258,25 @@ __device__ __forceinline__ Frag<bf16> kt_frag(const bf16* tile, int t, const KtL
   return f;
 }
 
+// ---- Distance windows of replaced items -----------------------------------------------------------
+// A lane reads 4 consecutive window entries x .. x+3 whose start x has the same residue c = x % 4
+// for the whole item (a per-lane constant).  The window is kept in 4 copies, copy c shifted down by
+// c (copy c, index y holds entry y + c), so those 4 entries are one aligned float4 of copy c.  Four
+// consecutive lanes read the same index of the four copies, so the copies are win_pad(WIN) floats
+// apart, 16 mod 64 dwords: the 16 lanes of a 16-byte read pass (4 indices x 4 copies) then fall on
+// 16 different 4-bank groups.
+__host__ __device__ constexpr int win_pad(int n) { return ((n + 63) & ~63) + 16; }
+__device__ __forceinline__ void win_store(float* win, int winp, int x, float v) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (x >= c) win[c * winp + x - c] = v;
+}
+// the lane's copy, offset so that entry x (x % 4 == c) is at base + x
+__device__ __forceinline__ const float* win_base(const float* win, int winp, int c) { return win + c * winp - c; }
+__device__ __forceinline__ float4 win_read4(const float* base, int x) {
+  return *reinterpret_cast<const float4*>(base + x);
+}
+
 // 4 consecutive elements of one row (bf16: 8 bytes, fp32: 16 bytes)
 template <typename TI>
 struct Quad;

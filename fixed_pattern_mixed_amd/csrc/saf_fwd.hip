@@ -56,6 +56,7 @@ struct FwdCfg {
   static constexpr int VT_ELEMS = BF ? BK * TileGeom<D>::LDR : D * LDT;  // V tile (below)
   static constexpr int WIN = BK + BQ;                    // distance window
   static constexpr int WPT = (WIN + NT - 1) / NT;        // window values per thread
+  static constexpr int WINP = win_pad(WIN);              // one of its 4 copies (win_store)
 };
 
 template <typename TI>
@@ -64,7 +65,9 @@ struct FwdSmem {
   TI* VT;       // V tile: bf16 [BK][D + 32] rows (tile_off, unswizzled: read only transposed, by
                 //   the LDS); fp32 [D][LDT] transposed, key-permuted, swizzled
   float* awin;  // [BK]        ea (or a*log2e) of the tile's keys
-  float* rwin;  // [WIN]       er (or r*log2e) of the tile's distance window
+  float* rwin;  // [4][WINP]   er (or r*log2e) of the tile's distance window; copy c holds the
+                //             window shifted by c, so that a lane reads its 4 consecutive distances
+                //             with one aligned 16-byte read (from copy (query % 32) % 4)
 };
 
 struct FwdItem {
@@ -78,7 +81,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
                                          const FwdItem& it) {
   using C = FwdCfg<TI, D, W>;
   constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP, kBQ = C::BQ, kNT = C::NT;
-  constexpr int LDT = C::LDT, WIN = C::WIN, WPT = C::WPT;
+  constexpr int LDT = C::LDT, WIN = C::WIN, WPT = C::WPT, WINP = C::WINP;
   constexpr bool ORD = KIND == kOrdinary, FACT = KIND == kProduct;
   const int T = it.T, h = it.h, q0 = it.q0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -128,7 +131,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
       for (int j = 0; j < WPT; ++j) {
         const int x = tid + j * kNT;
         const int dist = d0 + x;
-        if (x < WIN) sm.rwin[x] = (dist >= 0 && dist < T) ? rwr[j] * wscale : wfill;
+        if (x < WIN) win_store(sm.rwin, WINP, x, (dist >= 0 && dist < T) ? rwr[j] * wscale : wfill);
       }
     }
   };
@@ -143,6 +146,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   const float lz2_q = lz_q * kLog2e;
 
   const TileLane<D, false> vtl(lane);  // lane bases of the V tile's transposing reads (bf16)
+  const float* rbase = win_base(sm.rwin, WINP, l32 & 3);  // the lane's copy of the distance window
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -275,13 +279,15 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
         for (int g = 0; g < 4; ++g) {
           const int kk = 32 * s + 8 * g + 4 * hi;    // tile-relative first key of the run
           const float4 a4 = *reinterpret_cast<const float4*>(sm.awin + kk);
-          const int xr = (qi - q0) + (BK - 1) - kk;  // window index of distance qi - key
+          // distances qi - key of the run's 4 keys: window entries xr - e, e = 0..3, where
+          // xr - 3 = (qi - q0) + BK - 4 - kk = l32 mod 4 (kk, BK, 32w = 0 mod 4)
+          const int xr = (qi - q0) + (BK - 1) - kk;
+          const float4 r4 = win_read4(rbase, xr - 3);
           const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+          const float rv[4] = {r4.w, r4.z, r4.y, r4.x};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float rv = sm.rwin[xr - e];
-            pv[4 * g + e] = FACT ? av[e] * rv : __builtin_amdgcn_exp2f(av[e] + rv - lz2_q);
-          }
+          for (int e = 0; e < 4; ++e)
+            pv[4 * g + e] = FACT ? av[e] * rv[e] : __builtin_amdgcn_exp2f(av[e] + rv[e] - lz2_q);
         }
         Frag<TI> pf[2] = {to_frag<TI>(&pv[0]), to_frag<TI>(&pv[8])};
         l += frag_sum(pf[0]) + frag_sum(pf[1]);
@@ -326,7 +332,7 @@ void mixed_fwd_kernel(LayerArgs p) {
   __shared__ __attribute__((aligned(16))) TI Ks[C::BK * C::LDP];
   __shared__ __attribute__((aligned(16))) TI VT[C::VT_ELEMS];
   __shared__ __attribute__((aligned(16))) float awin[C::BK];
-  __shared__ float rwin[C::WIN];
+  __shared__ __attribute__((aligned(16))) float rwin[4 * C::WINP];
 
   const int T = p.T, H = p.H;
   const int BH = p.B * H;
