@@ -57,18 +57,32 @@ struct FwdCfg {
   static constexpr int WIN = BK + BQ;                    // distance window
   static constexpr int WPT = (WIN + NT - 1) / NT;        // window values per thread
   static constexpr int WINP = win_pad(WIN);              // one of its 4 copies (win_store)
+  // bf16 at d = 128 with 8 waves (one block per compute unit) double-buffers the key/value tiles:
+  // one barrier per tile, and the next tile's LDS stores overlap other waves' products
+  static constexpr int NSTAGE = (BF && D == 128 && W == 8) ? 2 : 1;
+  // a stage: the K tile (ordinary items) or the windows (replaced items) in one region, then V
+  static constexpr int KREG = ((BK * LDP * (int)sizeof(TI) > (BK + 4 * WINP) * 4 ? BK * LDP * (int)sizeof(TI)
+                                                                                  : (BK + 4 * WINP) * 4) + 15) & ~15;
+  static constexpr int STAGE = KREG + VT_ELEMS * (int)sizeof(TI);
 };
 
+// One stage of the staged tiles (LDS):
 template <typename TI>
 struct FwdSmem {
   TI* Ks;       // [BK][LDP]   K tile (ordinary items)
   TI* VT;       // V tile: bf16 [BK][D + 32] rows (tile_off, unswizzled: read only transposed, by
                 //   the LDS); fp32 [D][LDT] transposed, key-permuted, swizzled
-  float* awin;  // [BK]        ea (or a*log2e) of the tile's keys
+  float* awin;  // [BK]        ea (or a*log2e) of the tile's keys (replaced items; over Ks)
   float* rwin;  // [4][WINP]   er (or r*log2e) of the tile's distance window; copy c holds the
                 //             window shifted by c, so that a lane reads its 4 consecutive distances
                 //             with one aligned 16-byte read (from copy (query % 32) % 4)
 };
+template <typename TI, typename C>
+__device__ __forceinline__ FwdSmem<TI> fwd_stage(unsigned char* smem, int buf) {
+  unsigned char* b = smem + buf * C::STAGE;
+  float* awin = reinterpret_cast<float*>(b);
+  return FwdSmem<TI>{reinterpret_cast<TI*>(b), reinterpret_cast<TI*>(b + C::KREG), awin, awin + C::BK};
+}
 
 struct FwdItem {
   int b, h, q0, T, H;
@@ -77,7 +91,7 @@ struct FwdItem {
 };
 
 template <typename TI, int D, int KIND, int W>
-__device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& sm,
+__device__ __forceinline__ void fwd_item(const LayerArgs& p, unsigned char* smem,
                                          const FwdItem& it) {
   using C = FwdCfg<TI, D, W>;
   constexpr int BK = C::BK, NS = C::NS, LDP = C::LDP, kBQ = C::BQ, kNT = C::NT;
@@ -117,7 +131,8 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
       for (int j = 0; j < WPT; ++j) rwr[j] = rrow[min(max(d0 + tid + j * kNT, 0), T - 1)];
     }
   };
-  auto store_tile = [&](int k0) {
+  auto store_tile = [&](int buf, int k0) {
+    const FwdSmem<TI> sm = fwd_stage<TI, C>(smem, buf);
     if constexpr (C::BF)
       vreg.template store_tile<false>(sm.VT, tid);
     else
@@ -146,7 +161,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
   const float lz2_q = lz_q * kLog2e;
 
   const TileLane<D, false> vtl(lane);  // lane bases of the V tile's transposing reads (bf16)
-  const float* rbase = win_base(sm.rwin, WINP, l32 & 3);  // the lane's copy of the distance window
+  FwdSmem<TI> sm = fwd_stage<TI, C>(smem, 0);  // the stage being multiplied
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -237,14 +252,17 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
     }
   };
 
+  constexpr bool DB = C::NSTAGE == 2;
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
+  if (DB && nkt > 1) load_tile(BK);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BK;
     k_base = k0;
-    if (kt + 1 < nkt) load_tile(k0 + BK);
+    sm = fwd_stage<TI, C>(smem, DB ? (kt & 1) : 0);
+    if (!DB && kt + 1 < nkt) load_tile(k0 + BK);
 
     if (kPipe && ORD && k0 + BK - 1 <= qw && k0 + BK <= T) {
       // Every subtile of the tile is visible to all of the wave's queries (most tiles): no masks,
@@ -282,7 +300,7 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
           // distances qi - key of the run's 4 keys: window entries xr - e, e = 0..3, where
           // xr - 3 = (qi - q0) + BK - 4 - kk = l32 mod 4 (kk, BK, 32w = 0 mod 4)
           const int xr = (qi - q0) + (BK - 1) - kk;
-          const float4 r4 = win_read4(rbase, xr - 3);
+          const float4 r4 = win_read4(win_base(sm.rwin, WINP, l32 & 3), xr - 3);
           const float av[4] = {a4.x, a4.y, a4.z, a4.w};
           const float rv[4] = {r4.w, r4.z, r4.y, r4.x};
 #pragma unroll
@@ -296,10 +314,19 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
     }
     }
 
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      store_tile(k0 + BK);
+    if constexpr (DB) {
+      // the other stage's readers passed the previous barrier
+      if (kt + 1 < nkt) {
+        store_tile((kt + 1) & 1, k0 + BK);
+        if (kt + 2 < nkt) load_tile(k0 + 2 * BK);
+      }
       __syncthreads();
+    } else {
+      __syncthreads();
+      if (kt + 1 < nkt) {
+        store_tile(0, k0 + BK);
+        __syncthreads();
+      }
     }
   }
 
@@ -324,15 +351,17 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, const FwdSmem<TI>& 
 
 // Narrow items (W < 8) are launched only for grids of at most a few blocks per compute unit, where
 // occupancy cannot be high anyway: they get 256 registers (their staging registers, 4x those of a
-// wide item, would spill at 128).
+// wide item, would spill at 128), fp32 at d = 128 with 2 waves all 512 (it spills at 256).
+template <typename TI, int D>
+constexpr int fwd_waves_per_eu(int W) {
+  return (D == 64 && sizeof(TI) == 2 && W == 8) ? SAF_FWD_W64 : (sizeof(TI) == 4 && D == 128 && W == 2) ? 1 : 2;
+}
 template <typename TI, int D, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 && W == 8 ? SAF_FWD_W64 : 2)))
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<TI, D>(W))))
 void mixed_fwd_kernel(LayerArgs p) {
   using C = FwdCfg<TI, D, W>;
-  __shared__ __attribute__((aligned(16))) TI Ks[C::BK * C::LDP];
-  __shared__ __attribute__((aligned(16))) TI VT[C::VT_ELEMS];
-  __shared__ __attribute__((aligned(16))) float awin[C::BK];
-  __shared__ __attribute__((aligned(16))) float rwin[4 * C::WINP];
+  static_assert(C::NSTAGE * C::STAGE <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::NSTAGE * C::STAGE];
 
   const int T = p.T, H = p.H;
   const int BH = p.B * H;
@@ -348,13 +377,12 @@ void mixed_fwd_kernel(LayerArgs p) {
   it.q0 = (nqb - 1 - x / BHp) * C::BQ;  // heaviest query blocks first
   it.hoff = ((size_t)it.b * H + it.h) * (size_t)T * D;
   it.kvoff = ((size_t)it.b * p.Hkv + it.h / (H / p.Hkv)) * (size_t)T * D;
-  const FwdSmem<TI> sm{Ks, VT, awin, rwin};
   if (!is_replaced(p.rep, it.h))
-    fwd_item<TI, D, kOrdinary, W>(p, sm, it);
+    fwd_item<TI, D, kOrdinary, W>(p, smem, it);
   else if (p.pat.flag(it.h)[0] != 0)
-    fwd_item<TI, D, kProduct, W>(p, sm, it);
+    fwd_item<TI, D, kProduct, W>(p, smem, it);
   else
-    fwd_item<TI, D, kExponential, W>(p, sm, it);
+    fwd_item<TI, D, kExponential, W>(p, smem, it);
 }
 
 template <typename TI, int D, int W>
