@@ -25,6 +25,10 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 
+# per-file additions: the calibration kernels are vector-bound, and matrix products accumulated in
+# AGPRs would cost one register read per score entry before the vector work
+FILE_FLAGS = {"saf_calib.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(PKG, "_build")
@@ -35,7 +39,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,

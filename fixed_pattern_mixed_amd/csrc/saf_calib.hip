@@ -81,37 +81,39 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
     __syncthreads();
     if (kt + 1 < nkt) kreg.load(K, k0 + kBK, T, tid);
     if (k0 > qw + 31) continue;
-    float sv[NS][16];  // the tile's scores (masked entries -inf), unscaled
-    bool act[NS];
     // keys past a row's query or past the end exist only in diagonal or last tiles (wave-uniform)
     const bool edge = (k0 + kBK - 1 > qw) || (k0 + kBK > T) || (qw + 31 >= T);
     const float c2 = p.scale_log2;
+    // subtile s's scores, unscaled (masked: keys past the row's query or past the end -inf)
+    auto scores = [&](int s, f32x16& st, auto masked) {
+      const int ks = k0 + 32 * s;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t)
+        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+      if constexpr (decltype(masked)::value) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = ks + crow(r, hi);
+          st[r] = (key <= qi && key < T) ? st[r] : -INFINITY;
+        }
+      }
+    };
     // Lazy reference maximum: the row sum is taken relative to the current m, which any finite
     // value serves (lse = m + log2 of the sum), as long as no term overflows.  The sum shows that:
     // it is finite and at most 2^64 unless a term exceeds 2^64 (or m is still -inf, first tile).
-    // Only then is the tile's maximum formed and the sum rescaled and redone.
+    // Only then (rarely after a row's first tile) is the tile's maximum formed and the sum redone,
+    // from scores formed again rather than kept through the common path.
     float lsum = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
-      act[s] = ks <= qw + 31 && ks < T;
-      if (!act[s]) continue;
-      f32x16 st;
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t)
-        mma16(st, load8(Ks + (32 * s + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
-      // one copy per case (masking and sum together, so that the branch stays a branch)
+      if (ks > qw + 31 || ks >= T) continue;
+      // one copy per case, so that interior tiles carry no per-entry mask
       auto add_terms = [&](auto masked) {
+        f32x16 st;
+        scores(s, st, masked);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = st[r];
-          if constexpr (decltype(masked)::value) {
-            const int key = ks + crow(r, hi);
-            v = (key <= qi && key < T) ? v : -INFINITY;
-          }
-          sv[s][r] = v;
-          lsum += __builtin_amdgcn_exp2f(fmaf(v, c2, -m));
-        }
+        for (int r = 0; r < 16; ++r) lsum += __builtin_amdgcn_exp2f(fmaf(st[r], c2, -m));
       };
       if (edge)
         add_terms(std::true_type{});
@@ -119,13 +121,24 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
         add_terms(std::false_type{});
     }
     if (__any(!(lsum <= 0x1p64f))) {
+      float sv[NS][16];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        if (act[s]) {
+      for (int s = 0; s < NS; ++s) {
+        const int ks = k0 + 32 * s;
+        f32x16 st;
+        if (ks <= qw + 31 && ks < T) {
+          scores(s, st, std::true_type{});
+        } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sv[s][r]);
+          for (int r = 0; r < 16; ++r) st[r] = -INFINITY;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sv[s][r] = st[r];
+          tmax = fmaxf(tmax, st[r]);
+        }
+      }
       const float mnew = fmaxf(m, half_max(tmax) * c2);
       if (mnew == -INFINITY) {
         lsum = 0.f;  // a row with no visible key yet (only rows past the end): nothing to add
@@ -135,10 +148,8 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
         lsum = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-          if (act[s]) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) lsum += __builtin_amdgcn_exp2f(fmaf(sv[s][r], c2, -m));
-          }
+          for (int r = 0; r < 16; ++r) lsum += __builtin_amdgcn_exp2f(fmaf(sv[s][r], c2, -m));
       }
     }
     l += lsum;
@@ -192,12 +203,13 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
     }
   double ent = 0.0;  // sum over n and this lane's entries of A log2 A (KL score only)
 
-  // sequence n + 1's key tile, query fragments and row statistic are loaded while n is used
+  // sequence n + 1's key tile, query fragments and row statistic are loaded while n is used; the
+  // query fragments alternate between two register sets (no copy per sequence)
   const bool wave_sees = k0 <= qw + 31;  // this wave's queries see some of the tile's keys
   Chunks<TI, D, kBK, kNT> kreg;
-  Frag<TI> qn[D / 16];
-  float lse_n = 0.f;
-  auto prefetch = [&](int n) {
+  Frag<TI> qa[D / 16], qb[D / 16];
+  float la = 0.f, lb = 0.f;
+  auto prefetch = [&](int n, Frag<TI> (&qn)[D / 16], float& lse_n) {
     const size_t hoff = ((size_t)n * H + h) * (size_t)T * D;
     kreg.load(reinterpret_cast<const TI*>(p.k) + hoff, k0, T, tid);
     if (wave_sees) {
@@ -210,19 +222,14 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
       lse_n = p.lse2[((size_t)n * H + h) * T + qc];
     }
   };
-  prefetch(0);
-
-  for (int n = 0; n < N; ++n) {
-    const float lse2 = lse_n;
+  // sequence n with query fragments qf and row statistic lse2; prefetches n + 1 into (qn, lse_n)
+  auto step = [&](int n, const Frag<TI> (&qf)[D / 16], float lse2, Frag<TI> (&qn)[D / 16], float& lse_n) {
     const float inv_n = 1.f / (float)(n + 1);
-    Frag<TI> qf[D / 16];
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) qf[t] = qn[t];
     __syncthreads();
     kreg.template store<LDP>(Ks, tid);
     __syncthreads();
-    if (n + 1 < N) prefetch(n + 1);
-    if (!wave_sees) continue;
+    if (n + 1 < N) prefetch(n + 1, qn, lse_n);
+    if (!wave_sees) return;
     float ent_n = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -245,9 +252,11 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
           }
           const float x = fmaf(st[r], p.scale_log2, -lse2);  // log2 A
           const float a = valid ? __builtin_amdgcn_exp2f(x) : 0.f;
+          // explicit fused operations: the statistics are the same bits in every instantiation
+          // (with and without the KL sums), whatever the compiler would contract
           const float dlt = a - mean[s][r];
-          mean[s][r] += dlt * inv_n;
-          m2[s][r] += dlt * (a - mean[s][r]);
+          mean[s][r] = fmaf(dlt, inv_n, mean[s][r]);
+          m2[s][r] = fmaf(dlt, a - mean[s][r], m2[s][r]);
           if (KL) ent_n += valid ? a * x : 0.f;
         }
       };
@@ -257,6 +266,11 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
         update(std::false_type{});
     }
     if (KL) ent += (double)ent_n;
+  };
+  prefetch(0, qa, la);
+  for (int n = 0; n < N; n += 2) {
+    step(n, qa, la, qb, lb);
+    if (n + 1 < N) step(n + 1, qb, lb, qa, la);
   }
 
   // write the tile of Ahat (lane = query, registers = 4-key runs) and sum the deviations
