@@ -9,8 +9,10 @@
 //   dT(i,j) = P(i,j) (G(i,j) - delta_i),
 //   da[j] = sum_b sum_{i>=j} dT(i,j),      dr[k] = sum_b sum_i dT(i, i-k).
 //
-//   bwd_pattern  : one work item per (batch, replaced head, 128-key block), 4 waves x 32 keys
-//                  (lane = key), sweeping the query tiles at or below the diagonal.  G on the
+//   bwd_pattern  : one work item per (batch, replaced head, 128-key block), 8 waves: 4 key groups
+//                  of 32 keys (lane = key) x 2 contiguous halves of the query tiles at or below the
+//                  diagonal (the halves' column sums and the 32 distances at the cut are added
+//                  through LDS at the end, in a fixed order).  G on the
 //                  matrix cores (V of the lane's key in registers, dO rows from LDS), P from the
 //                  prepared pattern, dT.  da: per-lane column sums, written once per key.
 //                  dr: per 32 x 32 subtile, each lane writes its 16 dT values into a per-wave
@@ -31,11 +33,13 @@
 namespace saf {
 namespace {
 
-constexpr int kNT = 256;
+constexpr int kNT = 256;  // threads of the reduce kernels
+constexpr int kPgHalves = 2;
+constexpr int kPgNT = 256 * kPgHalves;  // threads of a bwd_pattern work item
 
 template <typename TI, int D>
 struct PgCfg {
-  static constexpr int BKV = 128;                         // keys per work item (4 waves x 32)
+  static constexpr int BKV = 128;                         // keys per work item (4 key groups x 32)
   static constexpr int BQ = sizeof(TI) == 2 ? 64 : 32;    // queries per staged tile
   static constexpr int NS = BQ / 32;                      // 32-query subtiles per tile
   static constexpr int LDP = D + 16 / (int)sizeof(TI);    // padded row of the dO tile
@@ -47,15 +51,21 @@ struct PgPrefetch {
   float rs, dl, rw;
 };
 
+// A work item's query sweep is cut into two contiguous halves, each taken by 4 waves (one per key
+// group): the longest item (the first key block sweeps every query) takes half as long.  Waves w
+// and w + 4 own the same 32 keys; their column sums and the 32 distances at the cut (which both
+// halves reach) are added through LDS at the end, half 0's part first.
 template <typename TI, int D>
-__global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList rl) {
+__global__ __launch_bounds__(kPgNT) void bwd_pattern_kernel(LayerArgs p, HeadList rl) {
   using C = PgCfg<TI, D>;
   constexpr int BKV = C::BKV, BQ = C::BQ, NS = C::NS, LDP = C::LDP, WIN = C::WIN, LDK = C::LDK;
-  __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDP];  // dO tile, rows
-  __shared__ __attribute__((aligned(16))) float rss[BQ];    // row scale (product form) or lse*log2e
-  __shared__ __attribute__((aligned(16))) float dls[BQ];    // delta per query
-  __shared__ float rwin[WIN];                               // er (product form) or r*log2e
-  __shared__ float skew[4][64 * LDK];                       // per wave: dT at [i - j + 31][i]
+  __shared__ __attribute__((aligned(16))) TI Gs[kPgHalves][BQ * LDP];  // dO tile of each half, rows
+  __shared__ __attribute__((aligned(16))) float rss[kPgHalves][BQ];    // row scale or lse*log2e
+  __shared__ __attribute__((aligned(16))) float dls[kPgHalves][BQ];    // delta per query
+  __shared__ float rwin[kPgHalves][WIN];                               // er or r*log2e
+  __shared__ float skew[2 * 4][63 * LDK];                              // per wave: dT at [i - j + 31][i]
+  __shared__ float xwin[4][32], xcol[4][32];                           // half 0's parts at the cut
+  __shared__ int xbase[4];
 
   const int T = p.T;
   const int R = rl.n;
@@ -67,13 +77,15 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
   const int kb = x / BRp;  // low key blocks see the most query tiles: heaviest first
   const int b = br / R, h = rl.h[br % R];
   const bool fact = p.pat.flag(h)[0] != 0;
-  const int nsb = (T + 31) / 32;  // 32-key sub-blocks (one per wave)
+  const int nsb = (T + 31) / 32;  // 32-key sub-blocks (one per key group)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kg = w & 3, half = w >> 2;
+  const int htid = tid & 255;  // thread index within the half
   const int l32 = lane & 31, hi = lane >> 5;
   const int kb0 = kb * BKV;
-  const int kw = kb0 + 32 * w;  // the wave's first key
-  const int kj = kw + l32;      // the lane's key
+  const int kw = kb0 + 32 * kg;  // the wave's first key
+  const int kj = kw + l32;       // the lane's key
   const bool kval = kj < T;
   const size_t hoff = ((size_t)b * p.H + h) * (size_t)T * D;
   const size_t soff = ((size_t)b * p.H + h) * (size_t)T;
@@ -85,14 +97,21 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
   const float wscale = fact ? 1.f : kLog2e;
   const float wfill = fact ? 0.f : -INFINITY;
   const float shift = fact ? p.pat.shift(h) : 0.f;
-  float* drp = p.drp + ((size_t)br * nsb + (kw >> 5)) * T;  // this wave's partial row, by distance
+  float* drp = p.drp + ((size_t)br * nsb + (kw >> 5)) * T;  // this key group's partial row, by distance
   float* sk = skew[w];
+  TI* Gh = Gs[half];
+  float* rsh = rss[half];
+  float* dlh = dls[half];
+  float* rwh = rwin[half];
   float win = 0.f;   // lane x: the wave's running sum for distance dbase + x
   int dbase = 0;     // distance of lane 0 (set by the first visible subtile)
   bool started = false;
+  float head = 0.f;  // half 1: its first window (distances at the cut), kept for the end
+  int head_base = 0;
+  bool stashed = false;
   // cells [x][row] with key row - x + 31 outside [0, 32) are never written: zero them once, so the
-  // distance sums below need no masks (row 63 stays zero too)
-  for (int e = tid; e < 4 * 64 * LDK; e += kNT) (&skew[0][0])[e] = 0.f;
+  // distance sums below need no masks
+  for (int e = tid; e < 2 * 4 * 63 * LDK; e += kPgNT) (&skew[0][0])[e] = 0.f;
 
   Frag<TI> vf[D / 16];
 #pragma unroll
@@ -102,42 +121,49 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
   if (kval) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
   float col = 0.f;  // sum over this lane's rows of dT(i, kj)
 
-  Chunks<TI, D, BQ, kNT> gch;
+  // the item's query tiles qt0 .. nqt-1: half 0 takes the first n0, half 1 the rest
+  const int nqt = (T + BQ - 1) / BQ;
+  const int qt0 = kb0 / BQ;
+  const int n0 = (nqt - qt0 + 1) / 2;
+  const int my0 = half ? qt0 + n0 : qt0, my1 = half ? nqt : qt0 + n0;  // this half's tiles
+  const bool has1 = qt0 + n0 < nqt;  // half 1 has tiles
+
+  Chunks<TI, D, BQ, 256> gch;
   PgPrefetch pf;
   // Raw loads from clamped (always valid) addresses; masks and conversions are applied when the
   // tile is stored (arithmetic on a value right after its load would make the wave wait for it).
   auto load_tile = [&](int q0) {
-    gch.load(G, q0, T, tid);
-    if (tid < BQ) {
-      const int q = min(q0 + tid, T - 1);
+    gch.load(G, q0, T, htid);
+    if (htid < BQ) {
+      const int q = min(q0 + htid, T - 1);
       pf.rs = lse[q];
       pf.dl = dlt[q];
     }
-    if (tid < WIN) pf.rw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
+    if (htid < WIN) pf.rw = rrow[min(max(q0 - (kb0 + BKV - 1) + htid, 0), T - 1)];
   };
   auto store_tile = [&](int q0) {
-    gch.template store<LDP>(Gs, tid);
-    if (tid < BQ) {
-      const bool in = q0 + tid < T;  // rows past the end get weight 0
-      rss[tid] = in ? (fact ? expf(shift - pf.rs) : pf.rs * kLog2e) : (fact ? 0.f : INFINITY);
-      dls[tid] = in ? pf.dl : 0.f;
+    gch.template store<LDP>(Gh, htid);
+    if (htid < BQ) {
+      const bool in = q0 + htid < T;  // rows past the end get weight 0
+      rsh[htid] = in ? (fact ? expf(shift - pf.rs) : pf.rs * kLog2e) : (fact ? 0.f : INFINITY);
+      dlh[htid] = in ? pf.dl : 0.f;
     }
-    if (tid < WIN) {
-      const int dist = q0 - (kb0 + BKV - 1) + tid;
-      rwin[tid] = (dist >= 0 && dist < T) ? pf.rw * wscale : wfill;
+    if (htid < WIN) {
+      const int dist = q0 - (kb0 + BKV - 1) + htid;
+      rwh[htid] = (dist >= 0 && dist < T) ? pf.rw * wscale : wfill;
     }
   };
 
-  const int nqt = (T + BQ - 1) / BQ;
-  const int qt0 = kb0 / BQ;
-  load_tile(qt0 * BQ);
-
-  for (int qt = qt0; qt < nqt; ++qt) {
+  if (my0 < my1) load_tile(my0 * BQ);
+  for (int step = 0; step < n0; ++step) {  // both halves step together (block-wide barriers)
+    const int qt = my0 + step;
+    const bool act = qt < my1;  // uniform over the half
     const int q0 = qt * BQ;
     __syncthreads();  // the previous tile's readers are done
-    store_tile(q0);
+    if (act) store_tile(q0);
     __syncthreads();
-    if (qt + 1 < nqt) load_tile(q0 + BQ);
+    if (act && qt + 1 < my1) load_tile(q0 + BQ);
+    if (!act) continue;
 
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -147,7 +173,7 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
       f32x16 gt;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t)
-        mma16(gt, load8(Gs + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
+        mma16(gt, load8(Gh + (32 * s + l32) * LDP + 16 * t + 8 * hi), vf[t], t == 0);
       // one copy of the entry loop per (form, edge) case: both are uniform over the subtile, and
       // tested per entry they would branch per entry; the mask is one select (bitwise conditions)
       auto entries = [&](auto fact_c, auto edge_c) {
@@ -155,15 +181,15 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
-          const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-          const float4 d4 = *reinterpret_cast<const float4*>(dls + qr);
+          const float4 l4 = *reinterpret_cast<const float4*>(rsh + qr);
+          const float4 d4 = *reinterpret_cast<const float4*>(dlh + qr);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
           const int xr = qr + (kb0 + BKV - 1) - kj;  // window index of distance (q0 + qr) - kj
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int q = q0 + qr + e;
-            const float rv = rwin[xr + e];
+            const float rv = rwh[xr + e];
             const float pp = kFact ? rv * lv[e] * akey : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
             float dt = pp * (gt[4 * g + e] - dv[e]);
             if constexpr (kEdge) dt = (kval & (q >= kj) & (q < T)) ? dt : 0.f;
@@ -180,32 +206,58 @@ __global__ __launch_bounds__(kNT) void bwd_pattern_kernel(LayerArgs p, HeadList 
         if (edge) entries(std::false_type{}, std::true_type{});
         else entries(std::false_type{}, std::false_type{});
       }
-      // distance sums of the subtile: lane x sums skewed row x (rows max(0, x-31) .. min(31, x));
-      // LDS accesses of one wave complete in order, so the stores above are visible here
+      // distance sums of the subtile: lane x < 63 sums skewed row x (rows max(0, x-31) ..
+      // min(31, x)); LDS accesses of one wave complete in order, so the stores above are visible
       __builtin_amdgcn_wave_barrier();
       float dsum = 0.f;
+      if (lane < 63) {
 #pragma unroll 8
-      for (int row = 0; row < 32; ++row) dsum += sk[lane * LDK + row];
+        for (int row = 0; row < 32; ++row) dsum += sk[lane * LDK + row];
+      }
       __builtin_amdgcn_wave_barrier();
       if (!started) {
         started = true;
         dbase = qs - kw - 31;
       }
       win += dsum;
-      // lanes 0..31 now hold final distances (no later subtile of this wave reaches them)
+      // lanes 0..31 now hold final distances (no later subtile of this wave reaches them); half 1
+      // keeps its first ones, which half 0's sweep also reaches, for the end
       const int dd = dbase + lane;
-      if (lane < 32 && dd >= 0) drp[dd] = win;
+      if (half == 1 && !stashed) {
+        stashed = true;
+        head = win;
+        head_base = dbase;
+      } else if (lane < 32 && dd >= 0) {
+        drp[dd] = win;
+      }
       win = __shfl_down(win, 32);
       if (lane >= 32) win = 0.f;
       dbase += 32;
     }
   }
-  {  // the distances still in the window, up to T - 1 - kw
+  // Half 0 hands its open window (the distances at the cut) and its column sums to half 1 when
+  // half 1 has tiles; otherwise, and in half 1, the open window is final.
+  col += __shfl_xor(col, 32);  // (all lanes: the partner lane must be active)
+  if (half == 0 && has1) {
+    if (lane < 32) {
+      xwin[kg][lane] = win;
+      xcol[kg][lane] = col;
+    }
+    if (lane == 0) xbase[kg] = started ? dbase : INT_MIN;
+  } else {
     const int dd = dbase + lane;
     if (started && lane < 32 && dd >= 0 && dd < T - kw) drp[dd] = win;
   }
-  col += __shfl_xor(col, 32);
-  if (hi == 0 && kval) p.dap[(size_t)br * T + kj] = col;
+  __syncthreads();
+  if (half == 1 && has1) {
+    if (stashed) {  // the cut's distances: half 0's part (if it reached them) + half 1's
+      const int dd = head_base + lane;
+      if (lane < 32 && dd >= 0) drp[dd] = (xbase[kg] == head_base ? xwin[kg][lane] : 0.f) + head;
+    }
+    if (hi == 0 && kval) p.dap[(size_t)br * T + kj] = xcol[kg][l32] + col;
+  } else if (half == 0 && !has1 && hi == 0 && kval) {
+    p.dap[(size_t)br * T + kj] = col;
+  }
 }
 
 constexpr int kSbChunk = 16;  // sub-block partial rows summed per thread by the first reduce stage
@@ -254,7 +306,7 @@ hipError_t launch_t(const LayerArgs& a, const HeadList& rl, hipStream_t s) {
   const int BRp = (a.B * rl.n + 7) & ~7;
   const long long blocks = (long long)BRp * ((a.T + C::BKV - 1) / C::BKV);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_pattern_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a, rl);
+  hipLaunchKernelGGL((bwd_pattern_kernel<TI, D>), dim3((unsigned)blocks), dim3(kPgNT), 0, s, a, rl);
   return hipGetLastError();
 }
 
