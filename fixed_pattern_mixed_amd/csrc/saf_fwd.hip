@@ -61,8 +61,16 @@ struct FwdCfg {
   // one barrier per tile, and the next tile's LDS stores overlap other waves' products
   static constexpr int NSTAGE = (BF && D == 128 && W == 8) ? 2 : 1;
   // a stage: the K tile (ordinary items) or the windows (replaced items) in one region, then V
-  static constexpr int KREG = ((BK * LDP * (int)sizeof(TI) > (BK + 4 * WINP) * 4 ? BK * LDP * (int)sizeof(TI)
-                                                                                  : (BK + 4 * WINP) * 4) + 15) & ~15;
+  // bf16 at d = 128 with 8 waves: replaced items cover two query blocks (each wave two 32-query
+  // subtiles, one per block; fwd_item_rep2).  Elsewhere the two accumulator sets do not fit the
+  // register budget (d = 64 runs four waves per SIMD in 128 registers).
+  static constexpr bool REP2 = BF && D == 128 && W == 8;
+  // the distance window of a replaced item, and its copies
+  static constexpr int WINR = BK + (REP2 ? 2 : 1) * BQ;
+  static constexpr int WINRP = win_pad(WINR);
+  static constexpr int WPTR = (WINR + NT - 1) / NT;
+  static constexpr int KBYTES = BK * LDP * (int)sizeof(TI), WBYTES = (BK + 4 * WINRP) * 4;
+  static constexpr int KREG = ((KBYTES > WBYTES ? KBYTES : WBYTES) + 15) & ~15;
   static constexpr int STAGE = KREG + VT_ELEMS * (int)sizeof(TI);
 };
 
@@ -349,6 +357,170 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, unsigned char* smem
   if (hi == 0) p.lse[((size_t)it.b * it.H + h) * T + qi] = lse;
 }
 
+// A replaced head's work item covers two query blocks, [q0, q0 + 2 BQ): each wave owns the 32-query
+// subtile q0 + 32w of the first and q0 + BQ + 32w of the second, so each staged V tile, each V^T
+// fragment read and each barrier serve twice the products of a one-block item (a replaced entry is
+// one multiply, so those fixed costs were most of the item).  Entries, windows and the row
+// normaliser are as in fwd_item.
+template <typename TI, int D, int KIND, int W>
+__device__ __forceinline__ void fwd_item_rep2(const LayerArgs& p, unsigned char* smem,
+                                              const FwdItem& it) {
+  using C = FwdCfg<TI, D, W>;
+  constexpr int BK = C::BK, NS = C::NS, kBQ = C::BQ, kNT = C::NT;
+  constexpr int LDT = C::LDT, WIN = C::WINR, WPT = C::WPTR, WINP = C::WINRP;
+  constexpr bool FACT = KIND == kProduct;
+  static_assert(KIND != kOrdinary, "replaced heads only");
+  const int T = it.T, h = it.h, q0 = it.q0;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qw0 = q0 + w * 32, qw1 = qw0 + kBQ;  // the wave's two subtiles
+  const int qi0 = qw0 + l32, qi1 = qw1 + l32;    // the lane's two queries
+  const TI* V = reinterpret_cast<const TI*>(p.v) + it.kvoff;
+  const float* arow = FACT ? p.pat.ea(h) : p.a + (size_t)h * p.pat_len;
+  const float* rrow = FACT ? p.pat.er(h) : p.r + (size_t)h * p.pat_len;
+  const float wscale = FACT ? 1.f : kLog2e;
+  const float wfill = FACT ? 0.f : -INFINITY;
+
+  const int kend = min(T, q0 + 2 * kBQ);
+  const int nkt = (kend + BK - 1) / BK;
+
+  std::conditional_t<C::BF, Chunks<TI, D, BK, kNT>, Blocks4<TI, D, BK, kNT>> vreg;
+  float awr = 0.f, rwr[WPT];
+  auto load_tile = [&](int k0) {
+    vreg.load(V, k0, T, tid);
+    const int d0 = q0 - k0 - (BK - 1);
+    if (tid < BK) awr = arow[min(k0 + tid, T - 1)];
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) rwr[j] = rrow[min(max(d0 + tid + j * kNT, 0), T - 1)];
+  };
+  auto store_tile = [&](int buf, int k0) {
+    const FwdSmem<TI> sm = fwd_stage<TI, C>(smem, buf);
+    if constexpr (C::BF)
+      vreg.template store_tile<false>(sm.VT, tid);
+    else
+      vreg.template store_cols<LDT>(sm.VT, tid);
+    const int d0 = q0 - k0 - (BK - 1);
+    if (tid < BK) sm.awin[tid] = (k0 + tid < T) ? awr * wscale : wfill;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int x = tid + j * kNT;
+      const int dist = d0 + x;
+      if (x < WIN) win_store(sm.rwin, WINP, x, (dist >= 0 && dist < T) ? rwr[j] * wscale : wfill);
+    }
+  };
+
+  const float lz0 = (KIND == kExponential && qi0 < T) ? p.pat.lz(h)[qi0] : 0.f;
+  const float lz1 = (KIND == kExponential && qi1 < T) ? p.pat.lz(h)[qi1] : 0.f;
+  const float lz20 = lz0 * kLog2e, lz21 = lz1 * kLog2e;
+  const TileLane<D, false> vtl(lane);
+
+  f32x16 oa0[D / 32], oa1[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    zero(oa0[c]);
+    zero(oa1[c]);
+  }
+  float l0 = 0.f, l1 = 0.f;
+  FwdSmem<TI> sm = fwd_stage<TI, C>(smem, 0);
+
+  // entries of query subtile (query qi at row offset qo = qi - q0) against 32-key subtile s
+  auto entries = [&](int s, int qo, float lz2, Frag<TI> (&pf)[2]) {
+    float pv[16];
+    const float* rb = win_base(sm.rwin, WINP, l32 & 3);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int kk = 32 * s + 8 * g + 4 * hi;
+      const float4 a4 = *reinterpret_cast<const float4*>(sm.awin + kk);
+      // window entries xr - e, xr - 3 = qo + BK - 4 - kk = l32 mod 4
+      const int xr = qo + (BK - 1) - kk;
+      const float4 r4 = win_read4(rb, xr - 3);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float rv[4] = {r4.w, r4.z, r4.y, r4.x};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pv[4 * g + e] = FACT ? av[e] * rv[e] : __builtin_amdgcn_exp2f(av[e] + rv[e] - lz2);
+    }
+    pf[0] = to_frag<TI>(&pv[0]);
+    pf[1] = to_frag<TI>(&pv[8]);
+    return frag_sum(pf[0]) + frag_sum(pf[1]);
+  };
+  auto vt_frag = [&](int s, int u, int c) {
+    if constexpr (C::BF)
+      return tile_tr_frag<D, false>(sm.VT, 32 * s + 16 * u, c, vtl);
+    else
+      return tt_frag<TI, LDT>(sm.VT, 32 * s + 16 * u, 32 * c + l32, hi);
+  };
+
+  constexpr bool DB = C::NSTAGE == 2;
+  load_tile(0);
+  store_tile(0, 0);
+  if (DB && nkt > 1) load_tile(BK);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BK;
+    sm = fwd_stage<TI, C>(smem, DB ? (kt & 1) : 0);
+    if (!DB && kt + 1 < nkt) load_tile(k0 + BK);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ks = k0 + 32 * s;
+      if (ks > qw1 + 31 || ks >= T) break;  // wave-uniform: nothing further visible to either subtile
+      Frag<TI> pf1[2];
+      l1 += entries(s, qi1 - q0, lz21, pf1);
+      if (ks <= qw0 + 31) {
+        // both subtiles see these keys: each V^T fragment feeds two products
+        Frag<TI> pf0[2];
+        l0 += entries(s, qi0 - q0, lz20, pf0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) {
+            const Frag<TI> vt = vt_frag(s, u, c);
+            mma16(oa0[c], vt, pf0[u]);
+            mma16(oa1[c], vt, pf1[u]);
+          }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) mma16(oa1[c], vt_frag(s, u, c), pf1[u]);
+      }
+    }
+    if constexpr (DB) {
+      if (kt + 1 < nkt) {
+        store_tile((kt + 1) & 1, k0 + BK);
+        if (kt + 2 < nkt) load_tile(k0 + 2 * BK);
+      }
+      __syncthreads();
+    } else {
+      __syncthreads();
+      if (kt + 1 < nkt) {
+        store_tile(0, k0 + BK);
+        __syncthreads();
+      }
+    }
+  }
+
+  // row normalisers and outputs of the two subtiles (as in fwd_item)
+  auto finish = [&](const f32x16 (&oacc)[D / 32], float l, int qi, float lz_q) {
+    const float lt = l + __shfl_xor(l, 32);
+    if (qi >= T) return;
+    const float inv = 1.f / lt;
+    const float lse = (FACT ? p.pat.shift(h) : lz_q) + logf(lt);
+    TI* O = reinterpret_cast<TI*>(p.out) + it.hoff + (size_t)qi * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dc = 32 * c + 8 * g + 4 * hi;
+        store4(O + dc, oacc[c][4 * g] * inv, oacc[c][4 * g + 1] * inv, oacc[c][4 * g + 2] * inv,
+               oacc[c][4 * g + 3] * inv);
+      }
+    if (hi == 0) p.lse[((size_t)it.b * it.H + h) * T + qi] = lse;
+  };
+  finish(oa0, l0, qi0, lz0);
+  finish(oa1, l1, qi1, lz1);
+}
+
 // Narrow items (W < 8) are launched only for grids of at most a few blocks per compute unit, where
 // occupancy cannot be high anyway: they get 256 registers (their staging registers, 4x those of a
 // wide item, would spill at 128), fp32 at d = 128 with 2 waves all 512 (it spills at 256).
@@ -377,12 +549,25 @@ void mixed_fwd_kernel(LayerArgs p) {
   it.q0 = (nqb - 1 - x / BHp) * C::BQ;  // heaviest query blocks first
   it.hoff = ((size_t)it.b * H + it.h) * (size_t)T * D;
   it.kvoff = ((size_t)it.b * p.Hkv + it.h / (H / p.Hkv)) * (size_t)T * D;
-  if (!is_replaced(p.rep, it.h))
+  if (!is_replaced(p.rep, it.h)) {
     fwd_item<TI, D, kOrdinary, W>(p, smem, it);
-  else if (p.pat.flag(it.h)[0] != 0)
-    fwd_item<TI, D, kProduct, W>(p, smem, it);
-  else
-    fwd_item<TI, D, kExponential, W>(p, smem, it);
+  } else {
+    const bool fact = p.pat.flag(it.h)[0] != 0;
+    if constexpr (C::REP2) {
+      // a replaced head's item at an even query block covers that block and the next; the item of
+      // the next block has nothing left to do
+      if ((it.q0 / C::BQ) & 1) return;
+      if (fact)
+        fwd_item_rep2<TI, D, kProduct, W>(p, smem, it);
+      else
+        fwd_item_rep2<TI, D, kExponential, W>(p, smem, it);
+    } else {
+      if (fact)
+        fwd_item<TI, D, kProduct, W>(p, smem, it);
+      else
+        fwd_item<TI, D, kExponential, W>(p, smem, it);
+    }
+  }
 }
 
 template <typename TI, int D, int W>
