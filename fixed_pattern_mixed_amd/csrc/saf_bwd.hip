@@ -103,13 +103,22 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   // padded rows and transposed copies
   constexpr bool kTr = sizeof(TI) == 2;
   constexpr int LDQ = kTr ? TileGeom<D>::LDR : LDP;
-  __shared__ __attribute__((aligned(16))) TI Qs[BQ * LDQ];   // Q tile, rows
-  __shared__ __attribute__((aligned(16))) TI Gs[BQ * LDQ];   // dO tile, rows
-  __shared__ __attribute__((aligned(16))) TI QT[kTr ? 8 : D * LDT];  // Q tile transposed [dim][query]
-  __shared__ __attribute__((aligned(16))) TI GT[kTr ? 8 : D * LDT];  // dO tile transposed [dcol][query]
-  __shared__ __attribute__((aligned(16))) float rss[BQ];     // row statistic per query
-  __shared__ __attribute__((aligned(16))) float dls[BQ];     // -delta per query
-  __shared__ __attribute__((aligned(16))) float rwin[4 * C::WINP];  // replaced: er / r*log2e window
+  // LDS: the sweep of an item with ordinary heads, or (bf16) the replaced-only sweep below, in one
+  // region
+  constexpr int E = (int)sizeof(TI);
+  constexpr int O_QS = 0, O_GS = O_QS + BQ * LDQ * E, O_QT = O_GS + BQ * LDQ * E;
+  constexpr int O_GT = O_QT + (kTr ? 16 : D * LDT * E), O_RS = O_GT + (kTr ? 16 : D * LDT * E);
+  constexpr int O_DL = O_RS + BQ * 4, O_RW = O_DL + BQ * 4, O_END = O_RW + 4 * C::WINP * 4;
+  constexpr int BQR = kTr ? 2 * BQ : BQ, WINR = BQR + BKV, WINRP = win_pad(WINR);
+  constexpr int R_RS = BQR * TileGeom<D>::LDR * E, R_RW = R_RS + BQR * 4, R_END = R_RW + 4 * WINRP * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[(O_END > R_END ? O_END : R_END)];
+  TI* Qs = reinterpret_cast<TI*>(smem + O_QS);    // Q tile, rows
+  TI* Gs = reinterpret_cast<TI*>(smem + O_GS);    // dO tile, rows
+  TI* QT = reinterpret_cast<TI*>(smem + O_QT);    // (fp32) Q tile transposed [dim][query]
+  TI* GT = reinterpret_cast<TI*>(smem + O_GT);    // (fp32) dO tile transposed [dcol][query]
+  float* rss = reinterpret_cast<float*>(smem + O_RS);   // row statistic per query
+  float* dls = reinterpret_cast<float*>(smem + O_DL);   // -delta per query
+  float* rwin = reinterpret_cast<float*>(smem + O_RW);  // replaced: er / r*log2e window (4 copies)
 
   const int T = p.T, H = p.H, Hkv = p.Hkv;
   const int GS = GROUPED ? H / Hkv : 1;  // query heads per key/value head (Hkv = H unless grouped)
@@ -154,264 +163,363 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   // head has its own factor, so it enters each entry.
   float vs = 1.f;
 
-  const int nqt = (T + BQ - 1) / BQ;
-  const int qt0 = kb0 / BQ;
-  for (int m = 0; m < GS; ++m) {
-    const int h = hk * GS + m;
-    const bool rep = is_replaced(p.rep, h);
-    const bool fact = rep && p.pat.flag(h)[0] != 0;
-    const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
-    const size_t soff = ((size_t)b * H + h) * (size_t)T;
-    const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
-    const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
-    const float* lse = p.lse + soff;
-    const float* dlt = p.delta + soff;
-    const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
-    const float wscale = fact ? 1.f : kLog2e;
-    const float wfill = fact ? 0.f : -INFINITY;
-    const float shift = fact ? p.pat.shift(h) : 0.f;
-    float akey = 0.f;  // replaced: the lane's key preference (ea, or a*log2e)
-    if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
-    const bool fold = fact && GS > 1;  // the key factor enters each entry
-    if (fact && GS == 1) vs = akey;
-
-    // The prefetch registers hold raw values (loads from clamped, always valid addresses): any
-    // arithmetic on a loaded value, or a select between it and a constant, would make the wave wait
-    // for the load there and then.  Masks and conversions are applied when the tile is stored.
-    KvPrefetch<TI, D> pf;
-    auto load_tile = [&](int q0) {
-      pf.g.load(G, q0, T, tid);
-      if (!rep) pf.q.load(Q, q0, T, tid);
-      if (tid < BQ) {
-        const int q = min(q0 + tid, T - 1);
-        pf.rs = lse[q];
-        pf.dl = dlt[q];  // (unused for a replaced head)
-      }
-      if (rep && tid < WIN) pf.rw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
-    };
-    auto store_tile = [&](int q0) {
-      if constexpr (kTr) {
-        pf.g.template store_tile<true>(Gs, tid);
-        if (!rep) pf.q.template store_tile<true>(Qs, tid);
-      } else {
-        pf.g.template store_cols<LDT>(GT, tid);
-        if (!rep) {
-          pf.g.template store_rows<LDP>(Gs, tid);
-          pf.q.template store_rows<LDP>(Qs, tid);
-          pf.q.template store_cols<LDT>(QT, tid);
-        }
-      }
-      if (tid < BQ) {
-        // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
-        // Rows past the end get weight 0 (their dO rows are zero; an unbounded weight times a zero
-        // row would not be zero).
-        const bool in = q0 + tid < T;
-        rss[tid] = in ? (fact ? expf(shift - pf.rs) : pf.rs * kLog2e) : (fact ? 0.f : INFINITY);
-        dls[tid] = (!rep && in) ? -pf.dl : 0.f;  // -delta: the initial value of the dP product
-      }
-      if (rep && tid < WIN) {
-        const int dist = q0 - (kb0 + BKV - 1) + tid;
-        win_store(rwin, C::WINP, tid, (dist >= 0 && dist < T) ? pf.rw * wscale : wfill);
-      }
-    };
-
-    // dO^T and Q^T fragments: rows row0 + perm_row(e, hi) (queries), column 32 c + l32
-    auto gt_frag = [&](int row0, int c) {
-      if constexpr (kTr)
-        return tile_tr_frag<D, true>(Gs, row0, c, tl);
-      else
-        return tt_frag<TI, LDT>(GT, row0, 32 * c + l32, hi);
-    };
-    auto qt_frag = [&](int row0, int c) {
-      if constexpr (kTr)
-        return tile_tr_frag<D, true>(Qs, row0, c, tl);
-      else
-        return tt_frag<TI, LDT>(QT, row0, 32 * c + l32, hi);
-    };
-    // Q and dO row fragments (lane = query row row_base + l32, columns 16t + 8hi ..)
-    auto q_row = [&](int row_base, int t) {
-      if constexpr (kTr)
-        return tile_row_frag<D, true>(Qs, row_base, t, tl);
-      else
-        return load8(Qs + (row_base + l32) * LDP + 16 * t + 8 * hi);
-    };
-    auto g_row = [&](int row_base, int t) {
-      if constexpr (kTr)
-        return tile_row_frag<D, true>(Gs, row_base, t, tl);
-      else
-        return load8(Gs + (row_base + l32) * LDP + 16 * t + 8 * hi);
-    };
-
-    if (qt0 < nqt) load_tile(qt0 * BQ);
-
-    for (int qt = qt0; qt < nqt; ++qt) {
-      const int q0 = qt * BQ;
-      __syncthreads();  // the previous tile's readers are done
-      store_tile(q0);
-      __syncthreads();
-      if (qt + 1 < nqt) load_tile(q0 + BQ);
-
-      // Ordinary head, both subtiles below the diagonal and inside the sequence (most tiles):
-      // straight-line code without masks, ordered so that subtile 1's score product is in flight
-      // during subtile 0's exponentials (and, at d = 128, its dP product during subtile 0's dV /
-      // dK products).
-      // The dP product of a subtile starts from -delta of its queries (read from LDS into the
-      // accumulator), so that it yields dP - delta and dS = P o (dP - delta) is one multiply.
-      auto neg_delta = [&](int s) {
-        f32x16 c;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 d4 = *reinterpret_cast<const float4*>(dls + 32 * s + 8 * g + 4 * hi);
-          c[4 * g] = d4.x;
-          c[4 * g + 1] = d4.y;
-          c[4 * g + 2] = d4.z;
-          c[4 * g + 3] = d4.w;
-        }
-        return c;
+  bool swept = false;
+  if constexpr (kTr) if (!any_ord) {
+    swept = true;
+    // Every query head of the item is replaced (bf16): P from the pattern, dV the only product, no
+    // Q tile and no K, V fragments, so tiles are 2 BQ queries tall (each wave: its 32 keys x four
+    // 32-query subtiles per tile), which halves the staging, barriers and statistics per product.
+    TI* Gr = reinterpret_cast<TI*>(smem);                // dO tile, rows
+    float* rsr = reinterpret_cast<float*>(smem + R_RS);  // row scale per query
+    float* rwr = reinterpret_cast<float*>(smem + R_RW);  // distance window (4 copies)
+    const float* rwb = win_base(rwr, WINRP, (3 - l32) & 3);
+    const int nqr = (T + BQR - 1) / BQR;
+    const int qr0 = kb0 / BQR;
+    for (int m = 0; m < GS; ++m) {
+      const int h = hk * GS + m;
+      const bool fact = p.pat.flag(h)[0] != 0;
+      const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+      const size_t soff = ((size_t)b * H + h) * (size_t)T;
+      const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
+      const float* lse = p.lse + soff;
+      const float* rrow = fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len;
+      const float wscale = fact ? 1.f : kLog2e;
+      const float wfill = fact ? 0.f : -INFINITY;
+      const float shift = fact ? p.pat.shift(h) : 0.f;
+      float akey = 0.f;
+      if (kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
+      const bool fold = fact && GS > 1;
+      if (fact && GS == 1) vs = akey;
+      Chunks<TI, D, BQR, kKvNT> pg;
+      float prs = 0.f, prw = 0.f;
+      auto load_tile = [&](int q0) {
+        pg.load(G, q0, T, tid);
+        if (tid < BQR) prs = lse[min(q0 + tid, T - 1)];
+        if (tid < WINR) prw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
       };
-      if (NS == 2 && !rep && q0 >= kw + 31 && q0 + BQ <= T && kw + 31 < T) {
-        auto grad_entries = [&](const f32x16& st, const f32x16& dpt, int s, float* pr, float* ds) {
+      auto store_tile = [&](int q0) {
+        pg.template store_tile<true>(Gr, tid);
+        if (tid < BQR) {
+          const bool in = q0 + tid < T;
+          rsr[tid] = in ? (fact ? expf(shift - prs) : prs * kLog2e) : (fact ? 0.f : INFINITY);
+        }
+        if (tid < WINR) {
+          const int dist = q0 - (kb0 + BKV - 1) + tid;
+          win_store(rwr, WINRP, tid, (dist >= 0 && dist < T) ? prw * wscale : wfill);
+        }
+      };
+      load_tile(qr0 * BQR);
+      for (int qt = qr0; qt < nqr; ++qt) {
+        const int q0 = qt * BQR;
+        __syncthreads();  // the previous tile's readers are done
+        store_tile(q0);
+        __syncthreads();
+        if (qt + 1 < nqr) load_tile(q0 + BQR);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float4 l4 = *reinterpret_cast<const float4*>(rss + 32 * s + 8 * g + 4 * hi);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        for (int sub = 0; sub < BQR / 32; ++sub) {
+          const int qs = q0 + 32 * sub;
+          if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
+          auto rep_entries = [&](auto fact_c, int u) {
+            constexpr bool kFact = decltype(fact_c)::value;
+            float pr[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              const float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
-              pr[r] = pp;
-              ds[r] = pp * dpt[r];
+            for (int g2 = 0; g2 < 2; ++g2) {
+              const int g = 2 * u + g2;
+              const int qr = 32 * sub + 8 * g + 4 * hi;  // tile row of register group g
+              const float4 l4 = *reinterpret_cast<const float4*>(rsr + qr);
+              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+              const int xr = qr + (kb0 + BKV - 1) - kj;  // = 3 - l32 mod 4
+              const float4 r4 = win_read4(rwb, xr);
+              const float rw4[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float pp = kFact ? rw4[e] * lv[e] : __builtin_amdgcn_exp2f(akey + rw4[e] - lv[e]);
+                if (kFact && fold) pp *= akey;
+                pr[4 * g2 + e] = pp;
+              }
             }
-          }
-        };
-        auto grad_products = [&](int s, const float* pr, const float* ds) {
+            return to_frag<TI>(pr);
+          };
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
-            const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
+            const Frag<TI> pfr = fact ? rep_entries(std::true_type{}, u) : rep_entries(std::false_type{}, u);
 #pragma unroll
             for (int c = 0; c < D / 32; ++c) {
-              mma16(dvT[c], gt_frag(32 * s + 16 * u, c), pfr);
-              mma16(dkT[c], qt_frag(32 * s + 16 * u, c), sfr);
+              if constexpr (kTr)
+                mma16(dvT[c], tile_tr_frag<D, true>(Gr, 32 * sub + 16 * u, c, tl), pfr);
             }
           }
-        };
-        f32x16 st0, dp0 = neg_delta(0), st1, dp1 = neg_delta(1);
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          mma16(st0, q_row(0, t), kf[t], t == 0);
-          mma16(dp0, g_row(0, t), vf[t]);
         }
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-          mma16(st1, q_row(32, t), kf[t], t == 0);
-        float pr[16], ds[16];
-        grad_entries(st0, dp0, 0, pr, ds);
-        if constexpr (D == 64) {
-          // 256-register budget (two waves per SIMD): subtile 0's products first keeps the
-          // live set smaller (measured faster at d = 64)
-          grad_products(0, pr, ds);
-#pragma unroll
-          for (int t = 0; t < D / 16; ++t)
-            mma16(dp1, g_row(32, t), vf[t]);
-        } else {
-#pragma unroll
-          for (int t = 0; t < D / 16; ++t)
-            mma16(dp1, g_row(32, t), vf[t]);
-          grad_products(0, pr, ds);
-        }
-        grad_entries(st1, dp1, 1, pr, ds);
-        grad_products(1, pr, ds);
-        continue;
       }
+      if (kj < T) {  // a replaced head's query gradient is zero
+        TI* dQ = reinterpret_cast<TI*>(p.dq) + hoff + (size_t)kj * D;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+  if (!swept) {
+    const int nqt = (T + BQ - 1) / BQ;
+    const int qt0 = kb0 / BQ;
+    for (int m = 0; m < GS; ++m) {
+      const int h = hk * GS + m;
+      const bool rep = is_replaced(p.rep, h);
+      const bool fact = rep && p.pat.flag(h)[0] != 0;
+      const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+      const size_t soff = ((size_t)b * H + h) * (size_t)T;
+      const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
+      const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
+      const float* lse = p.lse + soff;
+      const float* dlt = p.delta + soff;
+      const float* rrow = rep ? (fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len) : nullptr;
+      const float wscale = fact ? 1.f : kLog2e;
+      const float wfill = fact ? 0.f : -INFINITY;
+      const float shift = fact ? p.pat.shift(h) : 0.f;
+      float akey = 0.f;  // replaced: the lane's key preference (ea, or a*log2e)
+      if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
+      const bool fold = fact && GS > 1;  // the key factor enters each entry
+      if (fact && GS == 1) vs = akey;
 
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int qs = q0 + 32 * s;
-        if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
-        const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
-        float pr[16], ds[16];
-        if (!rep) {
-          f32x16 st, dpt = neg_delta(s);
-#pragma unroll
-          for (int t = 0; t < D / 16; ++t) {
-            mma16(st, q_row(32 * s, t), kf[t], t == 0);
-            mma16(dpt, g_row(32 * s, t), vf[t]);
+      // The prefetch registers hold raw values (loads from clamped, always valid addresses): any
+      // arithmetic on a loaded value, or a select between it and a constant, would make the wave wait
+      // for the load there and then.  Masks and conversions are applied when the tile is stored.
+      KvPrefetch<TI, D> pf;
+      auto load_tile = [&](int q0) {
+        pf.g.load(G, q0, T, tid);
+        if (!rep) pf.q.load(Q, q0, T, tid);
+        if (tid < BQ) {
+          const int q = min(q0 + tid, T - 1);
+          pf.rs = lse[q];
+          pf.dl = dlt[q];  // (unused for a replaced head)
+        }
+        if (rep && tid < WIN) pf.rw = rrow[min(max(q0 - (kb0 + BKV - 1) + tid, 0), T - 1)];
+      };
+      auto store_tile = [&](int q0) {
+        if constexpr (kTr) {
+          pf.g.template store_tile<true>(Gs, tid);
+          if (!rep) pf.q.template store_tile<true>(Qs, tid);
+        } else {
+          pf.g.template store_cols<LDT>(GT, tid);
+          if (!rep) {
+            pf.g.template store_rows<LDP>(Gs, tid);
+            pf.q.template store_rows<LDP>(Qs, tid);
+            pf.q.template store_cols<LDT>(QT, tid);
           }
-          // one copy per case; the mask is one select per entry (bitwise conditions: a
-          // short-circuit chain would branch per entry)
-          auto entries = [&](auto masked) {
+        }
+        if (tid < BQ) {
+          // ordinary / exponential form: lse in log2 units; product form: row scale exp(Ma+Mr-lse).
+          // Rows past the end get weight 0 (their dO rows are zero; an unbounded weight times a zero
+          // row would not be zero).
+          const bool in = q0 + tid < T;
+          rss[tid] = in ? (fact ? expf(shift - pf.rs) : pf.rs * kLog2e) : (fact ? 0.f : INFINITY);
+          dls[tid] = (!rep && in) ? -pf.dl : 0.f;  // -delta: the initial value of the dP product
+        }
+        if (rep && tid < WIN) {
+          const int dist = q0 - (kb0 + BKV - 1) + tid;
+          win_store(rwin, C::WINP, tid, (dist >= 0 && dist < T) ? pf.rw * wscale : wfill);
+        }
+      };
+
+      // dO^T and Q^T fragments: rows row0 + perm_row(e, hi) (queries), column 32 c + l32
+      auto gt_frag = [&](int row0, int c) {
+        if constexpr (kTr)
+          return tile_tr_frag<D, true>(Gs, row0, c, tl);
+        else
+          return tt_frag<TI, LDT>(GT, row0, 32 * c + l32, hi);
+      };
+      auto qt_frag = [&](int row0, int c) {
+        if constexpr (kTr)
+          return tile_tr_frag<D, true>(Qs, row0, c, tl);
+        else
+          return tt_frag<TI, LDT>(QT, row0, 32 * c + l32, hi);
+      };
+      // Q and dO row fragments (lane = query row row_base + l32, columns 16t + 8hi ..)
+      auto q_row = [&](int row_base, int t) {
+        if constexpr (kTr)
+          return tile_row_frag<D, true>(Qs, row_base, t, tl);
+        else
+          return load8(Qs + (row_base + l32) * LDP + 16 * t + 8 * hi);
+      };
+      auto g_row = [&](int row_base, int t) {
+        if constexpr (kTr)
+          return tile_row_frag<D, true>(Gs, row_base, t, tl);
+        else
+          return load8(Gs + (row_base + l32) * LDP + 16 * t + 8 * hi);
+      };
+
+      if (qt0 < nqt) load_tile(qt0 * BQ);
+
+      for (int qt = qt0; qt < nqt; ++qt) {
+        const int q0 = qt * BQ;
+        __syncthreads();  // the previous tile's readers are done
+        store_tile(q0);
+        __syncthreads();
+        if (qt + 1 < nqt) load_tile(q0 + BQ);
+
+        // Ordinary head, both subtiles below the diagonal and inside the sequence (most tiles):
+        // straight-line code without masks, ordered so that subtile 1's score product is in flight
+        // during subtile 0's exponentials (and, at d = 128, its dP product during subtile 0's dV /
+        // dK products).
+        // The dP product of a subtile starts from -delta of its queries (read from LDS into the
+        // accumulator), so that it yields dP - delta and dS = P o (dP - delta) is one multiply.
+        auto neg_delta = [&](int s) {
+          f32x16 c;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 d4 = *reinterpret_cast<const float4*>(dls + 32 * s + 8 * g + 4 * hi);
+            c[4 * g] = d4.x;
+            c[4 * g + 1] = d4.y;
+            c[4 * g + 2] = d4.z;
+            c[4 * g + 3] = d4.w;
+          }
+          return c;
+        };
+        if (NS == 2 && !rep && q0 >= kw + 31 && q0 + BQ <= T && kw + 31 < T) {
+          auto grad_entries = [&](const f32x16& st, const f32x16& dpt, int s, float* pr, float* ds) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
-              const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+              const float4 l4 = *reinterpret_cast<const float4*>(rss + 32 * s + 8 * g + 4 * hi);
               const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
-                float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
-                if constexpr (decltype(masked)::value) {
-                  const int q = q0 + qr + e;
-                  pp = ((q >= kj) & (q < T) & (kj < T)) ? pp : 0.f;
-                }
+                const float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
                 pr[r] = pp;
                 ds[r] = pp * dpt[r];
               }
             }
           };
-          if (edge)
-            entries(std::true_type{});
-          else
-            entries(std::false_type{});
-        } else {
-          // one copy per form (uniform over the head): selecting per entry would evaluate both
-          auto rep_entries = [&](auto fact_c) {
-            constexpr bool kFact = decltype(fact_c)::value;
+          auto grad_products = [&](int s, const float* pr, const float* ds) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int qr = 32 * s + 8 * g + 4 * hi;
-              const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
-              const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-              // window entries xr .. xr+3 of distances (q0 + qr + e) - kj; xr = 3 - l32 mod 4
-              const int xr = qr + (kb0 + BKV - 1) - kj;
-              const float4 r4 = win_read4(win_base(rwin, C::WINP, (3 - l32) & 3), xr);
-              const float rw4[4] = {r4.x, r4.y, r4.z, r4.w};
+            for (int u = 0; u < 2; ++u) {
+              const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
+              const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float rv = rw4[e];
-                float pp = kFact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
-                if (kFact && fold) pp *= akey;
-                pr[4 * g + e] = pp;
+              for (int c = 0; c < D / 32; ++c) {
+                mma16(dvT[c], gt_frag(32 * s + 16 * u, c), pfr);
+                mma16(dkT[c], qt_frag(32 * s + 16 * u, c), sfr);
               }
             }
           };
-          if (fact)
-            rep_entries(std::true_type{});
-          else
-            rep_entries(std::false_type{});
+          f32x16 st0, dp0 = neg_delta(0), st1, dp1 = neg_delta(1);
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t) {
+            mma16(st0, q_row(0, t), kf[t], t == 0);
+            mma16(dp0, g_row(0, t), vf[t]);
+          }
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t)
+            mma16(st1, q_row(32, t), kf[t], t == 0);
+          float pr[16], ds[16];
+          grad_entries(st0, dp0, 0, pr, ds);
+          if constexpr (D == 64) {
+            // 256-register budget (two waves per SIMD): subtile 0's products first keeps the
+            // live set smaller (measured faster at d = 64)
+            grad_products(0, pr, ds);
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+              mma16(dp1, g_row(32, t), vf[t]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+              mma16(dp1, g_row(32, t), vf[t]);
+            grad_products(0, pr, ds);
+          }
+          grad_entries(st1, dp1, 1, pr, ds);
+          grad_products(1, pr, ds);
+          continue;
         }
-        // dV^T[dcol][key] += dO^T[dcol][q] P[q][key];  dK^T[dim][key] += Q^T[dim][q] dS[q][key]
+
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c)
-            mma16(dvT[c], gt_frag(32 * s + 16 * u, c), pfr);
+        for (int s = 0; s < NS; ++s) {
+          const int qs = q0 + 32 * s;
+          if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
+          const bool edge = (qs < kw + 31) || (qs + 31 >= T) || (kw + 31 >= T);
+          float pr[16], ds[16];
           if (!rep) {
-            const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
+            f32x16 st, dpt = neg_delta(s);
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) {
+              mma16(st, q_row(32 * s, t), kf[t], t == 0);
+              mma16(dpt, g_row(32 * s, t), vf[t]);
+            }
+            // one copy per case; the mask is one select per entry (bitwise conditions: a
+            // short-circuit chain would branch per entry)
+            auto entries = [&](auto masked) {
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int qr = 32 * s + 8 * g + 4 * hi;  // tile row of register group g
+                const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int r = 4 * g + e;
+                  float pp = __builtin_amdgcn_exp2f(fmaf(st[r], c2, -lv[e]));
+                  if constexpr (decltype(masked)::value) {
+                    const int q = q0 + qr + e;
+                    pp = ((q >= kj) & (q < T) & (kj < T)) ? pp : 0.f;
+                  }
+                  pr[r] = pp;
+                  ds[r] = pp * dpt[r];
+                }
+              }
+            };
+            if (edge)
+              entries(std::true_type{});
+            else
+              entries(std::false_type{});
+          } else {
+            // one copy per form (uniform over the head): selecting per entry would evaluate both
+            auto rep_entries = [&](auto fact_c) {
+              constexpr bool kFact = decltype(fact_c)::value;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int qr = 32 * s + 8 * g + 4 * hi;
+                const float4 l4 = *reinterpret_cast<const float4*>(rss + qr);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                // window entries xr .. xr+3 of distances (q0 + qr + e) - kj; xr = 3 - l32 mod 4
+                const int xr = qr + (kb0 + BKV - 1) - kj;
+                const float4 r4 = win_read4(win_base(rwin, C::WINP, (3 - l32) & 3), xr);
+                const float rw4[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float rv = rw4[e];
+                  float pp = kFact ? rv * lv[e] : __builtin_amdgcn_exp2f(akey + rv - lv[e]);
+                  if (kFact && fold) pp *= akey;
+                  pr[4 * g + e] = pp;
+                }
+              }
+            };
+            if (fact)
+              rep_entries(std::true_type{});
+            else
+              rep_entries(std::false_type{});
+          }
+          // dV^T[dcol][key] += dO^T[dcol][q] P[q][key];  dK^T[dim][key] += Q^T[dim][q] dS[q][key]
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const Frag<TI> pfr = to_frag<TI>(&pr[8 * u]);
 #pragma unroll
             for (int c = 0; c < D / 32; ++c)
-              mma16(dkT[c], qt_frag(32 * s + 16 * u, c), sfr);
+              mma16(dvT[c], gt_frag(32 * s + 16 * u, c), pfr);
+            if (!rep) {
+              const Frag<TI> sfr = to_frag<TI>(&ds[8 * u]);
+#pragma unroll
+              for (int c = 0; c < D / 32; ++c)
+                mma16(dkT[c], qt_frag(32 * s + 16 * u, c), sfr);
+            }
           }
         }
       }
-    }
-    if (rep && kj < T) {  // a replaced head's query gradient is zero
-      TI* dQ = reinterpret_cast<TI*>(p.dq) + hoff + (size_t)kj * D;
+      if (rep && kj < T) {  // a replaced head's query gradient is zero
+        TI* dQ = reinterpret_cast<TI*>(p.dq) + hoff + (size_t)kj * D;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c)
+        for (int c = 0; c < D / 32; ++c)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
+          for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
+      }
     }
   }
 
