@@ -3,7 +3,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import TOL, Worst, all_heads, check_fwd, sample_rows
+from gpu_util import TOL, Worst, all_heads, check_bwd, check_fwd, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -118,3 +118,43 @@ def test_forward_full_size_sampled(name):
     wr = Worst("fwd sampled " + name)
     check_fwd(x, o, lse, all_heads(w.B, w.H), rows, TOL[w.torch_dtype], name, worst=wr)
     wr.report(workload=name)
+
+
+# bf16 at d = 128 with 8-wave items (grids of at least 256 items): a replaced head's item covers two
+# query blocks (each wave one 32-query subtile in each).  Product form on a ragged length (the last
+# query block pair reaches past T), and the exponential form (a pattern whose factorised weights
+# underflow), each with the backward's replaced-only key blocks.
+PAIRED = [
+    # B, H, T, wide-range pattern
+    (4, 16, 4000, False),
+    (2, 16, 2048, True),
+]
+
+
+@pytest.mark.parametrize("B,H,T,wide", PAIRED, ids=["B%dH%dT%d-%s" % (c[0], c[1], c[2], "exp" if c[3] else "prod") for c in PAIRED])
+def test_replaced_items_covering_two_query_blocks(B, H, T, wide):
+    saf = _saf()
+    d, dtype = 128, torch.bfloat16
+    rep = synth.replaced_mask(H, 4, "interleaved")
+    x = synth.layer_inputs(B, H, T, d, dtype, rep, ar_std=0.5, seed=71 + T)
+    if wide:  # one key preferred by 200 nats: exp(a - max a) is 0 in fp32 for every other key
+        for h in range(H):
+            if rep[h]:
+                x.a[h, T - 1] = 200.0
+    g = synth.layer_inputs(B, H, T, d, dtype, rep, ar_std=0.5, seed=71 + T, device="cuda")
+    g.a.copy_(x.a)
+    g.r.copy_(x.r)
+    pat = saf.prepare_pattern(rep, g.a, g.r)
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)
+    dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, pattern=pat)
+    torch.cuda.synchronize()
+    print("B%d H%d T%d wide=%s" % (B, H, T, wide), flush=True)
+    # every replaced slice and one ordinary slice per batch entry; rows of both query blocks of
+    # every pair, the last ones included
+    heads = [(b, h) for b in range(B) for h in range(H) if rep[h]] + [(b, 0) for b in range(B)]
+    rows = sample_rows(T, 96, seed=T)
+    wr = Worst("paired B%dH%dT%d" % (B, H, T))
+    check_fwd(x, o, lse, heads, rows, TOL[dtype], "paired fwd", worst=wr)
+    check_bwd(x, dq, dk, dv, [(b, h) for b in range(B) for h in range(H) if rep[h]], rows, rows,
+              TOL[dtype], "paired bwd", worst=wr)
+    wr.report()

@@ -67,6 +67,9 @@ SMALL = [
     (2, 6, 3, 200, 64, torch.float32, [1, 0, 0, 1, 1, 1]),
     (1, 8, 4, 129, 128, torch.bfloat16, [0, 0, 0, 0, 0, 0, 0, 0]),
     (1, 4, 2, 1, 64, torch.float32, [0, 1, 1, 0]),
+    # bf16 d = 128 (the 8-wave key-block kernel): a group of ordinary and replaced heads, and a
+    # group whose heads are all replaced (its replaced-only sweep, key factors in every entry)
+    (1, 8, 2, 257, 128, torch.bfloat16, [0, 0, 0, 1, 1, 1, 1, 1]),
 ]
 
 
