@@ -341,15 +341,23 @@ def fit_timing(torch, saf, ahat, stream, steps=400, lr=0.1, reps=2):
 
 
 def cpu_model():
-    """The host CPU's model name (from /proc/cpuinfo, as lscpu reports it)."""
+    """The host CPU's model name with its family / model / stepping numbers (from /proc/cpuinfo, as
+    lscpu reports them: some hosts give only a family name)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
-                if ln.startswith("model name"):
-                    return ln.split(":", 1)[1].strip()
+                if ":" not in ln:
+                    if info:
+                        break  # the first processor's block is enough
+                    continue
+                k, v = (t.strip() for t in ln.split(":", 1))
+                info.setdefault(k, v)
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    ids = ["%s %s" % (k, info[k]) for k in ("cpu family", "model", "stepping") if k in info]
+    return "%s (%s)" % (name, ", ".join(ids)) if ids else name
 
 
 def cpu_baseline(w, replaced, min_seconds=10.0):

@@ -31,6 +31,12 @@
 #ifndef SAF_FWD_BK
 #define SAF_FWD_BK 128
 #endif
+#ifndef SAF_FWD_SCHED_PV
+#define SAF_FWD_SCHED_PV 3  // vector instructions after each P V product of a pipelined block
+#endif
+#ifndef SAF_FWD_SCHED_S
+#define SAF_FWD_SCHED_S 3   // ... and after each score product
+#endif
 #ifndef SAF_FWD_W64
 #define SAF_FWD_W64 4  // minimum waves per SIMD requested for d = 64 (fits in 128 VGPRs)
 #endif
@@ -244,19 +250,20 @@ __device__ __forceinline__ void fwd_item(const LayerArgs& p, unsigned char* smem
   };
 
   // Scheduling groups of one pipelined block: 8 P V products (two transposing LDS reads each) and 8
-  // score products (one 16-byte LDS read each), each followed by three vector instructions.
+  // score products (one 16-byte LDS read each), each followed by SAF_FWD_SCHED_PV / _S vector
+  // instructions.
   auto interleave_block = [&]() {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // vector
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                 // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // matrix
+      __builtin_amdgcn_sched_group_barrier(0x002, SAF_FWD_SCHED_PV, 0);  // vector
     }
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, SAF_FWD_SCHED_S, 0);
     }
   };
 
