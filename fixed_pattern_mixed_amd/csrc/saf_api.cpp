@@ -114,7 +114,11 @@ static void fill_slot_order(saf::SlotOrder& o, const int* cost, int n) {
 
 void fill_order(saf::LayerArgs& la, const uint8_t* replaced) {
   int cost[saf::kMaxHeads];
-  for (int h = 0; h < la.H; ++h) cost[h] = replaced[h] ? 0 : 1;
+  la.n_ord = 0;
+  for (int h = 0; h < la.H; ++h) {
+    cost[h] = replaced[h] ? 0 : 1;
+    la.n_ord += cost[h];
+  }
   fill_slot_order(la.qord, cost, la.H);
   const int G = la.H / la.Hkv;
   for (int hk = 0; hk < la.Hkv; ++hk) {

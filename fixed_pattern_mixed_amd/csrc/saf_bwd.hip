@@ -966,7 +966,10 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   __shared__ __attribute__((aligned(16))) TI Vs[BK * LDP];   // V tile, rows
 
   const int T = p.T, H = p.H;
-  const int BH = p.B * H;
+  // the grid covers the ordinary slices only (the first B * n_ord slots; the replaced heads' zero
+  // dQ rows come from bwd_kv): blocks that would exit at once cost the launch more than their
+  // share (mixed layer at B=2, H=16, T=8192, d=128: 0.629 against 0.561 ms for the same 24 slices)
+  const int BH = p.B * p.n_ord;
   const int BHp = (BH + 7) & ~7;
   const int nqb = (T + BQ - 1) / BQ;
   const int x = blockIdx.x;
@@ -975,7 +978,6 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
   const int qb = nqb - 1 - x / BHp;  // heaviest query blocks first
   int b, h;
   p.qord.slice(bh, p.B, b, h);
-  if (is_replaced(p.rep, h)) return;  // replaced heads: zero dQ rows come from bwd_kv
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -1162,8 +1164,9 @@ hipError_t launch_kv_t(const LayerArgs& a, hipStream_t s) {
 
 template <typename TI, int D>
 hipError_t launch_dq_t(const LayerArgs& a, hipStream_t s) {
-  const int BHp = (a.B * a.H + 7) & ~7;
+  const int BHp = (a.B * a.n_ord + 7) & ~7;
   const long long blocks = (long long)BHp * ((a.T + DqCfg<TI, D>::BQ - 1) / DqCfg<TI, D>::BQ);
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_dq_kernel<TI, D>), dim3((unsigned)blocks), dim3(DqCfg<TI, D>::NT), 0, s, a);
   return hipGetLastError();

@@ -547,13 +547,32 @@ void mixed_fwd_kernel(LayerArgs p) {
   const int BHp = (BH + 7) & ~7;  // pad so that blockIdx % 8 (the XCD) depends on the slice only
   const int nqb = (T + C::BQ - 1) / C::BQ;
   const int x = blockIdx.x;
-  const int bh = x % BHp;
+  // Rows of the grid are query blocks, heaviest first; a row holds one block per slice slot.
+  int bh, row;
+  if constexpr (C::REP2) {
+    // A replaced head's item covers two query blocks (fwd_item_rep2), so it takes a slot in the
+    // even rows only: even rows hold every slot, odd rows the ordinary slots (the first B * n_ord),
+    // and no block of the grid is left without work but the padding.
+    const int BHo = p.B * p.n_ord, BHop = (BHo + 7) & ~7;
+    const int pair = x / (BHp + BHop), o = x % (BHp + BHop);
+    if (o < BHp) {
+      bh = o;
+      row = 2 * pair;
+    } else {
+      bh = o - BHp;
+      row = 2 * pair + 1;
+      if (bh >= BHo) return;
+    }
+  } else {
+    bh = x % BHp;
+    row = x / BHp;
+  }
   if (bh >= BH) return;
   FwdItem it;
   it.T = T;
   it.H = H;
   p.qord.slice(bh, p.B, it.b, it.h);
-  it.q0 = (nqb - 1 - x / BHp) * C::BQ;  // heaviest query blocks first
+  it.q0 = (nqb - 1 - row) * C::BQ;  // heaviest query blocks first
   it.hoff = ((size_t)it.b * H + it.h) * (size_t)T * D;
   it.kvoff = ((size_t)it.b * p.Hkv + it.h / (H / p.Hkv)) * (size_t)T * D;
   if (!is_replaced(p.rep, it.h)) {
@@ -561,9 +580,9 @@ void mixed_fwd_kernel(LayerArgs p) {
   } else {
     const bool fact = p.pat.flag(it.h)[0] != 0;
     if constexpr (C::REP2) {
-      // a replaced head's item at an even query block covers that block and the next; the item of
-      // the next block has nothing left to do
-      if ((it.q0 / C::BQ) & 1) return;
+      // even row 2k: the k-th pair from the end, query blocks 2 (nqr - 1 - k) and the next
+      const int nqr = (nqb + 1) / 2;
+      it.q0 = 2 * (nqr - 1 - row / 2) * C::BQ;
       if (fact)
         fwd_item_rep2<TI, D, kProduct, W>(p, smem, it);
       else
@@ -581,7 +600,11 @@ template <typename TI, int D, int W>
 hipError_t launch_fwd_w(const LayerArgs& a, hipStream_t s) {
   const int BHp = (a.B * a.H + 7) & ~7;
   const int nqb = (a.T + 32 * W - 1) / (32 * W);
-  const long long blocks = (long long)BHp * nqb;
+  long long blocks = (long long)BHp * nqb;
+  if (FwdCfg<TI, D, W>::REP2) {  // odd rows: the ordinary slots only
+    const int BHop = (a.B * a.n_ord + 7) & ~7;
+    blocks = (long long)BHp * ((nqb + 1) / 2) + (long long)BHop * (nqb / 2);
+  }
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((mixed_fwd_kernel<TI, D, W>), dim3((unsigned)blocks), dim3(64 * W), 0, s, a);
   return hipGetLastError();

@@ -70,6 +70,8 @@ struct LayerArgs {
   uint64_t rep[kMaxHeads / 64];  // bit h set = head h is replaced
   // Work-item order of the (batch, head) slices, for query heads and for key/value heads.
   SlotOrder qord, kvord;
+  int n_ord;         // query heads that are not replaced: qord lists them first, so the first
+                     // B * n_ord query slots are the ordinary slices
   const void* q;
   const void* k;
   const void* v;
