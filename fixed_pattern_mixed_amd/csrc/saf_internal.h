@@ -72,6 +72,8 @@ struct LayerArgs {
   SlotOrder qord, kvord;
   int n_ord;         // query heads that are not replaced: qord lists them first, so the first
                      // B * n_ord query slots are the ordinary slices
+  int n_kv_ro;       // key/value heads whose query heads are all replaced (kvord lists them last)
+  int kv_s0, kv_ns;  // bwd_kv: the key/value slots [kv_s0, kv_s0 + kv_ns) of one launch
   const void* q;
   const void* k;
   const void* v;
@@ -160,7 +162,11 @@ __host__ __device__ inline size_t fit_state_stride(int T) { return ((size_t)15 *
 hipError_t launch_pattern_prepare(const LayerArgs& a, hipStream_t s);
 hipError_t launch_mixed_fwd(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);
+// bwd_kv over all key/value slots, or (when bwd_kv_split) as two launches: the slots with an
+// ordinary query head, then the replaced-only ones.
+enum KvPart { kKvAll = 0, kKvOrdinary = 1, kKvReplacedOnly = 2 };
+bool bwd_kv_split(const LayerArgs& a, bool bf16);
+hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s, int part);
 hipError_t launch_bwd_dq(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pattern(const LayerArgs& a, const HeadList& rl, bool bf16, hipStream_t s);
 hipError_t launch_pattern_grad_reduce(const LayerArgs& a, const HeadList& rl, hipStream_t s);
