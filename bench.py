@@ -39,26 +39,17 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 
 
-def kernel_flops(B, T, d, replaced, Hkv=None, split=False):
-    """Algorithmic flops of one launch of each kernel (GEMM work the method defines).  split: the
-    key/value kernel ran as two launches, "bwd_kv" over the key/value heads with an ordinary query
-    head and "bwd_kv_rep" over those whose query heads are all replaced (dV only)."""
+def kernel_flops(B, T, d, replaced):
+    """Algorithmic flops of one launch of each kernel (GEMM work the method defines)."""
     c = T * (T + 1) / 2.0
     n_rep = sum(1 for x in replaced if x)
     n_ord = len(replaced) - n_rep
-    G = len(replaced) // (Hkv or len(replaced))
-    groups = [replaced[g:g + G] for g in range(0, len(replaced), G)]
-    kv_ro = sum(G * 2 * d for grp in groups if all(grp))  # dV of the replaced-only groups
-    out = {
+    return {
         "mixed_fwd": B * c * (n_ord * 4 * d + n_rep * 2 * d),    # S, PV (ordinary); PV (replaced)
         "bwd_kv": B * c * (n_ord * 8 * d + n_rep * 2 * d),      # S, dP, dV, dK; dV (replaced)
         "bwd_dq": B * c * (n_ord * 2 * d),                   # dQ (S, dP re-formed: not counted)
         "bwd_pre": 0.0,
     }
-    if split:
-        out["bwd_kv"] -= B * c * kv_ro
-        out["bwd_kv_rep"] = B * c * kv_ro
-    return out
 
 
 def measured_traffic(workload, kernel):
@@ -454,7 +445,7 @@ def config_line(torch, saf, name, dev, steps):
     rep = w.replaced()
     lay = Layer(saf, torch, w, rep, dev, draw_on="cuda")
     var, (t, summ) = variants_of(torch, saf, w, dev, steps, mixed=lay, draw_on="cuda")
-    kf = kernel_flops(w.B, w.T, w.d, rep, w.kv_heads, split="bwd_kv_rep" in summ)
+    kf = kernel_flops(w.B, w.T, w.d, rep)
     kernels = {}
     for kname, st in summ.items():
         ent = {"avg_ms": round(st["avg_ms"], 4)}
@@ -528,7 +519,7 @@ def main():
     t_step = time_steps(torch, layer, args.steps, args.warmup, trace)
     tokens = w.B * w.T
     flops = total_flops(w.B, w.T, w.d, replaced, w.backward)
-    kf = kernel_flops(w.B, w.T, w.d, replaced, w.kv_heads, split="bwd_kv_rep" in trace.summary())
+    kf = kernel_flops(w.B, w.T, w.d, replaced)
 
     kernels = {}
     for name, s in trace.summary().items():

@@ -121,11 +121,11 @@ void fill_order(saf::LayerArgs& la, const uint8_t* replaced) {
   }
   fill_slot_order(la.qord, cost, la.H);
   const int G = la.H / la.Hkv;
-  la.n_kv_ro = 0;
+  la.n_kv_ord = 0;
   for (int hk = 0; hk < la.Hkv; ++hk) {
     cost[hk] = 0;
     for (int m = 0; m < G; ++m) cost[hk] += !replaced[hk * G + m];
-    la.n_kv_ro += cost[hk] == 0;
+    la.n_kv_ord += cost[hk] > 0;
   }
   fill_slot_order(la.kvord, cost, la.Hkv);
 }
@@ -546,13 +546,7 @@ static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
     e = traced("bwd_dq", side->s, [&] { return saf::launch_bwd_dq(la, bf, side->s); });
     if (e != hipSuccess) return hip_fail(e, "backward query-block launch");
   }
-  if (saf::bwd_kv_split(la, bf)) {
-    e = traced("bwd_kv", stream, [&] { return saf::launch_bwd_kv(la, bf, stream, saf::kKvOrdinary); });
-    if (e != hipSuccess) return hip_fail(e, "backward key-block launch");
-    e = traced("bwd_kv_rep", stream, [&] { return saf::launch_bwd_kv(la, bf, stream, saf::kKvReplacedOnly); });
-  } else {
-    e = traced("bwd_kv", stream, [&] { return saf::launch_bwd_kv(la, bf, stream, saf::kKvAll); });
-  }
+  e = traced("bwd_kv", stream, [&] { return saf::launch_bwd_kv(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward key-block launch");
   if (side) {  // join
     if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return hip_fail(e, "backward join");

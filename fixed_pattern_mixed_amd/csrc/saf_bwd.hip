@@ -27,8 +27,7 @@
 //             sums over the group; dK is zero when every head of the group is replaced.
 //             bf16 at d = 128 runs the wide variant instead: 8 waves, two per SIMD, K and V staged
 //             transposed in LDS rather than held in registers, two waves per 32 keys (one per
-//             32-query half of a tile), Q / dO tiles double-buffered.  Its key/value heads whose
-//             query heads are all replaced run as a second launch (bwd_kv_rep) after the others.
+//             32-query half of a tile), Q / dO tiles double-buffered.
 //   bwd_dq  : one work item per (batch, ordinary head, 32-query block per wave), lane = query: S^T = K Q^T,
 //             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal
 //             (bf16: K^T fragments by transposing reads of the K row tile; fp32: K is also staged
@@ -123,14 +122,10 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
 
   const int T = p.T, H = p.H, Hkv = p.Hkv;
   const int GS = GROUPED ? H / Hkv : 1;  // query heads per key/value head (Hkv = H unless grouped)
-  const int BH = p.kv_ns;  // this launch's key/value slots (from kv_s0)
-  const int BHp = (BH + 7) & ~7;
-  const int x = blockIdx.x;
-  const int bh = x % BHp;
-  if (bh >= BH) return;
-  const int kb = x / BHp;  // low key blocks see the most query tiles: heaviest first
+  int bh, kb;  // low key blocks see the most query tiles: heaviest first
+  if (!kv_grid_item(p.B, Hkv, p.n_kv_ord, (T + BKV - 1) / BKV, blockIdx.x, bh, kb)) return;
   int b, hk;
-  p.kvord.slice(p.kv_s0 + bh, p.B, b, hk);
+  p.kvord.slice(bh, p.B, b, hk);
   bool any_ord = false;
   for (int m = 0; m < GS; ++m) any_ord |= !is_replaced(p.rep, hk * GS + m);
 
@@ -561,9 +556,7 @@ static_assert(RED <= SMEM && SMEM <= 160 * 1024, "LDS budget");
 static_assert(BKV == kKT && D == kKT, "one transposed tile per key block");
 }  // namespace wide
 
-// PART: kKvAll (each item finds out whether its group has an ordinary query head) or
-// kKvReplacedOnly (a launch over replaced-only key/value heads, compiled without the ordinary path).
-template <bool GROUPED, int PART>
+template <bool GROUPED>
 __global__ __launch_bounds__(wide::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kv_wide_kernel(LayerArgs p) {
   using namespace wide;
@@ -578,17 +571,12 @@ void bwd_kv_wide_kernel(LayerArgs p) {
 
   const int T = p.T, H = p.H, Hkv = p.Hkv;
   const int GS = GROUPED ? H / Hkv : 1;
-  const int BH = p.kv_ns;  // this launch's key/value slots (from kv_s0)
-  const int BHp = (BH + 7) & ~7;
-  const int x = blockIdx.x;
-  const int bh = x % BHp;
-  if (bh >= BH) return;
-  const int kb = x / BHp;  // low key blocks see the most query tiles: heaviest first
+  int bh, kb;  // low key blocks see the most query tiles: heaviest first
+  if (!kv_grid_item(p.B, Hkv, p.n_kv_ord, (T + BKV - 1) / BKV, blockIdx.x, bh, kb)) return;
   int b, hk;
-  p.kvord.slice(p.kv_s0 + bh, p.B, b, hk);
+  p.kvord.slice(bh, p.B, b, hk);
   bool any_ord = false;
-  if (PART == kKvAll)
-    for (int m = 0; m < GS; ++m) any_ord |= !is_replaced(p.rep, hk * GS + m);
+  for (int m = 0; m < GS; ++m) any_ord |= !is_replaced(p.rep, hk * GS + m);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int kg = w & 3, qh = w >> 2;  // the wave's key group (32 keys) and query half
@@ -1145,41 +1133,24 @@ hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
 #ifndef SAF_KV_WIDE
 #define SAF_KV_WIDE 1  // bf16 at d = 128: the 8-wave kernel (0: the 4-wave one)
 #endif
-#ifndef SAF_KV_SPLIT
-#define SAF_KV_SPLIT 1
-#endif
-// One launch over the key/value slots [s0, s0 + ns) of kvord.
-template <typename TI, int D, int PART>
-hipError_t launch_kv_range(LayerArgs a, int s0, int ns, hipStream_t s) {
-  a.kv_s0 = s0;
-  a.kv_ns = ns;
-  const int BHp = (ns + 7) & ~7;
+template <typename TI, int D>
+hipError_t launch_kv_t(const LayerArgs& a, hipStream_t s) {
   if constexpr (sizeof(TI) == 2 && D == 128 && SAF_KV_WIDE) {
-    const long long blocks = (long long)BHp * ((a.T + wide::BKV - 1) / wide::BKV);
+    const long long blocks = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + wide::BKV - 1) / wide::BKV);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (a.Hkv == a.H)
-      hipLaunchKernelGGL((bwd_kv_wide_kernel<false, PART>), dim3((unsigned)blocks), dim3(wide::NT), 0, s, a);
+      hipLaunchKernelGGL((bwd_kv_wide_kernel<false>), dim3((unsigned)blocks), dim3(wide::NT), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_kv_wide_kernel<true, PART>), dim3((unsigned)blocks), dim3(wide::NT), 0, s, a);
+      hipLaunchKernelGGL((bwd_kv_wide_kernel<true>), dim3((unsigned)blocks), dim3(wide::NT), 0, s, a);
     return hipGetLastError();
   }
-  const long long blocks = (long long)BHp * ((a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV);
+  const long long blocks = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.Hkv == a.H)
     hipLaunchKernelGGL((bwd_kv_kernel<TI, D, false>), dim3((unsigned)blocks), dim3(kKvNT), 0, s, a);
   else
     hipLaunchKernelGGL((bwd_kv_kernel<TI, D, true>), dim3((unsigned)blocks), dim3(kKvNT), 0, s, a);
   return hipGetLastError();
-}
-
-template <typename TI, int D>
-hipError_t launch_kv_t(const LayerArgs& a, hipStream_t s, int part) {
-  const int all = a.B * a.Hkv, ro = a.B * a.n_kv_ro;
-  // the ordinary part runs the general instance: compiled without the replaced-only path the
-  // kernel took 256 registers instead of 238 and ran 2.7% slower
-  if (part == kKvOrdinary) return launch_kv_range<TI, D, kKvAll>(a, 0, all - ro, s);
-  if (part == kKvReplacedOnly) return launch_kv_range<TI, D, kKvReplacedOnly>(a, all - ro, ro, s);
-  return launch_kv_range<TI, D, kKvAll>(a, 0, all, s);
 }
 
 template <typename TI, int D>
@@ -1198,17 +1169,9 @@ hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16_in, hipStream_t s) {
   if (bf16_in) return a.d == 64 ? launch_pre_t<bf16, 64>(a, s) : launch_pre_t<bf16, 128>(a, s);
   return a.d == 64 ? launch_pre_t<float, 64>(a, s) : launch_pre_t<float, 128>(a, s);
 }
-// With the 8-wave kernel (one block per compute unit), the key/value heads whose query heads are
-// all replaced (dV only; kvord lists them last) run as a second grid after the others: in one grid
-// with the ordinary items they cost the launch 11% more than the two grids apart (1B-shaped layer:
-// 24 ordinary slices 0.824 ms and 8 replaced ones 0.117 ms alone, 1.02 ms together; 0.97 ms
-// split).  The 4-wave kernels (d = 64, fp32) run mixed grids as fast as split ones (split: +1-2%).
-bool bwd_kv_split(const LayerArgs& a, bool bf16_in) {
-  return SAF_KV_SPLIT && SAF_KV_WIDE && bf16_in && a.d == 128 && a.n_kv_ro > 0 && a.n_kv_ro < a.Hkv;
-}
-hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16_in, hipStream_t s, int part) {
-  if (bf16_in) return a.d == 64 ? launch_kv_t<bf16, 64>(a, s, part) : launch_kv_t<bf16, 128>(a, s, part);
-  return a.d == 64 ? launch_kv_t<float, 64>(a, s, part) : launch_kv_t<float, 128>(a, s, part);
+hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16_in, hipStream_t s) {
+  if (bf16_in) return a.d == 64 ? launch_kv_t<bf16, 64>(a, s) : launch_kv_t<bf16, 128>(a, s);
+  return a.d == 64 ? launch_kv_t<float, 64>(a, s) : launch_kv_t<float, 128>(a, s);
 }
 hipError_t launch_bwd_dq(const LayerArgs& a, bool bf16_in, hipStream_t s) {
   if (bf16_in) return a.d == 64 ? launch_dq_t<bf16, 64>(a, s) : launch_dq_t<bf16, 128>(a, s);

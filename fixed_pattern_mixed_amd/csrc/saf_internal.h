@@ -72,8 +72,7 @@ struct LayerArgs {
   SlotOrder qord, kvord;
   int n_ord;         // query heads that are not replaced: qord lists them first, so the first
                      // B * n_ord query slots are the ordinary slices
-  int n_kv_ro;       // key/value heads whose query heads are all replaced (kvord lists them last)
-  int kv_s0, kv_ns;  // bwd_kv: the key/value slots [kv_s0, kv_s0 + kv_ns) of one launch
+  int n_kv_ord;      // key/value heads with an ordinary query head: kvord lists them first
   const void* q;
   const void* k;
   const void* v;
@@ -162,11 +161,7 @@ __host__ __device__ inline size_t fit_state_stride(int T) { return ((size_t)15 *
 hipError_t launch_pattern_prepare(const LayerArgs& a, hipStream_t s);
 hipError_t launch_mixed_fwd(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16, hipStream_t s);
-// bwd_kv over all key/value slots, or (when bwd_kv_split) as two launches: the slots with an
-// ordinary query head, then the replaced-only ones.
-enum KvPart { kKvAll = 0, kKvOrdinary = 1, kKvReplacedOnly = 2 };
-bool bwd_kv_split(const LayerArgs& a, bool bf16);
-hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s, int part);
+hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dq(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pattern(const LayerArgs& a, const HeadList& rl, bool bf16, hipStream_t s);
 hipError_t launch_pattern_grad_reduce(const LayerArgs& a, const HeadList& rl, hipStream_t s);
@@ -209,5 +204,28 @@ __host__ __device__ inline int calib_groups(int n_qt) {
 }
 
 __host__ __device__ inline bool is_replaced(const uint64_t* rep, int h) { return (rep[h >> 6] >> (h & 63)) & 1ull; }
+
+// bwd_kv grid: key/value slot bh and key block kb of block x, or false for a padding block.  The grid
+// runs in two sections, the key/value heads with an ordinary query head (the first B * n_kv_ord
+// slots of kvord), then those whose query heads are all replaced (dV only), each section by rows
+// of one key block, heaviest (lowest) key blocks first, a row's width padded to a multiple of 8 so
+// that blockIdx % 8 (the XCD) depends on the slot only.  With the cheap replaced-only items
+// interleaved in the rows of the ordinary ones, the 8-wave kernel at d = 128 ran 7% slower.
+__host__ __device__ inline int kv_grid_blocks(int B, int Hkv, int n_kv_ord, int nkb) {
+  const int s1 = B * n_kv_ord, s2 = B * (Hkv - n_kv_ord);
+  return (((s1 + 7) & ~7) + ((s2 + 7) & ~7)) * nkb;
+}
+__host__ __device__ inline bool kv_grid_item(int B, int Hkv, int n_kv_ord, int nkb, int x, int& bh, int& kb) {
+  const int s1 = B * n_kv_ord, s1p = (s1 + 7) & ~7;
+  if (x < s1p * nkb) {
+    bh = x % s1p;
+    kb = x / s1p;
+    return bh < s1;
+  }
+  const int y = x - s1p * nkb, s2 = B * (Hkv - n_kv_ord), s2p = (s2 + 7) & ~7;
+  bh = s1 + y % s2p;
+  kb = y / s2p;
+  return y % s2p < s2;
+}
 
 }  // namespace saf
