@@ -28,6 +28,9 @@
 //             bf16 at d = 128 runs the wide variant instead: 8 waves, two per SIMD, K and V staged
 //             transposed in LDS rather than held in registers, two waves per 32 keys (one per
 //             32-query half of a tile), Q / dO tiles double-buffered.
+//             The grid runs the key/value heads with an ordinary query head first, then those
+//             whose query heads are all replaced; bf16 at d = 64 runs the latter in bwd_dv_rep
+//             (8 waves, 256 keys per item) when they are at least a third of the heads.
 //   bwd_dq  : one work item per (batch, ordinary head, 32-query block per wave), lane = query: S^T = K Q^T,
 //             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal
 //             (bf16: K^T fragments by transposing reads of the K row tile; fp32: K is also staged
@@ -123,7 +126,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
   const int T = p.T, H = p.H, Hkv = p.Hkv;
   const int GS = GROUPED ? H / Hkv : 1;  // query heads per key/value head (Hkv = H unless grouped)
   int bh, kb;  // low key blocks see the most query tiles: heaviest first
-  if (!kv_grid_item(p.B, Hkv, p.n_kv_ord, (T + BKV - 1) / BKV, blockIdx.x, bh, kb)) return;
+  if (!kv_grid_item(p.B, Hkv, p.n_kv_ord, (T + BKV - 1) / BKV, blockIdx.x, bh, kb, !p.kv_rep_apart)) return;
   int b, hk;
   p.kvord.slice(bh, p.B, b, hk);
   bool any_ord = false;
@@ -532,6 +535,156 @@ __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(TI) == 2 ? 2 : 1))) void bw
              dvT[c][4 * g + 3] * vs);
       store4(dK + dc, dkT[c][4 * g] * ks, dkT[c][4 * g + 1] * ks, dkT[c][4 * g + 2] * ks,
              dkT[c][4 * g + 3] * ks);
+    }
+}
+
+// ----------------------------------------------------------------------------- bwd_dv_rep
+// bf16: the key/value heads whose query heads are all replaced (the second section of the bwd_kv
+// grid) as a kernel of their own.  Such an item needs no Q tile, no K, V fragments and no dK: per
+// query head of the group, dV^T += dO^T P over the 128-query dO tiles at or below its keys, P from
+// the prepared pattern.  8 waves x 32 keys share each staged dO tile (twice the keys of the 4-wave
+// bwd_kv item, so half the staging and barriers per product); tiles are double-buffered (one
+// barrier per tile).  The items also write the zero dQ rows of their keys and the zero dK rows.
+namespace rep {
+constexpr int NW = 8, NT = 64 * NW, BK = 32 * NW, BQ = 128;
+constexpr int WIN = BQ + BK, WINP = win_pad(WIN);
+template <int D>
+struct Geo {
+  static constexpr int G = BQ * TileGeom<D>::LDR * 2;  // dO tile (tile_off, swizzled), bytes
+  static constexpr int RS = G, RW = RS + BQ * 4, STAGE = RW + 4 * WINP * 4;
+};
+}  // namespace rep
+
+template <int D, bool GROUPED>
+__global__ __launch_bounds__(rep::NT) void bwd_dv_rep_kernel(LayerArgs p) {
+  using namespace rep;
+  using TI = bf16;
+  using Gm = Geo<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * Gm::STAGE];
+  const int T = p.T, H = p.H, Hkv = p.Hkv;
+  const int GS = GROUPED ? H / Hkv : 1;
+  const int nkb = (T + BK - 1) / BK;
+  const int s1 = p.B * p.n_kv_ord, s2 = p.B * Hkv - s1, s2p = (s2 + 7) & ~7;
+  const int x = blockIdx.x;
+  if (x % s2p >= s2) return;
+  const int kb = x / s2p;  // low key blocks see the most query tiles: heaviest first
+  if (kb >= nkb) return;
+  int b, hk;
+  p.kvord.slice(s1 + x % s2p, p.B, b, hk);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int kb0 = kb * BK;
+  const int kw = kb0 + 32 * w;  // the wave's first key
+  const int kj = kw + l32;      // the lane's key
+  const size_t kvoff = ((size_t)b * Hkv + hk) * (size_t)T * D;
+  const TileLane<D, true> tl(lane);
+  f32x16 dvT[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) zero(dvT[c]);
+  // the window copy a lane reads: its 4 distances start at x = 3 - l32 (mod 4)
+  const int wcopy = (3 - l32) & 3;
+  const int nqt = (T + BQ - 1) / BQ, qt0 = kb0 / BQ;
+  float vs = 1.f;
+
+  for (int m = 0; m < GS; ++m) {
+    const int h = hk * GS + m;
+    const bool fact = p.pat.flag(h)[0] != 0;
+    const size_t hoff = ((size_t)b * H + h) * (size_t)T * D;
+    const TI* G = reinterpret_cast<const TI*>(p.dout) + hoff;
+    const float* lse = p.lse + ((size_t)b * H + h) * (size_t)T;
+    const float* rrow = fact ? p.pat.er(h) : p.r + (size_t)h * p.pat_len;
+    const float wscale = fact ? 1.f : kLog2e;
+    const float wfill = fact ? 0.f : -INFINITY;
+    const float shift = fact ? p.pat.shift(h) : 0.f;
+    float akey = 0.f;
+    if (kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
+    const bool fold = fact && GS > 1;  // in a group each head has its own key factor
+    if (fact && GS == 1) vs = akey;
+    Chunks<TI, D, BQ, NT> pg;
+    float prs = 0.f, prw = 0.f;
+    auto load_tile = [&](int q0) {
+      pg.load(G, q0, T, tid);
+      if (tid < BQ) prs = lse[min(q0 + tid, T - 1)];
+      if (tid < WIN) prw = rrow[min(max(q0 - (kb0 + BK - 1) + tid, 0), T - 1)];
+    };
+    auto store_tile = [&](int buf, int q0) {
+      unsigned char* st = smem + buf * Gm::STAGE;
+      pg.template store_tile<true>(reinterpret_cast<TI*>(st), tid);
+      if (tid < BQ) {
+        const bool in = q0 + tid < T;
+        reinterpret_cast<float*>(st + Gm::RS)[tid] =
+            in ? (fact ? expf(shift - prs) : prs * kLog2e) : (fact ? 0.f : INFINITY);
+      }
+      if (tid < WIN) {
+        const int dist = q0 - (kb0 + BK - 1) + tid;
+        win_store(reinterpret_cast<float*>(st + Gm::RW), WINP, tid,
+                  (dist >= 0 && dist < T) ? prw * wscale : wfill);
+      }
+    };
+    load_tile(qt0 * BQ);
+    store_tile(0, qt0 * BQ);
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; ++qt) {
+      const int q0 = qt * BQ, buf = (qt - qt0) & 1;
+      if (qt + 1 < nqt) load_tile(q0 + BQ);
+      const unsigned char* st = smem + buf * Gm::STAGE;
+      const TI* Gr = reinterpret_cast<const TI*>(st);
+      const float* rsr = reinterpret_cast<const float*>(st + Gm::RS);
+      const float* rwb = win_base(reinterpret_cast<const float*>(st + Gm::RW), WINP, wcopy);
+#pragma unroll
+      for (int sub = 0; sub < BQ / 32; ++sub) {
+        const int qs = q0 + 32 * sub;
+        if (qs + 31 < kw || qs >= T || kw >= T) continue;  // wave-uniform: nothing visible
+        auto entries = [&](auto fact_c, int u) {
+          constexpr bool kFact = decltype(fact_c)::value;
+          float pr[8];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int qr = 32 * sub + 8 * (2 * u + g2) + 4 * hi;  // tile row of the 4-query run
+            const float4 l4 = *reinterpret_cast<const float4*>(rsr + qr);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float4 r4 = win_read4(rwb, qr + (kb0 + BK - 1) - kj);
+            const float rw4[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float pp = kFact ? rw4[e] * lv[e] : __builtin_amdgcn_exp2f(akey + rw4[e] - lv[e]);
+              if (kFact && fold) pp *= akey;
+              pr[4 * g2 + e] = pp;
+            }
+          }
+          return to_frag<TI>(pr);
+        };
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const Frag<TI> pf = fact ? entries(std::true_type{}, u) : entries(std::false_type{}, u);
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) mma16(dvT[c], tile_tr_frag<D, true>(Gr, 32 * sub + 16 * u, c, tl), pf);
+        }
+      }
+      // the other stage's readers passed the previous barrier
+      if (qt + 1 < nqt) store_tile(buf ^ 1, q0 + BQ);
+      __syncthreads();
+    }
+    if (kj < T) {  // a replaced head's query gradient is zero
+      TI* dQ = reinterpret_cast<TI*>(p.dq) + hoff + (size_t)kj * D;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) store4(dQ + 32 * c + 8 * g + 4 * hi, 0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  if (kj >= T) return;
+  TI* dV = reinterpret_cast<TI*>(p.dv) + kvoff + (size_t)kj * D;
+  TI* dK = reinterpret_cast<TI*>(p.dk) + kvoff + (size_t)kj * D;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dc = 32 * c + 8 * g + 4 * hi;
+      store4(dV + dc, dvT[c][4 * g] * vs, dvT[c][4 * g + 1] * vs, dvT[c][4 * g + 2] * vs,
+             dvT[c][4 * g + 3] * vs);
+      store4(dK + dc, 0.f, 0.f, 0.f, 0.f);
     }
 }
 
@@ -1133,8 +1286,40 @@ hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
 #ifndef SAF_KV_WIDE
 #define SAF_KV_WIDE 1  // bf16 at d = 128: the 8-wave kernel (0: the 4-wave one)
 #endif
+// bf16 at d = 64: the replaced-only key/value heads run in bwd_dv_rep (8 waves, 256 keys per item)
+// when they are at least a third of the key/value heads; the 4-wave kernel's grid then holds the
+// others.  124M layer at 4K (d = 64): all heads replaced, bwd_kv 0.22 -> 0.17 ms; half replaced (8K)
+// -4.5%; a quarter replaced +3-6% (the separate grid is small and adds a kernel boundary), so there
+// the replaced-only items stay in the 4-wave grid's second section.
+#ifndef SAF_KV_REP_KERNEL
+#define SAF_KV_REP_KERNEL 1
+#endif
 template <typename TI, int D>
-hipError_t launch_kv_t(const LayerArgs& a, hipStream_t s) {
+hipError_t launch_kv_t(const LayerArgs& a0, hipStream_t s) {
+  LayerArgs a = a0;
+  a.kv_rep_apart = 0;
+  if constexpr (sizeof(TI) == 2 && D == 64 && SAF_KV_REP_KERNEL) {
+    if (a.n_kv_ord < a.Hkv && 2 * (a.Hkv - a.n_kv_ord) >= a.n_kv_ord) {
+      a.kv_rep_apart = 1;
+      const int s2 = a.B * (a.Hkv - a.n_kv_ord);
+      const long long nb1 = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV, false);
+      const long long nb2 = (long long)((s2 + 7) & ~7) * ((a.T + rep::BK - 1) / rep::BK);
+      if (nb1 > 0x7fffffffLL || nb2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      if (nb1 > 0) {
+        if (a.Hkv == a.H)
+          hipLaunchKernelGGL((bwd_kv_kernel<TI, D, false>), dim3((unsigned)nb1), dim3(kKvNT), 0, s, a);
+        else
+          hipLaunchKernelGGL((bwd_kv_kernel<TI, D, true>), dim3((unsigned)nb1), dim3(kKvNT), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      if (a.Hkv == a.H)
+        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, false>), dim3((unsigned)nb2), dim3(rep::NT), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, true>), dim3((unsigned)nb2), dim3(rep::NT), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (sizeof(TI) == 2 && D == 128 && SAF_KV_WIDE) {
     const long long blocks = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + wide::BKV - 1) / wide::BKV);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

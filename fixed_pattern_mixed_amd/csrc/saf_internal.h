@@ -73,6 +73,7 @@ struct LayerArgs {
   int n_ord;         // query heads that are not replaced: qord lists them first, so the first
                      // B * n_ord query slots are the ordinary slices
   int n_kv_ord;      // key/value heads with an ordinary query head: kvord lists them first
+  int kv_rep_apart;  // bwd_kv: the replaced-only key/value heads run in bwd_dv_rep, not in its grid
   const void* q;
   const void* k;
   const void* v;
@@ -211,18 +212,21 @@ __host__ __device__ inline bool is_replaced(const uint64_t* rep, int h) { return
 // of one key block, heaviest (lowest) key blocks first, a row's width padded to a multiple of 8 so
 // that blockIdx % 8 (the XCD) depends on the slot only.  With the cheap replaced-only items
 // interleaved in the rows of the ordinary ones, the 8-wave kernel at d = 128 ran 7% slower.
-__host__ __device__ inline int kv_grid_blocks(int B, int Hkv, int n_kv_ord, int nkb) {
-  const int s1 = B * n_kv_ord, s2 = B * (Hkv - n_kv_ord);
+// rep_sec = false: the grid holds the first section only (the replaced-only heads run elsewhere).
+__host__ __device__ inline int kv_grid_blocks(int B, int Hkv, int n_kv_ord, int nkb, bool rep_sec = true) {
+  const int s1 = B * n_kv_ord, s2 = rep_sec ? B * (Hkv - n_kv_ord) : 0;
   return (((s1 + 7) & ~7) + ((s2 + 7) & ~7)) * nkb;
 }
-__host__ __device__ inline bool kv_grid_item(int B, int Hkv, int n_kv_ord, int nkb, int x, int& bh, int& kb) {
+__host__ __device__ inline bool kv_grid_item(int B, int Hkv, int n_kv_ord, int nkb, int x, int& bh, int& kb,
+                                             bool rep_sec = true) {
   const int s1 = B * n_kv_ord, s1p = (s1 + 7) & ~7;
   if (x < s1p * nkb) {
     bh = x % s1p;
     kb = x / s1p;
     return bh < s1;
   }
-  const int y = x - s1p * nkb, s2 = B * (Hkv - n_kv_ord), s2p = (s2 + 7) & ~7;
+  const int y = x - s1p * nkb, s2 = rep_sec ? B * (Hkv - n_kv_ord) : 0, s2p = (s2 + 7) & ~7;
+  if (s2p == 0) return false;
   bh = s1 + y % s2p;
   kb = y / s2p;
   return y % s2p < s2;

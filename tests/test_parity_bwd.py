@@ -22,6 +22,9 @@ SMALL = [
     (2, 4, 300, 64, torch.bfloat16, 2, "interleaved", 0.5),
     (1, 4, 257, 128, torch.bfloat16, 1, "contiguous", 0.5),
     (1, 12, 520, 64, torch.bfloat16, 6, "interleaved", 0.5),
+    # bf16 d = 64 with every head replaced: the replaced-only key/value kernel alone (wide-range
+    # patterns: product and exponential forms), ragged T
+    (1, 4, 300, 64, torch.bfloat16, 4, "all", 3.0),
 ]
 
 
