@@ -120,22 +120,26 @@ def test_forward_full_size_sampled(name):
     wr.report(workload=name)
 
 
-# bf16 at d = 128 with 8-wave items (grids of at least 256 items): a replaced head's item covers two
-# query blocks (each wave one 32-query subtile in each).  Product form on a ragged length (the last
-# query block pair reaches past T), and the exponential form (a pattern whose factorised weights
-# underflow), each with the backward's replaced-only key blocks.
+# bf16 with 8-wave items (grids of at least 256 items).  At d = 128 a replaced head's item covers two
+# query blocks (each wave one 32-query subtile in each); at d = 64, with a third or more of the heads
+# replaced, the backward runs the replaced-only key blocks in a kernel of their own (bwd_dv_rep).
+# Product form on a ragged length (the last query block pair reaches past T), and the exponential
+# form (a pattern whose factorised weights underflow).
 PAIRED = [
-    # B, H, T, wide-range pattern
-    (4, 16, 4000, False),
-    (2, 16, 2048, True),
+    # B, H, T, wide-range pattern, d, replaced heads (interleaved)
+    (4, 16, 4000, False, 128, 4),
+    (2, 16, 2048, True, 128, 4),
+    (4, 8, 2100, False, 64, 4),
+    (2, 16, 2304, True, 64, 16),
 ]
 
 
-@pytest.mark.parametrize("B,H,T,wide", PAIRED, ids=["B%dH%dT%d-%s" % (c[0], c[1], c[2], "exp" if c[3] else "prod") for c in PAIRED])
-def test_replaced_items_covering_two_query_blocks(B, H, T, wide):
+@pytest.mark.parametrize("B,H,T,wide,d,R", PAIRED,
+                         ids=["B%dH%dT%d-d%d-R%d-%s" % (c[0], c[1], c[2], c[4], c[5], "exp" if c[3] else "prod") for c in PAIRED])
+def test_replaced_items_covering_two_query_blocks(B, H, T, wide, d, R):
     saf = _saf()
-    d, dtype = 128, torch.bfloat16
-    rep = synth.replaced_mask(H, 4, "interleaved")
+    dtype = torch.bfloat16
+    rep = synth.replaced_mask(H, R, "interleaved")
     x = synth.layer_inputs(B, H, T, d, dtype, rep, ar_std=0.5, seed=71 + T)
     if wide:  # one key preferred by 200 nats: exp(a - max a) is 0 in fp32 for every other key
         for h in range(H):
@@ -151,7 +155,7 @@ def test_replaced_items_covering_two_query_blocks(B, H, T, wide):
     print("B%d H%d T%d wide=%s" % (B, H, T, wide), flush=True)
     # every replaced slice and one ordinary slice per batch entry; rows of both query blocks of
     # every pair, the last ones included
-    heads = [(b, h) for b in range(B) for h in range(H) if rep[h]] + [(b, 0) for b in range(B)]
+    heads = sorted(set([(b, h) for b in range(B) for h in range(H) if rep[h]] + [(b, 0) for b in range(B)]))
     rows = sample_rows(T, 96, seed=T)
     wr = Worst("paired B%dH%dT%d" % (B, H, T))
     check_fwd(x, o, lse, heads, rows, TOL[dtype], "paired fwd", worst=wr)
