@@ -43,8 +43,15 @@ constexpr int kBK = kCalibKTile;  // 64
 #ifndef SAF_LSE_WAVES
 #define SAF_LSE_WAVES 8
 #endif
+#ifndef SAF_LSE_KT
+#define SAF_LSE_KT 64
+#endif
+#ifndef SAF_LSE_PIPE
+#define SAF_LSE_PIPE 1
+#endif
 template <typename TI, int D, int W>
 __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
+  constexpr int kBK = SAF_LSE_KT;
   constexpr int NS = kBK / 32;
   constexpr int LDP = D + 16 / (int)sizeof(TI);
   constexpr int kNT = 64 * W, kBQ = 32 * W;
@@ -104,6 +111,20 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
     // Only then (rarely after a row's first tile) is the tile's maximum formed and the sum redone,
     // from scores formed again rather than kept through the common path.
     float lsum = 0.f;
+    if (SAF_LSE_PIPE && !edge) {
+      // interior tile (every subtile visible, no masks): subtile s+1's score product is issued
+      // before subtile s's exponentials, so that the matrix cores and the vector units overlap
+      float ls4[4] = {0.f, 0.f, 0.f, 0.f};
+      f32x16 sc[2];
+      scores(0, sc[0], std::false_type{});
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s + 1 < NS) scores(s + 1, sc[(s + 1) & 1], std::false_type{});
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ls4[r & 3] += __builtin_amdgcn_exp2f(fmaf(sc[s & 1][r], c2, -m));
+      }
+      lsum = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+    } else {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
@@ -119,6 +140,7 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
         add_terms(std::true_type{});
       else
         add_terms(std::false_type{});
+    }
     }
     if (__any(!(lsum <= 0x1p64f))) {
       float sv[NS][16];
