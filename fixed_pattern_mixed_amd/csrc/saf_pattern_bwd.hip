@@ -211,8 +211,11 @@ __global__ __launch_bounds__(kPgNT) void bwd_pattern_kernel(LayerArgs p, HeadLis
       __builtin_amdgcn_wave_barrier();
       float dsum = 0.f;
       if (lane < 63) {
-#pragma unroll 8
-        for (int row = 0; row < 32; ++row) dsum += sk[lane * LDK + row];
+        // four partial sums in a fixed order: no chain of 32 dependent additions
+        float ds4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int row = 0; row < 32; ++row) ds4[row & 3] += sk[lane * LDK + row];
+        dsum = (ds4[0] + ds4[1]) + (ds4[2] + ds4[3]);
       }
       __builtin_amdgcn_wave_barrier();
       if (!started) {
