@@ -180,6 +180,12 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
   if (qi < T && hi == 0) p.lse2[(size_t)nh * T + qi] = m + log2f(lt);
 }
 
+#ifndef SAF_STATS_PIPE
+#define SAF_STATS_PIPE 1
+#endif
+#ifndef SAF_STATS_SCHED
+#define SAF_STATS_SCHED 8  // vector instructions after each interleaved product
+#endif
 template <typename TI, int D, bool KL>
 __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
   constexpr int NS = kBK / 32;
@@ -253,6 +259,39 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
     if (n + 1 < N) prefetch(n + 1, qn, lse_n);
     if (!wave_sees) return;
     float ent_n = 0.f;
+#if SAF_STATS_PIPE
+    if (NS == 2 && k0 + kBK - 1 <= qw && k0 + kBK <= T && qw + 31 < T) {
+      // interior tile (both subtiles visible to every query of the wave, no masks): subtile 1's
+      // score product is issued between the vector operations of subtile 0's update
+      f32x16 st0, st1;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) mma16(st0, load8(Ks + l32 * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t)
+        mma16(st1, load8(Ks + (32 + l32) * LDP + 16 * t + 8 * hi), qf[t], t == 0);
+      auto upd = [&](int s, const f32x16& st) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = fmaf(st[r], p.scale_log2, -lse2);  // log2 A
+          const float a = __builtin_amdgcn_exp2f(x);
+          const float dlt = a - mean[s][r];
+          mean[s][r] = fmaf(dlt, inv_n, mean[s][r]);
+          m2[s][r] = fmaf(dlt, a - mean[s][r], m2[s][r]);
+          if (KL) ent_n += a * x;
+        }
+      };
+      upd(0, st0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix
+        __builtin_amdgcn_sched_group_barrier(0x002, SAF_STATS_SCHED, 0);  // vector
+      }
+      upd(1, st1);
+      if (KL) ent += (double)ent_n;
+      return;
+    }
+#endif
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
