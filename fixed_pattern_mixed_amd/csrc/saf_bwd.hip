@@ -29,8 +29,8 @@
 //             transposed in LDS rather than held in registers, two waves per 32 keys (one per
 //             32-query half of a tile), Q / dO tiles double-buffered.
 //             The grid runs the key/value heads with an ordinary query head first, then those
-//             whose query heads are all replaced; bf16 at d = 64 runs the latter in bwd_dv_rep
-//             (8 waves, 256 keys per item) when they are at least a third of the heads.
+//             whose query heads are all replaced; bf16 runs the latter in bwd_dv_rep (8 waves,
+//             256 keys per item) when they are at least a third of the heads.
 //   bwd_dq  : one work item per (batch, ordinary head, 32-query block per wave), lane = query: S^T = K Q^T,
 //             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal
 //             (bf16: K^T fragments by transposing reads of the K row tile; fp32: K is also staged
@@ -725,7 +725,7 @@ void bwd_kv_wide_kernel(LayerArgs p) {
   const int T = p.T, H = p.H, Hkv = p.Hkv;
   const int GS = GROUPED ? H / Hkv : 1;
   int bh, kb;  // low key blocks see the most query tiles: heaviest first
-  if (!kv_grid_item(p.B, Hkv, p.n_kv_ord, (T + BKV - 1) / BKV, blockIdx.x, bh, kb)) return;
+  if (!kv_grid_item(p.B, Hkv, p.n_kv_ord, (T + BKV - 1) / BKV, blockIdx.x, bh, kb, !p.kv_rep_apart)) return;
   int b, hk;
   p.kvord.slice(bh, p.B, b, hk);
   bool any_ord = false;
@@ -1286,14 +1286,16 @@ hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
 #ifndef SAF_KV_WIDE
 #define SAF_KV_WIDE 1  // bf16 at d = 128: the 8-wave kernel (0: the 4-wave one)
 #endif
-// bf16 at d = 64: the replaced-only key/value heads run in bwd_dv_rep (8 waves, 256 keys per item)
-// when they are at least a third of the key/value heads; the 4-wave kernel's grid then holds the
-// others.  124M layer at 4K (d = 64): all heads replaced, bwd_kv 0.22 -> 0.17 ms; half replaced (8K)
-// -4.5%; a quarter replaced +3-6% (the separate grid is small and adds a kernel boundary), so there
-// the replaced-only items stay in the 4-wave grid's second section.
+// bf16: the replaced-only key/value heads run in bwd_dv_rep (8 waves, 256 keys per item) when they
+// are at least a third of the key/value heads; the grid of bwd_kv then holds the others.  124M layer
+// at 4K (d = 64): all heads replaced, bwd_kv 0.22 -> 0.17 ms; half replaced (8K) -4.5%; a quarter
+// replaced +3-6% (the separate grid is small and adds a kernel boundary), so there the replaced-only
+// items stay in the grid's second section.  1B-shaped layer (d = 128, 8-wave bwd_kv): all replaced
+// 0.43 -> 0.36 ms, a quarter replaced +5%.
 #ifndef SAF_KV_REP_KERNEL
 #define SAF_KV_REP_KERNEL 1
 #endif
+
 template <typename TI, int D>
 hipError_t launch_kv_t(const LayerArgs& a0, hipStream_t s) {
   LayerArgs a = a0;
@@ -1321,6 +1323,28 @@ hipError_t launch_kv_t(const LayerArgs& a0, hipStream_t s) {
     }
   }
   if constexpr (sizeof(TI) == 2 && D == 128 && SAF_KV_WIDE) {
+#if SAF_KV_REP_KERNEL
+    if (a.n_kv_ord < a.Hkv && 2 * (a.Hkv - a.n_kv_ord) >= a.n_kv_ord) {
+      a.kv_rep_apart = 1;
+      const int s2 = a.B * (a.Hkv - a.n_kv_ord);
+      const long long nb1 = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + wide::BKV - 1) / wide::BKV, false);
+      const long long nb2 = (long long)((s2 + 7) & ~7) * ((a.T + rep::BK - 1) / rep::BK);
+      if (nb1 > 0x7fffffffLL || nb2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      if (nb1 > 0) {
+        if (a.Hkv == a.H)
+          hipLaunchKernelGGL((bwd_kv_wide_kernel<false>), dim3((unsigned)nb1), dim3(wide::NT), 0, s, a);
+        else
+          hipLaunchKernelGGL((bwd_kv_wide_kernel<true>), dim3((unsigned)nb1), dim3(wide::NT), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      if (a.Hkv == a.H)
+        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, false>), dim3((unsigned)nb2), dim3(rep::NT), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, true>), dim3((unsigned)nb2), dim3(rep::NT), 0, s, a);
+      return hipGetLastError();
+    }
+#endif
     const long long blocks = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + wide::BKV - 1) / wide::BKV);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (a.Hkv == a.H)
