@@ -1296,70 +1296,49 @@ hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
 #define SAF_KV_REP_KERNEL 1
 #endif
 
+// The key-block kernel (8-wave for bf16 at d = 128, else 4-wave) over both sections of its grid, or
+// over the first one only (rep_sec = false: the replaced-only key/value heads run in bwd_dv_rep).
 template <typename TI, int D>
-hipError_t launch_kv_t(const LayerArgs& a0, hipStream_t s) {
-  LayerArgs a = a0;
-  a.kv_rep_apart = 0;
-  if constexpr (sizeof(TI) == 2 && D == 64 && SAF_KV_REP_KERNEL) {
-    if (a.n_kv_ord < a.Hkv && 2 * (a.Hkv - a.n_kv_ord) >= a.n_kv_ord) {
-      a.kv_rep_apart = 1;
-      const int s2 = a.B * (a.Hkv - a.n_kv_ord);
-      const long long nb1 = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV, false);
-      const long long nb2 = (long long)((s2 + 7) & ~7) * ((a.T + rep::BK - 1) / rep::BK);
-      if (nb1 > 0x7fffffffLL || nb2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-      if (nb1 > 0) {
-        if (a.Hkv == a.H)
-          hipLaunchKernelGGL((bwd_kv_kernel<TI, D, false>), dim3((unsigned)nb1), dim3(kKvNT), 0, s, a);
-        else
-          hipLaunchKernelGGL((bwd_kv_kernel<TI, D, true>), dim3((unsigned)nb1), dim3(kKvNT), 0, s, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
-      if (a.Hkv == a.H)
-        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, false>), dim3((unsigned)nb2), dim3(rep::NT), 0, s, a);
-      else
-        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, true>), dim3((unsigned)nb2), dim3(rep::NT), 0, s, a);
-      return hipGetLastError();
-    }
-  }
-  if constexpr (sizeof(TI) == 2 && D == 128 && SAF_KV_WIDE) {
-#if SAF_KV_REP_KERNEL
-    if (a.n_kv_ord < a.Hkv && 2 * (a.Hkv - a.n_kv_ord) >= a.n_kv_ord) {
-      a.kv_rep_apart = 1;
-      const int s2 = a.B * (a.Hkv - a.n_kv_ord);
-      const long long nb1 = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + wide::BKV - 1) / wide::BKV, false);
-      const long long nb2 = (long long)((s2 + 7) & ~7) * ((a.T + rep::BK - 1) / rep::BK);
-      if (nb1 > 0x7fffffffLL || nb2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-      if (nb1 > 0) {
-        if (a.Hkv == a.H)
-          hipLaunchKernelGGL((bwd_kv_wide_kernel<false>), dim3((unsigned)nb1), dim3(wide::NT), 0, s, a);
-        else
-          hipLaunchKernelGGL((bwd_kv_wide_kernel<true>), dim3((unsigned)nb1), dim3(wide::NT), 0, s, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
-      if (a.Hkv == a.H)
-        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, false>), dim3((unsigned)nb2), dim3(rep::NT), 0, s, a);
-      else
-        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, true>), dim3((unsigned)nb2), dim3(rep::NT), 0, s, a);
-      return hipGetLastError();
-    }
-#endif
-    const long long blocks = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + wide::BKV - 1) / wide::BKV);
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+hipError_t launch_kv_grid(const LayerArgs& a, bool rep_sec, hipStream_t s) {
+  constexpr bool kWide = sizeof(TI) == 2 && D == 128 && SAF_KV_WIDE;
+  constexpr int BKV = kWide ? wide::BKV : KvCfg<TI, D>::BKV;
+  const long long blocks = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + BKV - 1) / BKV, rep_sec);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (blocks == 0) return hipSuccess;
+  if constexpr (kWide) {
     if (a.Hkv == a.H)
       hipLaunchKernelGGL((bwd_kv_wide_kernel<false>), dim3((unsigned)blocks), dim3(wide::NT), 0, s, a);
     else
       hipLaunchKernelGGL((bwd_kv_wide_kernel<true>), dim3((unsigned)blocks), dim3(wide::NT), 0, s, a);
-    return hipGetLastError();
+  } else {
+    if (a.Hkv == a.H)
+      hipLaunchKernelGGL((bwd_kv_kernel<TI, D, false>), dim3((unsigned)blocks), dim3(kKvNT), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_kv_kernel<TI, D, true>), dim3((unsigned)blocks), dim3(kKvNT), 0, s, a);
   }
-  const long long blocks = kv_grid_blocks(a.B, a.Hkv, a.n_kv_ord, (a.T + KvCfg<TI, D>::BKV - 1) / KvCfg<TI, D>::BKV);
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (a.Hkv == a.H)
-    hipLaunchKernelGGL((bwd_kv_kernel<TI, D, false>), dim3((unsigned)blocks), dim3(kKvNT), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_kv_kernel<TI, D, true>), dim3((unsigned)blocks), dim3(kKvNT), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename TI, int D>
+hipError_t launch_kv_t(const LayerArgs& a0, hipStream_t s) {
+  LayerArgs a = a0;
+  a.kv_rep_apart = 0;
+  if constexpr (sizeof(TI) == 2) {
+    const int n_ro = a.Hkv - a.n_kv_ord;  // replaced-only key/value heads
+    if (SAF_KV_REP_KERNEL && n_ro > 0 && 2 * n_ro >= a.n_kv_ord) {
+      a.kv_rep_apart = 1;
+      const long long nb = (long long)((a.B * n_ro + 7) & ~7) * ((a.T + rep::BK - 1) / rep::BK);
+      if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      const hipError_t e = launch_kv_grid<TI, D>(a, false, s);
+      if (e != hipSuccess) return e;
+      if (a.Hkv == a.H)
+        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, false>), dim3((unsigned)nb), dim3(rep::NT), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dv_rep_kernel<D, true>), dim3((unsigned)nb), dim3(rep::NT), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  return launch_kv_grid<TI, D>(a, true, s);
 }
 
 template <typename TI, int D>
