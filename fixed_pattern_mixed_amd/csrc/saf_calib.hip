@@ -388,27 +388,26 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
 
 // Zeros of Ahat right of the diagonal tiles: in the rows of query tile I, the columns from
 // kBQ (I + 1) on (the key tiles J with J kBK > I kBQ + kBQ - 1, which calib_stats skips).  One block
-// per (head, query tile).
+// per (head, query tile, group of kZeroRows rows): rows outer, columns across the threads.
+constexpr int kZeroRows = 16;
 __global__ __launch_bounds__(kNT) void calib_zero_kernel(CalibArgs p) {
+  constexpr int RG = kBQ / kZeroRows;
   const int T = p.T;
-  const int h = blockIdx.x / p.n_qt, I = blockIdx.x % p.n_qt;
+  const int h = blockIdx.x / (p.n_qt * RG), I = (blockIdx.x / RG) % p.n_qt, g = blockIdx.x % RG;
   const int c0 = (I + 1) * kBQ;
   if (c0 >= T) return;
-  const int r0 = I * kBQ, nr = min(kBQ, T - r0);
-  float* A = p.ahat + (size_t)h * T * T + (size_t)r0 * T;
+  const int r0 = I * kBQ + g * kZeroRows, r1 = min(r0 + kZeroRows, T);
+  float* A = p.ahat + (size_t)h * T * T;
   if ((T & 3) == 0) {  // rows and c0 are 16-byte aligned
-    const int w4 = (T - c0) >> 2;
-    const long long n = (long long)nr * w4;
-    for (long long e = threadIdx.x; e < n; e += kNT) {
-      const int r = (int)(e / w4), c = c0 + 4 * (int)(e % w4);
-      *reinterpret_cast<float4*>(A + (size_t)r * T + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = r0; r < r1; ++r) {
+      float* row = A + (size_t)r * T;
+      for (int c = c0 + 4 * (int)threadIdx.x; c < T; c += 4 * kNT)
+        *reinterpret_cast<float4*>(row + c) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   } else {
-    const int w1 = T - c0;
-    const long long n = (long long)nr * w1;
-    for (long long e = threadIdx.x; e < n; e += kNT) {
-      const int r = (int)(e / w1), c = c0 + (int)(e % w1);
-      A[(size_t)r * T + c] = 0.f;
+    for (int r = r0; r < r1; ++r) {
+      float* row = A + (size_t)r * T;
+      for (int c = c0 + (int)threadIdx.x; c < T; c += kNT) row[c] = 0.f;
     }
   }
 }
@@ -475,7 +474,7 @@ hipError_t launch_calib_stats(const CalibArgs& a, bool bf16_in, hipStream_t s) {
   return a.d == 64 ? launch_stats_t<float, 64>(a, s) : launch_stats_t<float, 128>(a, s);
 }
 hipError_t launch_calib_zero(const CalibArgs& a, hipStream_t s) {
-  const long long blocks = (long long)a.H * a.n_qt;
+  const long long blocks = (long long)a.H * a.n_qt * (kBQ / kZeroRows);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(calib_zero_kernel, dim3((unsigned)blocks), dim3(kNT), 0, s, a);
   return hipGetLastError();
