@@ -121,11 +121,16 @@ def test_pattern_longer_than_input_uses_prefix():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_bitwise_repeatable():
+# a quarter of the heads replaced (the replaced-only key/value heads in bwd_kv's second section), half
+# replaced (bwd_dv_rep), and bf16 d = 128 on a grid of 8-wave items (paired replaced forward items)
+REPEAT = [(2, 12, 700, 64, 3), (2, 12, 700, 64, 6), (2, 16, 2048, 128, 4), (1, 16, 1000, 128, 8)]
+
+
+@pytest.mark.parametrize("B,H,T,d,R", REPEAT, ids=["B%dH%dT%dd%dR%d" % c for c in REPEAT])
+def test_bitwise_repeatable(B, H, T, d, R):
     """Every output element is written by one work item and summed in a fixed order."""
     saf = _saf()
-    B, H, T, d = 2, 12, 700, 64
-    rep = synth.replaced_mask(H, 3)
+    rep = synth.replaced_mask(H, R)
     g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=8, device="cuda")
     outs = []
     for _ in range(2):
