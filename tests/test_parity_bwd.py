@@ -25,6 +25,10 @@ SMALL = [
     # bf16 d = 64 with every head replaced: the replaced-only key/value kernel alone (wide-range
     # patterns: product and exponential forms), ragged T
     (1, 4, 300, 64, torch.bfloat16, 4, "all", 3.0),
+    # bf16, half the heads replaced (the replaced-only key/value heads in bwd_dv_rep beside the
+    # key-block kernel): one position, and a length shorter than one 256-key item at d = 128
+    (1, 4, 1, 64, torch.bfloat16, 2, "interleaved", 0.5),
+    (2, 4, 200, 128, torch.bfloat16, 2, "contiguous", 1.0),
 ]
 
 
