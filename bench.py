@@ -489,8 +489,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this layer has no exchange between GPUs and this "
-              "build runs on a single MI355X (--gpus %d, WORLD_SIZE %d requested)"
+        print("bench.py measures one GPU only: the layer has no exchange between GPUs, and a "
+              "multi-GPU run is not provided (--gpus %d, WORLD_SIZE %d requested)"
               % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
