@@ -286,11 +286,15 @@ size_t calib_tiles(int T, int* nqt, int* nkt) {
   *nkt = (T + saf::kCalibKTile - 1) / saf::kCalibKTile;
   return (size_t)(*nqt) * (*nkt);
 }
+// bf16 queries in fragment order (CalibArgs::qfrag): 2 bytes per element of the padded rows
+size_t calib_qfrag_bytes(int N, int H, int nqt, int d) {
+  return align_up(2 * (size_t)N * H * nqt * saf::kCalibQTile * d);
+}
 size_t calib_ws(int N, int H, int T, int d) {
-  (void)d;
   int nqt, nkt;
   const size_t tiles = calib_tiles(T, &nqt, &nkt);
-  return align_up(sizeof(float) * (size_t)N * H * T) + 2 * align_up(sizeof(double) * (size_t)H * tiles);
+  return align_up(sizeof(float) * (size_t)N * H * T) + 2 * align_up(sizeof(double) * (size_t)H * tiles) +
+         calib_qfrag_bytes(N, H, nqt, d);
 }
 
 }  // namespace
@@ -723,6 +727,7 @@ saf_status saf_calibrate(saf_dtype dt, int N, int H, int T, int d, const void* q
   ca.n_ag = saf::calib_groups(ca.n_qt);
   ca.klp = reinterpret_cast<double*>(reinterpret_cast<char*>(ca.m2) + align_up(sizeof(double) * (size_t)H * tiles));
   const bool bf = dt == SAF_BF16;
+  ca.qfrag = bf ? reinterpret_cast<char*>(ca.klp) + align_up(sizeof(double) * (size_t)H * tiles) : nullptr;
   hipError_t e = traced("calib_lse", stream, [&] { return saf::launch_calib_lse(ca, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "calibration statistics launch");
   e = traced("calib_stats", stream, [&] { return saf::launch_calib_stats(ca, bf, stream); });

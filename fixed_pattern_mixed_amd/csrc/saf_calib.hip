@@ -77,6 +77,18 @@ __global__ __launch_bounds__(64 * W) void calib_lse_kernel(CalibArgs p) {
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
     qf[t] = qi < T ? load8(Q + (size_t)qi * D + 16 * t + 8 * hi) : zero_frag<TI>();
+  if constexpr (sizeof(TI) == 2) {
+    // bf16: the fragments also go to the workspace in the order calib_stats reads them (per 32
+    // rows and fragment one contiguous 1 KB piece, rows past the end zero): that pass re-reads
+    // them for every sequence and tile, and row-major reads would fetch each 128-byte line in
+    // four partial pieces
+    const int nb = p.n_qt * kCalibQTile / 32;
+    if (qw < nb * 32) {
+      TI* F = reinterpret_cast<TI*>(p.qfrag) + ((size_t)nh * nb + qw / 32) * (32 * D);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) *reinterpret_cast<bf16x8*>(F + 512 * t + 8 * lane) = qf[t].v;
+    }
+  }
   float m = -INFINITY, l = 0.f;
   const int nkt = (min(T, q0 + kBQ) + kBK - 1) / kBK;
   Chunks<TI, D, kBK, kNT> kreg;  // the next key tile, in flight while the current one is used
@@ -244,9 +256,17 @@ __global__ __launch_bounds__(kNT) void calib_stats_kernel(CalibArgs p) {
       // rows past the end read row T-1 (always valid; a select with a constant would wait for the
       // load): their entries are masked out
       const int qc = min(qi, T - 1);
-      const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
+      if constexpr (sizeof(TI) == 2) {
+        // the fragments calib_lse wrote in this order (rows past the end are zero there)
+        const int nb = p.n_qt * kCalibQTile / 32;
+        const TI* F = reinterpret_cast<const TI*>(p.qfrag) + (((size_t)n * H + h) * nb + qw / 32) * (32 * D);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) qn[t] = load8(Q + (size_t)qc * D + 16 * t + 8 * hi);
+        for (int t = 0; t < D / 16; ++t) qn[t] = load8(F + 512 * t + 8 * lane);
+      } else {
+        const TI* Q = reinterpret_cast<const TI*>(p.q) + hoff;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) qn[t] = load8(Q + (size_t)qc * D + 16 * t + 8 * hi);
+      }
       lse_n = p.lse2[((size_t)n * H + h) * T + qc];
     }
   };
@@ -444,6 +464,7 @@ __global__ __launch_bounds__(kNT) void calib_reduce_kernel(CalibArgs p) {
 template <typename TI, int D>
 hipError_t launch_lse_t(const CalibArgs& a, hipStream_t s) {
   constexpr int W = SAF_LSE_WAVES;
+  static_assert((32 * W) % kCalibQTile == 0, "calib_lse items cover whole statistics query tiles");
   const int NHp = (a.N * a.H + 7) & ~7;  // slices per XCD x 8
   const long long blocks = (long long)NHp * ((a.T + 32 * W - 1) / (32 * W));
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

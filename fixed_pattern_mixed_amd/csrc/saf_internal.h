@@ -103,6 +103,8 @@ struct CalibArgs {
   const void* q;     // [N][H][T][d]
   const void* k;
   float* lse2;       // [N][H][T] workspace: log2-sum-exp2 of scaled scores
+  void* qfrag;       // bf16: [N][H][n_qt * kCalibQTile / 32][d / 16][64][8] workspace, the queries
+                     // in the order of the statistics pass's operand fragments; fp32: unused
   double* m2;        // [H][tiles] workspace: per-tile sums of squared deviations
   double* klp;       // [H][tiles] workspace: per-tile KL sums (log2 units), when skl is requested
   float* ahat;       // [H][T][T]

@@ -26,6 +26,9 @@ SMALL = [
     (3, 2, 129, 128, torch.float32),
     (5, 3, 256, 64, torch.bfloat16),
     (8, 2, 1024, 128, torch.bfloat16),
+    # bf16 edges of the fragment-order query copy: one row; one row past a 128-row tile
+    (2, 1, 1, 64, torch.bfloat16),
+    (3, 2, 130, 128, torch.bfloat16),
 ]
 
 
