@@ -48,6 +48,7 @@ def kernel_flops(B, T, d, replaced):
         "mixed_fwd": B * c * (n_ord * 4 * d + n_rep * 2 * d),    # S, PV (ordinary); PV (replaced)
         "bwd_kv": B * c * (n_ord * 8 * d + n_rep * 2 * d),      # S, dP, dV, dK; dV (replaced)
         "bwd_dq": B * c * (n_ord * 2 * d),                   # dQ (S, dP re-formed: not counted)
+        "bwd_dq_ds": B * c * (n_ord * 2 * d),                # dQ from the stored dS
         "bwd_pre": 0.0,
     }
 
@@ -73,7 +74,7 @@ def measured_traffic(workload, kernel):
 
 def total_flops(B, T, d, replaced, backward):
     kf = kernel_flops(B, T, d, replaced)
-    return kf["mixed_fwd"] + (kf["bwd_kv"] + kf["bwd_dq"] if backward else 0.0)
+    return kf["mixed_fwd"] + (kf["bwd_kv"] + kf["bwd_dq"] if backward else 0.0)  # one dQ kernel runs
 
 
 class Layer:
@@ -93,13 +94,18 @@ class Layer:
         self.lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
         self.dq = torch.empty_like(x.q)
         self.dk, self.dv = torch.empty_like(x.k), torch.empty_like(x.v)
-        nb = max(saf.saf_attn_bwd_workspace_size(B, H, T, d), 256)
+        self.dt = saf.SAF_BF16 if w.dtype == "bf16" else saf.SAF_F32
+        # the backward workspace with room for the stored dS where the library keeps it (bf16,
+        # d = 128, no grouped heads); nb_min: the smaller one, with which dQ re-forms S and dP
+        self.nb_min = max(saf.saf_attn_bwd_workspace_size(B, H, T, d), 256)
+        nb = saf.saf_attn_bwd_ds_workspace_size(self.dt, B, H, self.Hkv, T, d, sum(1 for x in replaced if x))
+        nb = nb if self.nb_min < nb <= self.nb_min + saf.DS_WORKSPACE_MAX else self.nb_min
         nf = max(saf.saf_attn_fwd_workspace_size(B, H, T, d), 256)
         self.ws_b = torch.empty(nb, dtype=torch.uint8, device=dev)
         self.ws_f = torch.empty(nf, dtype=torch.uint8, device=dev)
         self.nb, self.nf = nb, nf
+        self.recompute_ds = False  # True: pass the smaller workspace (dQ re-forms S and dP)
         self.mask = saf._mask(replaced, H)
-        self.dt = saf.SAF_BF16 if w.dtype == "bf16" else saf.SAF_F32
         self.stream = torch.cuda.current_stream(dev).cuda_stream
         # the replaced heads' pattern is a frozen buffer: its normaliser is prepared once, as when
         # the pattern is installed, and reused by every step
@@ -120,12 +126,13 @@ class Layer:
 
     def bwd(self):
         s, w, x = self.saf, self.w, self.x
+        nb = self.nb_min if self.recompute_ds else self.nb
         st = s.saf_attn_bwd_gqa(self.dt, w.B, w.H, self.Hkv, w.T, w.d, x.q.data_ptr(),
                                 x.k.data_ptr(), x.v.data_ptr(), self.o.data_ptr(),
                                 x.dout.data_ptr(), self.lse.data_ptr(), self.mask, x.a.data_ptr(),
                                 x.r.data_ptr(), x.a.shape[1], self.pattern.data_ptr(), 0.0,
                                 self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(),
-                                self.ws_b.data_ptr(), self.nb, self.stream)
+                                self.ws_b.data_ptr(), nb, self.stream)
         s._check(st, "saf_attn_bwd")
 
     def step(self):
@@ -569,6 +576,15 @@ def main():
             saf.saf_set_backward_overlap(0)
             var["backward_overlap"] = {"ms_per_step": round(to * 1e3, 4),
                                        "tokens_per_s": round(tokens / to, 1)}
+            if layer.nb > layer.nb_min:  # the backward with dQ re-forming S and dP (no stored dS)
+                layer.recompute_ds = True
+                tr = saf.KernelTrace(capacity=4 * (max(5, args.steps // 3) + 1))
+                tq = time_steps(torch, layer, max(5, args.steps // 3), 2, tr)
+                layer.recompute_ds = False
+                var["dq_recomputed"] = {"ms_per_step": round(tq * 1e3, 4),
+                                        "tokens_per_s": round(tokens / tq, 1),
+                                        "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in tr.summary().items()}}
+                tr.close()
         out["variants"] = var
 
     if not args.no_configs and args.configs:

@@ -61,6 +61,8 @@ _lib.saf_attn_fwd_workspace_size.argtypes = [_i, _i, _i, _i]
 _lib.saf_attn_fwd_workspace_size.restype = _sz
 _lib.saf_attn_bwd_workspace_size.argtypes = [_i, _i, _i, _i]
 _lib.saf_attn_bwd_workspace_size.restype = _sz
+_lib.saf_attn_bwd_ds_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+_lib.saf_attn_bwd_ds_workspace_size.restype = _sz
 _lib.saf_calibrate_workspace_size.argtypes = [_i, _i, _i, _i]
 _lib.saf_calibrate_workspace_size.restype = _sz
 _lib.saf_last_error.argtypes = []
@@ -117,6 +119,7 @@ saf_attn_bwd_pattern = _lib.saf_attn_bwd_pattern
 saf_attn_bwd_pattern_workspace_size = _lib.saf_attn_bwd_pattern_workspace_size
 saf_attn_fwd_workspace_size = _lib.saf_attn_fwd_workspace_size
 saf_attn_bwd_workspace_size = _lib.saf_attn_bwd_workspace_size
+saf_attn_bwd_ds_workspace_size = _lib.saf_attn_bwd_ds_workspace_size
 saf_calibrate_workspace_size = _lib.saf_calibrate_workspace_size
 saf_pattern_size = _lib.saf_pattern_size
 saf_pattern_prepare = _lib.saf_pattern_prepare
@@ -260,9 +263,16 @@ def fwd(q, k, v, replaced, a=None, r=None, scale=None, out=None, lse=None, patte
     return o, lse
 
 
-def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None, pattern=None):
+# Largest extra backward workspace bwd() allocates to keep dS between the two backward kernels.
+DS_WORKSPACE_MAX = 16 << 30
+
+
+def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None, pattern=None, keep_ds=True):
     """Backward of the mixed layer.  Returns (dq [B, H, T, d], dk, dv [B, Hkv, T, d]); replaced
-    heads get dq = 0 and add nothing to dk."""
+    heads get dq = 0 and add nothing to dk.  keep_ds: pass the workspace of
+    saf_attn_bwd_ds_workspace_size where the library keeps the ordinary heads' dS between its two
+    backward kernels (bf16, d = 128, Hkv = H) and the extra room is at most DS_WORKSPACE_MAX bytes;
+    False: the smaller workspace, with which dQ forms S and dP again."""
     import torch
     if v is None or v.dim() != 4 or dout is None or dout.dim() != 4:
         raise ValueError("v must be [B, Hkv, T, d] and dout [B, H, T, d]")
@@ -282,6 +292,11 @@ def bwd(q, k, v, o, dout, lse, replaced, a=None, r=None, scale=None, pattern=Non
     dq = torch.empty_like(dout)
     dk, dv = torch.empty_like(v), torch.empty_like(v)
     ws_n = saf_attn_bwd_workspace_size(B, H, T, d)
+    if keep_ds:
+        n_rep = sum(1 for x in replaced if int(x))
+        big = saf_attn_bwd_ds_workspace_size(dt, B, H, Hkv, T, d, n_rep)
+        if ws_n < big <= ws_n + DS_WORKSPACE_MAX:
+            ws_n = big
     ws = _ws(ws_n, v.device)
     pat_len = a.shape[-1] if a is not None else 0
     st = saf_attn_bwd_gqa(dt, B, H, Hkv, T, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),

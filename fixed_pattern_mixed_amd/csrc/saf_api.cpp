@@ -235,6 +235,12 @@ size_t bwd_ws(int B, int H, int T, int d) {
   return pattern_bytes(H, T) + align_up(sizeof(float) * (size_t)B * H * T);  // pattern, delta
 }
 
+// The backward keeps the ordinary heads' dS between its two kernels (bwd_kv stores it, bwd_dq_ds
+// reads it) for bf16 at d = 128 without grouped key/value heads, when the workspace has room.
+bool ds_path(saf_dtype dt, int d, int H, int Hkv, int n_ord) {
+  return dt == SAF_BF16 && d == 128 && Hkv == H && n_ord > 0;
+}
+
 size_t pgrad_ws(int B, int H, int T, int d) {
   (void)d;
   const size_t nkb = (size_t)(T + saf::pattern_grad_sub_block() - 1) / saf::pattern_grad_sub_block();
@@ -310,6 +316,15 @@ size_t saf_attn_bwd_workspace_size(int B, int H, int T, int d) {
   if (!sizes_ok(B, H, T, d)) return SIZE_MAX;
   if (B == 0 || T == 0) return 0;
   return bwd_ws(B, H, T, d);
+}
+
+size_t saf_attn_bwd_ds_workspace_size(saf_dtype dt, int B, int H, int Hkv, int T, int d, int n_replaced) {
+  if (!sizes_ok(B, H, T, d) || Hkv < 1 || Hkv > H || H % Hkv != 0 || n_replaced < 0 || n_replaced > H)
+    return SIZE_MAX;
+  if (B == 0 || T == 0) return 0;
+  const size_t base = bwd_ws(B, H, T, d);
+  if (!ds_path(dt, d, H, Hkv, H - n_replaced)) return base;
+  return base + align_up(saf::ds_bytes(B, H - n_replaced, T));
 }
 
 static saf_status fwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, const void* q,
@@ -541,9 +556,27 @@ static saf_status bwd_impl(saf_dtype dt, int B, int H, int Hkv, int T, int d, co
   la.dq = dq; la.dk = dk; la.dv = dv;
   if ((st = setup_pattern(la, any_rep, pattern, T, ws, stream, "pattern preparation")) != SAF_OK) return st;
   const bool bf = dt == SAF_BF16;
+  SideStream* side = (any_ord && allow_side) ? side_stream() : nullptr;
+  int n_ord = 0;
+  for (int h = 0; h < H; ++h) n_ord += !replaced[h];
+  // dS kept in the workspace (its room after the pattern and delta): one stream, the key-block
+  // kernel first
+  const bool keep_ds = !lib_ws && !side && ds_path(dt, d, H, Hkv, n_ord) &&
+                       ws_bytes - need >= saf::ds_bytes(B, n_ord, T);
+  if (keep_ds) {
+    la.dsw = reinterpret_cast<char*>(ws) + need;
+    const long long n32 = (T + 31) / 32;
+    la.ds_ntri = n32 * (n32 + 1) / 2;
+  }
   hipError_t e = traced("bwd_pre", stream, [&] { return saf::launch_bwd_pre(la, bf, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-  SideStream* side = (any_ord && allow_side) ? side_stream() : nullptr;
+  if (keep_ds) {
+    e = traced("bwd_kv", stream, [&] { return saf::launch_bwd_kv(la, bf, stream); });
+    if (e != hipSuccess) return hip_fail(e, "backward key-block launch");
+    e = traced("bwd_dq_ds", stream, [&] { return saf::launch_bwd_dq_ds(la, stream); });
+    if (e != hipSuccess) return hip_fail(e, "backward query-block launch");
+    return SAF_OK;
+  }
   if (side) {  // fork: the query-block kernel on the side stream after the preprocess
     if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return hip_fail(e, "backward fork");
     if ((e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess) return hip_fail(e, "backward fork");

@@ -36,9 +36,16 @@
 //             dP^T = V dO^T, dS^T, dQ^T += K^T dS^T over the key tiles at or below the diagonal
 //             (bf16: K^T fragments by transposing reads of the K row tile; fp32: K is also staged
 //             transposed).  8 waves per item for bf16 at d = 128, else 4.
+//   bwd_dq_ds: bf16 at d = 128 (no grouped heads) when the caller's workspace has room for dS:
+//             bwd_kv then also stores the dS fragments it forms (2 bytes per causal entry of an
+//             ordinary head), and this kernel, launched after it, computes dQ^T += K^T dS^T from
+//             them with the work items of bwd_dq: one product per entry instead of three.
 // Every output element is written by exactly one work item and summed in a fixed order, so the
-// backward is bitwise repeatable.  S and dP are formed twice (once per kernel): seven products per
-// entry of an ordinary head instead of five, traded for having no atomic traffic.
+// backward is bitwise repeatable.  Without the stored dS, S and dP are formed twice (once per
+// kernel): seven products per entry of an ordinary head instead of five, traded for having no
+// atomic traffic; with it, five, for 2 x 2 bytes of HBM traffic per causal entry (dS written and
+// read once).  Both give the same dQ bits: the same bf16 dS enters the same sums in the same
+// order.
 #include <type_traits>
 
 #include "saf_device.h"
@@ -689,6 +696,9 @@ __global__ __launch_bounds__(rep::NT) void bwd_dv_rep_kernel(LayerArgs p) {
     }
 }
 
+#ifndef SAF_DS_NT
+#define SAF_DS_NT 1  // the stored dS is written with non-temporal stores (0: plain stores)
+#endif
 // ----------------------------------------------------------------------------- bwd_kv, wide
 // bf16 at d = 128.  Holding a wave's K and V fragments (64 registers) next to its dK, dV accumulators
 // (128) leaves one wave per SIMD, which then waits on every dependency of its own chain.  Here the
@@ -898,6 +908,12 @@ void bwd_kv_wide_kernel(LayerArgs p) {
       if (rep && kj < T) akey = fact ? p.pat.ea(h)[kj] : p.a[(size_t)h * p.pat_len + kj] * kLog2e;
       const bool fold = fact && GS > 1;  // the key factor enters each entry
       if (fact && GS == 1) vs = akey;
+      // ordinary head, workspace holding dS: this lane's part of the slice's stored subtiles
+      // (key/value heads shared by several query heads keep re-forming dS in bwd_dq: that
+      // instance of the kernel has no registers to spare)
+      bf16* dsh = nullptr;
+      if (!GROUPED && p.dsw && !rep)
+        dsh = reinterpret_cast<bf16*>(p.dsw) + ((size_t)b * p.n_ord + ord_rank(p.rep, h)) * (size_t)p.ds_ntri * kDsPiece;
 
       // prefetch registers hold raw loads (clamped addresses); masks and conversions at the store
       Chunks<bf16, D, BQ, NT> pq, pg;
@@ -941,10 +957,13 @@ void bwd_kv_wide_kernel(LayerArgs p) {
         const bf16* Gb = Gs + buf * TILE;
         const float* rsb = rss + buf * BQ + 32 * qh;
         const float* dlb = dls + buf * BQ + 32 * qh;
-        if (qs + 31 >= kw && qs < T && kw < T) {  // wave-uniform: something visible
+        // dS of the subtile (ordinary heads), kept for its store below
+        Frag<bf16> sf[2];
+        const bool vis = qs + 31 >= kw && qs < T && kw < T;
+        if (vis) {  // wave-uniform: something visible
           // P (and dS = P o (dP - delta)) of the subtile as operand fragments of its two k16 steps:
           // only fragments, not 32 fp32 entries, are live where the head kinds' branches meet
-          Frag<bf16> pf[2], sf[2];
+          Frag<bf16> pf[2];
           if (!rep) {
             // S = Q K^T and dP = dO V^T (-delta is added per entry: as the products' initial value it
             // would hold 16 more registers through them)
@@ -1030,10 +1049,23 @@ void bwd_kv_wide_kernel(LayerArgs p) {
             }
           }
         }
-        if (qt + 1 < nqt) {
-          store_tile(buf ^ 1, q0 + BQ);  // that buffer's readers passed the previous barrier
-          if (qt + 2 < nqt) load_tile(q0 + 2 * BQ);
+        if (qt + 1 < nqt) store_tile(buf ^ 1, q0 + BQ);  // that buffer's readers passed the previous barrier
+        if (!GROUPED && dsh && vis) {
+          // the subtile's dS for bwd_dq_ds, both fragments (1 KB per wave each), streamed past the
+          // caches (read once, by the next kernel; the Q and dO tiles other key blocks re-read stay
+          // in L2).  Issued after the wait for the prefetched tile above, so that the next such
+          // wait (which covers every outstanding memory operation) finds them long finished.
+          const int ib = qs >> 5, jb = kw >> 5;
+          bf16x8* dst = reinterpret_cast<bf16x8*>(dsh + ((size_t)ib * (ib + 1) / 2 + jb) * kDsPiece + 8 * lane);
+#if SAF_DS_NT
+          __builtin_nontemporal_store(sf[0].v, dst);
+          __builtin_nontemporal_store(sf[1].v, dst + 64);
+#else
+          dst[0] = sf[0].v;
+          dst[64] = sf[1].v;
+#endif
         }
+        if (qt + 2 < nqt) load_tile(q0 + 2 * BQ);
         __syncthreads();
       }
       if (rep && qh == 0 && kj < T) {  // a replaced head's query gradient is zero
@@ -1274,6 +1306,143 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
              dqT[c][4 * g + 2] * sc, dqT[c][4 * g + 3] * sc);
 }
 
+// ---------------------------------------------------------------------------------- bwd_dq_ds
+// bf16 at d = 128, when the workspace holds the dS that bwd_kv stored: dQ^T += K^T dS^T over the
+// key tiles at or below the diagonal, the one product of dQ (S and dP are not formed again).  Work
+// items as in bwd_dq (8 waves x 32 queries, lane = query, K tiles of 64 keys staged as rows and
+// read transposed).  A wave's stored subtiles (its query block ib, key blocks jb <= ib) are read by
+// that wave only: each 2 KB subtile is prefetched with the K tile, copied into the wave's own LDS
+// region in four quarters (fragment u, lane half) kDsBlk elements apart, and read back with the
+// transposing read as the B operand: lane l, slot e gets dS[query l % 32][key 16 ub +
+// perm_row(e, l / 32)] -- the source lane 4j + a of a 16-lane group addresses key 16 ub + 8 rd +
+// 4 hi + j and queries 16 g + 4a .. +3, which the store keeps contiguous in quarter 2g + (a & 1)
+// at position 4 (a >> 1).  The padding puts the four quarters a read meets on disjoint 16-bank
+// segments.
+namespace dqs {
+constexpr int W = 8, NT = 64 * W, D = 128, BQ = 32 * W, BK = 64, NS = BK / 32;
+constexpr int BLK = 288;      // LDS elements per quarter of a subtile (256 + 32 of padding)
+constexpr int SUB = 4 * BLK;  // LDS elements per subtile
+}  // namespace dqs
+
+// element offset, in a subtile's LDS region, of the 4 values lane `lane` addresses in read rd of
+// k16 step ub
+__device__ __forceinline__ int ds_tr_off(int lane, int ub, int rd) {
+  const int jp = (lane & 15) >> 2, a = lane & 3, g = (lane >> 4) & 1, hi = lane >> 5;
+  const int key = 16 * ub + 8 * rd + 4 * hi + jp;
+  return (2 * g + (a & 1)) * dqs::BLK + 8 * key + 4 * (a >> 1);
+}
+
+__global__ __launch_bounds__(dqs::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_ds_kernel(LayerArgs p) {
+  using namespace dqs;
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
+  typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BK * TileGeom<D>::LDR];  // K tile, rows
+  __shared__ __attribute__((aligned(16))) bf16 Ds[W][NS * SUB];            // per wave: dS subtiles
+
+  const int T = p.T, H = p.H;
+  const int BH = p.B * p.n_ord;
+  const int BHp = (BH + 7) & ~7;
+  const int nqb = (T + BQ - 1) / BQ;
+  const int x = blockIdx.x;
+  const int bh = x % BHp;
+  if (bh >= BH) return;
+  const int qb = nqb - 1 - x / BHp;  // heaviest query blocks first
+  int b, h;
+  p.qord.slice(bh, p.B, b, h);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int q0 = qb * BQ;
+  const int qw = q0 + 32 * w;
+  const int qi = qw + l32;
+  const int ib = qw >> 5;  // the wave's query block
+  const size_t kvoff = ((size_t)b * p.Hkv + h / (H / p.Hkv)) * (size_t)T * D;
+  const bf16* K = reinterpret_cast<const bf16*>(p.k) + kvoff;
+  // the wave's row of stored subtiles (ib, 0 .. ib), at this lane's 16 bytes
+  const bf16* drow = reinterpret_cast<const bf16*>(p.dsw) +
+                     (((size_t)b * p.n_ord + ord_rank(p.rep, h)) * (size_t)p.ds_ntri +
+                      (size_t)ib * (ib + 1) / 2) * kDsPiece + 8 * lane;
+  bf16* Dw = Ds[w];
+
+  f32x16 dqT[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) zero(dqT[c]);
+
+  static_assert(NS == 2, "two 32-key subtiles per K tile");
+  Chunks<bf16, D, BK, NT> pk;
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+  u32x4 d00 = {}, d01 = {}, d10 = {}, d11 = {};  // prefetched subtiles: [subtile][fragment]
+  // the K tile and, where bwd_kv stored them (key blocks jb <= ib inside the sequence;
+  // wave-uniform), the wave's two subtiles of the tile
+  const bool wave_in = qw < T;  // waves past the end have no stored row (and write no dQ)
+  // (dS first: it comes from HBM, read once and past the caches; K is mostly in L2)
+  auto load_tile = [&](int k0) {
+    const int jb = k0 >> 5;
+    const u32x4* src = reinterpret_cast<const u32x4*>(drow + (size_t)jb * kDsPiece);
+    if (wave_in && jb <= ib) {
+      d00 = __builtin_nontemporal_load(src);
+      d01 = __builtin_nontemporal_load(src + 64);
+    }
+    if (wave_in && jb + 1 <= ib && 32 * (jb + 1) < T) {
+      d10 = __builtin_nontemporal_load(src + kDsPiece / 8);
+      d11 = __builtin_nontemporal_load(src + kDsPiece / 8 + 64);
+    }
+    pk.load(K, k0, T, tid);
+  };
+  const TileLane<D, true> tl(lane);
+
+  const int kend = min(T, q0 + BQ);
+  const int nkt = (kend + BK - 1) / BK;
+  load_tile(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BK;
+    __syncthreads();  // the previous tile's readers of Ks are done
+    pk.template store_tile<true>(Ks, tid);
+    // this wave's subtiles into its own region (its earlier reads of the region were issued
+    // before these writes, and one wave's LDS operations complete in order)
+    if (wave_in) {
+      const int jb = k0 >> 5;
+      bf16* dst = Dw + hi * BLK + 8 * l32;
+      if (jb <= ib) {
+        *reinterpret_cast<u32x4*>(dst) = d00;
+        *reinterpret_cast<u32x4*>(dst + 2 * BLK) = d01;
+      }
+      if (jb + 1 <= ib && 32 * (jb + 1) < T) {
+        *reinterpret_cast<u32x4*>(dst + SUB) = d10;
+        *reinterpret_cast<u32x4*>(dst + SUB + 2 * BLK) = d11;
+      }
+    }
+    __syncthreads();
+    if (kt + 1 < nkt) load_tile(k0 + BK);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ks = k0 + 32 * s;
+      if (ks > qw + 31 || ks >= T || !wave_in) break;  // wave-uniform: the rest of the tile is above the diagonal
+#pragma unroll
+      for (int ub = 0; ub < 2; ++ub) {
+        const bf16* rb = Dw + s * SUB;
+        const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rb + ds_tr_off(lane, ub, 0)));
+        const bf16x4v hv = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rb + ds_tr_off(lane, ub, 1)));
+        Frag<bf16> sf;
+        sf.v = __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) mma16(dqT[c], tile_tr_frag<D, true>(Ks, 32 * s + 16 * ub, c, tl), sf);
+      }
+    }
+  }
+
+  if (qi >= T) return;
+  bf16* dQ = reinterpret_cast<bf16*>(p.dq) + ((size_t)b * H + h) * (size_t)T * D + (size_t)qi * D;
+  const float sc = p.scale;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      store4(dQ + 32 * c + 8 * g + 4 * hi, dqT[c][4 * g] * sc, dqT[c][4 * g + 1] * sc,
+             dqT[c][4 * g + 2] * sc, dqT[c][4 * g + 3] * sc);
+}
+
 template <typename TI, int D>
 hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
   constexpr int RPB = kNT / (D / 8);
@@ -1352,8 +1521,19 @@ hipError_t launch_dq_t(const LayerArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_dq_ds(const LayerArgs& a, hipStream_t s) {
+  const int BHp = (a.B * a.n_ord + 7) & ~7;
+  const long long blocks = (long long)BHp * ((a.T + dqs::BQ - 1) / dqs::BQ);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.d != dqs::D || !a.dsw) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_dq_ds_kernel, dim3((unsigned)blocks), dim3(dqs::NT), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+hipError_t launch_bwd_dq_ds(const LayerArgs& a, hipStream_t s) { return launch_dq_ds(a, s); }
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16_in, hipStream_t s) {
   if (bf16_in) return a.d == 64 ? launch_pre_t<bf16, 64>(a, s) : launch_pre_t<bf16, 128>(a, s);
   return a.d == 64 ? launch_pre_t<float, 64>(a, s) : launch_pre_t<float, 128>(a, s);

@@ -92,6 +92,14 @@ struct LayerArgs {
   float* da;         // [H][pat_len] outputs (rows of replaced heads)
   float* dr;
   void* out;         // forward: o
+  // bf16 at d = 128, when the workspace holds it: dS of every ordinary slice, written by bwd_kv
+  // and read by bwd_dq_ds.  Per slice (b * n_ord + ordinary rank of h) the 32 x 32 subtiles on or
+  // below the diagonal, packed row by row (query block ib, key blocks 0 .. ib: subtile
+  // ib (ib + 1) / 2 + jb), each as its two B-operand fragments of bwd_kv's dK product: element
+  // u * 512 + L * 8 + e = dS[32 ib + 16 u + perm_row(e, L / 32)][32 jb + L % 32], L = 0..63.
+  // nullptr: bwd_kv stores nothing and bwd_dq re-forms dS.
+  void* dsw;
+  long long ds_ntri;  // subtiles per slice: n32 (n32 + 1) / 2, n32 = ceil(T / 32)
   void* dq;
   void* dk;
   void* dv;
@@ -166,6 +174,8 @@ hipError_t launch_mixed_fwd(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_pre(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_kv(const LayerArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dq(const LayerArgs& a, bool bf16, hipStream_t s);
+// dQ from the dS that bwd_kv stored (a.dsw set; bf16, d = 128 only)
+hipError_t launch_bwd_dq_ds(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bwd_pattern(const LayerArgs& a, const HeadList& rl, bool bf16, hipStream_t s);
 hipError_t launch_pattern_grad_reduce(const LayerArgs& a, const HeadList& rl, hipStream_t s);
 int pattern_grad_sub_block();  // keys per dr partial row of bwd_pattern (one per wave)
@@ -207,6 +217,19 @@ __host__ __device__ inline int calib_groups(int n_qt) {
 }
 
 __host__ __device__ inline bool is_replaced(const uint64_t* rep, int h) { return (rep[h >> 6] >> (h & 63)) & 1ull; }
+// Index of head h among the ordinary heads (those below it that are not replaced).
+__host__ __device__ inline int ord_rank(const uint64_t* rep, int h) {
+  int n = h;
+  for (int w = 0; w < (h >> 6); ++w) n -= __builtin_popcountll(rep[w]);
+  if (h & 63) n -= __builtin_popcountll(rep[h >> 6] & ((1ull << (h & 63)) - 1ull));
+  return n;
+}
+constexpr int kDsPiece = 1024;  // bf16 elements of one stored 32 x 32 dS subtile
+// Bytes of the stored dS of B * n_ord ordinary slices of length T.
+__host__ __device__ inline size_t ds_bytes(int B, int n_ord, int T) {
+  const size_t n32 = ((size_t)T + 31) / 32;
+  return (size_t)B * n_ord * (n32 * (n32 + 1) / 2) * kDsPiece * 2;
+}
 
 // bwd_kv grid: key/value slot bh and key block kb of block x, or false for a padding block.  The grid
 // runs in two sections, the key/value heads with an ordinary query head (the first B * n_kv_ord

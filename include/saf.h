@@ -70,6 +70,15 @@ typedef enum { SAF_F32 = 0, SAF_BF16 = 1 } saf_dtype;
 size_t saf_attn_fwd_workspace_size(int B, int H, int T, int d);
 size_t saf_attn_bwd_workspace_size(int B, int H, int T, int d);
 size_t saf_calibrate_workspace_size(int N, int H, int T, int d);
+/* A larger backward workspace with which saf_attn_bwd / saf_attn_bwd_gqa keep the ordinary heads'
+ * dS = P o (dP - delta) between their two kernels instead of forming S and dP a second time for dQ
+ * (three products per entry become one).  It applies to bf16 at d = 128 without grouped key/value
+ * heads (Hkv = H) and with at least one ordinary head (n_replaced < H); the extra room is
+ * 2 * B * (H - n_replaced) * n32 (n32 + 1) / 2 * 1024 bytes, n32 = ceil(T / 32) (bf16 32 x 32
+ * subtiles on or below the diagonal: about B * (H - n_replaced) * T^2 bytes).  Returns
+ * saf_attn_bwd_workspace_size(B, H, T, d) where the path does not apply, 0 for an empty call and
+ * SIZE_MAX for sizes out of range. */
+size_t saf_attn_bwd_ds_workspace_size(saf_dtype dt, int B, int H, int Hkv, int T, int d, int n_replaced);
 
 /*
  * Prepared fixed pattern (optional).                            [Notes §二.3, Eq.(3); §二.4]
@@ -108,6 +117,12 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
  *   q, k, v, o, dout : [B][H][T][d] dt;   lse : [B][H][T] fp32 as written by saf_attn_fwd for
  *   the same q, k, v, replaced, a, r, scale;   dq, dk, dv : [B][H][T][d] dt (written).
  *   pattern : as for saf_attn_fwd (NULL or prepared).
+ * Two kernels follow a row-statistic pass: a key-block kernel (dK, dV) and a query-block kernel
+ * (dQ).  With ws_bytes >= saf_attn_bwd_ds_workspace_size(...) for this call's shapes and number of
+ * replaced heads (bf16, d = 128, Hkv = H), the key-block kernel stores dS in the workspace and the
+ * query-block kernel reads it (they then run one after the other on `stream`, also with the
+ * overlap option below); otherwise the query-block kernel forms S and dP again.  Both paths give
+ * the same values up to the order of fp32 additions.
  */
 saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
                         const void* v, const void* o, const void* dout, const float* lse,
@@ -242,7 +257,9 @@ const char* saf_last_error(void);
  * first use, kept for the thread's life, default priority) beside the key-block kernel: both depend
  * only on the preprocess and write disjoint outputs.  The fork and join are event record / wait
  * pairs on the caller's stream (a graph capture of that stream records them), so the call keeps its
- * stream semantics and its results are bitwise the same.  Faster where the two kernels leave each
+ * stream semantics and its results are bitwise those of the call without overlap and with a
+ * workspace of saf_attn_bwd_workspace_size bytes (the stored-dS path, which orders the two
+ * kernels, is not taken while overlap is enabled).  Faster where the two kernels leave each
  * other's tails idle (e.g. half the heads replaced at 8K context); per-kernel durations from
  * saf_trace_* then overlap.
  */

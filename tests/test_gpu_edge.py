@@ -221,14 +221,14 @@ def test_wide_range_pattern_uses_exponential_form(dtype):
     check_bwd(x, dq, dk, dv, heads, None, None, TOL[dtype], "wide")
 
 
-@pytest.mark.parametrize("overlap", [0, 1])
-def test_graph_capture_of_forward_and_backward_replays_exactly(overlap):
+@pytest.mark.parametrize("overlap,d", [(0, 64), (1, 64), (0, 128)])
+def test_graph_capture_of_forward_and_backward_replays_exactly(overlap, d):
     """fwd + bwd captured into a HIP graph (with overlap on, the backward forks its query-block
-    kernel onto a side stream and joins back) replay to the bits of the eager calls, with eager work
-    between replays."""
+    kernel onto a side stream and joins back; at d = 128 the backward keeps dS in its workspace)
+    replay to the bits of the eager calls, with eager work between replays."""
     saf = _saf()
     saf.saf_set_backward_overlap(overlap)
-    B, H, T, d = 2, 4, 300, 64
+    B, H, T = 2, 4, 300
     rep = [0, 1, 0, 1]
     g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=17, device="cuda")
     pat = saf.prepare_pattern(rep, g.a, g.r)

@@ -273,3 +273,61 @@ def test_kt_without_the_xor_conflicts():
         hi, i = lane >> 5, lane & 15
         addrs.append((8 * hi + (i >> 2)) * KKT + 16 * ((lane >> 4) & 1) + 4 * (i & 3))
     assert banks_max(addrs, 8, 32) == 4
+
+
+# ---- stored dS subtiles (saf_bwd.hip: bwd_kv's dS store, bwd_dq_ds's ds_tr_off) ------------------
+# The wide key-block kernel stores each 32 x 32 subtile of dS as its two B-operand fragments:
+# element u * 512 + L * 8 + e holds dS[query 16u + perm_row(e, L // 32)][key L % 32].  bwd_dq_ds
+# copies the 1024 elements into LDS in four quarters (u, L // 32) of 256 elements placed DS_BLK
+# elements apart, and reads the dQ product's B operand (lane = query, slots = keys) back with the
+# transposing read.
+DS_BLK = 288
+
+
+def ds_lds_pos(raw):
+    """LDS element position of stored element `raw` (0 .. 1023) within a subtile's region."""
+    return (raw // 256) * DS_BLK + raw % 256
+
+
+def ds_tr_off(lane, ub, rd):
+    """Element address lane `lane` issues for read rd (keys +0..3 / +8..11) of k16 step ub."""
+    jp, a, g, hi = (lane & 15) >> 2, lane & 3, (lane >> 4) & 1, lane >> 5
+    key = 16 * ub + 8 * rd + 4 * hi + jp
+    return (2 * g + (a & 1)) * DS_BLK + 8 * key + 4 * (a >> 1)
+
+
+def ds_subtile_mem():
+    """The LDS region after the copy: each element names its (query, key)."""
+    mem = [None] * (4 * DS_BLK)
+    for u, L, e in itertools.product(range(2), range(64), range(8)):
+        raw = 512 * u + 8 * L + e
+        q, key = 16 * u + perm_row(e, L // 32), L % 32
+        assert mem[ds_lds_pos(raw)] is None
+        mem[ds_lds_pos(raw)] = (q, key)
+    return mem
+
+
+def test_stored_ds_read_gives_the_dq_b_operand():
+    """Slot e of lane l: dS[query l % 32][key 16 ub + perm_row(e, l // 32)], the order in which the
+    K^T fragment (tile_tr_frag of the K row tile) carries the keys."""
+    mem = ds_subtile_mem()
+    for ub in range(2):
+        lo = [ds_tr_off(l, ub, 0) for l in range(64)]
+        hi = [ds_tr_off(l, ub, 1) for l in range(64)]
+        for a in lo + hi:  # 8-byte aligned, inside the region, never padding
+            assert (2 * a) % 8 == 0 and 0 <= a and a + 3 < 4 * DS_BLK and a % DS_BLK + 3 < 256
+        vlo, vhi = tr_read(lo, mem), tr_read(hi, mem)
+        for lane in range(64):
+            frag = vlo[lane] + vhi[lane]
+            assert frag == [(lane & 31, 16 * ub + perm_row(e, lane >> 5)) for e in range(8)]
+
+
+def test_stored_ds_copy_and_reads_are_free_of_bank_conflicts():
+    """The copy (lane L writes its 16 bytes of fragment u) and both reads of each k16 step; with
+    the quarters 256 elements apart (no padding) the reads would be 4-way conflicted."""
+    for u in range(2):
+        assert banks_max([ds_lds_pos(512 * u + 8 * L) for L in range(64)], 16, 16) == 1
+    for ub, rd in itertools.product(range(2), range(2)):
+        assert banks_max([ds_tr_off(l, ub, rd) for l in range(64)], 8, 32) == 1
+    unpadded = [ds_tr_off(l, 0, 0) - ((2 * ((l >> 4) & 1) + (l & 1)) * (DS_BLK - 256)) for l in range(64)]
+    assert banks_max(unpadded, 8, 32) == 4

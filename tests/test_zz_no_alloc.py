@@ -51,7 +51,8 @@ def test_noalloc_backward_matches_the_workspace_call():
         g = synth.layer_inputs(B, H, T, d, dtype, rep, seed=T + d, device="cuda")
         pat = saf.prepare_pattern(rep, g.a, g.r) if prepared else None
         o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)
-        ref = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, pattern=pat)
+        # the workspace call with the same kernels (the no-allocation call never keeps dS)
+        ref = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, pattern=pat, keep_ds=False)
         got = tuple(torch.full_like(t, float("nan")) for t in ref)
         _bwd_noalloc(saf, g, o, lse, rep, pat, got)
         torch.cuda.synchronize()
@@ -67,7 +68,7 @@ def test_noalloc_backward_replays_from_a_graph():
     rep = [0, 1, 0, 1]
     g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=41, device="cuda")
     o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
-    ref = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
+    ref = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, keep_ds=False)
     out = tuple(torch.empty_like(t) for t in ref)
     graph = torch.cuda.CUDAGraph()
     cs = torch.cuda.Stream()
