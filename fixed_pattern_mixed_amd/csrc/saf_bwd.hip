@@ -1318,8 +1318,11 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
 // 4 hi + j and queries 16 g + 4a .. +3, which the store keeps contiguous in quarter 2g + (a & 1)
 // at position 4 (a >> 1).  The padding puts the four quarters a read meets on disjoint 16-bank
 // segments.
+#ifndef SAF_DQDS_WAVES
+#define SAF_DQDS_WAVES 8  // waves (32 queries each) per bwd_dq_ds work item
+#endif
 namespace dqs {
-constexpr int W = 8, NT = 64 * W, D = 128, BQ = 32 * W, BK = 64, NS = BK / 32;
+constexpr int W = SAF_DQDS_WAVES, NT = 64 * W, D = 128, BQ = 32 * W, BK = 64, NS = BK / 32;
 constexpr int BLK = 288;      // LDS elements per quarter of a subtile (256 + 32 of padding)
 constexpr int SUB = 4 * BLK;  // LDS elements per subtile
 }  // namespace dqs
