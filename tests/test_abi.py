@@ -59,6 +59,29 @@ def bwd(dt=1, B=2, H=4, T=64, d=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE, g=FAKE, lse=
                             dk, dv, ws, ws_n, None)
 
 
+
+def test_stored_ds_workspace_size():
+    """The larger backward workspace with room for the stored dS: bf16, d = 128, Hkv = H and an
+    ordinary head; 2 bytes per entry of the 32 x 32 subtiles on or below the diagonal of each
+    ordinary slice, after the plain workspace (256-byte aligned); the plain size elsewhere."""
+    f = saf.saf_attn_bwd_ds_workspace_size
+    for B, H, T, R in [(2, 16, 8192, 4), (1, 4, 257, 1), (3, 2, 33, 0), (1, 2, 1, 1)]:
+        base = saf.saf_attn_bwd_workspace_size(B, H, T, 128)
+        n32 = (T + 31) // 32
+        extra = 2 * B * (H - R) * (n32 * (n32 + 1) // 2) * 1024
+        assert f(saf.SAF_BF16, B, H, H, T, 128, R) == base + (extra + 255) // 256 * 256
+    assert f(saf.SAF_BF16, 2, 16, 16, 8192, 128, 4) - saf.saf_attn_bwd_workspace_size(2, 16, 8192, 128) == 1616904192  # 1.6 GB at the 1B shape
+    base = saf.saf_attn_bwd_workspace_size(2, 8, 512, 128)
+    assert f(saf.SAF_F32, 2, 8, 8, 512, 128, 1) == base          # fp32: dQ forms S and dP again
+    assert f(saf.SAF_BF16, 2, 8, 2, 512, 128, 1) == base         # grouped key/value heads
+    assert f(saf.SAF_BF16, 2, 8, 8, 512, 128, 8) == base         # no ordinary head
+    assert f(saf.SAF_BF16, 2, 8, 8, 512, 64, 1) == saf.saf_attn_bwd_workspace_size(2, 8, 512, 64)
+    assert f(saf.SAF_BF16, 0, 8, 8, 512, 128, 1) == 0
+    for bad in [(saf.SAF_BF16, 2, 8, 3, 512, 128, 1), (saf.SAF_BF16, 2, 8, 8, 512, 128, 9),
+                (saf.SAF_BF16, 2, 8, 8, 512, 128, -1), (saf.SAF_BF16, 2, 8, 8, 512, 96, 1),
+                (saf.SAF_BF16, 2, 8, 8, 65537, 128, 1)]:
+        assert f(*bad) == SIZE_MAX, bad
+
 @pytest.mark.parametrize("case,kw,status", [
     ("unsupported d", dict(d=96), saf.SAF_ERR_UNSUPPORTED),
     ("too many heads", dict(H=300, rep=_mask(*([0] * 300))), saf.SAF_ERR_UNSUPPORTED),
