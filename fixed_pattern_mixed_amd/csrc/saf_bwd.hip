@@ -1335,7 +1335,10 @@ __device__ __forceinline__ int ds_tr_off(int lane, int ub, int rd) {
   return (2 * g + (a & 1)) * dqs::BLK + 8 * key + 4 * (a >> 1);
 }
 
-__global__ __launch_bounds__(dqs::NT) __attribute__((amdgpu_waves_per_eu(2)))
+#ifndef SAF_DQDS_WPE
+#define SAF_DQDS_WPE 2  // waves per SIMD bwd_dq_ds is compiled for (4 caps it at 128 registers: spills)
+#endif
+__global__ __launch_bounds__(dqs::NT) __attribute__((amdgpu_waves_per_eu(SAF_DQDS_WPE)))
 void bwd_dq_ds_kernel(LayerArgs p) {
   using namespace dqs;
   typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
@@ -1373,51 +1376,42 @@ void bwd_dq_ds_kernel(LayerArgs p) {
   for (int c = 0; c < D / 32; ++c) zero(dqT[c]);
 
   static_assert(NS == 2, "two 32-key subtiles per K tile");
-  Chunks<bf16, D, BK, NT> pk;
   typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-  u32x4 d00 = {}, d01 = {}, d10 = {}, d11 = {};  // prefetched subtiles: [subtile][fragment]
-  // the K tile and, where bwd_kv stored them (key blocks jb <= ib inside the sequence;
-  // wave-uniform), the wave's two subtiles of the tile
+  struct DsTile {  // a key tile's two stored subtiles, this lane's 16 bytes of each fragment
+    u32x4 s0u0, s0u1, s1u0, s1u1;
+  };
   const bool wave_in = qw < T;  // waves past the end have no stored row (and write no dQ)
-  // (dS first: it comes from HBM, read once and past the caches; K is mostly in L2)
-  auto load_tile = [&](int k0) {
+  // the wave's subtiles of key tile k0 where bwd_kv stored them (key blocks jb <= ib inside the
+  // sequence; wave-uniform), from HBM past the caches (read once)
+  auto load_ds = [&](int k0, DsTile& t) {
     const int jb = k0 >> 5;
     const u32x4* src = reinterpret_cast<const u32x4*>(drow + (size_t)jb * kDsPiece);
     if (wave_in && jb <= ib) {
-      d00 = __builtin_nontemporal_load(src);
-      d01 = __builtin_nontemporal_load(src + 64);
+      t.s0u0 = __builtin_nontemporal_load(src);
+      t.s0u1 = __builtin_nontemporal_load(src + 64);
     }
     if (wave_in && jb + 1 <= ib && 32 * (jb + 1) < T) {
-      d10 = __builtin_nontemporal_load(src + kDsPiece / 8);
-      d11 = __builtin_nontemporal_load(src + kDsPiece / 8 + 64);
+      t.s1u0 = __builtin_nontemporal_load(src + kDsPiece / 8);
+      t.s1u1 = __builtin_nontemporal_load(src + kDsPiece / 8 + 64);
     }
-    pk.load(K, k0, T, tid);
+  };
+  // into the wave's own region (its earlier reads of the region were issued before these writes,
+  // and one wave's LDS operations complete in order)
+  auto store_ds = [&](int k0, const DsTile& t) {
+    if (!wave_in) return;
+    const int jb = k0 >> 5;
+    bf16* dst = Dw + hi * BLK + 8 * l32;
+    if (jb <= ib) {
+      *reinterpret_cast<u32x4*>(dst) = t.s0u0;
+      *reinterpret_cast<u32x4*>(dst + 2 * BLK) = t.s0u1;
+    }
+    if (jb + 1 <= ib && 32 * (jb + 1) < T) {
+      *reinterpret_cast<u32x4*>(dst + SUB) = t.s1u0;
+      *reinterpret_cast<u32x4*>(dst + SUB + 2 * BLK) = t.s1u1;
+    }
   };
   const TileLane<D, true> tl(lane);
-
-  const int kend = min(T, q0 + BQ);
-  const int nkt = (kend + BK - 1) / BK;
-  load_tile(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * BK;
-    __syncthreads();  // the previous tile's readers of Ks are done
-    pk.template store_tile<true>(Ks, tid);
-    // this wave's subtiles into its own region (its earlier reads of the region were issued
-    // before these writes, and one wave's LDS operations complete in order)
-    if (wave_in) {
-      const int jb = k0 >> 5;
-      bf16* dst = Dw + hi * BLK + 8 * l32;
-      if (jb <= ib) {
-        *reinterpret_cast<u32x4*>(dst) = d00;
-        *reinterpret_cast<u32x4*>(dst + 2 * BLK) = d01;
-      }
-      if (jb + 1 <= ib && 32 * (jb + 1) < T) {
-        *reinterpret_cast<u32x4*>(dst + SUB) = d10;
-        *reinterpret_cast<u32x4*>(dst + SUB + 2 * BLK) = d11;
-      }
-    }
-    __syncthreads();
-    if (kt + 1 < nkt) load_tile(k0 + BK);
+  auto products = [&](int k0) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int ks = k0 + 32 * s;
@@ -1433,6 +1427,29 @@ void bwd_dq_ds_kernel(LayerArgs p) {
         for (int c = 0; c < D / 32; ++c) mma16(dqT[c], tile_tr_frag<D, true>(Ks, 32 * s + 16 * ub, c, tl), sf);
       }
     }
+  };
+
+  // dS is prefetched two key tiles ahead (two register sets taken in turn), K one tile ahead
+  const int kend = min(T, q0 + BQ);
+  const int nkt = (kend + BK - 1) / BK;
+  Chunks<bf16, D, BK, NT> pk;
+  DsTile da = {}, db = {};
+  load_ds(0, da);
+  if (nkt > 1) load_ds(BK, db);
+  pk.load(K, 0, T, tid);
+  auto step = [&](int kt, DsTile& cur) {
+    const int k0 = kt * BK;
+    __syncthreads();  // the previous tile's readers of Ks are done
+    pk.template store_tile<true>(Ks, tid);
+    store_ds(k0, cur);
+    __syncthreads();
+    if (kt + 2 < nkt) load_ds(k0 + 2 * BK, cur);
+    if (kt + 1 < nkt) pk.load(K, k0 + BK, T, tid);
+    products(k0);
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(kt, da);
+    if (kt + 1 < nkt) step(kt + 1, db);
   }
 
   if (qi >= T) return;
