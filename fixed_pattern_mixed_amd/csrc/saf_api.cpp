@@ -319,7 +319,8 @@ size_t saf_attn_bwd_workspace_size(int B, int H, int T, int d) {
 }
 
 size_t saf_attn_bwd_ds_workspace_size(saf_dtype dt, int B, int H, int Hkv, int T, int d, int n_replaced) {
-  if (!sizes_ok(B, H, T, d) || Hkv < 1 || Hkv > H || H % Hkv != 0 || n_replaced < 0 || n_replaced > H)
+  if ((dt != SAF_F32 && dt != SAF_BF16) || !sizes_ok(B, H, T, d) || Hkv < 1 || Hkv > H ||
+      H % Hkv != 0 || n_replaced < 0 || n_replaced > H)
     return SIZE_MAX;
   if (B == 0 || T == 0) return 0;
   const size_t base = bwd_ws(B, H, T, d);

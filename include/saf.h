@@ -77,7 +77,7 @@ size_t saf_calibrate_workspace_size(int N, int H, int T, int d);
  * 2 * B * (H - n_replaced) * n32 (n32 + 1) / 2 * 1024 bytes, n32 = ceil(T / 32) (bf16 32 x 32
  * subtiles on or below the diagonal: about B * (H - n_replaced) * T^2 bytes).  Returns
  * saf_attn_bwd_workspace_size(B, H, T, d) where the path does not apply, 0 for an empty call and
- * SIZE_MAX for sizes out of range. */
+ * SIZE_MAX for sizes out of range or an unknown dtype. */
 size_t saf_attn_bwd_ds_workspace_size(saf_dtype dt, int B, int H, int Hkv, int T, int d, int n_replaced);
 
 /*

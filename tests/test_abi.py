@@ -79,7 +79,7 @@ def test_stored_ds_workspace_size():
     assert f(saf.SAF_BF16, 0, 8, 8, 512, 128, 1) == 0
     for bad in [(saf.SAF_BF16, 2, 8, 3, 512, 128, 1), (saf.SAF_BF16, 2, 8, 8, 512, 128, 9),
                 (saf.SAF_BF16, 2, 8, 8, 512, 128, -1), (saf.SAF_BF16, 2, 8, 8, 512, 96, 1),
-                (saf.SAF_BF16, 2, 8, 8, 65537, 128, 1)]:
+                (saf.SAF_BF16, 2, 8, 8, 65537, 128, 1), (7, 2, 8, 8, 512, 128, 1)]:
         assert f(*bad) == SIZE_MAX, bad
 
 @pytest.mark.parametrize("case,kw,status", [
