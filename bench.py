@@ -3,7 +3,8 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input held in HBM: the
 mixed forward (ordinary and replaced heads in one grid) followed by the mixed backward (delta
-preprocess, key-block kernel, query-block dQ kernel).  Forward-only workloads (prefill) time the
+preprocess, key-block kernel, query-block dQ kernel; bf16 at d=128 with the workspace that keeps dS
+between the two, the key-block kernel also stores dS and the dQ kernel reads it).  Forward-only workloads (prefill) time the
 forward alone.  Prints ONE JSON line.
 
 The headline workload is the largest fwd+bwd configuration that fits one GPU: one GPU's share of
@@ -157,20 +158,31 @@ def spin_up(torch, seconds=0.3):
     return round((time.perf_counter() - t0) * 1e3, 1)
 
 
-def time_steps(torch, layer, steps, warmup, trace=None):
+def time_steps(torch, layer, steps, warmup, trace=None, per_step=None):
+    """Seconds per step over `steps` steps after `warmup` untimed ones.  per_step: a list that
+    receives each step's duration in ms, from HIP events recorded between the steps on the stream
+    the library launches on."""
     for _ in range(warmup):
         layer.step()
     torch.cuda.synchronize()
     if trace is not None:
         trace.begin()
+    ev = None
+    if per_step is not None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
         layer.step()
+        if ev is not None:
+            ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if trace is not None:
         trace.end()
         trace.collect()
+    if ev is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     return (t1 - t0) / steps
 
 
@@ -401,6 +413,36 @@ def cpu_baseline(w, replaced, min_seconds=10.0):
     }
 
 
+def step_spread(per_step):
+    """Median, minimum and maximum of the per-step durations (ms)."""
+    v = sorted(per_step)
+    if not v:
+        return None
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"median": round(med, 4), "min": round(v[0], 4), "max": round(v[-1], 4), "n": n}
+
+
+def cpu_calibration_baseline(w):
+    """The fp64 oracle's calibration (Eq. (1) rows and the mean map) on one head of the workload's
+    calibration shape (all N sequences, full T; Q, K N(0,1) rounded to bf16), scaled to all heads:
+    estimated ms per saf_calibrate call of the same shape."""
+    import oracle
+    import torch
+    N, H, T, d = w.calib_N, w.H, w.T, w.d
+    g = torch.Generator().manual_seed(1437)
+    q = torch.randn((N, T, d), generator=g).to(torch.bfloat16).double().numpy()
+    k = torch.randn((N, T, d), generator=g).to(torch.bfloat16).double().numpy()
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.head_calibrate(q, k)
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * H * 1e3, 1), "unit": "ms per call (estimated)",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "head 0 of %d (all %d sequences, full T=%d, d=%d) in %.1f s, scaled by %d"
+                      % (H, N, T, d, dt, H)}
+
+
 def rotate_timings(torch, saf, layers, steps, rounds=2):
     """Time each layer of `layers` (label -> Layer) for `steps` steps, in turn, `rounds` times, and
     keep each one's best round: (seconds per step, per-kernel summary).  Alternating keeps slow
@@ -523,7 +565,8 @@ def main():
     layer = Layer(saf, torch, w, replaced, dev)
     spin_ms = spin_up(torch)
     trace = saf.KernelTrace(capacity=4 * (args.steps + 1))
-    t_step = time_steps(torch, layer, args.steps, args.warmup, trace)
+    per_step = []
+    t_step = time_steps(torch, layer, args.steps, args.warmup, trace, per_step)
     tokens = w.B * w.T
     flops = total_flops(w.B, w.T, w.d, replaced, w.backward)
     kf = kernel_flops(w.B, w.T, w.d, replaced)
@@ -562,6 +605,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"},
         "tflops": round(flops / t_step / 1e12, 1),
         "pct_bf16_peak": round(100 * flops / t_step / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "step_ms": step_spread(per_step),
         "kernels": kernels,
         "pattern_prepare_ms": round(layer.prepare_ms, 3),
         "gpu_spin_up_ms": spin_ms,
@@ -604,6 +648,8 @@ def main():
         cw = synth.WORKLOADS[args.calibration_workload]
         if cw.calib_N:
             out["calibration"] = calibration(torch, saf, cw)
+            if not args.no_cpu_baseline:
+                out["calibration"]["cpu_baseline"] = cpu_calibration_baseline(cw)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, replaced)

@@ -70,3 +70,12 @@ def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("x", "kern") is None
     src.write_text("kernel v2\n")  # the kernel changed since the counters were taken
     assert bench.measured_traffic("w", "kern") is None
+
+
+def test_step_spread():
+    """Median (middle value, or the mean of the middle two), minimum and maximum of the per-step
+    durations; nothing for no steps."""
+    import bench
+    assert bench.step_spread([1.0, 3.0, 2.0, 5.0]) == {"median": 2.5, "min": 1.0, "max": 5.0, "n": 4}
+    assert bench.step_spread([2.0, 9.0, 4.0]) == {"median": 4.0, "min": 2.0, "max": 9.0, "n": 3}
+    assert bench.step_spread([]) is None
