@@ -423,24 +423,28 @@ def step_spread(per_step):
     return {"median": round(med, 4), "min": round(v[0], 4), "max": round(v[-1], 4), "n": n}
 
 
-def cpu_calibration_baseline(w):
-    """The fp64 oracle's calibration (Eq. (1) rows and the mean map) on one head of the workload's
-    calibration shape (all N sequences, full T; Q, K N(0,1) rounded to bf16), scaled to all heads:
-    estimated ms per saf_calibrate call of the same shape."""
+def cpu_calibration_baseline(w, min_seconds=10.0):
+    """The fp64 oracle's calibration (Eq. (1) rows and the mean map) on whole heads of the
+    workload's calibration shape (all N sequences, full T; Q, K N(0,1) rounded to bf16), one head
+    after another until at least min_seconds of CPU work (or every head) is done, scaled to all
+    heads: estimated ms per saf_calibrate call of the same shape."""
     import oracle
     import torch
     N, H, T, d = w.calib_N, w.H, w.T, w.d
     g = torch.Generator().manual_seed(1437)
-    q = torch.randn((N, T, d), generator=g).to(torch.bfloat16).double().numpy()
-    k = torch.randn((N, T, d), generator=g).to(torch.bfloat16).double().numpy()
     oracle.build()
-    t0 = time.perf_counter()
-    oracle.head_calibrate(q, k)
-    dt = time.perf_counter() - t0
-    return {"value": round(dt * H * 1e3, 1), "unit": "ms per call (estimated)",
+    n_h, dt = 0, 0.0
+    while n_h < H and dt < min_seconds:
+        q = torch.randn((N, T, d), generator=g).to(torch.bfloat16).double().numpy()
+        k = torch.randn((N, T, d), generator=g).to(torch.bfloat16).double().numpy()
+        t0 = time.perf_counter()
+        oracle.head_calibrate(q, k)
+        dt += time.perf_counter() - t0
+        n_h += 1
+    return {"value": round(dt / n_h * H * 1e3, 1), "unit": "ms per call (estimated)",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "head 0 of %d (all %d sequences, full T=%d, d=%d) in %.1f s, scaled by %d"
-                      % (H, N, T, d, dt, H)}
+            "sample": "%d of %d heads (all %d sequences, full T=%d, d=%d) in %.1f s, scaled to %d heads"
+                      % (n_h, H, N, T, d, dt, H)}
 
 
 def rotate_timings(torch, saf, layers, steps, rounds=2):
