@@ -120,9 +120,9 @@ saf_status saf_attn_fwd(saf_dtype dt, int B, int H, int T, int d, const void* q,
  * Two kernels follow a row-statistic pass: a key-block kernel (dK, dV) and a query-block kernel
  * (dQ).  With ws_bytes >= saf_attn_bwd_ds_workspace_size(...) for this call's shapes and number of
  * replaced heads (bf16, d = 128, Hkv = H), the key-block kernel stores dS in the workspace and the
- * query-block kernel reads it (they then run one after the other on `stream`, also with the
- * overlap option below); otherwise the query-block kernel forms S and dP again.  Both paths give
- * the same values up to the order of fp32 additions.
+ * query-block kernel, launched after it on `stream`, reads it (not while the overlap option below
+ * is enabled); otherwise the query-block kernel forms S and dP again.  Both paths give the same
+ * values up to the order of fp32 additions.
  */
 saf_status saf_attn_bwd(saf_dtype dt, int B, int H, int T, int d, const void* q, const void* k,
                         const void* v, const void* o, const void* dout, const float* lse,
