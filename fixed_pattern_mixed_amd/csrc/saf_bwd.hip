@@ -12,7 +12,8 @@
 //             or exp(a[j] + r[i-j] - lse_i) where the prepared pattern flags that form.
 //
 // Kernels (one stream, launched bwd_pre, bwd_dq, bwd_kv: the two after the preprocess are
-// independent, and bwd_kv, second, finds the tiles it shares with bwd_dq in the caches):
+// independent, and bwd_kv, second, finds the tiles it shares with bwd_dq in the caches; with dS
+// kept in the workspace: bwd_pre, bwd_kv, bwd_dq_ds):
 //   bwd_pre : delta_i = rowsum(dO o O) of ordinary heads (of replaced heads for the pattern
 //             gradient, which reuses this kernel).
 //   bwd_kv  : one work item per (batch, key/value head, 128-key block), both head kinds in one
