@@ -67,6 +67,44 @@ def test_maximum_length():
     assert torch.count_nonzero(dq[0, 1]) == 0 and torch.count_nonzero(dk[0, 1]) == 0
 
 
+def test_maximum_length_with_stored_ds():
+    """T = 65536 at bf16, d = 128, one ordinary and one replaced head: the backward keeps dS in
+    its workspace (4.3 GB: element offsets past 2^31).  Sampled dQ rows of the ordinary head
+    (always including the first and the last position) against the oracle, and dQ, dK, dV against
+    the backward that forms S and dP again."""
+    saf = _saf()
+    T, d = 65536, 128
+    rep = [False, True]
+    x = synth.layer_inputs(1, 2, T, d, torch.bfloat16, rep, ar_std=0.5, seed=66)
+    g = synth.layer_inputs(1, 2, T, d, torch.bfloat16, rep, ar_std=0.5, seed=66, device="cuda")
+    assert saf.saf_attn_bwd_ds_workspace_size(saf.SAF_BF16, 1, 2, 2, T, d, 1) > (4 << 30)
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    tr = saf.KernelTrace(capacity=8)
+    tr.begin()
+    dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r)
+    tr.end()
+    torch.cuda.synchronize()
+    tr.collect()
+    assert "bwd_dq_ds" in tr.summary()
+    tr.close()
+    dq2, dk2, dv2 = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, keep_ds=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    err = (dq.double() - dq2.double()).abs().amax(dim=-1)
+    scale = dq2.double().abs().amax(dim=-1)
+    assert bool(torch.all(err <= TOL[torch.bfloat16] * scale + 1e-30))
+    rows = sample_rows(T, 64, seed=8)
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    idx = torch.as_tensor(rows, dtype=torch.long, device="cuda")
+    rq, _, _ = oracle.head_bwd(0, x.v[0, 0], x.dout[0, 0], q=x.q[0, 0], k=x.k[0, 0], qrows=rows,
+                               want_dk=False, want_dv=False)
+    wr = Worst("T=65536 stored dS")
+    wr.add(f64(dq[0, 0].index_select(0, idx)), rq, TOL[torch.bfloat16], "dq", T=T, rows=rows,
+           rounding=lambda r: dq_uncancelled_scale(x.q[0, 0], x.k[0, 0], x.v[0, 0], x.dout[0, 0], r))
+    wr.report()
+    assert torch.count_nonzero(dq[0, 1]) == 0 and torch.count_nonzero(dk[0, 1]) == 0
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_replaced_heads_never_read_q_k(dtype):
     saf = _saf()
