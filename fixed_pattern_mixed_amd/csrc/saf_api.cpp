@@ -639,6 +639,7 @@ saf_status saf_attn_bwd_pattern(saf_dtype dt, int B, int H, int T, int d, const 
 
   la.B = B; la.H = H; la.T = T; la.d = d;
   la.Hkv = H;
+  fill_order(la, replaced);  // the preprocess takes the replaced slices from the query order
   la.pat_len = pat_len;
   la.v = v; la.o = o; la.dout = dout;
   la.a = a; la.r = r;

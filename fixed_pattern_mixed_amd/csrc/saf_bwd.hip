@@ -58,26 +58,48 @@ namespace {
 constexpr int kNT = 256;
 
 // ------------------------------------------------------------------------------------ bwd_pre
+// Work items: (slice of a head whose delta is wanted, chunk of kPreRows x RPB rows); a row's D
+// elements are spread over D / 8 lanes, and each thread takes kPreRows rows (their loads issued
+// together).  The other heads' rows are not written: bwd_kv selects them away, and the query-block
+// kernels read only ordinary slices.
+constexpr int kPreRows = 4;
 template <typename TI, int D>
 __global__ __launch_bounds__(kNT) void bwd_pre_kernel(LayerArgs p) {
   constexpr int G = D / 8;      // lanes per row, 8 elements each
-  constexpr int RPB = kNT / G;  // rows per block
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / G;
+  constexpr int RPB = kNT / G;  // rows per pass of the block
+  constexpr int NR = kPreRows;  // passes: rows per thread
+  const int T = p.T;
+  // the wanted heads' slices: the ordinary ones (the first B * n_ord slots of the query order) or,
+  // for the pattern gradient, the replaced ones (the rest)
+  const int s0 = p.delta_rep ? p.B * p.n_ord : 0;
+  const int ns = p.delta_rep ? p.B * (p.H - p.n_ord) : p.B * p.n_ord;
+  const int chunks = (T + RPB * NR - 1) / (RPB * NR);
+  const int slot = blockIdx.x / chunks, c = blockIdx.x % chunks;
+  if (slot >= ns) return;
+  int b, h;
+  p.qord.slice(s0 + slot, p.B, b, h);
+  const size_t base = ((size_t)b * p.H + h) * T;
+  const TI* O = reinterpret_cast<const TI*>(p.o) + base * D;
+  const TI* dO = reinterpret_cast<const TI*>(p.dout) + base * D;
   const int part = threadIdx.x % G;
-  const long long total = (long long)p.B * p.H * p.T;
-  float acc = 0.f;
-  const bool valid = row < total;
-  const int h = valid ? (int)((row / p.T) % p.H) : 0;
-  const bool want = valid && (is_replaced(p.rep, h) == (p.delta_rep != 0));
-  if (want) {
-    const Frag<TI> of = load8(reinterpret_cast<const TI*>(p.o) + row * D + part * 8);
-    const Frag<TI> gf = load8(reinterpret_cast<const TI*>(p.dout) + row * D + part * 8);
+  const int r0 = c * RPB * NR + threadIdx.x / G;
+  Frag<TI> of[NR], gf[NR];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)of.v[e] * (float)gf.v[e];
+  for (int i = 0; i < NR; ++i) {
+    const int row = r0 + i * RPB;
+    of[i] = row < T ? load8(O + (size_t)row * D + part * 8) : zero_frag<TI>();
+    gf[i] = row < T ? load8(dO + (size_t)row * D + part * 8) : zero_frag<TI>();
   }
 #pragma unroll
-  for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (valid && part == 0) p.delta[row] = acc;
+  for (int i = 0; i < NR; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)of[i].v[e] * (float)gf[i].v[e];
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    const int row = r0 + i * RPB;
+    if (part == 0 && row < T) p.delta[base + row] = acc;
+  }
 }
 
 // ------------------------------------------------------------------------------------ bwd_kv
@@ -1466,9 +1488,10 @@ void bwd_dq_ds_kernel(LayerArgs p) {
 
 template <typename TI, int D>
 hipError_t launch_pre_t(const LayerArgs& a, hipStream_t s) {
-  constexpr int RPB = kNT / (D / 8);
-  const long long rows = (long long)a.B * a.H * a.T;
-  const long long blocks = (rows + RPB - 1) / RPB;
+  constexpr int RPC = kNT / (D / 8) * kPreRows;  // rows per work item
+  const long long ns = (long long)a.B * (a.delta_rep ? a.H - a.n_ord : a.n_ord);
+  const long long blocks = ns * ((a.T + RPC - 1) / RPC);
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_pre_kernel<TI, D>), dim3((unsigned)blocks), dim3(kNT), 0, s, a);
   return hipGetLastError();
