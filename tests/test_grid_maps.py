@@ -63,3 +63,51 @@ def test_kv_grid(grid_prog, B, Hkv, nko, nkb, rep_sec):
             assert (bh - sec_lo) % 8 == x % 8
         kbs = [kb for _, _, kb in sorted(sec)]
         assert kbs == sorted(kbs)  # heaviest (lowest) key blocks first
+
+
+# ---- the stored dS (saf_internal.h: ord_rank, ds_bytes; bwd_kv stores, bwd_dq_ds reads) ----------
+@pytest.fixture(scope="module")
+def ds_prog(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not found")
+    exe = str(tmp_path_factory.mktemp("ds") / "ds_index")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-std=c++17",
+           "-I" + os.path.join(ROOT, "fixed_pattern_mixed_amd", "csrc"), "-I" + os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "ds_index.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return exe
+
+
+def _masks():
+    import random
+    rnd = random.Random(5)
+    out = ["0001" * 4, "0" * 12, "1" * 7 + "0", "0" * 256, "01" * 128]
+    out += ["".join(rnd.choice("01") for _ in range(H)) for H in (63, 64, 65, 130, 200, 256)]
+    return [m if "0" in m else m[:-1] + "0" for m in out]
+
+
+@pytest.mark.parametrize("mask", _masks(), ids=lambda m: "H%d" % len(m))
+def test_stored_ds_slots_and_size(ds_prog, mask):
+    """An ordinary head's slice of the stored dS is b * n_ord + (its rank among the ordinary
+    heads): the ranks number the ordinary heads 0, 1, ... in head order (the replaced-head mask
+    spans several 64-bit words for H > 64), so the B * n_ord slices tile the region once; the region
+    is 2 bytes per element of the 32 x 32 subtiles on or below the diagonal, 1024 per subtile."""
+    for B, T in ((1, 1), (2, 8192), (3, 97), (1, 65536)):
+        out = subprocess.run([ds_prog, str(B), str(T), mask], capture_output=True, text=True,
+                             check=True).stdout.split("\n")
+        n_ord, nbytes = (int(v) for v in out[0].split())
+        ranks = [tuple(int(v) for v in line.split()) for line in out[1:1 + n_ord]]
+        assert n_ord == mask.count("0")
+        assert [h for h, _ in ranks] == [h for h, c in enumerate(mask) if c == "0"]
+        assert [r for _, r in ranks] == list(range(n_ord))
+        n32 = (T + 31) // 32
+        assert nbytes == 2 * B * n_ord * (n32 * (n32 + 1) // 2) * 1024
+
+
+def test_stored_ds_subtile_index_is_a_packing():
+    """Subtile (ib, jb <= ib) of a slice at ib (ib + 1) / 2 + jb: every index of [0, n32 (n32 + 1) / 2)
+    once, and a query block's subtiles contiguous (the order bwd_dq_ds reads them)."""
+    for n32 in (1, 2, 7, 256):
+        idx = [ib * (ib + 1) // 2 + jb for ib in range(n32) for jb in range(ib + 1)]
+        assert idx == list(range(n32 * (n32 + 1) // 2))
