@@ -112,3 +112,36 @@ def test_stored_ds_path_matches_the_recomputing_path(B, H, T, R, placement):
     err = (x - y).abs().amax(dim=-1, keepdim=True)
     assert bool(torch.all(err <= TOL[torch.bfloat16] * scale + 1e-30)), float((err / scale.clamp_min(1e-30)).max())
     print("dQ bitwise equal between the paths:", torch.equal(dq1, dq2), flush=True)
+
+
+# The stored-dS backward against the oracle, every row of every slice: with the pattern prepared
+# once and passed in (the benchmark's launch configuration), with wide-range patterns (std 3: the
+# exponential form on the replaced heads beside the stored dS of the ordinary ones), and with more
+# heads and sequences than one 8-wave item covers.
+DS_ORACLE = [
+    (2, 4, 300, 1, "interleaved", 0.5, True),
+    (1, 4, 257, 2, "contiguous", 3.0, False),
+    (4, 8, 160, 2, "interleaved", 0.5, False),
+    (1, 3, 640, 0, "interleaved", 0.5, False),
+]
+
+
+@pytest.mark.parametrize("B,H,T,R,placement,std,prepared", DS_ORACLE,
+                         ids=["B%dH%dT%d-R%d-std%g%s" % (c[0], c[1], c[2], c[3], c[5], "-prep" if c[6] else "") for c in DS_ORACLE])
+def test_stored_ds_backward_full_compare(B, H, T, R, placement, std, prepared):
+    saf = _saf()
+    d = 128
+    rep = synth.replaced_mask(H, R, placement)
+    x = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, ar_std=std, seed=91 + T)
+    g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, ar_std=std, seed=91 + T, device="cuda")
+    pat = saf.prepare_pattern(rep, g.a, g.r) if prepared and R else None
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r, pattern=pat)
+    tr = saf.KernelTrace(capacity=8)
+    tr.begin()
+    dq, dk, dv = saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r, pattern=pat)
+    tr.end()
+    torch.cuda.synchronize()
+    tr.collect()
+    assert "bwd_dq_ds" in tr.summary()
+    tr.close()
+    check_bwd(x, dq, dk, dv, all_heads(B, H), None, None, TOL[torch.bfloat16], "stored dS")
