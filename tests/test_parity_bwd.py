@@ -145,3 +145,40 @@ def test_stored_ds_backward_full_compare(B, H, T, R, placement, std, prepared):
     assert "bwd_dq_ds" in tr.summary()
     tr.close()
     check_bwd(x, dq, dk, dv, all_heads(B, H), None, None, TOL[torch.bfloat16], "stored dS")
+
+
+def test_stored_ds_needs_the_whole_room():
+    """Through the C ABI: with ws_bytes one short of saf_attn_bwd_ds_workspace_size the backward
+    takes the re-forming path (bwd_dq), with the full size the stored-dS path (bwd_dq_ds); the
+    results agree (dK, dV bitwise, dQ row by row)."""
+    saf = _saf()
+    B, H, T, d = 2, 4, 300, 128
+    rep = [0, 1, 0, 0]
+    g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=44, device="cuda")
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    big = saf.saf_attn_bwd_ds_workspace_size(saf.SAF_BF16, B, H, H, T, d, sum(rep))
+    assert big > saf.saf_attn_bwd_workspace_size(B, H, T, d)
+    ws = torch.empty(big, dtype=torch.uint8, device="cuda")
+    outs, names = [], []
+    for n in (big - 1, big):
+        out = tuple(torch.full_like(g.q, float("nan")) for _ in range(3))
+        tr = saf.KernelTrace(capacity=8)
+        tr.begin()
+        st = saf.saf_attn_bwd(saf.SAF_BF16, B, H, T, d, g.q.data_ptr(), g.k.data_ptr(), g.v.data_ptr(),
+                              o.data_ptr(), g.dout.data_ptr(), lse.data_ptr(), saf._mask(rep, H),
+                              g.a.data_ptr(), g.r.data_ptr(), T, None, 0.0, out[0].data_ptr(),
+                              out[1].data_ptr(), out[2].data_ptr(), ws.data_ptr(), n,
+                              torch.cuda.current_stream().cuda_stream)
+        tr.end()
+        assert st == saf.SAF_OK, saf.saf_last_error()
+        torch.cuda.synchronize()
+        tr.collect()
+        names.append(set(tr.summary()))
+        tr.close()
+        outs.append(out)
+    assert "bwd_dq" in names[0] and "bwd_dq_ds" not in names[0]
+    assert "bwd_dq_ds" in names[1] and "bwd_dq" not in names[1]
+    (dq1, dk1, dv1), (dq2, dk2, dv2) = outs
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    err = (dq1.double() - dq2.double()).abs().amax(dim=-1)
+    assert bool(torch.all(err <= TOL[torch.bfloat16] * dq1.double().abs().amax(dim=-1) + 1e-30))
