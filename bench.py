@@ -413,6 +413,18 @@ def cpu_baseline(w, replaced, min_seconds=10.0):
     }
 
 
+def backward_unit(kernels, kf):
+    """The backward's kernels as one unit (the preprocess, the key-block kernel and whichever dQ
+    kernel ran): summed average durations and their algorithmic flops (dQ counted once)."""
+    names = [k for k in ("bwd_pre", "bwd_kv", "bwd_dq", "bwd_dq_ds", "bwd_dv_rep") if k in kernels]
+    if "bwd_kv" not in names:
+        return None
+    ms = sum(kernels[k]["avg_ms"] for k in names)
+    fl = kf["bwd_kv"] + kf["bwd_dq"]
+    return {"kernels": names, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            "pct_bf16_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
+
 def step_spread(per_step):
     """Median, minimum and maximum of the per-step durations (ms)."""
     v = sorted(per_step)
@@ -614,6 +626,7 @@ def main():
         "pattern_prepare_ms": round(layer.prepare_ms, 3),
         "gpu_spin_up_ms": spin_ms,
         "roofline": roofline,
+        "backward": backward_unit(kernels, kf),
     }
 
     if not args.no_variants:

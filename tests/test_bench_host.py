@@ -79,3 +79,17 @@ def test_step_spread():
     assert bench.step_spread([1.0, 3.0, 2.0, 5.0]) == {"median": 2.5, "min": 1.0, "max": 5.0, "n": 4}
     assert bench.step_spread([2.0, 9.0, 4.0]) == {"median": 4.0, "min": 2.0, "max": 9.0, "n": 3}
     assert bench.step_spread([]) is None
+
+
+def test_backward_unit():
+    """The backward as one unit: the summed durations of its kernels (whichever dQ kernel ran) and
+    the algorithmic flops of the key-block work plus one dQ product; nothing for forward-only runs."""
+    import bench
+    rep = [0, 0, 0, 1] * 4
+    kf = bench.kernel_flops(2, 8192, 128, rep)
+    ks = {"bwd_pre": {"avg_ms": 0.02}, "bwd_kv": {"avg_ms": 1.0}, "bwd_dq_ds": {"avg_ms": 0.38},
+          "mixed_fwd": {"avg_ms": 0.5}}
+    u = bench.backward_unit(ks, kf)
+    assert u["kernels"] == ["bwd_pre", "bwd_kv", "bwd_dq_ds"] and abs(u["ms"] - 1.4) < 1e-9
+    assert abs(u["tflops"] - (kf["bwd_kv"] + kf["bwd_dq"]) / 1.4e-3 / 1e12) < 0.1
+    assert bench.backward_unit({"mixed_fwd": {"avg_ms": 0.5}}, kf) is None
