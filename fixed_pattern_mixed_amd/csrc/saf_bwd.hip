@@ -1334,8 +1334,9 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TI) == 2 ? 2 : 1))) void bwd_dq_kernel
 // key tiles at or below the diagonal, the one product of dQ (S and dP are not formed again).  Work
 // items as in bwd_dq (8 waves x 32 queries, lane = query, K tiles of 64 keys staged as rows and
 // read transposed).  A wave's stored subtiles (its query block ib, key blocks jb <= ib) are read by
-// that wave only: each 2 KB subtile is prefetched with the K tile, copied into the wave's own LDS
-// region in four quarters (fragment u, lane half) kDsBlk elements apart, and read back with the
+// that wave only: each 2 KB subtile is prefetched two key tiles ahead (the K tile one ahead),
+// copied into the wave's own LDS region in four quarters (fragment u, lane half) BLK elements
+// apart, and read back with the
 // transposing read as the B operand: lane l, slot e gets dS[query l % 32][key 16 ub +
 // perm_row(e, l / 32)] -- the source lane 4j + a of a 16-lane group addresses key 16 ub + 8 rd +
 // 4 hi + j and queries 16 g + 4a .. +3, which the store keeps contiguous in quarter 2g + (a & 1)
