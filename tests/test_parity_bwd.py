@@ -182,3 +182,26 @@ def test_stored_ds_needs_the_whole_room():
     assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
     err = (dq1.double() - dq2.double()).abs().amax(dim=-1)
     assert bool(torch.all(err <= TOL[torch.bfloat16] * dq1.double().abs().amax(dim=-1) + 1e-30))
+
+
+def test_binding_falls_back_beyond_its_cap(monkeypatch):
+    """bwd() passes the smaller workspace when the stored dS would need more than
+    DS_WORKSPACE_MAX bytes: the backward then forms S and dP again (bwd_dq), with the same dK, dV."""
+    saf = _saf()
+    B, H, T, d = 1, 4, 200, 128
+    rep = [0, 1, 0, 0]
+    g = synth.layer_inputs(B, H, T, d, torch.bfloat16, rep, seed=45, device="cuda")
+    o, lse = saf.fwd(g.q, g.k, g.v, rep, g.a, g.r)
+    outs, names = [], []
+    for cap in (saf.DS_WORKSPACE_MAX, 1024):
+        monkeypatch.setattr(saf, "DS_WORKSPACE_MAX", cap)
+        tr = saf.KernelTrace(capacity=8)
+        tr.begin()
+        outs.append(saf.bwd(g.q, g.k, g.v, o, g.dout, lse, rep, g.a, g.r))
+        tr.end()
+        torch.cuda.synchronize()
+        tr.collect()
+        names.append(set(tr.summary()))
+        tr.close()
+    assert "bwd_dq_ds" in names[0] and "bwd_dq" in names[1] and "bwd_dq_ds" not in names[1]
+    assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][2], outs[1][2])
