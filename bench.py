@@ -145,17 +145,23 @@ class Layer:
 def spin_up(torch, seconds=0.3):
     """Bring the GPU out of its idle clocks before anything is timed: a plain bf16 matrix product
     loop for `seconds` (not part of the hot path; the W warm-up steps and K timed steps follow).
-    Without it the first few milliseconds of timing run at ramping clocks."""
+    Without it the first few milliseconds of timing run at ramping clocks.  Returns the loop's
+    duration (ms) and the library GEMM's rate over its last 8 products (TFLOP/s): a reference for
+    what the matrix cores sustain on this board with a vendor-tuned dense product."""
     a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
     t0 = time.perf_counter()
     n = 0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     while time.perf_counter() - t0 < seconds:
+        ev0.record()
         for _ in range(8):
             b = a @ a
+        ev1.record()
         torch.cuda.synchronize()
         n += 8
+    gemm = 8 * 2.0 * 8192 ** 3 / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
     del a, b
-    return round((time.perf_counter() - t0) * 1e3, 1)
+    return round((time.perf_counter() - t0) * 1e3, 1), round(gemm, 1)
 
 
 def time_steps(torch, layer, steps, warmup, trace=None, per_step=None):
@@ -579,7 +585,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     replaced = w.replaced()
     layer = Layer(saf, torch, w, replaced, dev)
-    spin_ms = spin_up(torch)
+    spin_ms, gemm_tflops = spin_up(torch)
     trace = saf.KernelTrace(capacity=4 * (args.steps + 1))
     per_step = []
     t_step = time_steps(torch, layer, args.steps, args.warmup, trace, per_step)
@@ -625,6 +631,7 @@ def main():
         "kernels": kernels,
         "pattern_prepare_ms": round(layer.prepare_ms, 3),
         "gpu_spin_up_ms": spin_ms,
+        "reference_gemm_tflops": gemm_tflops,
         "roofline": roofline,
         "backward": backward_unit(kernels, kf),
     }
