@@ -549,6 +549,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
+    ap.add_argument("--dq-recomputed", action="store_true",
+                    help="time the headline layer with the smaller backward workspace (dQ forms S and "
+                         "dP again) instead of the one that keeps dS")
     ap.add_argument("--no-pattern-grad", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--calibration-workload", default="l1b_t8192",
@@ -585,6 +588,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     replaced = w.replaced()
     layer = Layer(saf, torch, w, replaced, dev)
+    layer.recompute_ds = args.dq_recomputed
     spin_ms, gemm_tflops = spin_up(torch)
     trace = saf.KernelTrace(capacity=4 * (args.steps + 1))
     per_step = []
@@ -624,6 +628,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "T": w.T, "d": w.d,
                    "replaced_heads": [h for h, x in enumerate(replaced) if x],
                    "pass": "fwd+bwd" if w.backward else "fwd",
+                   "backward": ("dq_recomputed" if layer.recompute_ds or layer.nb == layer.nb_min
+                                else "stored_ds") if w.backward else None,
                    "global_batch": w.B, "seq_len": w.T, "parallelism": "single-gpu"},
         "tflops": round(flops / t_step / 1e12, 1),
         "pct_bf16_peak": round(100 * flops / t_step / 1e12 / PEAK_BF16_TFLOPS, 2),
