@@ -138,15 +138,22 @@ __global__ __launch_bounds__(kNT) void fit_init_kernel(FitArgs p) {
 
 // The step kernels split positions and the summed index into blocks of kCB = 1024: a block
 // (position block, index block) stages its index block's factors and the shifted factors it needs
-// (a window of 2 kCB values) in LDS; each thread owns 4 consecutive positions and keeps 8 window
-// values in registers, reusing half of them per step, so one broadcast read and four window reads
-// feed 16 (or 32) fp64 multiply-adds.  Partial sums per index block are added in a fixed order by
+// (a window of 2 kCB values) in LDS; each thread owns kPP consecutive positions and keeps kPP + 4
+// window values in registers, sliding them by 4 per step, so four broadcast reads and four window
+// reads feed 4 kPP (or 8 kPP) fp64 multiply-adds.  Each position's sum runs over the summed index
+// in ascending order whatever kPP is.  Partial sums per index block are added in a fixed order by
 // the next kernel.
 #ifndef SAF_FIT_CB
 #define SAF_FIT_CB 1024
 #endif
+#ifndef SAF_FIT_PP
+#define SAF_FIT_PP 4
+#endif
 constexpr int kCB = SAF_FIT_CB;
-constexpr int kSNT = kCB / 4;  // threads of a step block: 4 positions each
+constexpr int kPP = SAF_FIT_PP;  // positions per thread
+constexpr int kNW = kPP + 4;     // window registers
+constexpr int kSNT = kCB / kPP;  // threads of a step block
+static_assert(kCB % kPP == 0 && kPP % 4 == 0 && kSNT % 64 == 0, "fit step block shape");
 // The gradient kernel's windows are stored with one pad double after every 64 slots: its window
 // reads are 32 bytes apart per lane (4 positions per thread), which without padding puts lanes 8
 // apart on the same LDS banks.  Chosen by measurement over paddings of 1-4 doubles every 8-512
@@ -175,31 +182,33 @@ __global__ __launch_bounds__(kSNT) void fit_zpart_kernel(FitArgs p) {
     ers[y] = (d >= 0 && d < T) ? er[d] : 0.0;  // negative distance: a future key, weight 0
   }
   __syncthreads();
-  // row i0 + 4t + u and key k0 + kk + j read ers[4t + u - kk - j + kCB - 1] = W[3 + u - j] with
-  // W = ers[base .. base + 7], base = 4t + kCB - 4 - kk
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  int base = 4 * tid + kCB - 4;
-  double W[8];
+  // row i0 + P t + u and key k0 + kk + j (P = kPP) read ers[P t + u - kk - j + kCB - 1] = W[3 + u - j]
+  // with W = ers[base .. base + P + 3], base = P t + kCB - 4 - kk: slots 0 .. 2 kCB - 1 over all t, kk
+  double acc[kPP];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) W[q] = ers[base + q];
+  for (int u = 0; u < kPP; ++u) acc[u] = 0.0;
+  int base = kPP * tid + kCB - 4;
+  double W[kNW];
+#pragma unroll
+  for (int q = 0; q < kNW; ++q) W[q] = ers[base + q];
   for (int kk = 0; kk < kCB; kk += 4) {
     const double e4[4] = {eas[kk], eas[kk + 1], eas[kk + 2], eas[kk + 3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = fma(e4[j], W[3 + u - j], acc[u]);
+      for (int u = 0; u < kPP; ++u) acc[u] = fma(e4[j], W[3 + u - j], acc[u]);
     if (kk + 4 < kCB) {  // slide the window down by 4
       base -= 4;
 #pragma unroll
-      for (int q = 7; q >= 4; --q) W[q] = W[q - 4];
+      for (int q = kNW - 1; q >= 4; --q) W[q] = W[q - 4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) W[q] = ers[base + q];
     }
   }
   double* zp = p.zpart + ((size_t)h * nb + kc) * T;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = i0 + 4 * tid + u;
+  for (int u = 0; u < kPP; ++u) {
+    const int i = i0 + kPP * tid + u;
     if (i < T) zp[i] = acc[u];
   }
 }
@@ -243,13 +252,15 @@ __global__ __launch_bounds__(kSNT) void fit_gpart_kernel(FitArgs p) {
     eas[wslot(y)] = ok ? ea[o] : 0.0;
   }
   __syncthreads();
-  // position x0 + 4t + u and index i0 + ii + j read slot ii + j - 4t - u + kCB - 1 = base + 3 + j - u
-  // with base = ii - 4t + kCB - 4
-  double cs[4] = {0.0, 0.0, 0.0, 0.0}, ds[4] = {0.0, 0.0, 0.0, 0.0};
-  int base = kCB - 4 - 4 * tid;
-  double Wr[8], Wa[8];
+  // position x0 + P t + u and index i0 + ii + j (P = kPP) read slot ii + j - P t - u + kCB - 1 =
+  // base + P - 1 + j - u with base = ii - P t + kCB - P: slots 0 .. 2 kCB - 1 over all t, ii
+  double cs[kPP], ds[kPP];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int u = 0; u < kPP; ++u) cs[u] = ds[u] = 0.0;
+  int base = kCB - kPP - kPP * tid;
+  double Wr[kNW], Wa[kNW];
+#pragma unroll
+  for (int q = 0; q < kNW; ++q) {
     Wr[q] = ers[wslot(base + q)];
     Wa[q] = eas[wslot(base + q)];
   }
@@ -258,19 +269,19 @@ __global__ __launch_bounds__(kSNT) void fit_gpart_kernel(FitArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        cs[u] = fma(Wr[3 + j - u], w4[j], cs[u]);
-        ds[u] = fma(Wa[3 + j - u], w4[j], ds[u]);
+      for (int u = 0; u < kPP; ++u) {
+        cs[u] = fma(Wr[kPP - 1 + j - u], w4[j], cs[u]);
+        ds[u] = fma(Wa[kPP - 1 + j - u], w4[j], ds[u]);
       }
     if (ii + 4 < kCB) {  // slide the windows up by 4
       base += 4;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kNW - 4; ++q) {
         Wr[q] = Wr[q + 4];
         Wa[q] = Wa[q + 4];
       }
 #pragma unroll
-      for (int q = 4; q < 8; ++q) {
+      for (int q = kNW - 4; q < kNW; ++q) {
         Wr[q] = ers[wslot(base + q)];
         Wa[q] = eas[wslot(base + q)];
       }
@@ -278,8 +289,8 @@ __global__ __launch_bounds__(kSNT) void fit_gpart_kernel(FitArgs p) {
   }
   double* gp = p.gpart + ((size_t)h * nb + ic) * 2 * (size_t)T;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int x = x0 + 4 * tid + u;
+  for (int u = 0; u < kPP; ++u) {
+    const int x = x0 + kPP * tid + u;
     if (x < T) {
       gp[x] = cs[u];
       gp[T + x] = ds[u];
